@@ -1,0 +1,188 @@
+/*
+ * ptq1.h -- C ABI of the MI355X (gfx950) PTQ1_0 ternary linear layer.
+ *
+ * The method: weights quantised to -1, 0, +1 with one 16-bit scale per 128
+ * weights, five trits packed into a byte in base 3 (1.75 bits per weight),
+ * after every weight matrix was multiplied by a 1024-wide Walsh-Hadamard
+ * butterfly with a sign pattern; at inference the same rotation is applied to
+ * the activations before every folded matmul and undone on embedding rows
+ * ("A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally", section
+ * "What Bonsai is").  A trit is read from its byte on the float pipeline as
+ * floor(3^(n+1) u) - 3 floor(3^n u), u = byte/256 (same page, section
+ * "What Ferrox does with it").  Decode is a matvec, prefill a GEMM, and the
+ * feed-forward block is gate and up, SwiGLU, down (section "Speed, and where
+ * it goes").
+ *
+ * Layout of one PTQ1_0 block (28 bytes):
+ *   bytes 0..25  trit bytes; weight 5i+n of the block is base-3 digit n of
+ *                byte i (n = 0 most significant), digit d means weight d-1;
+ *                byte 25 holds weights 125..127 in digits 0..2, digits 3..4
+ *                are padding (written as 1, ignored when read);
+ *   bytes 26..27 the block scale, IEEE binary16, little-endian.
+ * A packed matrix [n][k] is row-major: row r is k/128 consecutive blocks.
+ * Weight (r, c) = scale(r, c/128) * trit(r, c).
+ *
+ * Rotation R of a row x of width k (k a multiple of 1024): every 1024-wide
+ * chunk c becomes (1/32) H (s * c), with H the natural-order Sylvester
+ * Hadamard matrix and s the 1024 signs (one vector for every chunk).
+ * R is orthogonal; the inverse applied to embedding rows is s * ((1/32) H c).
+ *
+ * Conventions for every call:
+ *   - pointers are device pointers (hipMalloc'd or equivalent) unless stated;
+ *     all memory is owned by the caller; weights are only read;
+ *   - work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting; a fault during execution surfaces at the caller's
+ *     stream synchronisation, as usual in HIP;
+ *   - on any status other than PTQ1_OK nothing has been enqueued (except
+ *     PTQ1_ERR_HIP, which reports a failed launch);
+ *   - ptq1_last_error() then names the refused argument (thread-local);
+ *   - the library keeps no global state and allocates no memory; calls that
+ *     need scratch take a caller-owned workspace `ws` of at least the size
+ *     the matching *_workspace_bytes() returns, 256-byte aligned, whose
+ *     contents on entry are ignored; two calls in flight must not share a
+ *     workspace;
+ *   - `float *` buffers must be 16-byte aligned, `blocks` 16-byte aligned;
+ *   - sizes are int64_t; products are checked for overflow.
+ */
+#ifndef PTQ1_H
+#define PTQ1_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PTQ1_BLOCK_WEIGHTS 128
+#define PTQ1_TRIT_BYTES 26
+#define PTQ1_BLOCK_BYTES 28
+#define PTQ1_HADAMARD 1024
+
+typedef enum ptq1_status {
+    PTQ1_OK = 0,
+    PTQ1_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    PTQ1_ERR_SHAPE = 2,       /* a size is negative or not a multiple it must be    */
+    PTQ1_ERR_ALIGN = 3,       /* a pointer is not aligned as stated above          */
+    PTQ1_ERR_OVERFLOW = 4,    /* a derived byte count or index overflows int64     */
+    PTQ1_ERR_UNSUPPORTED = 5, /* a well-formed request this library does not run   */
+    PTQ1_ERR_WORKSPACE = 6,   /* ws is NULL or smaller than *_workspace_bytes()    */
+    PTQ1_ERR_ALIAS = 7,       /* an output overlaps an input it must not overlap   */
+    PTQ1_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed        */
+} ptq1_status;
+
+/* Human-readable name of a status.  Never NULL. */
+const char *ptq1_status_string(ptq1_status s);
+
+/* Message of the last non-OK status returned on this thread ("" if none).
+ * Never NULL; valid until the next call on this thread. */
+const char *ptq1_last_error(void);
+
+/* Copies the compiled geometry {weights per block, trit bytes, block bytes,
+ * Hadamard width} into out[0..n) (n <= 4).  PTQ1_ERR_NULL / PTQ1_ERR_SHAPE. */
+ptq1_status ptq1_geometry(int32_t *out, int32_t n);
+
+/* Bytes of a packed [n][k] matrix: n * (k/128) * 28, or -1 if n < 0, k < 0,
+ * k % 128 != 0 or the product overflows. */
+int64_t ptq1_packed_bytes(int64_t n, int64_t k);
+
+/* Codec encode ("What Bonsai is": five trits per byte in base 3, one 16-bit
+ * scale per 128 weights).
+ *   trits      int8 [n][k], values in {-1, 0, +1} (other values are clamped
+ *              to the nearest of these);
+ *   scales_f16 binary16 bit patterns [n][k/128], copied verbatim;
+ *   blocks     output, ptq1_packed_bytes(n, k) bytes.
+ * Each byte carries the code v = sum_n (t_n + 1) 3^(4-n) as the smallest
+ * byte b with floor(243 b / 256) = v, i.e. b = ceil(256 v / 243).
+ * Errors: NULL, SHAPE (k % 128), ALIGN (blocks), OVERFLOW. */
+ptq1_status ptq1_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k,
+                      uint8_t *blocks, hipStream_t stream);
+
+/* Codec decode ("What Ferrox does with it": digit n of u = b/256 read on the
+ * float pipeline).  w [n][k] fp32 = binary16 scale * (digit - 1), exact.
+ * Errors: NULL, SHAPE, ALIGN, OVERFLOW. */
+ptq1_status ptq1_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t stream);
+
+/* Rotation of activations ("What Bonsai is": the rotation applied to the
+ * activations before every matmul of a folded weight).
+ *   x, y  fp32 [m][k], k % 1024 == 0; y may equal x (in place), otherwise
+ *         they must not overlap;
+ *   signs1024  fp32 [1024], +-1.0 (other values are used as given and break
+ *         orthogonality).
+ * Errors: NULL, SHAPE (k % 1024), ALIGN, ALIAS (partial overlap), OVERFLOW. */
+ptq1_status hadamard_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs1024,
+                            hipStream_t stream);
+
+/* Embedding lookup with the rotation undone ("What Bonsai is": undo the
+ * rotation on the embedding table after each lookup).
+ *   table  fp32 [n_table][d] row-major, rows stored rotated, d % 1024 == 0;
+ *   ids    int32 [n_rows] device array of row indices, or NULL for rows
+ *          0..n_rows-1; an id outside [0, n_table) yields a row of NaN;
+ *   out    fp32 [n_rows][d]: out[i] = s * ((1/32) H table[ids[i]]) per chunk.
+ * Errors: NULL, SHAPE (d % 1024, n_rows > n_table without ids), ALIGN,
+ * ALIAS, OVERFLOW. */
+ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t d,
+                                   const int32_t *ids, int64_t n_rows, const float *signs1024,
+                                   float *out, hipStream_t stream);
+
+/* Batch-1 decode matvec ("What Ferrox does with it": the decode matvec reads
+ * every block once and peels trits on the float pipeline).
+ *   y[r] = (residual ? residual[r] : 0) + sum_c W[r][c] * xr[c],
+ *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
+ *   blocks  packed [n][k]; x fp32 [k]; residual fp32 [n] or NULL; y fp32 [n]
+ *   (y may equal residual, must not overlap x or blocks).
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
+size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k);
+ptq1_status ptq1_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+                        const float *signs1024, const float *residual, float *y, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Gate and up projections of one token in one pass over a shared rotated
+ * input ("Speed, and where it goes": paired projections fused into one GPU
+ * submission).
+ *   w_gate, w_up  packed [f][d]; x fp32 [d]; g, u fp32 [f]:
+ *   g = W_gate R x, u = W_up R x (R skipped when signs1024 == NULL).
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
+size_t ptq1_gate_up_workspace_bytes(int64_t f, int64_t d);
+ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, int64_t d,
+                         const float *x, const float *signs1024, float *g, float *u, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* SwiGLU ("Speed, and where it goes": gate, SwiGLU, down):
+ * h[i] = g[i] / (1 + exp(-g[i])) * u[i], fp32 [len].  h may equal g or u.
+ * Errors: NULL, SHAPE (len < 0), ALIGN. */
+ptq1_status ptq1_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t stream);
+
+/* Multi-token prefill GEMM ("What Ferrox does with it": a GEMM for prefill).
+ *   Y [m][n] fp32 = bf16(R X) . W^T: X fp32 [m][k] is rotated (when
+ *   signs1024 != NULL) and rounded to bf16 (nearest even); trits enter bf16
+ *   MFMA exactly; each 128-weight block's partial sum is scaled by its fp16
+ *   scale in fp32; accumulation is fp32.
+ *   1 <= m <= 65536; k % 128 == 0 (k % 1024 == 0 with signs).
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED (m). */
+size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+ptq1_status ptq1_gemm(const uint8_t *blocks, int64_t n, int64_t k, const float *x, int64_t m,
+                      const float *signs1024, float *y, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* One feed-forward block on m tokens ("Speed, and where it goes": the whole
+ * block -- rotation, gate, SwiGLU, down -- enqueued as one sequence):
+ *   a     = (mean(x^2) + rms_eps)^(-1/2) per token if rms_eps > 0, else 1
+ *   g, u  = a * (W_gate R x), a * (W_up R x)      (W_gate, W_up packed [f][d])
+ *   h     = silu(g) * u
+ *   x_out = x + W_down R h                        (W_down packed [d][f])
+ * m == 1 runs the fp32 matvec path, m >= 2 the bf16-MFMA GEMM path.
+ * d % 1024 == 0, f % 1024 == 0; x_out may equal x.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED. */
+size_t ptq1_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
+ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                           const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                           const float *signs1024, float rms_eps, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTQ1_H */

@@ -1,0 +1,269 @@
+"""Python binding of ``libptq1.so`` (the C ABI in ``include/ptq1.h``).
+
+Argument marshalling only: every function passes device pointers of torch
+tensors and ``torch.cuda.current_stream()`` to the C entry point of the same
+name and raises :class:`Ptq1Error` on a non-OK status.  torch supplies device
+memory and streams; every step of the computation runs in the HIP kernels.
+There is no fallback: if the library is not built, importing the binding's
+functions raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libptq1.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "ptq1.h")
+
+BLOCK_WEIGHTS = 128
+TRIT_BYTES = 26
+BLOCK_BYTES = 28
+HADAMARD = 1024
+
+STATUS = {0: "PTQ1_OK", 1: "PTQ1_ERR_NULL", 2: "PTQ1_ERR_SHAPE", 3: "PTQ1_ERR_ALIGN",
+          4: "PTQ1_ERR_OVERFLOW", 5: "PTQ1_ERR_UNSUPPORTED", 6: "PTQ1_ERR_WORKSPACE",
+          7: "PTQ1_ERR_ALIAS", 8: "PTQ1_ERR_HIP"}
+
+
+class Ptq1Error(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+i64, sz, p = C.c_int64, C.c_size_t, C.c_void_p
+
+_SIGS = {
+    "ptq1_status_string": ([C.c_int], C.c_char_p),
+    "ptq1_last_error": ([], C.c_char_p),
+    "ptq1_geometry": ([p, C.c_int32], C.c_int),
+    "ptq1_packed_bytes": ([i64, i64], i64),
+    "ptq1_pack": ([p, p, i64, i64, p, p], C.c_int),
+    "ptq1_dequant": ([p, i64, i64, p, p], C.c_int),
+    "hadamard_rotate": ([p, p, i64, i64, p, p], C.c_int),
+    "hadamard_unrotate_rows": ([p, i64, i64, p, i64, p, p, p], C.c_int),
+    "ptq1_matvec_workspace_bytes": ([i64, i64], sz),
+    "ptq1_matvec": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
+    "ptq1_gate_up_workspace_bytes": ([i64, i64], sz),
+    "ptq1_gate_up": ([p, p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
+    "ptq1_swiglu": ([p, p, p, i64, p], C.c_int),
+    "ptq1_gemm_workspace_bytes": ([i64, i64, i64], sz),
+    "ptq1_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
+    "ptq1_ffn_workspace_bytes": ([i64, i64, i64], sz),
+    "ptq1_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, sz, p], C.c_int),
+}
+
+
+def lib():
+    """The loaded C library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m ternary_weight_ptq1_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/ptq1.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b([a-z_0-9]+)\s*\(", text.split('extern "C" {', 1)[1])
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Ptq1Error(fn, status, lib().ptq1_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ws(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ------------------------------------------------------------------ codec ----
+
+def ptq1_geometry() -> tuple[int, int, int, int]:
+    out = (C.c_int32 * 4)()
+    _check("ptq1_geometry", lib().ptq1_geometry(C.cast(out, p), 4))
+    return tuple(out)
+
+
+def ptq1_packed_bytes(n: int, k: int) -> int:
+    return lib().ptq1_packed_bytes(n, k)
+
+
+def ptq1_pack(trits: torch.Tensor, scales_f16: torch.Tensor, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """int8 trits [n, k] + binary16 bit patterns [n, k/128] (int16 or float16) -> uint8 [n, k/128*28]."""
+    _dev(trits, "trits", torch.int8)
+    _dev(scales_f16, "scales_f16", (torch.int16, torch.float16, torch.uint16))
+    n, k = trits.shape
+    if out is None:
+        out = torch.empty((n, (k // BLOCK_WEIGHTS) * BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
+    _dev(out, "blocks", torch.uint8)
+    _check("ptq1_pack", lib().ptq1_pack(_ptr(trits), _ptr(scales_f16), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def ptq1_dequant(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    _dev(blocks, "blocks", torch.uint8)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
+    _dev(out, "w", torch.float32)
+    _check("ptq1_dequant", lib().ptq1_dequant(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------- rotation ----
+
+def hadamard_rotate(x: torch.Tensor, signs1024: torch.Tensor, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Rotate the rows of x [m, k] (or [k]); out may be x."""
+    _dev(x, "x", torch.float32)
+    _dev(signs1024, "signs1024", torch.float32)
+    k = x.shape[-1]
+    m = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "y", torch.float32)
+    _check("hadamard_rotate", lib().hadamard_rotate(_ptr(x), _ptr(out), m, k, _ptr(signs1024),
+                                                    _stream(stream)))
+    return out
+
+
+def hadamard_unrotate_rows(table: torch.Tensor, signs1024: torch.Tensor, ids: torch.Tensor | None = None,
+                           n_rows: int | None = None, out: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    _dev(table, "table", torch.float32)
+    _dev(signs1024, "signs1024", torch.float32)
+    n_table, d = table.shape
+    if ids is not None:
+        _dev(ids, "ids", torch.int32)
+        n_rows = ids.numel()
+    elif n_rows is None:
+        n_rows = n_table
+    if out is None:
+        out = torch.empty((n_rows, d), dtype=torch.float32, device=table.device)
+    _dev(out, "out", torch.float32)
+    _check("hadamard_unrotate_rows",
+           lib().hadamard_unrotate_rows(_ptr(table), n_table, d, _ptr(ids), n_rows, _ptr(signs1024),
+                                        _ptr(out), _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------- decode ----
+
+def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
+                residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev(blocks, "blocks", torch.uint8)
+    _dev(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev(out, "y", torch.float32)
+    ws, wsb = _ws(lib().ptq1_matvec_workspace_bytes(n, k), x.device, ws)
+    _check("ptq1_matvec", lib().ptq1_matvec(_ptr(blocks), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
+                                            _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def ptq1_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, f: int, d: int, x: torch.Tensor,
+                 signs1024: torch.Tensor | None, g: torch.Tensor | None = None,
+                 u: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    _dev(w_gate, "w_gate", torch.uint8)
+    _dev(w_up, "w_up", torch.uint8)
+    _dev(x, "x", torch.float32)
+    if g is None:
+        g = torch.empty(f, dtype=torch.float32, device=x.device)
+    if u is None:
+        u = torch.empty(f, dtype=torch.float32, device=x.device)
+    ws, wsb = _ws(lib().ptq1_gate_up_workspace_bytes(f, d), x.device, ws)
+    _check("ptq1_gate_up", lib().ptq1_gate_up(_ptr(w_gate), _ptr(w_up), f, d, _ptr(x), _ptr(signs1024),
+                                              _ptr(g), _ptr(u), _ptr(ws), wsb, _stream(stream)))
+    return g, u
+
+
+def ptq1_swiglu(g: torch.Tensor, u: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    _dev(g, "g", torch.float32)
+    _dev(u, "u", torch.float32)
+    if out is None:
+        out = torch.empty_like(g)
+    _check("ptq1_swiglu", lib().ptq1_swiglu(_ptr(g), _ptr(u), _ptr(out), g.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- prefill ----
+
+def ptq1_gemm(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev(blocks, "blocks", torch.uint8)
+    _dev(x, "x", torch.float32)
+    m = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, "y", torch.float32)
+    ws, wsb = _ws(lib().ptq1_gemm_workspace_bytes(m, n, k), x.device, ws)
+    _check("ptq1_gemm", lib().ptq1_gemm(_ptr(blocks), n, k, _ptr(x), m, _ptr(signs1024), _ptr(out),
+                                        _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                   signs1024: torch.Tensor, d: int, f: int, rms_eps: float = 0.0,
+                   out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """x [m, d] -> x + W_down R(silu(a W_gate R x) * (a W_up R x)); out may be x."""
+    _dev(x, "x", torch.float32)
+    for w, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _dev(w, nm, torch.uint8)
+    m = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "x_out", torch.float32)
+    ws, wsb = _ws(lib().ptq1_ffn_workspace_bytes(m, d, f), x.device, ws)
+    _check("ptq1_ffn_block", lib().ptq1_ffn_block(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up),
+                                                  _ptr(w_down), _ptr(signs1024), float(rms_eps), _ptr(ws),
+                                                  wsb, _stream(stream)))
+    return out
+
+
+def workspace_bytes(kind: str, *shape) -> int:
+    fn = {"matvec": "ptq1_matvec_workspace_bytes", "gate_up": "ptq1_gate_up_workspace_bytes",
+          "gemm": "ptq1_gemm_workspace_bytes", "ffn": "ptq1_ffn_workspace_bytes"}[kind]
+    return int(getattr(lib(), fn)(*shape))

@@ -1,0 +1,458 @@
+// api.cpp -- the extern "C" boundary declared in include/ptq1.h.
+//
+// Every entry point validates all arguments on the host before anything is
+// enqueued (null pointers, shapes, alignment, overlap, int64 overflow,
+// workspace size) and names the refused argument in ptq1_last_error().
+// Conventions follow "Why I Am Building Another Inference Engine", Level 4:
+// the C header is the ABI, every call returns a status the caller checks,
+// and sizes are computed with checked arithmetic.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ptq1.h"
+#include "ptq1_geometry.h"
+#include "ptq1_launch.h"
+
+static_assert(PTQ1_BLOCK_WEIGHTS == ptq1::kBlockWeights, "public header and geometry agree");
+static_assert(PTQ1_TRIT_BYTES == ptq1::kTritBytes, "public header and geometry agree");
+static_assert(PTQ1_BLOCK_BYTES == ptq1::kBlockBytes, "public header and geometry agree");
+static_assert(PTQ1_HADAMARD == ptq1::kHadamard, "public header and geometry agree");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ptq1_status fail(ptq1_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+ptq1_status ok()
+{
+    g_last_error.clear();
+    return PTQ1_OK;
+}
+
+ptq1_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(PTQ1_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (na <= 0 || nb <= 0 || a == nullptr || b == nullptr) return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + static_cast<uintptr_t>(nb) && pb < pa + static_cast<uintptr_t>(na);
+}
+
+constexpr uintptr_t kAlign = 16;
+constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxGemmM = 65536;
+constexpr int64_t kMaxGridX = 2147483647;
+constexpr int64_t kMaxGridY = 65535;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Packed bytes with every check; -1 on a bad shape or overflow.
+int64_t packed_bytes(int64_t n, int64_t k)
+{
+    if (n < 0 || k < 0 || k % ptq1::kBlockWeights != 0) return -1;
+    int64_t nb_bytes, total;
+    if (!mul_ok(k / ptq1::kBlockWeights, ptq1::kBlockBytes, &nb_bytes)) return -1;
+    if (!mul_ok(n, nb_bytes, &total)) return -1;
+    return total;
+}
+
+// Shared validation of a packed matrix argument.
+ptq1_status check_matrix(const uint8_t *blocks, const char *name, int64_t n, int64_t k,
+                         bool need_1024, int64_t *bytes)
+{
+    if (n < 0) return fail(PTQ1_ERR_SHAPE, "%s: n = %lld is negative", name, (long long)n);
+    if (k < 0) return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is negative", name, (long long)k);
+    if (k % ptq1::kBlockWeights != 0)
+        return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is not a multiple of %d", name, (long long)k,
+                    ptq1::kBlockWeights);
+    if (need_1024 && k % ptq1::kHadamard != 0)
+        return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is not a multiple of %d (rotation chunks)", name,
+                    (long long)k, ptq1::kHadamard);
+    const int64_t b = packed_bytes(n, k);
+    if (b < 0) return fail(PTQ1_ERR_OVERFLOW, "%s: packed size of [%lld][%lld] overflows", name,
+                           (long long)n, (long long)k);
+    if (b > 0 && blocks == nullptr) return fail(PTQ1_ERR_NULL, "%s is NULL", name);
+    if (b > 0 && !aligned(blocks, kAlign)) return fail(PTQ1_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    *bytes = b;
+    return PTQ1_OK;
+}
+
+ptq1_status check_floats(const void *p, const char *name, int64_t count, int64_t *bytes)
+{
+    int64_t b;
+    if (count < 0) return fail(PTQ1_ERR_SHAPE, "%s: negative element count", name);
+    if (!mul_ok(count, 4, &b)) return fail(PTQ1_ERR_OVERFLOW, "%s: byte size overflows", name);
+    if (count > 0 && p == nullptr) return fail(PTQ1_ERR_NULL, "%s is NULL", name);
+    if (count > 0 && !aligned(p, kAlign)) return fail(PTQ1_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    *bytes = b;
+    return PTQ1_OK;
+}
+
+ptq1_status check_signs(const float *signs, bool required)
+{
+    if (signs == nullptr) {
+        if (required) return fail(PTQ1_ERR_NULL, "signs1024 is NULL");
+        return PTQ1_OK;
+    }
+    if (!aligned(signs, kAlign)) return fail(PTQ1_ERR_ALIGN, "signs1024 is not 16-byte aligned");
+    return PTQ1_OK;
+}
+
+ptq1_status check_ws(const void *ws, size_t ws_bytes, size_t need, const char *fn)
+{
+    if (need == 0) return PTQ1_OK;
+    if (ws == nullptr) return fail(PTQ1_ERR_WORKSPACE, "%s: ws is NULL (%zu bytes needed)", fn, need);
+    if (ws_bytes < need)
+        return fail(PTQ1_ERR_WORKSPACE, "%s: ws_bytes = %zu < %zu needed", fn, ws_bytes, need);
+    if (!aligned(ws, kWsAlign)) return fail(PTQ1_ERR_ALIGN, "%s: ws is not 256-byte aligned", fn);
+    return PTQ1_OK;
+}
+
+#define PTQ1_TRY(expr)                         \
+    do {                                       \
+        const ptq1_status _s = (expr);         \
+        if (_s != PTQ1_OK) return _s;          \
+    } while (0)
+
+int64_t nseg_of(int64_t k) { return (k + ptq1::kHadamard - 1) / ptq1::kHadamard; }
+
+// ---- workspace layouts -------------------------------------------------------
+size_t mv_ws(int64_t rows, int64_t k)
+{
+    return round_up(ptq1::matvec_part_floats(rows, k) * sizeof(float), kWsAlign);
+}
+
+size_t gemm_ws(int64_t m, int64_t k)
+{
+    return round_up(static_cast<size_t>(ptq1::gemm_m_pad(m)) * static_cast<size_t>(k) * 2, kWsAlign);
+}
+
+struct FfnWs {
+    size_t part = 0, g = 0, u = 0, h = 0, xb = 0, total = 0;  // byte offsets
+};
+
+FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
+{
+    FfnWs L;
+    size_t off = 0;
+    if (m == 1) {
+        const size_t part_a = mv_ws(2 * f, d), part_b = mv_ws(d, f);
+        L.part = off;
+        off += part_a > part_b ? part_a : part_b;
+        L.g = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
+        L.u = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
+        L.h = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
+    } else {
+        L.xb = off;
+        off += gemm_ws(m, d > f ? d : f);
+        L.g = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
+        L.u = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
+    }
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ptq1_status_string(ptq1_status s)
+{
+    switch (s) {
+        case PTQ1_OK: return "PTQ1_OK";
+        case PTQ1_ERR_NULL: return "PTQ1_ERR_NULL";
+        case PTQ1_ERR_SHAPE: return "PTQ1_ERR_SHAPE";
+        case PTQ1_ERR_ALIGN: return "PTQ1_ERR_ALIGN";
+        case PTQ1_ERR_OVERFLOW: return "PTQ1_ERR_OVERFLOW";
+        case PTQ1_ERR_UNSUPPORTED: return "PTQ1_ERR_UNSUPPORTED";
+        case PTQ1_ERR_WORKSPACE: return "PTQ1_ERR_WORKSPACE";
+        case PTQ1_ERR_ALIAS: return "PTQ1_ERR_ALIAS";
+        case PTQ1_ERR_HIP: return "PTQ1_ERR_HIP";
+    }
+    return "PTQ1_ERR_UNKNOWN";
+}
+
+const char *ptq1_last_error(void) { return g_last_error.c_str(); }
+
+ptq1_status ptq1_geometry(int32_t *out, int32_t n)
+{
+    if (out == nullptr) return fail(PTQ1_ERR_NULL, "out is NULL");
+    if (n < 0 || n > 4) return fail(PTQ1_ERR_SHAPE, "n = %d outside [0, 4]", n);
+    const int32_t g[4] = {ptq1::kBlockWeights, ptq1::kTritBytes, ptq1::kBlockBytes, ptq1::kHadamard};
+    for (int32_t i = 0; i < n; ++i) out[i] = g[i];
+    return ok();
+}
+
+int64_t ptq1_packed_bytes(int64_t n, int64_t k) { return packed_bytes(n, k); }
+
+ptq1_status ptq1_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k,
+                      uint8_t *blocks, hipStream_t stream)
+{
+    int64_t bytes;
+    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, false, &bytes));
+    if (bytes == 0) return ok();
+    int64_t nt;
+    if (!mul_ok(n, k, &nt)) return fail(PTQ1_ERR_OVERFLOW, "trits: n * k overflows");
+    if (trits == nullptr) return fail(PTQ1_ERR_NULL, "trits is NULL");
+    if (scales_f16 == nullptr) return fail(PTQ1_ERR_NULL, "scales_f16 is NULL");
+    if (!aligned(scales_f16, 2)) return fail(PTQ1_ERR_ALIGN, "scales_f16 is not 2-byte aligned");
+    const int64_t ns = n * (k / ptq1::kBlockWeights);
+    if (overlaps(blocks, bytes, trits, nt) || overlaps(blocks, bytes, scales_f16, 2 * ns))
+        return fail(PTQ1_ERR_ALIAS, "blocks overlaps an input");
+    return hip_status(ptq1::launch_pack(trits, scales_f16, n, k, blocks, stream), "ptq1_pack");
+}
+
+ptq1_status ptq1_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t stream)
+{
+    int64_t bytes, wb, nk;
+    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, false, &bytes));
+    if (!mul_ok(n, k, &nk)) return fail(PTQ1_ERR_OVERFLOW, "w: n * k overflows");
+    PTQ1_TRY(check_floats(w, "w", nk, &wb));
+    if (nk == 0) return ok();
+    if (overlaps(w, wb, blocks, bytes)) return fail(PTQ1_ERR_ALIAS, "w overlaps blocks");
+    return hip_status(ptq1::launch_dequant(blocks, n, k, w, stream), "ptq1_dequant");
+}
+
+ptq1_status hadamard_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs1024,
+                            hipStream_t stream)
+{
+    if (m < 0 || k < 0) return fail(PTQ1_ERR_SHAPE, "m or k is negative");
+    if (k % ptq1::kHadamard != 0)
+        return fail(PTQ1_ERR_SHAPE, "k = %lld is not a multiple of %d", (long long)k, ptq1::kHadamard);
+    int64_t mk, xb, yb;
+    if (!mul_ok(m, k, &mk)) return fail(PTQ1_ERR_OVERFLOW, "m * k overflows");
+    PTQ1_TRY(check_floats(x, "x", mk, &xb));
+    PTQ1_TRY(check_floats(y, "y", mk, &yb));
+    if (mk == 0) return ok();
+    PTQ1_TRY(check_signs(signs1024, true));
+    if (x != y && overlaps(x, xb, y, yb)) return fail(PTQ1_ERR_ALIAS, "y partially overlaps x");
+    if (overlaps(y, yb, signs1024, 4 * ptq1::kHadamard)) return fail(PTQ1_ERR_ALIAS, "y overlaps signs1024");
+    if (mk / ptq1::kHadamard > kMaxGridX) return fail(PTQ1_ERR_UNSUPPORTED, "more than 2^31-1 chunks");
+    return hip_status(ptq1::launch_rotate(x, y, m, k, signs1024, stream), "hadamard_rotate");
+}
+
+ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t d,
+                                   const int32_t *ids, int64_t n_rows, const float *signs1024,
+                                   float *out, hipStream_t stream)
+{
+    if (n_table < 0 || d < 0 || n_rows < 0) return fail(PTQ1_ERR_SHAPE, "negative size");
+    if (d % ptq1::kHadamard != 0)
+        return fail(PTQ1_ERR_SHAPE, "d = %lld is not a multiple of %d", (long long)d, ptq1::kHadamard);
+    if (ids == nullptr && n_rows > n_table)
+        return fail(PTQ1_ERR_SHAPE, "n_rows = %lld > n_table = %lld without ids", (long long)n_rows,
+                    (long long)n_table);
+    int64_t tn, on, tb, ob;
+    if (!mul_ok(n_table, d, &tn)) return fail(PTQ1_ERR_OVERFLOW, "n_table * d overflows");
+    if (!mul_ok(n_rows, d, &on)) return fail(PTQ1_ERR_OVERFLOW, "n_rows * d overflows");
+    PTQ1_TRY(check_floats(out, "out", on, &ob));
+    if (on == 0) return ok();
+    PTQ1_TRY(check_floats(table, "table", tn, &tb));
+    if (tn == 0 && ids == nullptr) return fail(PTQ1_ERR_SHAPE, "empty table");
+    PTQ1_TRY(check_signs(signs1024, true));
+    if (ids != nullptr && !aligned(ids, 4)) return fail(PTQ1_ERR_ALIGN, "ids is not 4-byte aligned");
+    if (overlaps(out, ob, table, tb)) return fail(PTQ1_ERR_ALIAS, "out overlaps table");
+    if (ids != nullptr && overlaps(out, ob, ids, 4 * n_rows)) return fail(PTQ1_ERR_ALIAS, "out overlaps ids");
+    if (on / ptq1::kHadamard > kMaxGridX) return fail(PTQ1_ERR_UNSUPPORTED, "more than 2^31-1 chunks");
+    return hip_status(ptq1::launch_unrotate_rows(table, n_table, d, ids, n_rows, signs1024, out, stream),
+                      "hadamard_unrotate_rows");
+}
+
+size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k)
+{
+    if (packed_bytes(n, k) < 0) return 0;
+    return mv_ws(n, k);
+}
+
+ptq1_status ptq1_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+                        const float *signs1024, const float *residual, float *y, void *ws,
+                        size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, xb, yb;
+    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, signs1024 != nullptr, &wb));
+    PTQ1_TRY(check_floats(y, "y", n, &yb));
+    if (n == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", k, &xb));
+    PTQ1_TRY(check_signs(signs1024, false));
+    if (residual != nullptr) {
+        int64_t rb;
+        PTQ1_TRY(check_floats(residual, "residual", n, &rb));
+        if (residual != y && overlaps(residual, rb, y, yb))
+            return fail(PTQ1_ERR_ALIAS, "y partially overlaps residual");
+    }
+    const size_t need = mv_ws(n, k);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_matvec"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, blocks, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps blocks");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, blocks, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    if (nseg_of(k) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
+    float *part = static_cast<float *>(ws);
+    hipError_t e = ptq1::launch_matvec_part(blocks, n, nullptr, 0, k, x, signs1024, part, stream);
+    if (e == hipSuccess) e = ptq1::launch_reduce_rows(part, n, nseg_of(k), residual, y, stream);
+    return hip_status(e, "ptq1_matvec");
+}
+
+size_t ptq1_gate_up_workspace_bytes(int64_t f, int64_t d)
+{
+    if (packed_bytes(f, d) < 0 || f > INT64_MAX / 2) return 0;
+    return mv_ws(2 * f, d);
+}
+
+ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, int64_t d,
+                         const float *x, const float *signs1024, float *g, float *u, void *ws,
+                         size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wgb, wub, xb, gb, ub;
+    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, signs1024 != nullptr, &wgb));
+    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, signs1024 != nullptr, &wub));
+    PTQ1_TRY(check_floats(g, "g", f, &gb));
+    PTQ1_TRY(check_floats(u, "u", f, &ub));
+    if (f == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", d, &xb));
+    PTQ1_TRY(check_signs(signs1024, false));
+    const size_t need = mv_ws(2 * f, d);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gate_up"));
+    if (overlaps(g, gb, u, ub)) return fail(PTQ1_ERR_ALIAS, "g overlaps u");
+    if (overlaps(g, gb, x, xb) || overlaps(u, ub, x, xb)) return fail(PTQ1_ERR_ALIAS, "g or u overlaps x");
+    if (overlaps(ws, (int64_t)need, g, gb) || overlaps(ws, (int64_t)need, u, ub) ||
+        overlaps(ws, (int64_t)need, x, xb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    if (nseg_of(d) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
+    float *part = static_cast<float *>(ws);
+    hipError_t e = ptq1::launch_matvec_part(w_gate, f, w_up, f, d, x, signs1024, part, stream);
+    if (e == hipSuccess)
+        e = ptq1::launch_reduce_gate_up(part, f, nseg_of(d), g, u, nullptr, nullptr, d, 0.0f, stream);
+    return hip_status(e, "ptq1_gate_up");
+}
+
+ptq1_status ptq1_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t stream)
+{
+    int64_t gb, ub, hb;
+    PTQ1_TRY(check_floats(g, "g", len, &gb));
+    PTQ1_TRY(check_floats(u, "u", len, &ub));
+    PTQ1_TRY(check_floats(h, "h", len, &hb));
+    if (len == 0) return ok();
+    if ((h != g && overlaps(h, hb, g, gb)) || (h != u && overlaps(h, hb, u, ub)))
+        return fail(PTQ1_ERR_ALIAS, "h partially overlaps g or u");
+    return hip_status(ptq1::launch_swiglu(g, u, h, len, stream), "ptq1_swiglu");
+}
+
+size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (packed_bytes(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
+    if (m == 0) return 0;
+    return gemm_ws(m, k);
+}
+
+ptq1_status ptq1_gemm(const uint8_t *blocks, int64_t n, int64_t k, const float *x, int64_t m,
+                      const float *signs1024, float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, mk, mn, xb, yb;
+    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, signs1024 != nullptr, &wb));
+    if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
+    if (!mul_ok(m, k, &mk) || !mul_ok(m, n, &mn)) return fail(PTQ1_ERR_OVERFLOW, "m * k or m * n overflows");
+    PTQ1_TRY(check_floats(y, "y", mn, &yb));
+    if (mn == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", mk, &xb));
+    PTQ1_TRY(check_signs(signs1024, false));
+    const size_t need = gemm_ws(m, k);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, blocks, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps blocks");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, blocks, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    const int64_t m_pad = ptq1::gemm_m_pad(m);
+    uint16_t *xbf = static_cast<uint16_t *>(ws);
+    hipError_t e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, k, signs1024, 0.0f, xbf, stream);
+    if (e == hipSuccess)
+        e = ptq1::launch_gemm(xbf, m, m_pad, k, blocks, n, nullptr, 0, y, nullptr, nullptr, stream);
+    return hip_status(e, "ptq1_gemm");
+}
+
+size_t ptq1_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
+{
+    if (m < 0 || m > kMaxGemmM || packed_bytes(f, d) < 0 || packed_bytes(d, f) < 0 || f > INT64_MAX / 2)
+        return 0;
+    if (m == 0) return 0;
+    return ffn_layout(m, d, f).total;
+}
+
+ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                           const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                           const float *signs1024, float rms_eps, void *ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    int64_t wgb, wub, wdb, md, xb, ob;
+    if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
+    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, true, &wgb));
+    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, true, &wub));
+    PTQ1_TRY(check_matrix(w_down, "w_down", d, f, true, &wdb));
+    if (!mul_ok(m, d, &md)) return fail(PTQ1_ERR_OVERFLOW, "m * d overflows");
+    PTQ1_TRY(check_floats(x_out, "x_out", md, &ob));
+    if (md == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", md, &xb));
+    PTQ1_TRY(check_signs(signs1024, true));
+    if (x_out != x && overlaps(x_out, ob, x, xb)) return fail(PTQ1_ERR_ALIAS, "x_out partially overlaps x");
+    if (overlaps(x_out, ob, w_gate, wgb) || overlaps(x_out, ob, w_up, wub) || overlaps(x_out, ob, w_down, wdb))
+        return fail(PTQ1_ERR_ALIAS, "x_out overlaps a weight matrix");
+    if (f == 0) return fail(PTQ1_ERR_SHAPE, "f = 0");
+    const FfnWs L = ffn_layout(m, d, f);
+    PTQ1_TRY(check_ws(ws, ws_bytes, L.total, "ptq1_ffn_block"));
+    if (overlaps(ws, (int64_t)L.total, x, xb) || overlaps(ws, (int64_t)L.total, x_out, ob))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps x or x_out");
+    if (nseg_of(f) > kMaxGridY || nseg_of(d) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d or f too large");
+    char *w = static_cast<char *>(ws);
+    hipError_t e;
+    if (m == 1) {
+        float *part = reinterpret_cast<float *>(w + L.part);
+        float *g = reinterpret_cast<float *>(w + L.g);
+        float *u = reinterpret_cast<float *>(w + L.u);
+        float *h = reinterpret_cast<float *>(w + L.h);
+        e = ptq1::launch_matvec_part(w_gate, f, w_up, f, d, x, signs1024, part, stream);
+        if (e == hipSuccess)
+            e = ptq1::launch_reduce_gate_up(part, f, nseg_of(d), g, u, h, rms_eps > 0.0f ? x : nullptr, d,
+                                            rms_eps, stream);
+        if (e == hipSuccess) e = ptq1::launch_matvec_part(w_down, d, nullptr, 0, f, h, signs1024, part, stream);
+        if (e == hipSuccess) e = ptq1::launch_reduce_rows(part, d, nseg_of(f), x, x_out, stream);
+    } else {
+        const int64_t m_pad = ptq1::gemm_m_pad(m);
+        uint16_t *xbf = reinterpret_cast<uint16_t *>(w + L.xb);
+        float *g = reinterpret_cast<float *>(w + L.g);
+        float *u = reinterpret_cast<float *>(w + L.u);
+        e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, d, signs1024, rms_eps, xbf, stream);
+        if (e == hipSuccess) e = ptq1::launch_gemm(xbf, m, m_pad, d, w_gate, f, w_up, f, g, u, nullptr, stream);
+        if (e == hipSuccess) e = ptq1::launch_prep_bf16(nullptr, g, u, m, m_pad, f, signs1024, 0.0f, xbf, stream);
+        if (e == hipSuccess)
+            e = ptq1::launch_gemm(xbf, m, m_pad, f, w_down, d, nullptr, 0, x_out, nullptr, x, stream);
+    }
+    return hip_status(e, "ptq1_ffn_block");
+}
+
+}  // extern "C"

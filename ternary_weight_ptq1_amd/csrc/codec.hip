@@ -1,0 +1,94 @@
+// codec.hip -- PTQ1_0 encode (pack) and decode (dequant) kernels.
+//
+// Format: "A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally",
+// section "What Bonsai is" (five trits per byte in base 3, one 16-bit scale
+// per 128 weights); the decode reads digits on the float pipeline as in
+// section "What Ferrox does with it".
+#include "ptq1_device.h"
+#include "ptq1_launch.h"
+
+namespace ptq1 {
+
+// One thread per output byte.  Trit bytes carry v = sum_n (t_n + 1) 3^(4-n)
+// (padding digits are 1) as the smallest byte b with floor(243 b / 256) = v,
+// b = ceil(256 v / 243); bytes 26..27 are the scale, little-endian.
+__global__ void __launch_bounds__(256) k_pack(const int8_t *__restrict__ trits,
+                                              const uint16_t *__restrict__ scales, int64_t nb,
+                                              int64_t k, int64_t total, uint8_t *__restrict__ out)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t blk = t / kBlockBytes;
+        const int i = static_cast<int>(t - blk * kBlockBytes);
+        const int64_t row = blk / nb;
+        const int64_t b = blk - row * nb;
+        uint32_t byte;
+        if (i < kTritBytes) {
+            const int8_t *src = trits + row * k + b * kBlockWeights + kTritsPerByte * i;
+            uint32_t v = 0;
+#pragma unroll
+            for (int n = 0; n < kTritsPerByte; ++n) {
+                int dgt = 1;
+                if (kTritsPerByte * i + n < kBlockWeights) {
+                    const int tv = src[n];
+                    dgt = tv < -1 ? 0 : (tv > 1 ? 2 : tv + 1);
+                }
+                v = 3u * v + static_cast<uint32_t>(dgt);
+            }
+            byte = (256u * v + 242u) / 243u;
+        } else {
+            const uint32_t s = scales[row * nb + b];
+            byte = (i == kScaleOffset) ? (s & 0xffu) : (s >> 8);
+        }
+        out[t] = static_cast<uint8_t>(byte);
+    }
+}
+
+// One thread per weight: digit (c mod 128) mod 5 of byte (c mod 128) / 5.
+__global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ blocks, int64_t nb,
+                                                 int64_t k, int64_t total, float *__restrict__ w)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = t / k;
+        const int64_t c = t - row * k;
+        const int64_t b = c / kBlockWeights;
+        const int j = static_cast<int>(c - b * kBlockWeights);
+        const uint8_t *blk = blocks + (row * nb + b) * kBlockBytes;
+        const float byte = static_cast<float>(blk[j / kTritsPerByte]);
+        const float dgt = peel_digit(byte, j % kTritsPerByte);
+        const uint32_t sb = blk[kScaleOffset] | (static_cast<uint32_t>(blk[kScaleOffset + 1]) << 8);
+        w[t] = half_bits_to_float(sb) * (dgt - 1.0f);
+    }
+}
+
+static unsigned grid_for(int64_t total, int threads)
+{
+    int64_t g = (total + threads - 1) / threads;
+    const int64_t cap = 256 * 1024;  // grid-stride beyond this
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return static_cast<unsigned>(g);
+}
+
+hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
+                       uint8_t *blocks, hipStream_t s)
+{
+    const int64_t nb = k / kBlockWeights;
+    const int64_t total = n * nb * kBlockBytes;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pack, dim3(grid_for(total, 256)), dim3(256), 0, s, trits, scales, nb, k,
+                       total, blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s)
+{
+    const int64_t total = n * k;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_dequant, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks,
+                       k / kBlockWeights, k, total, w);
+    return hipGetLastError();
+}
+
+}  // namespace ptq1

@@ -1,0 +1,249 @@
+// gemm.hip -- multi-token prefill: PTQ1_0 weights decoded into LDS as exact
+// bf16 trits, activations rotated and rounded to bf16, bf16 MFMA with fp32
+// accumulation and the per-block scale applied in fp32.
+//
+// "A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally":
+//   - "What Ferrox does with it": a GEMM for prefill, trits read with the
+//     float-pipeline peel;
+//   - "What Bonsai is": activations rotated before every folded matmul.
+// Each 128-weight block's MFMA partial sum is multiplied by that block's
+// scale in fp32 (never folded into bf16), so the only rounding beyond fp32
+// is the bf16 rounding of the rotated activations.
+#include "ptq1_device.h"
+#include "ptq1_launch.h"
+
+namespace ptq1 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Activation prep: one wavefront per (row, 1024-chunk).
+//   input  = x (times the row's RMS scale when rms_eps > 0), or silu(g) * u
+//   output = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
+// Rows in [m, m_pad) are written as zeros so MFMA tiles need no row guard.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kRotThreads) k_prep_bf16(
+    const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
+    int64_t m, int64_t k, const float *__restrict__ signs, float rms_eps,
+    uint16_t *__restrict__ xb)
+{
+    const int64_t cpr = (k + kHadamard - 1) / kHadamard;  // == k / 1024 when signs are given
+    const int64_t row = blockIdx.x / cpr;
+    const int64_t ch = blockIdx.x - row * cpr;
+    const int lane = threadIdx.x;
+    const int64_t e0 = ch * kHadamard;  // first element of this chunk in the row
+    uint16_t *dst = xb + row * k + e0;
+    if (row >= m) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j)
+            if (e0 + lane + kWave * j < k) dst[lane + kWave * j] = 0;
+        return;
+    }
+    float a = 1.0f;
+    if (x != nullptr && rms_eps > 0.0f) {
+        const float *xr = x + row * k;
+        float s = 0.0f;
+        for (int64_t i = lane; i < k; i += kWave) s = fmaf(xr[i], xr[i], s);
+#pragma unroll
+        for (int h = kWave / 2; h > 0; h >>= 1) s += __shfl_xor(s, h, kWave);
+        a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
+    }
+    float v[kRotPerLane];
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) {
+        const int64_t e = e0 + lane + kWave * j;
+        float in = 0.0f;
+        if (e < k) {
+            const int64_t i = row * k + e;
+            if (x != nullptr) {
+                in = x[i] * a;
+            } else {
+                const float gv = g[i];
+                in = gv / (1.0f + expf(-gv)) * u[i];
+            }
+        }
+        v[j] = signs ? in * signs[lane + kWave * j] : in;
+    }
+    if (signs != nullptr) {
+        fwht1024_wave(v);
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] *= (1.0f / 32.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j)
+        if (e0 + lane + kWave * j < k) dst[lane + kWave * j] = f32_to_bf16_rne(v[j]);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM.  Workgroup tile BM (tokens) x BN (weight rows); 4 waves in a
+// WM x WN grid, each owning TM x TN 32x32 output tiles of
+// v_mfma_f32_32x32x16_bf16.  K advances one PTQ1_0 block (128) per step:
+//   A: the bf16 activation tile [BM][128] is copied to LDS;
+//   B: the weight tile's 28-byte blocks are read once, trits peeled on the
+//      float pipeline and written to LDS as exact bf16 -1/0/+1; the scale
+//      goes to LDS as fp32;
+//   16 x K=16 MFMAs accumulate the block's partial product from zero, then
+//   acc += partial * scale[column] in fp32.
+// Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
+// and B[8(l/32)+j][l%32], j = 0..7; result register r of lane l is
+// D[8(r/4) + 4(l/32) + r%4][l%32].
+// ---------------------------------------------------------------------------
+constexpr int kLdsK = kGemmKB + 8;  // padded row (bf16 elements): 272 B, conflict-free b128 reads
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
+    const uint16_t *__restrict__ xb, int64_t m, int64_t k, const uint8_t *__restrict__ w0,
+    int64_t n0, const uint8_t *__restrict__ w1, int64_t n1, float *__restrict__ y0,
+    float *__restrict__ y1, const float *residual)
+{
+    static_assert(WM * WN * kWave == kGemmThreads, "4 waves");
+    constexpr int TM = BM / WM / 32;
+    constexpr int TN = BN / WN / 32;
+    static_assert(TM >= 1 && TN >= 1, "tile");
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM][kLdsK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][kLdsK];
+    __shared__ float ssc[BN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t rows = n0 + n1;
+    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * BN;
+    const int64_t tile_m = static_cast<int64_t>(blockIdx.y) * BM;
+    const int64_t nb = k / kBlockWeights;
+    const int64_t pitch = nb * kBlockBytes;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    for (int64_t kb = 0; kb < nb; ++kb) {
+        // ---- A tile: BM rows x 128 bf16, 16 B per copy
+        for (int c = tid; c < BM * (kGemmKB / 8); c += kGemmThreads) {
+            const int r = c / (kGemmKB / 8), p = c % (kGemmKB / 8);
+            const uint4 v = *reinterpret_cast<const uint4 *>(xb + (tile_m + r) * k + kb * kGemmKB + p * 8);
+            *reinterpret_cast<uint4 *>(&As[r][p * 8]) = v;
+        }
+        // ---- B tile: BN rows x 7 dwords; peel 4 (or 2) trit bytes per dword
+        for (int c = tid; c < BN * kBlockDwords; c += kGemmThreads) {
+            const int r = c / kBlockDwords, q = c % kBlockDwords;
+            const int64_t rv = tile_n + r;
+            uint32_t dw = 0x80808080u;  // byte 128 = code 121 = all digits 1 = zero weights
+            if (rv < rows) {
+                const uint8_t *wrow = (rv < n0) ? (w0 + rv * pitch) : (w1 + (rv - n0) * pitch);
+                dw = reinterpret_cast<const uint32_t *>(wrow + kb * kBlockBytes)[q];
+            }
+            const int nbytes = (q == kBlockDwords - 1) ? 2 : 4;
+            for (int t = 0; t < nbytes; ++t) {
+                const int i = 4 * q + t;
+                const Peel5 p = peel5(static_cast<float>((dw >> (8 * t)) & 0xffu));
+                const float dg[5] = {p.d0, p.d1, p.d2, p.d3, p.d4};
+#pragma unroll
+                for (int n = 0; n < kTritsPerByte; ++n) {
+                    const int j = kTritsPerByte * i + n;
+                    if (j < kBlockWeights)
+                        Bs[r][j] = static_cast<uint16_t>(__builtin_bit_cast(uint32_t, dg[n] - 1.0f) >> 16);
+                }
+            }
+            if (q == kBlockDwords - 1) ssc[r] = (rv < rows) ? half_bits_to_float(dw >> 16) : 0.0f;
+        }
+        __syncthreads();
+
+        f32x16 part[TM][TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[a][b][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kGemmKB / 16; ++ks) {
+            const int kof = ks * 16 + 8 * (lane / 32);
+            bf16x8 av[TM], bv[TN];
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+                av[a] = *reinterpret_cast<const bf16x8 *>(&As[wm * (BM / WM) + a * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+                bv[b] = *reinterpret_cast<const bf16x8 *>(&Bs[wn * (BN / WN) + b * 32 + (lane & 31)][kof]);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], part[a][b], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const float sc = ssc[wn * (BN / WN) + b * 32 + (lane & 31)];
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(part[a][b][r], sc, acc[a][b][r]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int64_t col = tile_n + wn * (BN / WN) + b * 32 + (lane & 31);
+            if (col >= rows) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = tile_m + wm * (BM / WM) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                if (row >= m) continue;
+                if (col < n0) {
+                    const int64_t o = row * n0 + col;
+                    y0[o] = residual ? residual[o] + acc[a][b][r] : acc[a][b][r];
+                } else {
+                    y1[row * n1 + (col - n0)] = acc[a][b][r];
+                }
+            }
+        }
+}
+
+int64_t gemm_m_pad(int64_t m)
+{
+    if (m <= 32) return 32;
+    return (m + 127) / 128 * 128;
+}
+
+hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int64_t m,
+                            int64_t m_pad, int64_t k, const float *signs, float rms_eps,
+                            uint16_t *xb, hipStream_t s)
+{
+    const int64_t nchunks = m_pad * ((k + kHadamard - 1) / kHadamard);
+    if (nchunks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_prep_bf16, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+                       g, u, m, k, signs, rms_eps, xb);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
+                       int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
+                       const float *residual, hipStream_t s)
+{
+    const int64_t rows = n0 + n1;
+    if (rows == 0 || m == 0) return hipSuccess;
+    if (m_pad == 32) {
+        constexpr int BM = 32, BN = 128;
+        const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), 1);
+        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, 1, 4>), grid, dim3(kGemmThreads), 0, s, xb, m, k, w0,
+                           n0, w1, n1, y0, y1, residual);
+    } else {
+        constexpr int BM = 128, BN = 64;
+        const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), static_cast<unsigned>(m_pad / BM));
+        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, 2, 2>), grid, dim3(kGemmThreads), 0, s, xb, m, k, w0,
+                           n0, w1, n1, y0, y1, residual);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ptq1

@@ -1,0 +1,49 @@
+// ptq1_geometry.h -- the one place the PTQ1_0 block geometry and the launch
+// geometry of every kernel are defined.  Host validation, launch code and
+// kernels all read these constants; ptq1_geometry() exports them so a test
+// can hold them against the public header and the oracle.
+//
+// Block format ("A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally",
+// section "What Bonsai is"): 128 ternary weights with one 16-bit scale, five
+// trits per byte in base 3 -> ceil(128/5) = 26 trit bytes, then the scale:
+// 28 bytes = 224 bits = 1.75 bits per weight.  The fold uses a 1024-wide
+// Walsh-Hadamard butterfly (same section).
+#pragma once
+#include <cstdint>
+
+namespace ptq1 {
+
+constexpr int kBlockWeights = 128;   // weights per block
+constexpr int kTritsPerByte = 5;     // 3^5 = 243 <= 256
+constexpr int kTritBytes = 26;       // ceil(128 / 5)
+constexpr int kScaleOffset = 26;     // fp16 scale, little-endian, after the trits
+constexpr int kBlockBytes = 28;      // 26 + 2
+constexpr int kBlockDwords = 7;      // 28 / 4
+constexpr int kHadamard = 1024;      // rotation width
+constexpr int kBlocksPerChunk = kHadamard / kBlockWeights;  // 8
+
+static_assert(kTritBytes * kTritsPerByte >= kBlockWeights, "trit bytes hold a block");
+static_assert((kTritBytes - 1) * kTritsPerByte < kBlockWeights, "no spare trit byte");
+static_assert(kBlockBytes == kTritBytes + 2 && kBlockBytes % 4 == 0, "block is whole dwords");
+
+// ---- launch geometry -------------------------------------------------------
+constexpr int kWave = 64;                       // CDNA wavefront
+
+// rotation: one wave per 1024-chunk, 16 values per lane
+constexpr int kRotThreads = kWave;
+constexpr int kRotPerLane = kHadamard / kWave;  // 16
+
+// float-peel matvec: lane <-> output row, workgroup <-> (row tile, 1024-chunk)
+constexpr int kMvWaves = 4;
+constexpr int kMvThreads = kMvWaves * kWave;    // 256 rows per workgroup
+constexpr int kMvRowsPerWg = kMvThreads;
+
+// reductions / element-wise kernels
+constexpr int kEwThreads = 256;
+
+// MFMA GEMM tile (bf16 32x32x16 MFMA, fp32 accumulate)
+constexpr int kGemmBN = 64;                     // weight rows per workgroup
+constexpr int kGemmKB = kBlockWeights;          // one PTQ1_0 block of K per step
+constexpr int kGemmThreads = 256;
+
+}  // namespace ptq1

@@ -1,0 +1,55 @@
+// ptq1_launch.h -- internal launchers (host side), one per kernel family.
+// Arguments are validated by the C ABI layer before any of these is called;
+// each returns the hipError_t of its launch(es).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace ptq1 {
+
+hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
+                       uint8_t *blocks, hipStream_t s);
+hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s);
+
+// rows of x [m][k] -> y, each 1024-chunk (1/32) H (signs * chunk)
+hipError_t launch_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs,
+                         hipStream_t s);
+// out[i] = signs * (1/32) H table[ids ? ids[i] : i]  per chunk
+hipError_t launch_unrotate_rows(const float *table, int64_t n_table, int64_t d, const int32_t *ids,
+                                int64_t n_rows, const float *signs, float *out, hipStream_t s);
+
+// ---- decode (m = 1) --------------------------------------------------------
+// Partial sums of the float-peel matvec over a "virtual" matrix whose rows
+// [0, n0) come from w0 and [n0, n0 + n1) from w1 (n1 = 0: one matrix).
+// part[seg][row], seg = 1024-wide K segment; x rotated per segment when
+// signs != nullptr.
+size_t matvec_part_floats(int64_t rows, int64_t k);
+hipError_t launch_matvec_part(const uint8_t *w0, int64_t n0, const uint8_t *w1, int64_t n1,
+                              int64_t k, const float *x, const float *signs, float *part,
+                              hipStream_t s);
+// y[r] = residual[r] + sum_seg part[seg][r]
+hipError_t launch_reduce_rows(const float *part, int64_t n, int64_t nseg, const float *residual,
+                              float *y, hipStream_t s);
+// g, u from the two halves of the virtual matrix; optionally h = silu(a g) (a u)
+// with a the RMS scale of x_rms (x_rms == nullptr: a = 1).
+hipError_t launch_reduce_gate_up(const float *part, int64_t f, int64_t nseg, float *g, float *u,
+                                 float *h, const float *x_rms, int64_t d, float rms_eps,
+                                 hipStream_t s);
+hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t s);
+
+// ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
+// xb [m_pad][k] bf16 = bf16(R (a * x)); rows >= m zero.  a = RMS scale if
+// rms_eps > 0.  When g/u are given instead of x, the input is silu(g) * u.
+int64_t gemm_m_pad(int64_t m);
+hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int64_t m,
+                            int64_t m_pad, int64_t k, const float *signs, float rms_eps,
+                            uint16_t *xb, hipStream_t s);
+// y [m][rows] (ldy) = xb . W^T (+ residual [m][rows] if given); rows of the
+// virtual matrix as in launch_matvec_part; the second matrix's outputs go to
+// y1 (same ld) when n1 > 0.
+hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
+                       int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
+                       const float *residual, hipStream_t s);
+
+}  // namespace ptq1

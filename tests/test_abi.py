@@ -1,0 +1,139 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/ptq1.h declares, agrees with the oracle on the block geometry, and
+refuses bad arguments before enqueuing anything (no GPU needed: every call
+below fails validation, so no HIP call is made)."""
+import ctypes as C
+
+import pytest
+
+import oracle
+import ternary_weight_ptq1_amd as P
+
+FAKE = 1 << 20  # a 16-byte-aligned fake device address, never dereferenced
+
+
+def L():
+    return P.lib()
+
+
+def test_library_exports_every_header_function():
+    names = P.header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L(), n), f"{n} declared in ptq1.h but not exported"
+    assert set(P._SIGS) == set(names)
+
+
+def test_geometry_single_source():
+    """One table, held together by a test ("A 27B model in 5.5 GB...",
+    section "What I learned building it": derive copies from one table)."""
+    g = P.ptq1_geometry()
+    assert g == (128, 26, 28, 1024)
+    assert g == (oracle.lib().orc_block_weights(), oracle.lib().orc_block_trit_bytes(),
+                 oracle.lib().orc_block_bytes(), oracle.lib().orc_hadamard_width())
+    assert (P.BLOCK_WEIGHTS, P.TRIT_BYTES, P.BLOCK_BYTES, P.HADAMARD) == g
+    hdr = open(P.HEADER).read()
+    for name, v in zip(("PTQ1_BLOCK_WEIGHTS", "PTQ1_TRIT_BYTES", "PTQ1_BLOCK_BYTES", "PTQ1_HADAMARD"), g):
+        assert f"#define {name} {v}" in hdr
+
+
+def test_packed_bytes():
+    assert P.ptq1_packed_bytes(17408, 5120) == 19_496_960
+    assert P.ptq1_packed_bytes(5120, 17408) == 19_496_960
+    assert P.ptq1_packed_bytes(1024, 1024) == 229_376
+    assert P.ptq1_packed_bytes(0, 128) == 0
+    assert P.ptq1_packed_bytes(1, 100) == -1
+    assert P.ptq1_packed_bytes(-1, 128) == -1
+    assert P.ptq1_packed_bytes(1 << 62, 1 << 20) == -1
+
+
+def test_status_strings():
+    for code, name in P.STATUS.items():
+        assert L().ptq1_status_string(code).decode() == name
+
+
+def _err(rc):
+    return rc, L().ptq1_last_error().decode()
+
+
+def test_pack_validation():
+    rc, msg = _err(L().ptq1_pack(None, C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE * 2), None))
+    assert rc == 1 and "trits" in msg
+    rc, msg = _err(L().ptq1_pack(C.c_void_p(FAKE), C.c_void_p(FAKE), 4, 100, C.c_void_p(FAKE * 2), None))
+    assert rc == 2 and "128" in msg
+    rc, msg = _err(L().ptq1_pack(C.c_void_p(FAKE), C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE * 2 + 4), None))
+    assert rc == 3 and "blocks" in msg
+    rc, msg = _err(L().ptq1_pack(C.c_void_p(FAKE), C.c_void_p(FAKE), 1 << 60, 1 << 20, C.c_void_p(FAKE * 2), None))
+    assert rc == 4
+    # output overlapping the trits
+    rc, msg = _err(L().ptq1_pack(C.c_void_p(FAKE), C.c_void_p(FAKE * 4), 4, 128, C.c_void_p(FAKE + 16), None))
+    assert rc == 7
+    # empty input is a no-op, not an error
+    assert L().ptq1_pack(None, None, 0, 128, None, None) == 0
+
+
+def test_rotate_validation():
+    s = C.c_void_p(FAKE * 8)
+    assert _err(L().hadamard_rotate(C.c_void_p(FAKE), C.c_void_p(FAKE * 2), 1, 1536, s, None))[0] == 2
+    assert _err(L().hadamard_rotate(C.c_void_p(FAKE), C.c_void_p(FAKE * 2), 1, 1024, None, None))[0] == 1
+    assert _err(L().hadamard_rotate(C.c_void_p(FAKE), C.c_void_p(FAKE + 4096), 2, 1024, s, None))[0] == 7
+    assert _err(L().hadamard_rotate(C.c_void_p(FAKE + 8), C.c_void_p(FAKE * 2), 1, 1024, s, None))[0] == 3
+    assert _err(L().hadamard_rotate(None, None, 0, 1024, None, None))[0] == 0
+
+
+def test_unrotate_validation():
+    s = C.c_void_p(FAKE * 8)
+    rc, msg = _err(L().hadamard_unrotate_rows(C.c_void_p(FAKE), 10, 1024, None, 11, s, C.c_void_p(FAKE * 4), None))
+    assert rc == 2 and "n_rows" in msg
+    rc, _ = _err(L().hadamard_unrotate_rows(C.c_void_p(FAKE), 10, 1000, None, 1, s, C.c_void_p(FAKE * 4), None))
+    assert rc == 2
+    rc, _ = _err(L().hadamard_unrotate_rows(C.c_void_p(FAKE), 10, 1024, None, 2, s, C.c_void_p(FAKE + 4096), None))
+    assert rc == 7
+
+
+def test_matvec_validation():
+    ws_need = L().ptq1_matvec_workspace_bytes(5120, 17408)
+    assert ws_need == 17 * 5120 * 4
+    B, X, Y, WS, S = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400, 500))
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, X, S, None, Y, None, 0, None))
+    assert rc == 6 and "ws" in msg
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, X, S, None, Y, WS, ws_need - 1, None))
+    assert rc == 6
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408 + 128, X, S, None, Y, WS, 1 << 30, None))
+    assert rc == 2 and "1024" in msg
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, X, S, None, C.c_void_p(FAKE * 200 + 64), WS, 1 << 30, None))
+    assert rc == 7
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, None, S, None, Y, WS, 1 << 30, None))
+    assert rc == 1 and "x" in msg
+    rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, X, S, None, Y, C.c_void_p(FAKE * 400 + 16), 1 << 30, None))
+    assert rc == 3
+
+
+def test_gemm_and_ffn_validation():
+    B, X, Y, WS, S = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400, 500))
+    rc, msg = _err(L().ptq1_gemm(B, 17408, 5120, X, 65537, S, Y, WS, 1 << 40, None))
+    assert rc == 5 and "m" in msg
+    rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, -1, S, Y, WS, 1 << 40, None))
+    assert rc == 2
+    need = L().ptq1_gemm_workspace_bytes(256, 17408, 5120)
+    assert need == 256 * 5120 * 2
+    rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, 256, S, Y, WS, need - 1, None))
+    assert rc == 6
+    W2, W3 = C.c_void_p(FAKE * 600), C.c_void_p(FAKE * 700)
+    rc, msg = _err(L().ptq1_ffn_block(X, Y, 1, 5120, 17408, B, W2, W3, None, 0.0, WS, 1 << 40, None))
+    assert rc == 1 and "signs" in msg
+    rc, _ = _err(L().ptq1_ffn_block(X, Y, 1, 5000, 17408, B, W2, W3, S, 0.0, WS, 1 << 40, None))
+    assert rc == 2
+    rc, _ = _err(L().ptq1_ffn_block(X, C.c_void_p(FAKE * 200 + 16), 2, 5120, 17408, B, W2, W3, S, 0.0, WS,
+                                    1 << 40, None))
+    assert rc == 7
+    assert L().ptq1_ffn_workspace_bytes(1, 5120, 17408) > 0
+    assert L().ptq1_ffn_workspace_bytes(8, 5120, 17408) >= 32 * 17408 * 2
+    assert L().ptq1_ffn_workspace_bytes(1, 5120, 17400) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        P.lib()

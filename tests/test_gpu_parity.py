@@ -1,0 +1,348 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (relative L2, ||got - ref|| / ||ref||):
+  bit-exact   ptq1_pack bytes, ptq1_dequant values (scale * trit is exact in fp32)
+  1e-5        fp32 paths: rotate, unrotate_rows, matvec, gate_up, swiglu,
+              ffn_block at m = 1
+  3e-3        bf16-MFMA GEMM (activations rounded to bf16 once)
+  6e-3        ffn_block at m >= 2 end to end (two bf16 roundings in sequence:
+              the rotated input of gate/up and the rotated SwiGLU output)
+Inputs come from the seeded generator; expected values only from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import synth.device as sdev
+import ternary_weight_ptq1_amd as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_FP32 = 1e-5
+TOL_BF16 = 3e-3
+TOL_FFN_BF16 = 6e-3
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def host_matrix(seed, tr, sc, n, k, row0=0):
+    return synth.trits(seed, tr, n, k, row0), synth.scales(seed, sc, n, k // 128, row0)
+
+
+def dev_pack(t, s):
+    return P.ptq1_pack(to_dev(t), to_dev(s.view(np.int16)))
+
+
+def dev_matrix(seed, tr, sc, n, k):
+    """Packed on the GPU from device-generated trits/scales (same generator)."""
+    t = sdev.trits(seed, tr, n, k)
+    s = sdev.scales(seed, sc, n, k // 128)
+    out = P.ptq1_pack(t, s)
+    del t, s
+    return out
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()
+    yield
+
+
+# ------------------------------------------------------------ generator ----
+
+def test_device_generator_matches_host():
+    t = host(sdev.trits(3, 12, 64, 1024, row0=5))
+    np.testing.assert_array_equal(t, synth.trits(3, 12, 64, 1024, row0=5))
+    s = host(sdev.scales(3, 13, 100, 40, row0=7)).view(np.uint16)
+    np.testing.assert_array_equal(s, synth.scales(3, 13, 100, 40, row0=7))
+    g = host(sdev.gauss(4, 10, 100000, start=123456))
+    np.testing.assert_array_equal(g, synth.gauss(4, 10, 100000, start=123456))
+
+
+# ---------------------------------------------------------------- codec ----
+
+@pytest.mark.parametrize("n,k,seed", [(1024, 1024, 0), (37, 384, 1), (1, 128, 2), (3, 1152, 3),
+                                      (17408, 5120, 1)])
+def test_pack_bit_exact(n, k, seed):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    got = host(dev_pack(t, s))
+    np.testing.assert_array_equal(got, oracle.pack(t, s))
+
+
+def test_pack_constant_patterns():
+    for val, byte in ((0, 128), (1, 255), (-1, 0)):
+        t = np.full((2, 256), val, np.int8)
+        s = np.full((2, 2), 0x3C00, np.uint16)
+        got = host(dev_pack(t, s)).reshape(-1, 28)
+        ref = oracle.pack(t, s).reshape(-1, 28)
+        np.testing.assert_array_equal(got, ref)
+        assert np.all(got[:, :25] == byte)
+
+
+def test_pack_worked_block():
+    t = np.zeros((1, 128), np.int8)
+    t[0, [0, 2, 3, 125, 126]] = [1, -1, 1, -1, 1]
+    s = np.array([[0x3C00]], np.uint16)
+    got = host(dev_pack(t, s))[0]
+    assert got[0] == 207 and got[25] == 71 and got[26] == 0 and got[27] == 60
+    assert np.all(got[1:25] == 128)
+
+
+@pytest.mark.parametrize("n,k,seed", [(1024, 1024, 0), (37, 384, 1)])
+def test_dequant_bit_exact(n, k, seed):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    blocks = oracle.pack(t, s)
+    got = host(P.ptq1_dequant(to_dev(blocks), n, k))
+    np.testing.assert_array_equal(got.astype(np.float64), oracle.dequant(blocks, n, k))
+
+
+def test_dequant_accepts_every_byte():
+    """All 256 byte values (including the 13 never produced by the encoder)
+    decode on the GPU exactly as the oracle decodes them."""
+    rng = np.random.default_rng(0)
+    n, k = 64, 1024
+    blocks = rng.integers(0, 256, size=(n, (k // 128) * 28), dtype=np.uint8).reshape(n, -1, 28)
+    blocks[0, 0, :26] = np.arange(26)
+    blocks[1, :, :26] = (np.arange(8 * 26).reshape(8, 26) + 26) % 256
+    sc = synth.scales(9, 2, n, k // 128).view(np.uint8).reshape(n, k // 128, 2)
+    blocks[:, :, 26:] = sc
+    blocks = blocks.reshape(n, -1)
+    got = host(P.ptq1_dequant(to_dev(blocks), n, k))
+    np.testing.assert_array_equal(got.astype(np.float64), oracle.dequant(blocks, n, k))
+
+
+# ------------------------------------------------------------- rotation ----
+
+@pytest.mark.parametrize("m,k,seed", [(1, 1024, 0), (3, 5120, 1), (1, 17408, 2), (512, 5120, 3)])
+def test_rotate(m, k, seed):
+    x = synth.activations(seed, m, k)
+    s = synth.signs(seed)
+    got = host(P.hadamard_rotate(to_dev(x), to_dev(s)))
+    assert rel_l2(got, oracle.rotate(x, s)) <= TOL_FP32
+
+
+def test_rotate_in_place_and_closed_form():
+    s = synth.signs(5)
+    x = np.zeros((2, 2048), np.float32)
+    x[0, 0] = 1.0
+    x[1, 1024:] = 1.0
+    xd = to_dev(x)
+    P.hadamard_rotate(xd, to_dev(np.ones(1024, np.float32)), out=xd)
+    got = host(xd)
+    np.testing.assert_array_equal(got[0, :1024], np.full(1024, 1 / 32, np.float32))
+    np.testing.assert_array_equal(got[0, 1024:], 0)
+    np.testing.assert_array_equal(got[1, 1024:], np.eye(1, 1024, 0, np.float32)[0] * 32)
+    y = synth.activations(6, 4, 3072)
+    yd = to_dev(y)
+    P.hadamard_rotate(yd, to_dev(s), out=yd)
+    assert rel_l2(host(yd), oracle.rotate(y, s)) <= TOL_FP32
+
+
+def test_unrotate_rows_small():
+    s = synth.signs(7)
+    tab = synth.table_rows(7, synth.S_TABLE, np.arange(300), 2048)
+    ids = np.array([0, 299, 17, 17, 150], np.int32)
+    got = host(P.hadamard_unrotate_rows(to_dev(tab), to_dev(s), ids=to_dev(ids)))
+    assert rel_l2(got, oracle.unrotate(tab[ids], s)) <= TOL_FP32
+    got2 = host(P.hadamard_unrotate_rows(to_dev(tab), to_dev(s), n_rows=3))
+    assert rel_l2(got2, oracle.unrotate(tab[:3], s)) <= TOL_FP32
+    bad = host(P.hadamard_unrotate_rows(to_dev(tab), to_dev(s), ids=to_dev(np.array([300, -1, 2], np.int32))))
+    assert np.all(np.isnan(bad[:2])) and rel_l2(bad[2], oracle.unrotate(tab[2:3], s)[0]) <= TOL_FP32
+    # rotate then unrotate round-trips
+    back = host(P.hadamard_unrotate_rows(P.hadamard_rotate(to_dev(tab[:4]), to_dev(s)), to_dev(s)))
+    assert rel_l2(back, tab[:4]) <= TOL_FP32
+
+
+def test_unrotate_rows_full_table():
+    """A 248320 x 5120 fp32 table (5.09 GB) generated on the device; rows 0,
+    248319 and seeded rows restored and compared with the oracle."""
+    V, d, seed = 248320, 5120, 2
+    s = synth.signs(seed)
+    table = sdev.gauss(seed, synth.S_TABLE, V * d).view(V, d)
+    ids = np.concatenate([[0, V - 1], synth.token_ids(seed, 6, V)]).astype(np.int32)
+    got = host(P.hadamard_unrotate_rows(table, to_dev(s), ids=to_dev(ids)))
+    del table
+    torch.cuda.empty_cache()
+    ref = oracle.unrotate(synth.table_rows(seed, synth.S_TABLE, ids, d), s)
+    for i in range(len(ids)):
+        assert rel_l2(got[i], ref[i]) <= TOL_FP32, f"row {ids[i]}"
+
+
+# --------------------------------------------------------------- matvec ----
+
+@pytest.mark.parametrize("n,k,seed,rot", [(1024, 1024, 0, True), (300, 384, 1, False), (257, 3072, 2, True),
+                                          (1, 128, 3, False), (5120, 17408, 2, True)])
+def test_matvec(n, k, seed, rot):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    blocks = oracle.pack(t, s)
+    x = synth.activations(seed, 1, k)[0]
+    sg = synth.signs(seed)
+    got = host(P.ptq1_matvec(to_dev(blocks), n, k, to_dev(x), to_dev(sg) if rot else None))
+    xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
+    assert rel_l2(got, oracle.matvec(blocks, n, k, xr)) <= TOL_FP32
+
+
+def test_matvec_residual_and_special_cases():
+    n, k = 96, 2048
+    x = synth.activations(4, 1, k)[0]
+    sg = synth.signs(4)
+    res = synth.gauss(4, 77, n)
+    t, s = host_matrix(4, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    got = host(P.ptq1_matvec(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
+    ref = res + oracle.matvec(b, n, k, oracle.rotate(x, sg))
+    assert rel_l2(got, ref) <= TOL_FP32
+    # all-zero trits: exactly zero
+    z = oracle.pack(np.zeros((n, k), np.int8), s)
+    np.testing.assert_array_equal(host(P.ptq1_matvec(to_dev(z), n, k, to_dev(x), to_dev(sg))), 0.0)
+    # zero scales in one block column remove exactly that block
+    s2 = s.copy()
+    s2[:, 3] = 0
+    b2 = oracle.pack(t, s2)
+    got2 = host(P.ptq1_matvec(to_dev(b2), n, k, to_dev(x), None))
+    assert rel_l2(got2, oracle.matvec(b2, n, k, x)) <= TOL_FP32
+
+
+def test_matvec_repeat_and_deterministic():
+    """50 fresh inputs (a missing barrier shows as a sporadic failure), and
+    bitwise-identical results when the same call repeats."""
+    n, k = 1024, 1024
+    for it in range(50):
+        seed = 100 + it
+        t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+        b = oracle.pack(t, s)
+        x = synth.activations(seed, 1, k)[0]
+        sg = synth.signs(seed)
+        bd, xd, sd = to_dev(b), to_dev(x), to_dev(sg)
+        y1 = host(P.ptq1_matvec(bd, n, k, xd, sd))
+        y2 = host(P.ptq1_matvec(bd, n, k, xd, sd))
+        np.testing.assert_array_equal(y1, y2)
+        if it % 10 == 0 or it == 49:
+            assert rel_l2(y1, oracle.matvec(b, n, k, oracle.rotate(x, sg))) <= TOL_FP32, f"seed {seed}"
+
+
+def test_gate_up_full_shape():
+    """Decode gate+up at the 27B-like shape: x[5120] -> two 17408 x 5120."""
+    d, f, seed = 5120, 17408, 1
+    tg, sg_ = host_matrix(seed, synth.S_GATE_TRITS, synth.S_GATE_SCALES, f, d)
+    tu, su = host_matrix(seed, synth.S_UP_TRITS, synth.S_UP_SCALES, f, d)
+    bg, bu = oracle.pack(tg, sg_), oracle.pack(tu, su)
+    del tg, tu
+    x = synth.activations(seed, 1, d)[0]
+    s = synth.signs(seed)
+    g, u = P.ptq1_gate_up(to_dev(bg), to_dev(bu), f, d, to_dev(x), to_dev(s))
+    xr = oracle.rotate(x, s)
+    assert rel_l2(host(g), oracle.matvec(bg, f, d, xr)) <= TOL_FP32
+    assert rel_l2(host(u), oracle.matvec(bu, f, d, xr)) <= TOL_FP32
+
+
+def test_swiglu():
+    g = synth.gauss(5, 1, 17408) * np.float32(3.0)
+    u = synth.gauss(5, 2, 17408)
+    g[:4] = [0.0, 30.0, -30.0, -88.0]
+    got = host(P.ptq1_swiglu(to_dev(g), to_dev(u)))
+    assert rel_l2(got, oracle.swiglu(g, u)) <= TOL_FP32
+
+
+# ----------------------------------------------------------------- GEMM ----
+
+@pytest.mark.parametrize("m,n,k,rot", [(1, 300, 1024, True), (2, 300, 1024, True), (8, 300, 2048, True),
+                                       (37, 300, 1024, True), (129, 200, 1024, True), (5, 130, 384, False)])
+def test_gemm_small(m, n, k, rot):
+    seed = 3
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    x = synth.activations(seed, m, k)
+    sg = synth.signs(seed)
+    got = host(P.ptq1_gemm(to_dev(b), n, k, to_dev(x), to_dev(sg) if rot else None))
+    xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
+    assert got.shape == (m, n)
+    assert rel_l2(got, oracle.gemm(b, n, k, xr)) <= TOL_BF16
+
+
+@pytest.fixture(scope="module")
+def prefill_weights():
+    n, k, seed = 17408, 5120, 3
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    return b, to_dev(b)
+
+
+@pytest.mark.parametrize("m", [128, 256, 512])
+def test_gemm_prefill_full_shape(m, prefill_weights):
+    """Prefill at M x 5120 -> 17408: every output computed on the GPU, 160
+    sampled weight rows (incl. the first and last) checked against the oracle."""
+    n, k, seed = 17408, 5120, 3
+    b, bd = prefill_weights
+    x = synth.activations(seed, m, k)
+    sg = synth.signs(seed)
+    got = host(P.ptq1_gemm(bd, n, k, to_dev(x), to_dev(sg)))
+    assert np.all(np.isfinite(got))
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed + m, 158, n)])).astype(np.int64)
+    ref = oracle.gemm(b, n, k, oracle.rotate(x, sg), rows=rows)
+    assert rel_l2(got[:, rows], ref) <= TOL_BF16
+
+
+# ------------------------------------------------------------ FFN block ----
+
+def _ffn_host(seed, d, f, layer=0):
+    mats = []
+    for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, f, d),
+                         (synth.S_UP_TRITS, synth.S_UP_SCALES, f, d),
+                         (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, d, f)):
+        t, s = host_matrix(seed, synth.layer_stream(tr, layer), synth.layer_stream(sc, layer), n, k)
+        mats.append(oracle.pack(t, s))
+    return mats
+
+
+@pytest.mark.parametrize("m,d,f,eps", [(1, 1024, 2048, 1e-6), (1, 2048, 1024, 0.0), (2, 1024, 2048, 1e-6),
+                                       (3, 1024, 3072, 0.0), (8, 1024, 2048, 1e-6)])
+def test_ffn_block_small(m, d, f, eps):
+    seed = 4
+    wg, wu, wd = _ffn_host(seed, d, f)
+    x = synth.activations(seed, m, d)
+    s = synth.signs(seed)
+    got = host(P.ptq1_ffn_block(to_dev(x), to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, eps))
+    ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, eps)
+    assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+
+
+def test_ffn_block_in_place():
+    d, f, seed = 1024, 2048, 6
+    wg, wu, wd = _ffn_host(seed, d, f)
+    s = synth.signs(seed)
+    for m in (1, 4):
+        x = synth.activations(seed, m, d)
+        xd = to_dev(x)
+        P.ptq1_ffn_block(xd, to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, 1e-6, out=xd)
+        ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
+        assert rel_l2(host(xd), ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_ffn_block_full_shape(m):
+    """One 27B-shaped block (d = 5120, f = 17408) with the RMS scale."""
+    d, f, seed = 5120, 17408, 4
+    wg, wu, wd = _ffn_host(seed, d, f)
+    x = synth.activations(seed, m, d)
+    s = synth.signs(seed)
+    got = host(P.ptq1_ffn_block(to_dev(x), to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, 1e-6))
+    ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
+    assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
