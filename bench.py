@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Throughput of the PTQ1_0 ternary linear layer on one MI355X.
+
+Step (the headline): one batch-1 decode token through one 27B-shaped
+feed-forward block, i.e. the whole decode hot path:
+    embedding row 248320 x 5120 -> unrotate (hadamard_unrotate_rows)
+    x[5120] -> rotate -> fused gate+up 5120 -> 2 x 17408  (ptq1_ffn_block, m = 1)
+            -> SwiGLU -> rotate -> down 17408 -> 5120 + residual
+Weights rotate over WEIGHT_SETS independent sets (936 MB, beyond the 256 MB
+Infinity Cache) so every step streams its 58.5 MB of PTQ1_0 blocks from HBM.
+value = algorithmic bytes per step / step time (decode matvec GB/s).
+
+Also reported (breakdown): cold gate+up alone, cold down alone, the hot
+1024 x 1024 matvec, the prefill GEMM at M = 128 / 256 / 512 (TFLOP/s), and
+the 64-layer FFN stack at batch 1 and 8 (layers/s); the fp64 oracle timed
+on the host's cores on a bounded sample (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+D, F, VOCAB, LAYERS = 5120, 17408, 248320, 64
+WEIGHT_SETS = 16
+BYTES_PER_WEIGHT = 28 / 128    # one PTQ1_0 block = 28 B per 128 weights
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def packed(n, k):
+    return n * (k // 128) * 28
+
+
+# algorithmic bytes (what the method must move; fp32 activations)
+GATE_UP_BYTES = 2 * packed(F, D) + 4 * D + 2 * 4 * F          # weights, x in, g & u out
+DOWN_BYTES = packed(D, F) + 4 * F + 4 * D + 4 * D             # weights, h in, residual in, out
+SWIGLU_BYTES = 3 * 4 * F                                      # g, u in, h out
+EMBED_BYTES = 2 * 4 * D                                       # one row in, one row out
+STEP_BYTES = GATE_UP_BYTES + SWIGLU_BYTES + DOWN_BYTES + EMBED_BYTES
+LAYER_WEIGHT_BYTES = 3 * packed(F, D)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--quick", action="store_true", help="headline only (no breakdown)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded path is a "
+              "design note, not built", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import synth.device as sdev
+    import ternary_weight_ptq1_amd as P
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    P.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps  # ms per call
+
+    def weight_set(seed, layer):
+        ls = synth.layer_stream
+        out = []
+        for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
+                             (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
+                             (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F)):
+            t = sdev.trits(seed, ls(tr, layer), n, k, device=dev)
+            s = sdev.scales(seed, ls(sc, layer), n, k // 128, device=dev)
+            out.append(P.ptq1_pack(t, s))
+            del t, s
+        return out
+
+    log("bench: generating inputs")
+    seed = 1
+    signs = torch.from_numpy(synth.signs(seed)).to(dev)
+    sets = [weight_set(seed, L) for L in range(WEIGHT_SETS)]
+    table = sdev.gauss(2, synth.S_TABLE, VOCAB * D, device=dev).view(VOCAB, D)
+    ids = torch.from_numpy(synth.token_ids(2, 4096, VOCAB)).to(dev)
+    emb = torch.empty((1, D), dtype=torch.float32, device=dev)
+    x_out = torch.empty(D, dtype=torch.float32, device=dev)
+    ws = torch.zeros(P.workspace_bytes("ffn", 1, D, F), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        W = sets[i % WEIGHT_SETS]
+        P.hadamard_unrotate_rows(table, signs, ids=ids[i % 4096:i % 4096 + 1], out=emb)
+        P.ptq1_ffn_block(emb, W[0], W[1], W[2], signs, D, F, rms_eps=1e-6, out=x_out, ws=ws)
+
+    log("bench: headline step")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: the fused gate+up decode matvec (cold), timed alone on the same stream
+    ws_gu = torch.zeros(P.workspace_bytes("gate_up", F, D), dtype=torch.uint8, device=dev)
+    xg = torch.from_numpy(synth.activations(seed, 1, D)[0]).to(dev)
+    g_buf = torch.empty(F, dtype=torch.float32, device=dev)
+    u_buf = torch.empty(F, dtype=torch.float32, device=dev)
+
+    def gate_up(i):
+        W = sets[i % WEIGHT_SETS]
+        P.ptq1_gate_up(W[0], W[1], F, D, xg, signs, g=g_buf, u=u_buf, ws=ws_gu)
+
+    ms_gu = timed(gate_up, max(args.steps, 100), args.warmup)
+    gu_gbs = GATE_UP_BYTES / (ms_gu * 1e-3) / 1e9
+
+    breakdown = {"gate_up_cold": {"us": ms_gu * 1e3, "GB/s": gu_gbs, "bytes": GATE_UP_BYTES}}
+    if not args.quick:
+        log("bench: breakdown")
+        ws_dn = torch.zeros(P.workspace_bytes("matvec", D, F), dtype=torch.uint8, device=dev)
+        h = torch.from_numpy(synth.gauss(seed, 99, F)).to(dev)
+        y = torch.empty(D, dtype=torch.float32, device=dev)
+
+        def down(i):
+            W = sets[i % WEIGHT_SETS]
+            P.ptq1_matvec(W[2], D, F, h, signs, residual=xg, out=y, ws=ws_dn)
+
+        ms_dn = timed(down, 200, 20)
+        breakdown["down_cold"] = {"us": ms_dn * 1e3, "GB/s": DOWN_BYTES / (ms_dn * 1e-3) / 1e9,
+                                  "bytes": DOWN_BYTES}
+
+        def unrot(i):
+            P.hadamard_unrotate_rows(table, signs, ids=ids[i % 4096:i % 4096 + 1], out=emb)
+
+        breakdown["embed_unrotate_row"] = {"us": timed(unrot, 200, 20) * 1e3}
+
+        # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
+        w0 = P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024), sdev.scales(0, synth.S_W_SCALES, 1024, 8))
+        x0 = torch.from_numpy(synth.activations(0, 1, 1024)[0]).to(dev)
+        s0 = torch.from_numpy(synth.signs(0)).to(dev)
+        ws0 = torch.zeros(P.workspace_bytes("matvec", 1024, 1024), dtype=torch.uint8, device=dev)
+        y0 = torch.empty(1024, dtype=torch.float32, device=dev)
+        ms0 = timed(lambda i: P.ptq1_matvec(w0, 1024, 1024, x0, s0, out=y0, ws=ws0), 500, 50)
+        breakdown["matvec_1024_hot"] = {"us": ms0 * 1e3}
+
+        # prefill GEMM (configuration 3)
+        wq = P.ptq1_pack(sdev.trits(3, synth.S_W_TRITS, F, D), sdev.scales(3, synth.S_W_SCALES, F, D // 128))
+        gemm = {}
+        for m in (128, 256, 512):
+            xm = torch.from_numpy(synth.activations(3, m, D)).to(dev)
+            ym = torch.empty((m, F), dtype=torch.float32, device=dev)
+            wsm = torch.zeros(P.workspace_bytes("gemm", m, F, D), dtype=torch.uint8, device=dev)
+            ms = timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 5)
+            gemm[f"M{m}"] = {"us": ms * 1e3, "TFLOP/s": 2.0 * m * F * D / (ms * 1e-3) / 1e12,
+                             "mfma_frac": 2.0 * m * F * D / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        breakdown["prefill_gemm"] = gemm
+
+        # 64-layer FFN stack (configuration 4): 3.74 GB of weights, cold by construction
+        del sets
+        torch.cuda.empty_cache()
+        stack = [weight_set(4, L) for L in range(LAYERS)]
+        stk = {}
+        for m in (1, 8):
+            xs = torch.from_numpy(synth.activations(4, m, D)).to(dev)
+            wss = torch.zeros(P.workspace_bytes("ffn", m, D, F), dtype=torch.uint8, device=dev)
+            xa = xs.clone()
+
+            def run_stack(i):
+                for L in range(LAYERS):
+                    W = stack[L]
+                    P.ptq1_ffn_block(xa, W[0], W[1], W[2], signs, D, F, rms_eps=1e-6, out=xa, ws=wss)
+
+            ms = timed(run_stack, 5, 1)
+            stk[f"M{m}"] = {"ms_per_stack": ms, "us_per_layer": ms * 1e3 / LAYERS,
+                            "layers_per_s": LAYERS / (ms * 1e-3),
+                            "weight_GB/s": LAYERS * LAYER_WEIGHT_BYTES / (ms * 1e-3) / 1e9,
+                            "finite": bool(torch.isfinite(xa).all().item())}
+        breakdown["ffn_stack_64"] = stk
+        del stack
+
+    cpu = None
+    if not args.no_cpu:
+        log("bench: oracle CPU baseline")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "decode matvec GB/s (27B-shaped FFN block, batch 1, cold weights)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode step: unrotate 1 row of a 248320x5120 fp32 table, then one "
+                               "FFN block x[5120] -> rotate -> gate+up 5120->2x17408 (PTQ1_0) -> "
+                               "SwiGLU -> rotate -> down 17408->5120 + residual, batch 1, RMS scale on, "
+                               f"{WEIGHT_SETS} rotating weight sets",
+                   "d": D, "f": F, "batch": 1, "weight_sets": WEIGHT_SETS,
+                   "step_bytes": STEP_BYTES, "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gate+up decode matvec (ptq1_gate_up, cold)",
+                     "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": GATE_UP_BYTES, "us_per_launch": round(ms_gu * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline():
+    """The fp64 oracle (as it stands) on this host's cores: one full-shape
+    FFN block at batch 1 (x[5120], 17408 x 5120 gate/up, 5120 x 17408 down),
+    repeated for about 10 s; same algorithmic bytes as the GPU step."""
+    import oracle
+    import synth
+
+    seed = 1
+    mats = []
+    for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
+                         (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
+                         (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F)):
+        mats.append(oracle.pack(synth.trits(seed, tr, n, k), synth.scales(seed, sc, n, k // 128)))
+    s = synth.signs(seed)
+    row = synth.table_rows(2, synth.S_TABLE, np.array([7]), D)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        e = oracle.embedding_unrotate(row, s)
+        oracle.ffn_block(e, mats[0], mats[1], mats[2], s, D, F, 1e-6)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    return {"value": round(STEP_BYTES * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{reps} decode steps (1 embedding row + 1 full 5120/17408 FFN block, fp64) in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
