@@ -36,11 +36,16 @@
  *   - on any status other than PTQ1_OK nothing has been enqueued (except
  *     PTQ1_ERR_HIP, which reports a failed launch);
  *   - ptq1_last_error() then names the refused argument (thread-local);
- *   - the library keeps no global state and allocates no memory; calls that
- *     need scratch take a caller-owned workspace `ws` of at least the size
- *     the matching *_workspace_bytes() returns, 256-byte aligned, whose
- *     contents on entry are ignored; two calls in flight must not share a
- *     workspace;
+ *   - the library allocates no memory; calls that need scratch take a
+ *     caller-owned workspace `ws` of at least the size the matching
+ *     *_workspace_bytes() returns, 256-byte aligned.  A workspace must be
+ *     zero-filled once before its first use (hipMemset or a fill kernel):
+ *     its first 256 KB hold per-row-group arrival counters that every
+ *     completed call leaves at zero again, the rest is scratch, so one
+ *     workspace may serve calls of any shape and entry point.  Calls that
+ *     share a workspace must be ordered on one stream; two calls in flight
+ *     at once must not share one.  The decode calls (matvec, gate_up,
+ *     ffn_block with m = 1) take at most 2^20 output rows per matrix;
  *   - `float *` buffers must be 16-byte aligned, `blocks` 16-byte aligned;
  *   - sizes are int64_t; products are checked for overflow.
  */
@@ -127,16 +132,26 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
                                    float *out, hipStream_t stream);
 
 /* Batch-1 decode matvec ("What Ferrox does with it": the decode matvec reads
- * every block once and peels trits on the float pipeline).
+ * every block once).
  *   y[r] = (residual ? residual[r] : 0) + sum_c W[r][c] * xr[c],
  *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
  *   blocks  packed [n][k]; x fp32 [k]; residual fp32 [n] or NULL; y fp32 [n]
  *   (y may equal residual, must not overlap x or blocks).
+ * One launch; trits are decoded through a per-slice table of byte-position x
+ * byte-value partial dot products built from xr, fp32 throughout.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k);
 ptq1_status ptq1_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
                         const float *signs1024, const float *residual, float *y, void *ws,
                         size_t ws_bytes, hipStream_t stream);
+
+/* The same matvec with every trit peeled on the float pipeline as the page
+ * describes ("What Ferrox does with it": floor(3^(n+1) u) - 3 floor(3^n u)),
+ * one lane per output row.  Same arguments, results and workspace size as
+ * ptq1_matvec; kept as the reference decode of the format. */
+ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+                                   const float *signs1024, const float *residual, float *y, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* Gate and up projections of one token in one pass over a shared rotated
  * input ("Speed, and where it goes": paired projections fused into one GPU

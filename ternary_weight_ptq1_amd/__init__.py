@@ -50,6 +50,7 @@ _SIGS = {
     "hadamard_unrotate_rows": ([p, i64, i64, p, i64, p, p, p], C.c_int),
     "ptq1_matvec_workspace_bytes": ([i64, i64], sz),
     "ptq1_matvec": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
+    "ptq1_matvec_float_peel": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
     "ptq1_gate_up_workspace_bytes": ([i64, i64], sz),
     "ptq1_gate_up": ([p, p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
     "ptq1_swiglu": ([p, p, p, i64, p], C.c_int),
@@ -112,7 +113,7 @@ def _ws(nbytes: int, device, ws):
         return None, 0
     if ws is not None and ws.numel() >= nbytes:
         return ws, ws.numel()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 # ------------------------------------------------------------------ codec ----
@@ -191,16 +192,21 @@ def hadamard_unrotate_rows(table: torch.Tensor, signs1024: torch.Tensor, ids: to
 
 def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
                 residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                ws: torch.Tensor | None = None, stream=None, fn: str = "ptq1_matvec") -> torch.Tensor:
+    """y = residual + W R x.  ws (if given) must have been zero-filled once."""
     _dev(blocks, "blocks", torch.uint8)
     _dev(x, "x", torch.float32)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=x.device)
     _dev(out, "y", torch.float32)
     ws, wsb = _ws(lib().ptq1_matvec_workspace_bytes(n, k), x.device, ws)
-    _check("ptq1_matvec", lib().ptq1_matvec(_ptr(blocks), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
-                                            _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    _check(fn, getattr(lib(), fn)(_ptr(blocks), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
+                                  _ptr(out), _ptr(ws), wsb, _stream(stream)))
     return out
+
+
+def ptq1_matvec_float_peel(blocks, n, k, x, signs1024, residual=None, out=None, ws=None, stream=None):
+    return ptq1_matvec(blocks, n, k, x, signs1024, residual, out, ws, stream, fn="ptq1_matvec_float_peel")
 
 
 def ptq1_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, f: int, d: int, x: torch.Tensor,

@@ -38,6 +38,17 @@ hipError_t launch_reduce_gate_up(const float *part, int64_t f, int64_t nseg, flo
                                  hipStream_t s);
 hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t s);
 
+// Lookup-table decode matvec (one launch): one matrix (nmat = 1: y =
+// residual + W xr) or two (nmat = 2: g, u = a W0 xr, a W1 xr; h = silu(g) u,
+// a = RMS scale of x_rms or 1).  part: lut_part_floats floats; cnt:
+// lut_counter_words zero words (left zero on completion).
+size_t lut_part_floats(int64_t n, int nmat, int64_t k);
+size_t lut_counter_words(int64_t n);
+hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
+                             const float *x, const float *signs, float *part, uint32_t *cnt,
+                             const float *residual, float *y, float *g, float *u, float *h,
+                             const float *x_rms, int64_t d_rms, float rms_eps, hipStream_t s);
+
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
 // xb [m_pad][k] bf16 = bf16(R (a * x)); rows >= m zero.  a = RMS scale if
 // rms_eps > 0.  When g/u are given instead of x, the input is silu(g) * u.

@@ -187,37 +187,94 @@ def test_unrotate_rows_full_table():
 
 # --------------------------------------------------------------- matvec ----
 
+MATVECS = ["ptq1_matvec", "ptq1_matvec_float_peel"]
+
+
+@pytest.mark.parametrize("fn", MATVECS)
 @pytest.mark.parametrize("n,k,seed,rot", [(1024, 1024, 0, True), (300, 384, 1, False), (257, 3072, 2, True),
-                                          (1, 128, 3, False), (5120, 17408, 2, True)])
-def test_matvec(n, k, seed, rot):
+                                          (1, 128, 3, False), (17, 640, 4, False), (5120, 17408, 2, True)])
+def test_matvec(fn, n, k, seed, rot):
     t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
     blocks = oracle.pack(t, s)
     x = synth.activations(seed, 1, k)[0]
     sg = synth.signs(seed)
-    got = host(P.ptq1_matvec(to_dev(blocks), n, k, to_dev(x), to_dev(sg) if rot else None))
+    got = host(getattr(P, fn)(to_dev(blocks), n, k, to_dev(x), to_dev(sg) if rot else None))
     xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
     assert rel_l2(got, oracle.matvec(blocks, n, k, xr)) <= TOL_FP32
 
 
-def test_matvec_residual_and_special_cases():
+@pytest.mark.parametrize("fn", MATVECS)
+def test_matvec_residual_and_special_cases(fn):
+    mv = getattr(P, fn)
     n, k = 96, 2048
     x = synth.activations(4, 1, k)[0]
     sg = synth.signs(4)
     res = synth.gauss(4, 77, n)
     t, s = host_matrix(4, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
     b = oracle.pack(t, s)
-    got = host(P.ptq1_matvec(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
+    got = host(mv(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
     ref = res + oracle.matvec(b, n, k, oracle.rotate(x, sg))
     assert rel_l2(got, ref) <= TOL_FP32
+    # in place on the residual
+    rd = to_dev(res)
+    mv(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=rd, out=rd)
+    assert rel_l2(host(rd), ref) <= TOL_FP32
     # all-zero trits: exactly zero
     z = oracle.pack(np.zeros((n, k), np.int8), s)
-    np.testing.assert_array_equal(host(P.ptq1_matvec(to_dev(z), n, k, to_dev(x), to_dev(sg))), 0.0)
+    np.testing.assert_array_equal(host(mv(to_dev(z), n, k, to_dev(x), to_dev(sg))), 0.0)
     # zero scales in one block column remove exactly that block
     s2 = s.copy()
     s2[:, 3] = 0
     b2 = oracle.pack(t, s2)
-    got2 = host(P.ptq1_matvec(to_dev(b2), n, k, to_dev(x), None))
+    got2 = host(mv(to_dev(b2), n, k, to_dev(x), None))
     assert rel_l2(got2, oracle.matvec(b2, n, k, x)) <= TOL_FP32
+
+
+def test_shared_workspace_across_calls():
+    """One zero-filled workspace reused by 60 calls of mixed shapes and entry
+    points: the per-group arrival counters must return to zero after every
+    call, or a later call would finish a row group early."""
+    shapes = [(1024, 1024, True), (300, 384, False), (5120, 3072, True), (33, 1024, True), (2048, 512, False)]
+    big = max(P.workspace_bytes("matvec", n, k) for n, k, _ in shapes)
+    big = max(big, P.workspace_bytes("gate_up", 1040, 2048), P.workspace_bytes("gemm", 40, 1024, 1024))
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    cases = []
+    for i, (n, k, rot) in enumerate(shapes):
+        t, s = host_matrix(20 + i, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+        b = oracle.pack(t, s)
+        x = synth.activations(20 + i, 1, k)[0]
+        sg = synth.signs(20 + i)
+        ref = oracle.matvec(b, n, k, oracle.rotate(x, sg) if rot else x)
+        cases.append((to_dev(b), n, k, to_dev(x), to_dev(sg) if rot else None, ref))
+    tg, sgl = host_matrix(30, synth.S_GATE_TRITS, synth.S_GATE_SCALES, 1040, 2048)
+    tu, su = host_matrix(30, synth.S_UP_TRITS, synth.S_UP_SCALES, 1040, 2048)
+    bg, bu = oracle.pack(tg, sgl), oracle.pack(tu, su)
+    xg = synth.activations(30, 1, 2048)[0]
+    s30 = synth.signs(30)
+    xr = oracle.rotate(xg, s30)
+    rg, ru = oracle.matvec(bg, 1040, 2048, xr), oracle.matvec(bu, 1040, 2048, xr)
+    dg, du, dx, ds = to_dev(bg), to_dev(bu), to_dev(xg), to_dev(s30)
+    xm = synth.activations(31, 40, 1024)
+    b0, n0, k0, _, s0, _ = cases[0]
+    rm = oracle.gemm(oracle.pack(*host_matrix(20, synth.S_W_TRITS, synth.S_W_SCALES, 1024, 1024)), 1024, 1024,
+                     oracle.rotate(xm, synth.signs(20)))
+    dxm = to_dev(xm)
+    for it in range(60):
+        if it % 6 == 5:
+            g, u = P.ptq1_gate_up(dg, du, 1040, 2048, dx, ds, ws=ws)
+            assert rel_l2(host(g), rg) <= TOL_FP32 and rel_l2(host(u), ru) <= TOL_FP32, f"iteration {it}"
+        elif it % 7 == 3:
+            b, n, k, x, sg, ref = cases[it % len(cases)]
+            y = P.ptq1_matvec_float_peel(b, n, k, x, sg, ws=ws)
+            assert rel_l2(host(y), ref) <= TOL_FP32, f"iteration {it} (float peel)"
+        elif it % 11 == 4:
+            y = P.ptq1_gemm(b0, n0, k0, dxm, s0, ws=ws)
+            assert rel_l2(host(y), rm) <= TOL_BF16, f"iteration {it} (gemm)"
+        else:
+            b, n, k, x, sg, ref = cases[it % len(cases)]
+            y = P.ptq1_matvec(b, n, k, x, sg, ws=ws)
+            assert rel_l2(host(y), ref) <= TOL_FP32, f"iteration {it} shape {(n, k)}"
+
 
 
 def test_matvec_repeat_and_deterministic():
@@ -236,6 +293,20 @@ def test_matvec_repeat_and_deterministic():
         np.testing.assert_array_equal(y1, y2)
         if it % 10 == 0 or it == 49:
             assert rel_l2(y1, oracle.matvec(b, n, k, oracle.rotate(x, sg))) <= TOL_FP32, f"seed {seed}"
+
+
+@pytest.mark.parametrize("f,d,rot", [(100, 1024, True), (17, 384, False)])
+def test_gate_up_small(f, d, rot):
+    seed = 8
+    tg, sg_ = host_matrix(seed, synth.S_GATE_TRITS, synth.S_GATE_SCALES, f, d)
+    tu, su = host_matrix(seed, synth.S_UP_TRITS, synth.S_UP_SCALES, f, d)
+    bg, bu = oracle.pack(tg, sg_), oracle.pack(tu, su)
+    x = synth.activations(seed, 1, d)[0]
+    s = synth.signs(seed)
+    g, u = P.ptq1_gate_up(to_dev(bg), to_dev(bu), f, d, to_dev(x), to_dev(s) if rot else None)
+    xr = oracle.rotate(x, s) if rot else x
+    assert rel_l2(host(g), oracle.matvec(bg, f, d, xr)) <= TOL_FP32
+    assert rel_l2(host(u), oracle.matvec(bu, f, d, xr)) <= TOL_FP32
 
 
 def test_gate_up_full_shape():
