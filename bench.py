@@ -103,7 +103,7 @@ def main() -> int:
                              (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F)):
             t = sdev.trits(seed, ls(tr, layer), n, k, device=dev)
             s = sdev.scales(seed, ls(sc, layer), n, k // 128, device=dev)
-            out.append(P.ptq1_pack(t, s))
+            out.append(P.ptq1_tile(P.ptq1_pack(t, s), n, k))
             del t, s
         return out
 
@@ -172,7 +172,8 @@ def main() -> int:
         breakdown["embed_unrotate_row"] = {"us": timed(unrot, 200, 20) * 1e3}
 
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
-        w0 = P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024), sdev.scales(0, synth.S_W_SCALES, 1024, 8))
+        w0 = P.ptq1_tile(P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024),
+                                     sdev.scales(0, synth.S_W_SCALES, 1024, 8)), 1024, 1024)
         x0 = torch.from_numpy(synth.activations(0, 1, 1024)[0]).to(dev)
         s0 = torch.from_numpy(synth.signs(0)).to(dev)
         ws0 = torch.zeros(P.workspace_bytes("matvec", 1024, 1024), dtype=torch.uint8, device=dev)
@@ -181,7 +182,8 @@ def main() -> int:
         breakdown["matvec_1024_hot"] = {"us": ms0 * 1e3}
 
         # prefill GEMM (configuration 3)
-        wq = P.ptq1_pack(sdev.trits(3, synth.S_W_TRITS, F, D), sdev.scales(3, synth.S_W_SCALES, F, D // 128))
+        wq = P.ptq1_tile(P.ptq1_pack(sdev.trits(3, synth.S_W_TRITS, F, D),
+                                     sdev.scales(3, synth.S_W_SCALES, F, D // 128)), F, D)
         gemm = {}
         for m in (128, 256, 512):
             xm = torch.from_numpy(synth.activations(3, m, D)).to(dev)

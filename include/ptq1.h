@@ -22,6 +22,16 @@
  * A packed matrix [n][k] is row-major: row r is k/128 consecutive blocks.
  * Weight (r, c) = scale(r, c/128) * trit(r, c).
  *
+ * Tiled layout (this library's device layout, not part of the format): the
+ * same 28-byte blocks reordered so that each tile of 32 rows x 2 blocks
+ * (256 weights of K) is 1792 contiguous bytes.  With T = ceil(k/256) tiles
+ * per 32-row band, tile (g, t) starts at byte (g*T + t) * 1792 and holds
+ * block j = 2t + b of row r = 32g + i at byte (2i + b) * 28 of the tile;
+ * places past the matrix (r >= n or j >= k/128) hold zero bytes.  The
+ * matvec, gate/up, GEMM and feed-forward calls read weights in this layout
+ * (ptq1_tile makes it from a packed matrix, once, at load time); pack,
+ * dequant and the float-peel matvec use the packed layout.
+ *
  * Rotation R of a row x of width k (k a multiple of 1024): every 1024-wide
  * chunk c becomes (1/32) H (s * c), with H the natural-order Sylvester
  * Hadamard matrix and s the 1024 signs (one vector for every chunk).
@@ -46,7 +56,7 @@
  *     share a workspace must be ordered on one stream; two calls in flight
  *     at once must not share one.  The decode calls (matvec, gate_up,
  *     ffn_block with m = 1) take at most 2^20 output rows per matrix;
- *   - `float *` buffers must be 16-byte aligned, `blocks` 16-byte aligned;
+ *   - `float *` buffers must be 16-byte aligned, weights 16-byte aligned;
  *   - sizes are int64_t; products are checked for overflow.
  */
 #ifndef PTQ1_H
@@ -64,6 +74,8 @@ extern "C" {
 #define PTQ1_TRIT_BYTES 26
 #define PTQ1_BLOCK_BYTES 28
 #define PTQ1_HADAMARD 1024
+#define PTQ1_TILE_ROWS 32
+#define PTQ1_TILE_BLOCKS 2
 
 typedef enum ptq1_status {
     PTQ1_OK = 0,
@@ -85,7 +97,8 @@ const char *ptq1_status_string(ptq1_status s);
 const char *ptq1_last_error(void);
 
 /* Copies the compiled geometry {weights per block, trit bytes, block bytes,
- * Hadamard width} into out[0..n) (n <= 4).  PTQ1_ERR_NULL / PTQ1_ERR_SHAPE. */
+ * Hadamard width, tile rows, tile blocks} into out[0..n) (n <= 6).
+ * PTQ1_ERR_NULL / PTQ1_ERR_SHAPE. */
 ptq1_status ptq1_geometry(int32_t *out, int32_t n);
 
 /* Bytes of a packed [n][k] matrix: n * (k/128) * 28, or -1 if n < 0, k < 0,
@@ -103,6 +116,18 @@ int64_t ptq1_packed_bytes(int64_t n, int64_t k);
  * Errors: NULL, SHAPE (k % 128), ALIGN (blocks), OVERFLOW. */
 ptq1_status ptq1_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k,
                       uint8_t *blocks, hipStream_t stream);
+
+/* Bytes of the tiled layout of an [n][k] matrix: ceil(n/32)*32 rows times
+ * ceil(k/256)*2 blocks of 28 bytes (equal to ptq1_packed_bytes when n % 32
+ * == 0 and k % 256 == 0), or -1 on a bad shape or overflow. */
+int64_t ptq1_tiled_bytes(int64_t n, int64_t k);
+
+/* Reorders a packed [n][k] matrix into the tiled layout described above
+ * (bytes of every block copied unchanged, padding written as zeros).
+ *   blocks  packed, ptq1_packed_bytes(n, k) bytes;
+ *   tiled   output, ptq1_tiled_bytes(n, k) bytes, must not overlap blocks.
+ * Errors: NULL, SHAPE (k % 128), ALIGN, ALIAS, OVERFLOW. */
+ptq1_status ptq1_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t stream);
 
 /* Codec decode ("What Ferrox does with it": digit n of u = b/256 read on the
  * float pipeline).  w [n][k] fp32 = binary16 scale * (digit - 1), exact.
@@ -135,20 +160,21 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
  * every block once).
  *   y[r] = (residual ? residual[r] : 0) + sum_c W[r][c] * xr[c],
  *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
- *   blocks  packed [n][k]; x fp32 [k]; residual fp32 [n] or NULL; y fp32 [n]
- *   (y may equal residual, must not overlap x or blocks).
+ *   tiled   [n][k] in the tiled layout; x fp32 [k]; residual fp32 [n] or
+ *   NULL; y fp32 [n] (y may equal residual, must not overlap x or tiled).
  * One launch; trits are decoded through a per-slice table of byte-position x
  * byte-value partial dot products built from xr, fp32 throughout.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k);
-ptq1_status ptq1_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                         const float *signs1024, const float *residual, float *y, void *ws,
                         size_t ws_bytes, hipStream_t stream);
 
 /* The same matvec with every trit peeled on the float pipeline as the page
  * describes ("What Ferrox does with it": floor(3^(n+1) u) - 3 floor(3^n u)),
- * one lane per output row.  Same arguments, results and workspace size as
- * ptq1_matvec; kept as the reference decode of the format. */
+ * one lane per output row, reading the packed (row-major) layout the page's
+ * kernel streams.  Same results and workspace size as ptq1_matvec, but
+ * `blocks` is packed [n][k], not tiled; kept as the page's own decode. */
 ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
                                    const float *signs1024, const float *residual, float *y, void *ws,
                                    size_t ws_bytes, hipStream_t stream);
@@ -156,7 +182,7 @@ ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, 
 /* Gate and up projections of one token in one pass over a shared rotated
  * input ("Speed, and where it goes": paired projections fused into one GPU
  * submission).
- *   w_gate, w_up  packed [f][d]; x fp32 [d]; g, u fp32 [f]:
+ *   w_gate, w_up  tiled [f][d]; x fp32 [d]; g, u fp32 [f]:
  *   g = W_gate R x, u = W_up R x (R skipped when signs1024 == NULL).
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_gate_up_workspace_bytes(int64_t f, int64_t d);
@@ -174,19 +200,20 @@ ptq1_status ptq1_swiglu(const float *g, const float *u, float *h, int64_t len, h
  *   signs1024 != NULL) and rounded to bf16 (nearest even); trits enter bf16
  *   MFMA exactly; each 128-weight block's partial sum is scaled by its fp16
  *   scale in fp32; accumulation is fp32.
- *   1 <= m <= 65536; k % 128 == 0 (k % 1024 == 0 with signs).
+ *   tiled [n][k] in the tiled layout; 1 <= m <= 65536; k % 128 == 0
+ *   (k % 1024 == 0 with signs).
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED (m). */
 size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
-ptq1_status ptq1_gemm(const uint8_t *blocks, int64_t n, int64_t k, const float *x, int64_t m,
+ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m,
                       const float *signs1024, float *y, void *ws, size_t ws_bytes,
                       hipStream_t stream);
 
 /* One feed-forward block on m tokens ("Speed, and where it goes": the whole
  * block -- rotation, gate, SwiGLU, down -- enqueued as one sequence):
  *   a     = (mean(x^2) + rms_eps)^(-1/2) per token if rms_eps > 0, else 1
- *   g, u  = a * (W_gate R x), a * (W_up R x)      (W_gate, W_up packed [f][d])
+ *   g, u  = a * (W_gate R x), a * (W_up R x)      (W_gate, W_up tiled [f][d])
  *   h     = silu(g) * u
- *   x_out = x + W_down R h                        (W_down packed [d][f])
+ *   x_out = x + W_down R h                        (W_down tiled [d][f])
  * m == 1 runs the fp32 matvec path, m >= 2 the bf16-MFMA GEMM path.
  * d % 1024 == 0, f % 1024 == 0; x_out may equal x.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED. */

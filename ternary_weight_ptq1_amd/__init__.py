@@ -23,6 +23,8 @@ BLOCK_WEIGHTS = 128
 TRIT_BYTES = 26
 BLOCK_BYTES = 28
 HADAMARD = 1024
+TILE_ROWS = 32
+TILE_BLOCKS = 2
 
 STATUS = {0: "PTQ1_OK", 1: "PTQ1_ERR_NULL", 2: "PTQ1_ERR_SHAPE", 3: "PTQ1_ERR_ALIGN",
           4: "PTQ1_ERR_OVERFLOW", 5: "PTQ1_ERR_UNSUPPORTED", 6: "PTQ1_ERR_WORKSPACE",
@@ -44,6 +46,8 @@ _SIGS = {
     "ptq1_last_error": ([], C.c_char_p),
     "ptq1_geometry": ([p, C.c_int32], C.c_int),
     "ptq1_packed_bytes": ([i64, i64], i64),
+    "ptq1_tiled_bytes": ([i64, i64], i64),
+    "ptq1_tile": ([p, i64, i64, p, p], C.c_int),
     "ptq1_pack": ([p, p, i64, i64, p, p], C.c_int),
     "ptq1_dequant": ([p, i64, i64, p, p], C.c_int),
     "hadamard_rotate": ([p, p, i64, i64, p, p], C.c_int),
@@ -118,9 +122,10 @@ def _ws(nbytes: int, device, ws):
 
 # ------------------------------------------------------------------ codec ----
 
-def ptq1_geometry() -> tuple[int, int, int, int]:
-    out = (C.c_int32 * 4)()
-    _check("ptq1_geometry", lib().ptq1_geometry(C.cast(out, p), 4))
+def ptq1_geometry() -> tuple[int, int, int, int, int, int]:
+    """(weights per block, trit bytes, block bytes, Hadamard width, tile rows, tile blocks)."""
+    out = (C.c_int32 * 6)()
+    _check("ptq1_geometry", lib().ptq1_geometry(C.cast(out, p), 6))
     return tuple(out)
 
 
@@ -138,6 +143,25 @@ def ptq1_pack(trits: torch.Tensor, scales_f16: torch.Tensor, out: torch.Tensor |
         out = torch.empty((n, (k // BLOCK_WEIGHTS) * BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
     _dev(out, "blocks", torch.uint8)
     _check("ptq1_pack", lib().ptq1_pack(_ptr(trits), _ptr(scales_f16), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def ptq1_tiled_bytes(n: int, k: int) -> int:
+    return lib().ptq1_tiled_bytes(n, k)
+
+
+def ptq1_tile(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Packed [n, k/128*28] uint8 -> the tiled device layout (flat uint8) the
+    matvec, gate/up, GEMM and feed-forward calls read."""
+    _dev(blocks, "blocks", torch.uint8)
+    nbytes = ptq1_tiled_bytes(n, k)
+    if nbytes < 0:
+        raise ValueError(f"bad shape [{n}][{k}]")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
+    _dev(out, "tiled", torch.uint8)
+    _check("ptq1_tile", lib().ptq1_tile(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
     return out
 
 
@@ -193,7 +217,8 @@ def hadamard_unrotate_rows(table: torch.Tensor, signs1024: torch.Tensor, ids: to
 def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
                 residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 ws: torch.Tensor | None = None, stream=None, fn: str = "ptq1_matvec") -> torch.Tensor:
-    """y = residual + W R x.  ws (if given) must have been zero-filled once."""
+    """y = residual + W R x, W tiled (ptq1_tile).  ws (if given) must have
+    been zero-filled once."""
     _dev(blocks, "blocks", torch.uint8)
     _dev(x, "x", torch.float32)
     if out is None:
@@ -206,6 +231,7 @@ def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024
 
 
 def ptq1_matvec_float_peel(blocks, n, k, x, signs1024, residual=None, out=None, ws=None, stream=None):
+    """The same matvec over the packed (row-major) layout, trits peeled on the float pipeline."""
     return ptq1_matvec(blocks, n, k, x, signs1024, residual, out, ws, stream, fn="ptq1_matvec_float_peel")
 
 

@@ -21,6 +21,8 @@ static_assert(PTQ1_BLOCK_WEIGHTS == ptq1::kBlockWeights, "public header and geom
 static_assert(PTQ1_TRIT_BYTES == ptq1::kTritBytes, "public header and geometry agree");
 static_assert(PTQ1_BLOCK_BYTES == ptq1::kBlockBytes, "public header and geometry agree");
 static_assert(PTQ1_HADAMARD == ptq1::kHadamard, "public header and geometry agree");
+static_assert(PTQ1_TILE_ROWS == ptq1::kTileRows, "public header and geometry agree");
+static_assert(PTQ1_TILE_BLOCKS == ptq1::kTileBlocks, "public header and geometry agree");
 
 namespace {
 
@@ -68,10 +70,11 @@ constexpr int64_t kMaxGridX = 2147483647;
 constexpr int64_t kMaxGridY = 65535;
 // Every workspace starts with a fixed counter region, so that calls of any
 // shape or entry point can share one zero-initialised workspace: the
-// lookup-table matvec keeps its per-16-row-group arrival counters there
+// lookup-table matvec keeps its per-32-row-group arrival counters there
 // (left at zero after each call) and nothing else ever writes it.
 constexpr size_t kCounterBytes = 256 * 1024;
-constexpr int64_t kMaxLutRows = static_cast<int64_t>(kCounterBytes / sizeof(uint32_t)) * 16;
+constexpr int64_t kMaxLutRows = int64_t{1} << 20;  // one counter per 32 rows: 32768 of 65536 words
+static_assert(kMaxLutRows / 32 <= static_cast<int64_t>(kCounterBytes / sizeof(uint32_t)), "counter region");
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -85,9 +88,25 @@ int64_t packed_bytes(int64_t n, int64_t k)
     return total;
 }
 
-// Shared validation of a packed matrix argument.
+// Tiled-layout bytes with every check; -1 on a bad shape or overflow.
+int64_t tiled_bytes(int64_t n, int64_t k)
+{
+    if (n < 0 || k < 0 || k % ptq1::kBlockWeights != 0) return -1;
+    const int64_t bands = n / ptq1::kTileRows + (n % ptq1::kTileRows != 0);
+    const int64_t nb = k / ptq1::kBlockWeights;
+    const int64_t tiles_k = nb / ptq1::kTileBlocks + (nb % ptq1::kTileBlocks != 0);
+    int64_t tiles, total;
+    if (!mul_ok(bands, tiles_k, &tiles)) return -1;
+    if (!mul_ok(tiles, ptq1::kTileBytes, &total)) return -1;
+    return total;
+}
+
+// The lookup-table matvec addresses a tiled matrix with 32-bit offsets.
+constexpr int64_t kMaxLutMatrixBytes = int64_t{1} << 31;
+
+// Shared validation of a packed (tiled = false) or tiled matrix argument.
 ptq1_status check_matrix(const uint8_t *blocks, const char *name, int64_t n, int64_t k,
-                         bool need_1024, int64_t *bytes)
+                         bool need_1024, int64_t *bytes, bool tiled = false)
 {
     if (n < 0) return fail(PTQ1_ERR_SHAPE, "%s: n = %lld is negative", name, (long long)n);
     if (k < 0) return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is negative", name, (long long)k);
@@ -97,9 +116,9 @@ ptq1_status check_matrix(const uint8_t *blocks, const char *name, int64_t n, int
     if (need_1024 && k % ptq1::kHadamard != 0)
         return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is not a multiple of %d (rotation chunks)", name,
                     (long long)k, ptq1::kHadamard);
-    const int64_t b = packed_bytes(n, k);
-    if (b < 0) return fail(PTQ1_ERR_OVERFLOW, "%s: packed size of [%lld][%lld] overflows", name,
-                           (long long)n, (long long)k);
+    const int64_t b = tiled ? tiled_bytes(n, k) : packed_bytes(n, k);
+    if (b < 0 || packed_bytes(n, k) < 0)
+        return fail(PTQ1_ERR_OVERFLOW, "%s: size of [%lld][%lld] overflows", name, (long long)n, (long long)k);
     if (b > 0 && blocks == nullptr) return fail(PTQ1_ERR_NULL, "%s is NULL", name);
     if (b > 0 && !aligned(blocks, kAlign)) return fail(PTQ1_ERR_ALIGN, "%s is not 16-byte aligned", name);
     *bytes = b;
@@ -224,13 +243,26 @@ const char *ptq1_last_error(void) { return g_last_error.c_str(); }
 ptq1_status ptq1_geometry(int32_t *out, int32_t n)
 {
     if (out == nullptr) return fail(PTQ1_ERR_NULL, "out is NULL");
-    if (n < 0 || n > 4) return fail(PTQ1_ERR_SHAPE, "n = %d outside [0, 4]", n);
-    const int32_t g[4] = {ptq1::kBlockWeights, ptq1::kTritBytes, ptq1::kBlockBytes, ptq1::kHadamard};
+    if (n < 0 || n > 6) return fail(PTQ1_ERR_SHAPE, "n = %d outside [0, 6]", n);
+    const int32_t g[6] = {ptq1::kBlockWeights, ptq1::kTritBytes, ptq1::kBlockBytes,
+                          ptq1::kHadamard,     ptq1::kTileRows,  ptq1::kTileBlocks};
     for (int32_t i = 0; i < n; ++i) out[i] = g[i];
     return ok();
 }
 
 int64_t ptq1_packed_bytes(int64_t n, int64_t k) { return packed_bytes(n, k); }
+
+int64_t ptq1_tiled_bytes(int64_t n, int64_t k) { return packed_bytes(n, k) < 0 ? -1 : tiled_bytes(n, k); }
+
+ptq1_status ptq1_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t stream)
+{
+    int64_t pb, tb;
+    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, false, &pb));
+    PTQ1_TRY(check_matrix(tiled, "tiled", n, k, false, &tb, true));
+    if (tb == 0) return ok();
+    if (overlaps(tiled, tb, blocks, pb)) return fail(PTQ1_ERR_ALIAS, "tiled overlaps blocks");
+    return hip_status(ptq1::launch_tile(blocks, n, k, tiled, stream), "ptq1_tile");
+}
 
 ptq1_status ptq1_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k,
                       uint8_t *blocks, hipStream_t stream)
@@ -315,11 +347,11 @@ namespace {
 
 ptq1_status check_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
                          const float *signs1024, const float *residual, float *y, void *ws,
-                         size_t ws_bytes, const char *fn, bool *empty)
+                         size_t ws_bytes, const char *fn, bool tiled, bool *empty)
 {
     int64_t wb, xb, yb;
     *empty = false;
-    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, signs1024 != nullptr, &wb));
+    PTQ1_TRY(check_matrix(blocks, tiled ? "tiled" : "blocks", n, k, signs1024 != nullptr, &wb, tiled));
     PTQ1_TRY(check_floats(y, "y", n, &yb));
     if (n == 0) {
         *empty = true;
@@ -336,27 +368,28 @@ ptq1_status check_matvec(const uint8_t *blocks, int64_t n, int64_t k, const floa
     const size_t need = ptq1_matvec_workspace_bytes(n, k);
     PTQ1_TRY(check_ws(ws, ws_bytes, need, fn));
     if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
-    if (overlaps(y, yb, blocks, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps blocks");
+    if (overlaps(y, yb, blocks, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps the weights");
     if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
         overlaps(ws, (int64_t)need, blocks, wb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
-    if (nseg_of(k) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
+    if (nseg_of(k) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
     if (n > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "n = %lld > %lld rows", (long long)n, (long long)kMaxLutRows);
+    if (tiled && wb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrix above 2 GiB");
     return PTQ1_OK;
 }
 
 }  // namespace
 
-ptq1_status ptq1_matvec(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                         const float *signs1024, const float *residual, float *y, void *ws,
                         size_t ws_bytes, hipStream_t stream)
 {
     bool empty;
-    PTQ1_TRY(check_matvec(blocks, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec", &empty));
+    PTQ1_TRY(check_matvec(tiled, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec", true, &empty));
     if (empty) return ok();
     const LutWs L = lut_layout(n, 1, k);
     char *w = static_cast<char *>(ws);
-    return hip_status(ptq1::launch_matvec_lut(blocks, nullptr, 1, n, k, x, signs1024,
+    return hip_status(ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024,
                                               reinterpret_cast<float *>(w + L.part),
                                               reinterpret_cast<uint32_t *>(w + L.cnt), residual, y,
                                               nullptr, nullptr, nullptr, nullptr, 0, 0.0f, stream),
@@ -369,7 +402,7 @@ ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, 
 {
     bool empty;
     PTQ1_TRY(check_matvec(blocks, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec_float_peel",
-                          &empty));
+                          false, &empty));
     if (empty) return ok();
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
     hipError_t e = ptq1::launch_matvec_part(blocks, n, nullptr, 0, k, x, signs1024, part, stream);
@@ -388,8 +421,8 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
                          size_t ws_bytes, hipStream_t stream)
 {
     int64_t wgb, wub, xb, gb, ub;
-    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, signs1024 != nullptr, &wgb));
-    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, signs1024 != nullptr, &wub));
+    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, signs1024 != nullptr, &wgb, true));
+    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, signs1024 != nullptr, &wub, true));
     PTQ1_TRY(check_floats(g, "g", f, &gb));
     PTQ1_TRY(check_floats(u, "u", f, &ub));
     if (f == 0) return ok();
@@ -402,8 +435,9 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
     if (overlaps(ws, (int64_t)need, g, gb) || overlaps(ws, (int64_t)need, u, ub) ||
         overlaps(ws, (int64_t)need, x, xb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
-    if (nseg_of(d) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
+    if (nseg_of(d) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
     if (f > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "f = %lld > %lld rows", (long long)f, (long long)kMaxLutRows);
+    if (wgb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
     const LutWs L = lut_layout(f, 2, d);
     char *w = static_cast<char *>(ws);
     return hip_status(ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024,
@@ -432,11 +466,11 @@ size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
     return gemm_ws(m, k);
 }
 
-ptq1_status ptq1_gemm(const uint8_t *blocks, int64_t n, int64_t k, const float *x, int64_t m,
+ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m,
                       const float *signs1024, float *y, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     int64_t wb, mk, mn, xb, yb;
-    PTQ1_TRY(check_matrix(blocks, "blocks", n, k, signs1024 != nullptr, &wb));
+    PTQ1_TRY(check_matrix(tiled, "tiled", n, k, signs1024 != nullptr, &wb, true));
     if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
     if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
     if (!mul_ok(m, k, &mk) || !mul_ok(m, n, &mn)) return fail(PTQ1_ERR_OVERFLOW, "m * k or m * n overflows");
@@ -447,15 +481,15 @@ ptq1_status ptq1_gemm(const uint8_t *blocks, int64_t n, int64_t k, const float *
     const size_t need = gemm_ws(m, k);
     PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm"));
     if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
-    if (overlaps(y, yb, blocks, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps blocks");
+    if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps tiled");
     if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
-        overlaps(ws, (int64_t)need, blocks, wb))
+        overlaps(ws, (int64_t)need, tiled, wb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
     const int64_t m_pad = ptq1::gemm_m_pad(m);
     uint16_t *xbf = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kCounterBytes);
     hipError_t e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, k, signs1024, 0.0f, xbf, stream);
     if (e == hipSuccess)
-        e = ptq1::launch_gemm(xbf, m, m_pad, k, blocks, n, nullptr, 0, y, nullptr, nullptr, stream);
+        e = ptq1::launch_gemm(xbf, m, m_pad, k, tiled, n, nullptr, 0, y, nullptr, nullptr, stream);
     return hip_status(e, "ptq1_gemm");
 }
 
@@ -475,9 +509,9 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
     int64_t wgb, wub, wdb, md, xb, ob;
     if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
     if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
-    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, true, &wgb));
-    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, true, &wub));
-    PTQ1_TRY(check_matrix(w_down, "w_down", d, f, true, &wdb));
+    PTQ1_TRY(check_matrix(w_gate, "w_gate", f, d, true, &wgb, true));
+    PTQ1_TRY(check_matrix(w_up, "w_up", f, d, true, &wub, true));
+    PTQ1_TRY(check_matrix(w_down, "w_down", d, f, true, &wdb, true));
     if (!mul_ok(m, d, &md)) return fail(PTQ1_ERR_OVERFLOW, "m * d overflows");
     PTQ1_TRY(check_floats(x_out, "x_out", md, &ob));
     if (md == 0) return ok();
@@ -491,9 +525,12 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
     PTQ1_TRY(check_ws(ws, ws_bytes, L.total, "ptq1_ffn_block"));
     if (overlaps(ws, (int64_t)L.total, x, xb) || overlaps(ws, (int64_t)L.total, x_out, ob))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps x or x_out");
-    if (nseg_of(f) > kMaxGridY || nseg_of(d) > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d or f too large");
+    if (nseg_of(f) * 4 > kMaxGridY || nseg_of(d) * 4 > kMaxGridY)
+        return fail(PTQ1_ERR_UNSUPPORTED, "d or f too large");
     if (m == 1 && (f > kMaxLutRows || d > kMaxLutRows))
         return fail(PTQ1_ERR_UNSUPPORTED, "d or f > %lld rows", (long long)kMaxLutRows);
+    if (m == 1 && (wgb > kMaxLutMatrixBytes || wdb > kMaxLutMatrixBytes))
+        return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
     char *w = static_cast<char *>(ws);
     hipError_t e;
     if (m == 1) {

@@ -1,4 +1,5 @@
-// codec.hip -- PTQ1_0 encode (pack) and decode (dequant) kernels.
+// codec.hip -- PTQ1_0 encode (pack) and decode (dequant) kernels, and the
+// reorder of packed blocks into the library's tiled device layout.
 //
 // Format: "A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally",
 // section "What Bonsai is" (five trits per byte in base 3, one 16-bit scale
@@ -62,6 +63,34 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ blo
     }
 }
 
+// Packed -> tiled reorder: one thread per 28-byte place of the tiled output
+// (tiles of kTileRows rows x kTileBlocks blocks, row bands outermost, rows
+// then blocks inside a tile); places past the matrix get zero bytes.
+__global__ void __launch_bounds__(256) k_tile(const uint8_t *__restrict__ blocks, int64_t n, int64_t nb,
+                                              int64_t tiles_k, int64_t total, uint8_t *__restrict__ tiled)
+{
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tile = o / kTileSlots;
+        const int pos = static_cast<int>(o - tile * kTileSlots);
+        const int64_t band = tile / tiles_k;
+        const int64_t t = tile - band * tiles_k;
+        const int64_t r = band * kTileRows + pos / kTileBlocks;
+        const int64_t j = t * kTileBlocks + pos % kTileBlocks;
+        uint32_t d[kBlockDwords];
+#pragma unroll
+        for (int q = 0; q < kBlockDwords; ++q) d[q] = 0;
+        if (r < n && j < nb) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(blocks + (r * nb + j) * kBlockBytes);
+#pragma unroll
+            for (int q = 0; q < kBlockDwords; ++q) d[q] = src[q];
+        }
+        uint32_t *dst = reinterpret_cast<uint32_t *>(tiled + o * kBlockBytes);
+#pragma unroll
+        for (int q = 0; q < kBlockDwords; ++q) dst[q] = d[q];
+    }
+}
+
 static unsigned grid_for(int64_t total, int threads)
 {
     int64_t g = (total + threads - 1) / threads;
@@ -88,6 +117,18 @@ hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w,
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(k_dequant, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks,
                        k / kBlockWeights, k, total, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t s)
+{
+    const int64_t nb = k / kBlockWeights;
+    const int64_t tiles_k = (nb + kTileBlocks - 1) / kTileBlocks;
+    const int64_t bands = (n + kTileRows - 1) / kTileRows;
+    const int64_t total = bands * tiles_k * kTileSlots;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_tile, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks, n, nb, tiles_k, total,
+                       tiled);
     return hipGetLastError();
 }
 

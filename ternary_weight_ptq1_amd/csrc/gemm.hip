@@ -80,9 +80,9 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_bf16(
 // WM x WN grid, each owning TM x TN 32x32 output tiles of
 // v_mfma_f32_32x32x16_bf16.  K advances one PTQ1_0 block (128) per step:
 //   A: the bf16 activation tile [BM][128] is copied to LDS;
-//   B: the weight tile's 28-byte blocks are read once, trits peeled on the
-//      float pipeline and written to LDS as exact bf16 -1/0/+1; the scale
-//      goes to LDS as fp32;
+//   B: the weight tile's 28-byte blocks (tiled layout) are read once, trits
+//      peeled on the float pipeline and written to LDS as exact bf16
+//      -1/0/+1; the scale goes to LDS as fp32;
 //   16 x K=16 MFMAs accumulate the block's partial product from zero, then
 //   acc += partial * scale[column] in fp32.
 // Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
     const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t tile_m = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t nb = k / kBlockWeights;
-    const int64_t pitch = nb * kBlockBytes;
+    const int64_t tiles_k = (nb + kTileBlocks - 1) / kTileBlocks;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -136,8 +136,11 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
             const int64_t rv = tile_n + r;
             uint32_t dw = 0x80808080u;  // byte 128 = code 121 = all digits 1 = zero weights
             if (rv < rows) {
-                const uint8_t *wrow = (rv < n0) ? (w0 + rv * pitch) : (w1 + (rv - n0) * pitch);
-                dw = reinterpret_cast<const uint32_t *>(wrow + kb * kBlockBytes)[q];
+                const int64_t rr = (rv < n0) ? rv : rv - n0;  // row of its own (tiled) matrix
+                const uint8_t *tile = ((rv < n0) ? w0 : w1) +
+                                      ((rr / kTileRows) * tiles_k + kb / kTileBlocks) * kTileBytes;
+                const int pos = static_cast<int>(rr % kTileRows) * kTileBlocks + static_cast<int>(kb % kTileBlocks);
+                dw = reinterpret_cast<const uint32_t *>(tile + pos * kBlockBytes)[q];
             }
             const int nbytes = (q == kBlockDwords - 1) ? 2 : 4;
             for (int t = 0; t < nbytes; ++t) {

@@ -12,30 +12,36 @@
 //
 //   T[slot][b] = sum_n (digit_n(b) - 1) * xr[k(slot, n)]
 //
-// is tabulated once per workgroup for each byte position (slot) of a 4-block
+// is tabulated once per workgroup for each byte position (slot) of a 2-block
 // K-slice and each of the 256 byte values b.  A row's slice dot product is
 // then sum_blocks scale * sum_slots T[slot][byte], one LDS lookup and one
 // add per five weights.  Digits are decoded once per (slot, b) entry, not
 // per weight.
 //
 // Layout on gfx950:
-//   - K is cut into slices of 4 blocks (512 weights, 112 bytes per row);
-//     the table of a slice is 112 slots x 256 fp32 = two 64 KB halves, entry
-//     address = (slot / 64) << 16 | b << 8 | (slot % 64) << 2, so one
-//     v_perm_b32 assembles the address from the data byte and a per-lane
-//     constant; slots 26, 27 of each block (the scale bytes) hold zeros;
-//   - a workgroup (512 threads, one per CU) owns one slice and a run of
-//     (matrix, 16-row group) units of it; wave 0 rotates the slice's
-//     1024-chunk of x in registers, all threads build the table, then each
-//     of the 8 waves processes exactly U units (U is a template parameter
-//     chosen per launch so the grid fits the CUs in one round), with all U
-//     units' weights requested before the table is built: lane = (row % 16,
-//     block of the slice); a lane reads its 28-byte block with two wide
-//     loads and rotates its 7 dwords (and the byte order within a dword) by
-//     a lane-dependent amount so the 32 lanes of a half-wave spread over LDS
-//     banks;
-//   - a unit's 4 block partials (times their fp16 scales) are summed across
-//     lanes with two xor-shuffles and written as split-K partials; a
+//   - K is cut into slices of 2 blocks (256 weights, 56 bytes per row); the
+//     table of a slice is 56 slots x 256 fp32 in one 64 KB bank-interleaved
+//     array, entry address = b << 8 | slot << 2, so one v_perm_b32
+//     assembles the address from the data byte and a per-lane constant byte;
+//     slots 26, 27 of each block (the scale bytes) hold zeros; at 64 KB, two
+//     workgroups share a CU, so one's latency-bound phases (rotation, table
+//     build, final reduction) overlap the other's lookups;
+//   - weights are read in the tiled layout: the 32 rows x 2 blocks of a unit
+//     are one contiguous 1792-byte tile, lane 2i + b holding block b of row
+//     i, so a wave's loads are fully used 128-byte lines (a row-major matrix
+//     would give each workgroup 56-byte pieces at the row pitch, which
+//     measured at well under half the bandwidth);
+//   - a workgroup (512 threads) owns one slice and a run of (matrix, 32-row
+//     group) units of it; wave 0 rotates the slice's 1024-chunk of x in
+//     registers, all threads build the table, then each of the 8 waves
+//     processes exactly U units (U is a template parameter chosen per launch
+//     so the grid fits two workgroups per CU), with all U units' weights
+//     requested before the table is built; a lane reads its 28-byte block
+//     with two wide loads and rotates its 7 dwords (and the byte order within
+//     a dword) by a lane-dependent amount so the 32 lanes of a half-wave
+//     (16 rows x 2 blocks) spread over LDS banks;
+//   - a unit's 2 block partials (times their fp16 scales) are summed across
+//     lanes with one xor-shuffle and written as split-K partials; a
 //     per-group counter (atomicInc with wrap, so it is back to zero after
 //     every launch) lets the last unit of a group sum the partials of all
 //     slices in fixed order and apply the epilogue: store, + residual, or
@@ -45,27 +51,30 @@
 
 namespace ptq1 {
 
-constexpr int kLutBlocks = 4;                          // blocks per K-slice
-constexpr int kLutSliceW = kLutBlocks * kBlockWeights;  // 512 weights
-constexpr int kLutSlots = kLutBlocks * kBlockBytes;    // 112 byte slots
+constexpr int kLutBlocks = 2;                          // blocks per K-slice
+constexpr int kLutSliceW = kLutBlocks * kBlockWeights;  // 256 weights
+constexpr int kLutSlots = kLutBlocks * kBlockBytes;    // 56 byte slots
 constexpr int kLutThreads = 512;
 constexpr int kLutWaves = kLutThreads / kWave;         // 8
-constexpr int kLutRows = 16;                           // rows per unit
-constexpr int kLutTableBytes = 2 * 65536;
+constexpr int kLutRows = 32;                           // rows per unit
+constexpr int kLutTableBytes = 65536;                  // 256 byte values x 64 slot columns x fp32
+static_assert(kLutRows == kTileRows && kLutBlocks == kTileBlocks, "a unit is one tile");
+static_assert(kLutRows * kLutBlocks == kWave, "one block per lane");
 
 // Per-lane dword rotation (rho) and byte rotation (sigma) for lanes 0..31
-// (lanes 32..63 repeat them): found by a search that minimises LDS bank
-// collisions of the 32 slots a half-wave reads per lookup.
-__constant__ uint8_t kLutRho[32] = {4, 6, 1, 3, 5, 3, 3, 0, 1, 3, 2, 1, 6, 6, 4, 0,
-                                    6, 1, 5, 2, 3, 3, 6, 5, 6, 0, 3, 6, 1, 0, 2, 5};
-__constant__ uint8_t kLutSig[32] = {0, 1, 1, 1, 0, 3, 0, 1, 0, 2, 3, 2, 2, 3, 3, 0,
-                                    3, 2, 1, 0, 0, 2, 2, 2, 1, 1, 1, 0, 3, 0, 3, 3};
+// (lanes 32..63 repeat them; lane 2i + b reads block b of row i): found by a
+// search that minimises LDS bank collisions of the 32 slots a half-wave
+// reads per lookup.
+__constant__ uint8_t kLutRho[32] = {4, 6, 6, 1, 1, 5, 3, 2, 5, 3, 3, 3, 3, 6, 0, 5,
+                                    1, 6, 3, 0, 2, 3, 1, 6, 6, 1, 6, 0, 4, 2, 0, 5};
+__constant__ uint8_t kLutSig[32] = {0, 3, 1, 2, 1, 1, 1, 0, 0, 0, 3, 2, 0, 2, 1, 2,
+                                    0, 1, 2, 1, 3, 1, 2, 0, 2, 3, 3, 0, 3, 3, 0, 3};
 
 struct LutArgs {
-    const uint8_t *w0, *w1;  // one or two packed [n][k] matrices
-    int64_t n, k, pitch;     // rows per matrix, K, bytes per row
+    const uint8_t *w0, *w1;  // one or two tiled [n][k] matrices
+    int64_t n, k;            // rows per matrix, K
     int nmat, nslices;
-    int64_t groups;          // ceil(n / 16)
+    int64_t groups;          // ceil(n / 32)
     int64_t units;           // nslices * nmat * groups
     int64_t units_per_wg;
     const float *x, *signs;
@@ -87,7 +96,7 @@ struct LutArgs {
 template <int BQ>
 __device__ __forceinline__ void lut_build_range(float *tab, int slot, const float (&xv)[5])
 {
-    const uint32_t base = (static_cast<uint32_t>(slot >> 6) << 16) | (static_cast<uint32_t>(slot & 63) << 2);
+    const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int b = 32 * BQ + i;
@@ -114,9 +123,9 @@ __device__ __forceinline__ void lut_store_part(float *p, float v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One unit = (slice s, matrix mat, 16-row group grp): the 7 dwords of the
-// lane's block (rotated order) plus the dword holding its scale.  Row
-// counts are below 2^20 (checked by the caller), so indices fit in int.
+// One unit = (slice s, matrix mat, 32-row group grp) = tile (grp, s) of
+// matrix mat.  Row counts are below 2^20 (checked by the caller), so
+// indices fit in int.
 struct LutUnit {
     int mat, grp, r;
     bool live;
@@ -136,22 +145,22 @@ __device__ __forceinline__ LutUnit lut_unit(const LutArgs &a, int64_t un, int s,
 }
 
 // A block's 7 dwords, read with two wide loads (16 + 12 bytes; blocks are
-// only dword-aligned, which gfx950 global loads accept).
+// only dword-aligned, which gfx950 global loads accept).  The lanes of a wave
+// cover one 1792-byte tile.
 typedef uint32_t lut_u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t lut_u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 
-__device__ __forceinline__ void lut_load(const LutArgs &a, const LutUnit &u, int s, int blk_l,
+__device__ __forceinline__ void lut_load(const LutArgs &a, const LutUnit &u, int s, int lane,
                                          uint32_t (&d)[kBlockDwords])
 {
     // Unconditional loads (a branch around them would make the compiler wait
-    // for each load before the next): a lane with no row or no block reads
-    // the matrix's first block instead and its scale is zeroed by the caller.
-    // Wave-uniform matrix base + 32-bit per-lane byte offset (matrices below
-    // 2 GiB, checked by the caller).
+    // for each load before the next): padding rows and blocks of the tiled
+    // layout exist (zero bytes) and their scale is zeroed by the caller.
+    // Wave-uniform matrix base + 32-bit per-lane byte offset (tiled matrices
+    // below 2 GiB, checked by the caller).
     const uint8_t *wm = u.mat ? a.w1 : a.w0;
-    const uint32_t keep = u.live ? 0xffffffffu : 0u;  // lane mask, no branch
-    const uint32_t off = (static_cast<uint32_t>(u.r) * static_cast<uint32_t>(a.pitch) +
-                          static_cast<uint32_t>(s * kLutBlocks + blk_l) * kBlockBytes) & keep;
+    const uint32_t off = (static_cast<uint32_t>(u.grp) * static_cast<uint32_t>(a.nslices) +
+                          static_cast<uint32_t>(s)) * kTileBytes + static_cast<uint32_t>(lane) * kBlockBytes;
     const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(wm + off);
     const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(wm + off + 16);
     d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
@@ -174,14 +183,14 @@ __device__ __forceinline__ void lut_rotate(uint32_t (&d)[kBlockDwords], int rho)
     }
 }
 
-// Finish up to four completed row groups at once (one whole wave): lane =
+// Finish up to two completed row groups at once (one whole wave): lane =
 // (group of the batch, row of the group); each lane sums its row's partials
 // over all slices in slice order and applies the epilogue.  Every partial of
-// a round of 32 slices is requested before any is summed.
-__device__ void lut_finish(const LutArgs &a, const int (&grp)[4], int ngrp, int lane, float rms_a)
+// a round of 16 slices is requested before any is summed.
+__device__ void lut_finish(const LutArgs &a, const int (&grp)[2], int ngrp, int lane, float rms_a)
 {
     constexpr int kPer = 16;
-    const int gi = lane >> 4;
+    const int gi = lane >> 5;
     const int64_t r_raw = gi < ngrp ? static_cast<int64_t>(grp[gi]) * kLutRows + (lane & (kLutRows - 1)) : a.n;
     const bool ok = r_raw < a.n;
     const int64_t r = ok ? r_raw : 0;  // clamped: every lane loads, no branch around the loads
@@ -218,11 +227,11 @@ __device__ void lut_finish(const LutArgs &a, const int (&grp)[4], int ngrp, int 
 }
 
 template <int U>
-__global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
+__global__ void __launch_bounds__(kLutThreads, 2) k_matvec_lut(LutArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    float *tab = reinterpret_cast<float *>(lds);                 // 128 KB table
-    float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 512 floats
+    float *tab = reinterpret_cast<float *>(lds);                 // 64 KB table
+    float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 256 floats
     float *red = xs + kLutSliceW;                               // 16 floats
 
     const int tid = threadIdx.x;
@@ -234,8 +243,8 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
     const int64_t k0 = static_cast<int64_t>(s) * kLutSliceW;
     const int kw = static_cast<int>(a.k - k0 < kLutSliceW ? a.k - k0 : kLutSliceW);
     const int nblk = kw / kBlockWeights;
-    const int row_l = lane & (kLutRows - 1);
-    const int blk_l = lane >> 4;  // block of the slice this lane reads
+    const int row_l = lane >> 1;  // row of the unit (tile) this lane reads
+    const int blk_l = lane & 1;   // block of the slice this lane reads
     const int rho = kLutRho[lane & 31], sig = kLutSig[lane & 31];
 
     // ---- this wave's U units of weights, requested before anything else
@@ -244,7 +253,7 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
     for (int i = 0; i < U; ++i) {
         const int64_t un = first + i < per_slice ? first + i : per_slice - 1;  // clamped: no branch
         lut_load(a, lut_unit(a, un + static_cast<int64_t>(s) * per_slice, s, per_slice, row_l, blk_l, nblk),
-                 s, blk_l, dat[i]);
+                 s, lane, dat[i]);
     }
 
     // ---- RMS scale of the block input (gate/up epilogue only)
@@ -260,14 +269,14 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
     if (a.signs != nullptr) {
         if (wave == 0) {
             const int64_t c0 = (k0 / kHadamard) * kHadamard;
-            const int half = static_cast<int>(k0 - c0);  // 0 or 512
+            const int part = static_cast<int>(k0 - c0);  // 0, 256, 512 or 768
             float v[kRotPerLane];
 #pragma unroll
             for (int j = 0; j < kRotPerLane; ++j) v[j] = a.x[c0 + lane + kWave * j] * a.signs[lane + kWave * j];
             fwht1024_wave(v);
 #pragma unroll
             for (int j = 0; j < kRotPerLane; ++j) {
-                const int e = lane + kWave * j - half;
+                const int e = lane + kWave * j - part;
                 if (e >= 0 && e < kLutSliceW) xs[e] = v[j] * (1.0f / 32.0f);
             }
         }
@@ -280,9 +289,10 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
         for (int w = 0; w < kLutWaves; ++w) t += red[w];
         rms_a = 1.0f / sqrtf(t / static_cast<float>(a.d_rms) + a.rms_eps);
     }
-    // ---- table: thread = (slot, 32-value ranges of the byte)
-    for (int bq = tid >> 7; bq < 8; bq += kLutThreads / 128) {
-        const int slot = tid & 127;
+    // ---- table: thread = (slot, 32-value range of the byte)
+    {
+        const int bq = tid >> 6;  // 0..7
+        const int slot = tid & 63;
         if (slot < kLutSlots) {
             const int blk = slot / kBlockBytes, i = slot % kBlockBytes;
             float xv[5];
@@ -306,34 +316,29 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
     __syncthreads();
 
     // ---- per-lane lookup constants.  Address of the lookup for byte c of
-    // the lane's j-th dword: (slot / 64) << 16 | byte << 8 | (slot % 64) << 2;
-    // bytes 0 and 2 of it are packed two per register (bytes {0, 2} for
-    // even c, {1, 3} for odd c) and v_perm_b32 inserts the data byte.
-    uint32_t P[kBlockDwords][2];
+    // the lane's j-th dword: byte << 8 | slot << 2; the four slot bytes of a
+    // dword are packed in one register (byte c) and v_perm_b32 inserts the
+    // data byte (selector: byte 0 <- P byte c, byte 1 <- data byte e, 0, 0).
+    uint32_t P[kBlockDwords];
     uint32_t S[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint32_t e = static_cast<uint32_t>((c + sig) & 3);
-        S[c] = ((c & 1) ? 0x0C070005u : 0x0C060004u) | (e << 8);
+        S[c] = 0x0C0C0000u | (e << 8) | static_cast<uint32_t>(4 + c);
     }
 #pragma unroll
     for (int j = 0; j < kBlockDwords; ++j) {
         const int q = (j + rho) % kBlockDwords;
+        uint32_t packed = 0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int c = 2 * h + cc;
-                const int slot = kBlockBytes * blk_l + 4 * q + ((c + sig) & 3);
-                packed |= (static_cast<uint32_t>(slot & 63) << 2) << (8 * cc);
-                packed |= static_cast<uint32_t>(slot >> 6) << (16 + 8 * cc);
-            }
-            P[j][h] = packed;
+        for (int c = 0; c < 4; ++c) {
+            const int slot = kBlockBytes * blk_l + 4 * q + ((c + sig) & 3);
+            packed |= (static_cast<uint32_t>(slot) << 2) << (8 * c);
         }
+        P[j] = packed;
     }
 
-    // ---- lookups, scale, 4-lane reduction, partial store
+    // ---- lookups, scale, 2-lane reduction, partial store
     typedef __attribute__((address_space(3))) const float lds_f32;
     int my_grp = 0;  // lane i records the group of unit i
 #pragma unroll
@@ -348,15 +353,14 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
         for (int j = 0; j < kBlockDwords; ++j) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t addr = __builtin_amdgcn_perm(P[j][c >> 1], dat[i][j], S[c]);
+                const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
                 const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
                 if ((c & 1) == 0) acc0 += t; else acc1 += t;
             }
         }
         float p = (acc0 + acc1) * scale;
-        p += __shfl_xor(p, 16, kWave);
-        p += __shfl_xor(p, 32, kWave);
-        if (unit_ok && lane < kLutRows && u.r < a.n)
+        p += __shfl_xor(p, 1, kWave);
+        if (unit_ok && blk_l == 0 && u.r < a.n)
             lut_store_part(a.part + (static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + u.r, p);
         if (lane == i) my_grp = u.grp;
     }
@@ -373,19 +377,19 @@ __global__ void __launch_bounds__(kLutThreads) k_matvec_lut(LutArgs a)
         if (lane < nu) old = atomicInc(&a.cnt[my_grp], target - 1u);
         uint64_t last = __ballot(lane < nu && old == target - 1u);
         while (last) {
-            int grp4[4];
+            int grp2[2];
             int ng = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                grp4[q] = 0;
+            for (int q = 0; q < 2; ++q) {
+                grp2[q] = 0;
                 if (last) {
                     const int i = __builtin_ctzll(last);
                     last &= last - 1;
-                    grp4[q] = __shfl(my_grp, i, kWave);
+                    grp2[q] = __shfl(my_grp, i, kWave);
                     ng = q + 1;
                 }
             }
-            lut_finish(a, grp4, ng, lane, rms_a);
+            lut_finish(a, grp2, ng, lane, rms_a);
         }
     }
 }
@@ -439,7 +443,6 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.w1 = w1;
     a.n = n;
     a.k = k;
-    a.pitch = (k / kBlockWeights) * kBlockBytes;
     a.nmat = nmat;
     a.nslices = static_cast<int>((k + kLutSliceW - 1) / kLutSliceW);
     a.groups = (n + kLutRows - 1) / kLutRows;
@@ -457,14 +460,14 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.d_rms = d_rms;
     a.rms_eps = rms_eps;
     // units per wave: the smallest U whose grid (slices x chunks of 8U units)
-    // fits the CUs in one round, else the largest U
+    // fits two workgroups per CU in one round, else the largest U
     const int64_t per_slice = static_cast<int64_t>(nmat) * a.groups;
     const int cus = device_cus();
-    static const int kUs[] = {1, 2, 3, 4, 6, 8, 12};
-    int U = 12;
+    static const int kUs[] = {1, 2, 3, 4, 6, 8};
+    int U = 8;
     for (int cand : kUs) {
         const int64_t chunks = (per_slice + kLutWaves * cand - 1) / (kLutWaves * cand);
-        if (chunks * a.nslices <= cus) {
+        if (chunks * a.nslices <= 2 * static_cast<int64_t>(cus)) {
             U = cand;
             break;
         }
@@ -477,8 +480,7 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
         case 3: return lut_launch<3>(a, chunks, s);
         case 4: return lut_launch<4>(a, chunks, s);
         case 6: return lut_launch<6>(a, chunks, s);
-        case 8: return lut_launch<8>(a, chunks, s);
-        default: return lut_launch<12>(a, chunks, s);
+        default: return lut_launch<8>(a, chunks, s);
     }
 }
 

@@ -26,6 +26,16 @@ static_assert(kTritBytes * kTritsPerByte >= kBlockWeights, "trit bytes hold a bl
 static_assert((kTritBytes - 1) * kTritsPerByte < kBlockWeights, "no spare trit byte");
 static_assert(kBlockBytes == kTritBytes + 2 && kBlockBytes % 4 == 0, "block is whole dwords");
 
+// ---- device weight layout (this library's, not the file format's) ----------
+// The blocks of a matrix reordered into tiles of 32 rows x 2 blocks: one tile
+// is 64 whole blocks = 1792 contiguous bytes, so a wave that needs 32 rows x
+// 256 weights of K reads one contiguous run instead of 32 strided pieces.
+constexpr int kTileRows = 32;
+constexpr int kTileBlocks = 2;
+constexpr int kTileSlots = kTileRows * kTileBlocks;   // 64 blocks
+constexpr int kTileBytes = kTileSlots * kBlockBytes;  // 1792
+static_assert(kTileBytes % 128 == 0, "tiles are whole 128-byte lines");
+
 // ---- launch geometry -------------------------------------------------------
 constexpr int kWave = 64;                       // CDNA wavefront
 

@@ -11,6 +11,8 @@ namespace ptq1 {
 hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
                        uint8_t *blocks, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s);
+// packed [n][k] -> tiled layout (kTileRows x kTileBlocks tiles, zero padding)
+hipError_t launch_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t s);
 
 // rows of x [m][k] -> y, each 1024-chunk (1/32) H (signs * chunk)
 hipError_t launch_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs,
@@ -38,10 +40,10 @@ hipError_t launch_reduce_gate_up(const float *part, int64_t f, int64_t nseg, flo
                                  hipStream_t s);
 hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t s);
 
-// Lookup-table decode matvec (one launch): one matrix (nmat = 1: y =
-// residual + W xr) or two (nmat = 2: g, u = a W0 xr, a W1 xr; h = silu(g) u,
-// a = RMS scale of x_rms or 1).  part: lut_part_floats floats; cnt:
-// lut_counter_words zero words (left zero on completion).
+// Lookup-table decode matvec (one launch) over tiled weights: one matrix
+// (nmat = 1: y = residual + W xr) or two (nmat = 2: g, u = a W0 xr, a W1 xr;
+// h = silu(g) u, a = RMS scale of x_rms or 1).  part: lut_part_floats
+// floats; cnt: lut_counter_words zero words (left zero on completion).
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 size_t lut_counter_words(int64_t n);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
@@ -56,9 +58,9 @@ int64_t gemm_m_pad(int64_t m);
 hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int64_t m,
                             int64_t m_pad, int64_t k, const float *signs, float rms_eps,
                             uint16_t *xb, hipStream_t s);
-// y [m][rows] (ldy) = xb . W^T (+ residual [m][rows] if given); rows of the
-// virtual matrix as in launch_matvec_part; the second matrix's outputs go to
-// y1 (same ld) when n1 > 0.
+// y [m][rows] (ldy) = xb . W^T (+ residual [m][rows] if given), W tiled;
+// rows of the virtual matrix as in launch_matvec_part; the second matrix's
+// outputs go to y1 (same ld) when n1 > 0.
 hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
                        int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
                        const float *residual, hipStream_t s);

@@ -28,12 +28,13 @@ def test_geometry_single_source():
     """One table, held together by a test ("A 27B model in 5.5 GB...",
     section "What I learned building it": derive copies from one table)."""
     g = P.ptq1_geometry()
-    assert g == (128, 26, 28, 1024)
-    assert g == (oracle.lib().orc_block_weights(), oracle.lib().orc_block_trit_bytes(),
-                 oracle.lib().orc_block_bytes(), oracle.lib().orc_hadamard_width())
-    assert (P.BLOCK_WEIGHTS, P.TRIT_BYTES, P.BLOCK_BYTES, P.HADAMARD) == g
+    assert g == (128, 26, 28, 1024, 32, 2)
+    assert g[:4] == (oracle.lib().orc_block_weights(), oracle.lib().orc_block_trit_bytes(),
+                     oracle.lib().orc_block_bytes(), oracle.lib().orc_hadamard_width())
+    assert (P.BLOCK_WEIGHTS, P.TRIT_BYTES, P.BLOCK_BYTES, P.HADAMARD, P.TILE_ROWS, P.TILE_BLOCKS) == g
     hdr = open(P.HEADER).read()
-    for name, v in zip(("PTQ1_BLOCK_WEIGHTS", "PTQ1_TRIT_BYTES", "PTQ1_BLOCK_BYTES", "PTQ1_HADAMARD"), g):
+    for name, v in zip(("PTQ1_BLOCK_WEIGHTS", "PTQ1_TRIT_BYTES", "PTQ1_BLOCK_BYTES", "PTQ1_HADAMARD",
+                        "PTQ1_TILE_ROWS", "PTQ1_TILE_BLOCKS"), g):
         assert f"#define {name} {v}" in hdr
 
 
@@ -50,6 +51,29 @@ def test_packed_bytes():
 def test_status_strings():
     for code, name in P.STATUS.items():
         assert L().ptq1_status_string(code).decode() == name
+
+
+def test_tiled_bytes():
+    # ceil(n/32)*32 rows x ceil(k/256)*2 blocks x 28 bytes
+    assert P.ptq1_tiled_bytes(17408, 5120) == 19_496_960
+    assert P.ptq1_tiled_bytes(5120, 17408) == 19_496_960
+    assert P.ptq1_tiled_bytes(1, 128) == 32 * 2 * 28
+    assert P.ptq1_tiled_bytes(33, 384) == 64 * 4 * 28
+    assert P.ptq1_tiled_bytes(0, 128) == 0
+    assert P.ptq1_tiled_bytes(1, 100) == -1
+    assert P.ptq1_tiled_bytes(1 << 62, 1 << 20) == -1
+
+
+def test_tile_validation():
+    rc, msg = _err(L().ptq1_tile(None, 4, 128, C.c_void_p(FAKE), None))
+    assert rc == 1 and "blocks" in msg
+    rc, msg = _err(L().ptq1_tile(C.c_void_p(FAKE), 4, 130, C.c_void_p(FAKE * 2), None))
+    assert rc == 2
+    rc, msg = _err(L().ptq1_tile(C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE * 2 + 8), None))
+    assert rc == 3 and "tiled" in msg
+    rc, msg = _err(L().ptq1_tile(C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE + 64), None))
+    assert rc == 7
+    assert L().ptq1_tile(None, 0, 128, None, None) == 0
 
 
 def _err(rc):

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Tolerances (relative L2, ||got - ref|| / ||ref||):
-  bit-exact   ptq1_pack bytes, ptq1_dequant values (scale * trit is exact in fp32)
+  bit-exact   ptq1_pack bytes, ptq1_tile bytes, ptq1_dequant values (scale *
+              trit is exact in fp32)
   1e-5        fp32 paths: rotate, unrotate_rows, matvec, gate_up, swiglu,
               ffn_block at m = 1
   3e-3        bf16-MFMA GEMM (activations rounded to bf16 once)
@@ -46,6 +47,22 @@ def host_matrix(seed, tr, sc, n, k, row0=0):
 
 def dev_pack(t, s):
     return P.ptq1_pack(to_dev(t), to_dev(s.view(np.int16)))
+
+
+def tiled(b, n, k):
+    """Device tiled layout of a packed matrix (host array or device tensor)."""
+    return P.ptq1_tile(b if isinstance(b, torch.Tensor) else to_dev(b), n, k)
+
+
+def tile_host(blocks, n, k):
+    """The tiled layout written out from its definition in include/ptq1.h:
+    tiles of 32 rows x 2 blocks, row bands outermost, block (32g + i, 2t + b)
+    at byte (2i + b) * 28 of tile g * T + t, zero bytes past the matrix."""
+    nb = k // 128
+    bands, tk = -(-n // 32), -(-nb // 2)
+    full = np.zeros((bands * 32, tk * 2, 28), np.uint8)
+    full[:n, :nb] = np.asarray(blocks).reshape(n, nb, 28)
+    return full.reshape(bands, 32, tk, 2, 28).transpose(0, 2, 1, 3, 4).reshape(-1)
 
 
 def dev_matrix(seed, tr, sc, n, k):
@@ -103,6 +120,22 @@ def test_pack_worked_block():
     got = host(dev_pack(t, s))[0]
     assert got[0] == 207 and got[25] == 71 and got[26] == 0 and got[27] == 60
     assert np.all(got[1:25] == 128)
+
+
+@pytest.mark.parametrize("n,k,seed", [(1, 128, 0), (33, 384, 1), (64, 1024, 2), (100, 640, 3), (31, 256, 4)])
+def test_tile_bit_exact(n, k, seed):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    got = host(tiled(b, n, k))
+    assert got.size == P.ptq1_tiled_bytes(n, k)
+    np.testing.assert_array_equal(got, tile_host(b, n, k))
+
+
+def test_tile_full_shape():
+    n, k = 17408, 5120
+    b = dev_matrix(1, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    got = host(tiled(b, n, k))
+    np.testing.assert_array_equal(got, tile_host(host(b), n, k))
 
 
 @pytest.mark.parametrize("n,k,seed", [(1024, 1024, 0), (37, 384, 1)])
@@ -190,6 +223,11 @@ def test_unrotate_rows_full_table():
 MATVECS = ["ptq1_matvec", "ptq1_matvec_float_peel"]
 
 
+def mv_weights(fn, b, n, k):
+    """The layout each matvec reads: tiled for the table decode, packed for the float peel."""
+    return tiled(b, n, k) if fn == "ptq1_matvec" else to_dev(b)
+
+
 @pytest.mark.parametrize("fn", MATVECS)
 @pytest.mark.parametrize("n,k,seed,rot", [(1024, 1024, 0, True), (300, 384, 1, False), (257, 3072, 2, True),
                                           (1, 128, 3, False), (17, 640, 4, False), (5120, 17408, 2, True)])
@@ -198,7 +236,7 @@ def test_matvec(fn, n, k, seed, rot):
     blocks = oracle.pack(t, s)
     x = synth.activations(seed, 1, k)[0]
     sg = synth.signs(seed)
-    got = host(getattr(P, fn)(to_dev(blocks), n, k, to_dev(x), to_dev(sg) if rot else None))
+    got = host(getattr(P, fn)(mv_weights(fn, blocks, n, k), n, k, to_dev(x), to_dev(sg) if rot else None))
     xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
     assert rel_l2(got, oracle.matvec(blocks, n, k, xr)) <= TOL_FP32
 
@@ -212,21 +250,21 @@ def test_matvec_residual_and_special_cases(fn):
     res = synth.gauss(4, 77, n)
     t, s = host_matrix(4, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
     b = oracle.pack(t, s)
-    got = host(mv(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
+    got = host(mv(mv_weights(fn, b, n, k), n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
     ref = res + oracle.matvec(b, n, k, oracle.rotate(x, sg))
     assert rel_l2(got, ref) <= TOL_FP32
     # in place on the residual
     rd = to_dev(res)
-    mv(to_dev(b), n, k, to_dev(x), to_dev(sg), residual=rd, out=rd)
+    mv(mv_weights(fn, b, n, k), n, k, to_dev(x), to_dev(sg), residual=rd, out=rd)
     assert rel_l2(host(rd), ref) <= TOL_FP32
     # all-zero trits: exactly zero
     z = oracle.pack(np.zeros((n, k), np.int8), s)
-    np.testing.assert_array_equal(host(mv(to_dev(z), n, k, to_dev(x), to_dev(sg))), 0.0)
+    np.testing.assert_array_equal(host(mv(mv_weights(fn, z, n, k), n, k, to_dev(x), to_dev(sg))), 0.0)
     # zero scales in one block column remove exactly that block
     s2 = s.copy()
     s2[:, 3] = 0
     b2 = oracle.pack(t, s2)
-    got2 = host(mv(to_dev(b2), n, k, to_dev(x), None))
+    got2 = host(mv(mv_weights(fn, b2, n, k), n, k, to_dev(x), None))
     assert rel_l2(got2, oracle.matvec(b2, n, k, x)) <= TOL_FP32
 
 
@@ -245,7 +283,7 @@ def test_shared_workspace_across_calls():
         x = synth.activations(20 + i, 1, k)[0]
         sg = synth.signs(20 + i)
         ref = oracle.matvec(b, n, k, oracle.rotate(x, sg) if rot else x)
-        cases.append((to_dev(b), n, k, to_dev(x), to_dev(sg) if rot else None, ref))
+        cases.append((to_dev(b), tiled(b, n, k), n, k, to_dev(x), to_dev(sg) if rot else None, ref))
     tg, sgl = host_matrix(30, synth.S_GATE_TRITS, synth.S_GATE_SCALES, 1040, 2048)
     tu, su = host_matrix(30, synth.S_UP_TRITS, synth.S_UP_SCALES, 1040, 2048)
     bg, bu = oracle.pack(tg, sgl), oracle.pack(tu, su)
@@ -253,9 +291,9 @@ def test_shared_workspace_across_calls():
     s30 = synth.signs(30)
     xr = oracle.rotate(xg, s30)
     rg, ru = oracle.matvec(bg, 1040, 2048, xr), oracle.matvec(bu, 1040, 2048, xr)
-    dg, du, dx, ds = to_dev(bg), to_dev(bu), to_dev(xg), to_dev(s30)
+    dg, du, dx, ds = tiled(bg, 1040, 2048), tiled(bu, 1040, 2048), to_dev(xg), to_dev(s30)
     xm = synth.activations(31, 40, 1024)
-    b0, n0, k0, _, s0, _ = cases[0]
+    _, b0, n0, k0, _, s0, _ = cases[0]
     rm = oracle.gemm(oracle.pack(*host_matrix(20, synth.S_W_TRITS, synth.S_W_SCALES, 1024, 1024)), 1024, 1024,
                      oracle.rotate(xm, synth.signs(20)))
     dxm = to_dev(xm)
@@ -264,15 +302,15 @@ def test_shared_workspace_across_calls():
             g, u = P.ptq1_gate_up(dg, du, 1040, 2048, dx, ds, ws=ws)
             assert rel_l2(host(g), rg) <= TOL_FP32 and rel_l2(host(u), ru) <= TOL_FP32, f"iteration {it}"
         elif it % 7 == 3:
-            b, n, k, x, sg, ref = cases[it % len(cases)]
+            b, _, n, k, x, sg, ref = cases[it % len(cases)]
             y = P.ptq1_matvec_float_peel(b, n, k, x, sg, ws=ws)
             assert rel_l2(host(y), ref) <= TOL_FP32, f"iteration {it} (float peel)"
         elif it % 11 == 4:
             y = P.ptq1_gemm(b0, n0, k0, dxm, s0, ws=ws)
             assert rel_l2(host(y), rm) <= TOL_BF16, f"iteration {it} (gemm)"
         else:
-            b, n, k, x, sg, ref = cases[it % len(cases)]
-            y = P.ptq1_matvec(b, n, k, x, sg, ws=ws)
+            _, bt, n, k, x, sg, ref = cases[it % len(cases)]
+            y = P.ptq1_matvec(bt, n, k, x, sg, ws=ws)
             assert rel_l2(host(y), ref) <= TOL_FP32, f"iteration {it} shape {(n, k)}"
 
 
@@ -287,7 +325,7 @@ def test_matvec_repeat_and_deterministic():
         b = oracle.pack(t, s)
         x = synth.activations(seed, 1, k)[0]
         sg = synth.signs(seed)
-        bd, xd, sd = to_dev(b), to_dev(x), to_dev(sg)
+        bd, xd, sd = tiled(b, n, k), to_dev(x), to_dev(sg)
         y1 = host(P.ptq1_matvec(bd, n, k, xd, sd))
         y2 = host(P.ptq1_matvec(bd, n, k, xd, sd))
         np.testing.assert_array_equal(y1, y2)
@@ -303,7 +341,7 @@ def test_gate_up_small(f, d, rot):
     bg, bu = oracle.pack(tg, sg_), oracle.pack(tu, su)
     x = synth.activations(seed, 1, d)[0]
     s = synth.signs(seed)
-    g, u = P.ptq1_gate_up(to_dev(bg), to_dev(bu), f, d, to_dev(x), to_dev(s) if rot else None)
+    g, u = P.ptq1_gate_up(tiled(bg, f, d), tiled(bu, f, d), f, d, to_dev(x), to_dev(s) if rot else None)
     xr = oracle.rotate(x, s) if rot else x
     assert rel_l2(host(g), oracle.matvec(bg, f, d, xr)) <= TOL_FP32
     assert rel_l2(host(u), oracle.matvec(bu, f, d, xr)) <= TOL_FP32
@@ -318,7 +356,7 @@ def test_gate_up_full_shape():
     del tg, tu
     x = synth.activations(seed, 1, d)[0]
     s = synth.signs(seed)
-    g, u = P.ptq1_gate_up(to_dev(bg), to_dev(bu), f, d, to_dev(x), to_dev(s))
+    g, u = P.ptq1_gate_up(tiled(bg, f, d), tiled(bu, f, d), f, d, to_dev(x), to_dev(s))
     xr = oracle.rotate(x, s)
     assert rel_l2(host(g), oracle.matvec(bg, f, d, xr)) <= TOL_FP32
     assert rel_l2(host(u), oracle.matvec(bu, f, d, xr)) <= TOL_FP32
@@ -342,7 +380,7 @@ def test_gemm_small(m, n, k, rot):
     b = oracle.pack(t, s)
     x = synth.activations(seed, m, k)
     sg = synth.signs(seed)
-    got = host(P.ptq1_gemm(to_dev(b), n, k, to_dev(x), to_dev(sg) if rot else None))
+    got = host(P.ptq1_gemm(tiled(b, n, k), n, k, to_dev(x), to_dev(sg) if rot else None))
     xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
     assert got.shape == (m, n)
     assert rel_l2(got, oracle.gemm(b, n, k, xr)) <= TOL_BF16
@@ -353,7 +391,7 @@ def prefill_weights():
     n, k, seed = 17408, 5120, 3
     t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
     b = oracle.pack(t, s)
-    return b, to_dev(b)
+    return b, tiled(b, n, k)
 
 
 @pytest.mark.parametrize("m", [128, 256, 512])
@@ -390,7 +428,7 @@ def test_ffn_block_small(m, d, f, eps):
     wg, wu, wd = _ffn_host(seed, d, f)
     x = synth.activations(seed, m, d)
     s = synth.signs(seed)
-    got = host(P.ptq1_ffn_block(to_dev(x), to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, eps))
+    got = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f, eps))
     ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, eps)
     assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
 
@@ -402,7 +440,7 @@ def test_ffn_block_in_place():
     for m in (1, 4):
         x = synth.activations(seed, m, d)
         xd = to_dev(x)
-        P.ptq1_ffn_block(xd, to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, 1e-6, out=xd)
+        P.ptq1_ffn_block(xd, tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f, 1e-6, out=xd)
         ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
         assert rel_l2(host(xd), ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
 
@@ -414,6 +452,7 @@ def test_ffn_block_full_shape(m):
     wg, wu, wd = _ffn_host(seed, d, f)
     x = synth.activations(seed, m, d)
     s = synth.signs(seed)
-    got = host(P.ptq1_ffn_block(to_dev(x), to_dev(wg), to_dev(wu), to_dev(wd), to_dev(s), d, f, 1e-6))
+    got = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f,
+                                1e-6))
     ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
     assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
