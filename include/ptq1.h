@@ -48,14 +48,13 @@
  *   - ptq1_last_error() then names the refused argument (thread-local);
  *   - the library allocates no memory; calls that need scratch take a
  *     caller-owned workspace `ws` of at least the size the matching
- *     *_workspace_bytes() returns, 256-byte aligned.  A workspace must be
- *     zero-filled once before its first use (hipMemset or a fill kernel):
- *     its first 256 KB hold per-row-group arrival counters that every
- *     completed call leaves at zero again, the rest is scratch, so one
+ *     *_workspace_bytes() returns, 256-byte aligned, with any contents: it
+ *     is scratch, written before it is read within each call, so one
  *     workspace may serve calls of any shape and entry point.  Calls that
  *     share a workspace must be ordered on one stream; two calls in flight
  *     at once must not share one.  The decode calls (matvec, gate_up,
- *     ffn_block with m = 1) take at most 2^20 output rows per matrix;
+ *     ffn_block with m = 1) take at most 2^20 output rows per matrix and
+ *     tiled matrices below 2 GiB;
  *   - `float *` buffers must be 16-byte aligned, weights 16-byte aligned;
  *   - sizes are int64_t; products are checked for overflow.
  */
@@ -162,8 +161,9 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
  *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
  *   tiled   [n][k] in the tiled layout; x fp32 [k]; residual fp32 [n] or
  *   NULL; y fp32 [n] (y may equal residual, must not overlap x or tiled).
- * One launch; trits are decoded through a per-slice table of byte-position x
- * byte-value partial dot products built from xr, fp32 throughout.
+ * Trits are decoded through a per-slice table of byte-position x byte-value
+ * partial dot products built from xr, fp32 throughout; two launches (split-K
+ * partials over 256-wide K-slices, then their sum in slice order).
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k);
 ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x,

@@ -117,7 +117,7 @@ def _ws(nbytes: int, device, ws):
         return None, 0
     if ws is not None and ws.numel() >= nbytes:
         return ws, ws.numel()
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 # ------------------------------------------------------------------ codec ----
@@ -217,8 +217,8 @@ def hadamard_unrotate_rows(table: torch.Tensor, signs1024: torch.Tensor, ids: to
 def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
                 residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 ws: torch.Tensor | None = None, stream=None, fn: str = "ptq1_matvec") -> torch.Tensor:
-    """y = residual + W R x, W tiled (ptq1_tile).  ws (if given) must have
-    been zero-filled once."""
+    """y = residual + W R x, W tiled (ptq1_tile).  ws: optional scratch of
+    at least workspace_bytes("matvec", n, k) bytes."""
     _dev(blocks, "blocks", torch.uint8)
     _dev(x, "x", torch.float32)
     if out is None:

@@ -68,13 +68,9 @@ constexpr size_t kWsAlign = 256;
 constexpr int64_t kMaxGemmM = 65536;
 constexpr int64_t kMaxGridX = 2147483647;
 constexpr int64_t kMaxGridY = 65535;
-// Every workspace starts with a fixed counter region, so that calls of any
-// shape or entry point can share one zero-initialised workspace: the
-// lookup-table matvec keeps its per-32-row-group arrival counters there
-// (left at zero after each call) and nothing else ever writes it.
-constexpr size_t kCounterBytes = 256 * 1024;
-constexpr int64_t kMaxLutRows = int64_t{1} << 20;  // one counter per 32 rows: 32768 of 65536 words
-static_assert(kMaxLutRows / 32 <= static_cast<int64_t>(kCounterBytes / sizeof(uint32_t)), "counter region");
+// Decode calls: rows per matrix (keeps the matvec grid's second dimension,
+// chunks of 32-row groups, far below its limit).
+constexpr int64_t kMaxLutRows = int64_t{1} << 20;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -165,52 +161,40 @@ ptq1_status check_ws(const void *ws, size_t ws_bytes, size_t need, const char *f
 int64_t nseg_of(int64_t k) { return (k + ptq1::kHadamard - 1) / ptq1::kHadamard; }
 
 // ---- workspace layouts -------------------------------------------------------
-// float-peel matvec: partials after the counter region
+// float-peel matvec: partials [1024-segment][row]
 size_t mv_ws(int64_t rows, int64_t k)
 {
-    return kCounterBytes + round_up(ptq1::matvec_part_floats(rows, k) * sizeof(float), kWsAlign);
+    return round_up(ptq1::matvec_part_floats(rows, k) * sizeof(float), kWsAlign);
 }
 
-// lookup-table decode: counters at 0, split-K partials after them
-struct LutWs {
-    size_t cnt = 0, part = 0, total = 0;
-};
-
-LutWs lut_layout(int64_t n, int nmat, int64_t k)
+// lookup-table decode: split-K partials [slice][matrix][row]
+size_t lut_ws(int64_t n, int nmat, int64_t k)
 {
-    LutWs L;
-    L.cnt = 0;
-    L.part = kCounterBytes;
-    L.total = L.part + round_up(ptq1::lut_part_floats(n, nmat, k) * sizeof(float), kWsAlign);
-    return L;
+    return round_up(ptq1::lut_part_floats(n, nmat, k) * sizeof(float), kWsAlign);
 }
 
-// GEMM: bf16 activations after the counter region
+// GEMM: bf16 activations [m_pad][k]
 size_t gemm_ws(int64_t m, int64_t k)
 {
-    return kCounterBytes +
-           round_up(static_cast<size_t>(ptq1::gemm_m_pad(m)) * static_cast<size_t>(k) * 2, kWsAlign);
+    return round_up(static_cast<size_t>(ptq1::gemm_m_pad(m)) * static_cast<size_t>(k) * 2, kWsAlign);
 }
 
 struct FfnWs {
-    size_t part = 0, cnt = 0, g = 0, u = 0, h = 0, xb = 0, total = 0;  // byte offsets
+    size_t part = 0, hr = 0, g = 0, u = 0, xb = 0, total = 0;  // byte offsets (hr: h at m = 1)
 };
 
 FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
 {
     FfnWs L;
-    L.cnt = 0;
-    size_t off = kCounterBytes;
+    size_t off = 0;
     if (m == 1) {
-        const size_t part_a = ptq1::lut_part_floats(f, 2, d), part_b = ptq1::lut_part_floats(d, 1, f);
+        const size_t part_a = lut_ws(f, 2, d), part_b = lut_ws(d, 1, f);
         L.part = off;
-        off += round_up((part_a > part_b ? part_a : part_b) * sizeof(float), kWsAlign);
-        L.g = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
-        L.u = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
-        L.h = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
+        off += part_a > part_b ? part_a : part_b;
+        L.hr = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
     } else {
         L.xb = off;
-        off += gemm_ws(m, d > f ? d : f) - kCounterBytes;
+        off += gemm_ws(m, d > f ? d : f);
         L.g = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
         L.u = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
     }
@@ -339,7 +323,7 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0) return 0;
-    const size_t a = mv_ws(n, k), b = lut_layout(n, 1, k).total;
+    const size_t a = mv_ws(n, k), b = lut_ws(n, 1, k);
     return a > b ? a : b;
 }
 
@@ -387,13 +371,10 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
     bool empty;
     PTQ1_TRY(check_matvec(tiled, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec", true, &empty));
     if (empty) return ok();
-    const LutWs L = lut_layout(n, 1, k);
-    char *w = static_cast<char *>(ws);
-    return hip_status(ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024,
-                                              reinterpret_cast<float *>(w + L.part),
-                                              reinterpret_cast<uint32_t *>(w + L.cnt), residual, y,
-                                              nullptr, nullptr, nullptr, nullptr, 0, 0.0f, stream),
-                      "ptq1_matvec");
+    float *part = static_cast<float *>(ws);
+    hipError_t e = ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024, part, stream);
+    if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
+    return hip_status(e, "ptq1_matvec");
 }
 
 ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
@@ -404,7 +385,7 @@ ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, 
     PTQ1_TRY(check_matvec(blocks, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec_float_peel",
                           false, &empty));
     if (empty) return ok();
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
+    float *part = static_cast<float *>(ws);
     hipError_t e = ptq1::launch_matvec_part(blocks, n, nullptr, 0, k, x, signs1024, part, stream);
     if (e == hipSuccess) e = ptq1::launch_reduce_rows(part, n, nseg_of(k), residual, y, stream);
     return hip_status(e, "ptq1_matvec_float_peel");
@@ -413,7 +394,7 @@ ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, 
 size_t ptq1_gate_up_workspace_bytes(int64_t f, int64_t d)
 {
     if (packed_bytes(f, d) < 0 || f > INT64_MAX / 2) return 0;
-    return lut_layout(f, 2, d).total;
+    return lut_ws(f, 2, d);
 }
 
 ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, int64_t d,
@@ -428,7 +409,7 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
     if (f == 0) return ok();
     PTQ1_TRY(check_floats(x, "x", d, &xb));
     PTQ1_TRY(check_signs(signs1024, false));
-    const size_t need = lut_layout(f, 2, d).total;
+    const size_t need = lut_ws(f, 2, d);
     PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gate_up"));
     if (overlaps(g, gb, u, ub)) return fail(PTQ1_ERR_ALIAS, "g overlaps u");
     if (overlaps(g, gb, x, xb) || overlaps(u, ub, x, xb)) return fail(PTQ1_ERR_ALIAS, "g or u overlaps x");
@@ -438,13 +419,11 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
     if (nseg_of(d) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
     if (f > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "f = %lld > %lld rows", (long long)f, (long long)kMaxLutRows);
     if (wgb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
-    const LutWs L = lut_layout(f, 2, d);
-    char *w = static_cast<char *>(ws);
-    return hip_status(ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024,
-                                              reinterpret_cast<float *>(w + L.part),
-                                              reinterpret_cast<uint32_t *>(w + L.cnt), nullptr, nullptr, g,
-                                              u, nullptr, nullptr, 0, 0.0f, stream),
-                      "ptq1_gate_up");
+    float *part = static_cast<float *>(ws);
+    hipError_t e = ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+    if (e == hipSuccess)
+        e = ptq1::launch_lut_gate_up_sum(part, f, d, nullptr, 0, 0.0f, g, u, nullptr, stream);
+    return hip_status(e, "ptq1_gate_up");
 }
 
 ptq1_status ptq1_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t stream)
@@ -486,7 +465,7 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
         overlaps(ws, (int64_t)need, tiled, wb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
     const int64_t m_pad = ptq1::gemm_m_pad(m);
-    uint16_t *xbf = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kCounterBytes);
+    uint16_t *xbf = static_cast<uint16_t *>(ws);
     hipError_t e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, k, signs1024, 0.0f, xbf, stream);
     if (e == hipSuccess)
         e = ptq1::launch_gemm(xbf, m, m_pad, k, tiled, n, nullptr, 0, y, nullptr, nullptr, stream);
@@ -534,16 +513,15 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
     char *w = static_cast<char *>(ws);
     hipError_t e;
     if (m == 1) {
+        // gate/up partials -> RMS scale and SwiGLU -> down partials over R h -> + x
         float *part = reinterpret_cast<float *>(w + L.part);
-        uint32_t *cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
-        float *g = reinterpret_cast<float *>(w + L.g);
-        float *u = reinterpret_cast<float *>(w + L.u);
-        float *h = reinterpret_cast<float *>(w + L.h);
-        e = ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, cnt, nullptr, nullptr, g, u, h,
-                                    rms_eps > 0.0f ? x : nullptr, d, rms_eps, stream);
+        float *h = reinterpret_cast<float *>(w + L.hr);
+        e = ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
         if (e == hipSuccess)
-            e = ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, part, cnt, x, x_out, nullptr,
-                                        nullptr, nullptr, nullptr, 0, 0.0f, stream);
+            e = ptq1::launch_lut_gate_up_sum(part, f, d, rms_eps > 0.0f ? x : nullptr, d, rms_eps, nullptr, nullptr,
+                                             h, stream);
+        if (e == hipSuccess) e = ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, part, stream);
+        if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, d, f, x, x_out, stream);
     } else {
         const int64_t m_pad = ptq1::gemm_m_pad(m);
         uint16_t *xbf = reinterpret_cast<uint16_t *>(w + L.xb);

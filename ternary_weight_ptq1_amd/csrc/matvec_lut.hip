@@ -25,7 +25,7 @@
 //     assembles the address from the data byte and a per-lane constant byte;
 //     slots 26, 27 of each block (the scale bytes) hold zeros; at 64 KB, two
 //     workgroups share a CU, so one's latency-bound phases (rotation, table
-//     build, final reduction) overlap the other's lookups;
+//     build) overlap the other's lookups;
 //   - weights are read in the tiled layout: the 32 rows x 2 blocks of a unit
 //     are one contiguous 1792-byte tile, lane 2i + b holding block b of row
 //     i, so a wave's loads are fully used 128-byte lines (a row-major matrix
@@ -33,19 +33,22 @@
 //     measured at well under half the bandwidth);
 //   - a workgroup (512 threads) owns one slice and a run of (matrix, 32-row
 //     group) units of it; wave 0 rotates the slice's 1024-chunk of x in
-//     registers, all threads build the table, then each of the 8 waves
-//     processes exactly U units (U is a template parameter chosen per launch
-//     so the grid fits two workgroups per CU), with all U units' weights
-//     requested before the table is built; a lane reads its 28-byte block
-//     with two wide loads and rotates its 7 dwords (and the byte order within
-//     a dword) by a lane-dependent amount so the 32 lanes of a half-wave
-//     (16 rows x 2 blocks) spread over LDS banks;
+//     registers (its loads requested before any weights: vector-memory loads
+//     return in order), all threads build the table, and each of the 8 waves
+//     processes U units (U is a template parameter chosen per launch so the
+//     grid fits two workgroups per CU) with kLutDepth units of weights in
+//     flight; a lane reads its 28-byte block with two wide loads and rotates
+//     its 7 dwords (and the byte order within a dword) by a lane-dependent
+//     amount so the 32 lanes of a half-wave (16 rows x 2 blocks) spread over
+//     LDS banks;
 //   - a unit's 2 block partials (times their fp16 scales) are summed across
-//     lanes with one xor-shuffle and written as split-K partials; a
-//     per-group counter (atomicInc with wrap, so it is back to zero after
-//     every launch) lets the last unit of a group sum the partials of all
-//     slices in fixed order and apply the epilogue: store, + residual, or
-//     (gate, up) -> RMS scale -> SwiGLU.  One launch, deterministic.
+//     lanes with one xor-shuffle and stored as split-K partials
+//     part[slice][matrix][row]; a second kernel sums each row's partials in
+//     slice order and applies the epilogue (+ residual, or RMS scale and
+//     SwiGLU).  The kernel boundary makes the partials visible across XCDs
+//     at once; finishing inside the matvec kernel instead (arrival counters
+//     and device-scope loads that bypass the L2) measured slower, its
+//     round trips to memory sitting at the end of the critical path.
 #include "ptq1_device.h"
 #include "ptq1_launch.h"
 
@@ -58,118 +61,111 @@ constexpr int kLutThreads = 512;
 constexpr int kLutWaves = kLutThreads / kWave;         // 8
 constexpr int kLutRows = 32;                           // rows per unit
 constexpr int kLutTableBytes = 65536;                  // 256 byte values x 64 slot columns x fp32
+constexpr int kLutDepth = 3;                           // units of weights in flight per wave
 static_assert(kLutRows == kTileRows && kLutBlocks == kTileBlocks, "a unit is one tile");
 static_assert(kLutRows * kLutBlocks == kWave, "one block per lane");
 
 // Per-lane dword rotation (rho) and byte rotation (sigma) for lanes 0..31
 // (lanes 32..63 repeat them; lane 2i + b reads block b of row i): found by a
 // search that minimises LDS bank collisions of the 32 slots a half-wave
-// reads per lookup.
-__constant__ uint8_t kLutRho[32] = {4, 6, 6, 1, 1, 5, 3, 2, 5, 3, 3, 3, 3, 6, 0, 5,
-                                    1, 6, 3, 0, 2, 3, 1, 6, 6, 1, 6, 0, 4, 2, 0, 5};
-__constant__ uint8_t kLutSig[32] = {0, 3, 1, 2, 1, 1, 1, 0, 0, 0, 3, 2, 0, 2, 1, 2,
-                                    0, 1, 2, 1, 3, 1, 2, 0, 2, 3, 3, 0, 3, 3, 0, 3};
+// reads per lookup.  Packed into 64-bit immediates so a lane derives its own
+// pair arithmetically (a table in memory would put a load latency in front
+// of the weight requests).
+constexpr uint8_t kLutRho[32] = {4, 6, 6, 1, 1, 5, 3, 2, 5, 3, 3, 3, 3, 6, 0, 5,
+                                 1, 6, 3, 0, 2, 3, 1, 6, 6, 1, 6, 0, 4, 2, 0, 5};
+constexpr uint8_t kLutSig[32] = {0, 3, 1, 2, 1, 1, 1, 0, 0, 0, 3, 2, 0, 2, 1, 2,
+                                 0, 1, 2, 1, 3, 1, 2, 0, 2, 3, 3, 0, 3, 3, 0, 3};
+
+constexpr uint64_t lut_pack_nibbles(const uint8_t (&t)[32], int first)
+{
+    uint64_t v = 0;
+    for (int i = 0; i < 16; ++i) v |= static_cast<uint64_t>(t[first + i] & 15) << (4 * i);
+    return v;
+}
+
+constexpr uint64_t lut_pack_pairs(const uint8_t (&t)[32])
+{
+    uint64_t v = 0;
+    for (int i = 0; i < 32; ++i) v |= static_cast<uint64_t>(t[i] & 3) << (2 * i);
+    return v;
+}
+
+constexpr uint64_t kLutRhoLo = lut_pack_nibbles(kLutRho, 0);
+constexpr uint64_t kLutRhoHi = lut_pack_nibbles(kLutRho, 16);
+constexpr uint64_t kLutSigAll = lut_pack_pairs(kLutSig);
+
+__device__ __forceinline__ int lut_rho(int lane)
+{
+    const int l = lane & 31;
+    return static_cast<int>(((l < 16 ? kLutRhoLo : kLutRhoHi) >> (4 * (l & 15))) & 15u);
+}
+
+__device__ __forceinline__ int lut_sig(int lane) { return static_cast<int>((kLutSigAll >> (2 * (lane & 31))) & 3u); }
 
 struct LutArgs {
     const uint8_t *w0, *w1;  // one or two tiled [n][k] matrices
     int64_t n, k;            // rows per matrix, K
     int nmat, nslices;
     int64_t groups;          // ceil(n / 32)
-    int64_t units;           // nslices * nmat * groups
-    int64_t units_per_wg;
-    const float *x, *signs;
+    const float *x, *signs;  // x [k], rotated here when signs != nullptr
     float *part;             // [nslices][nmat][n]
-    uint32_t *cnt;           // [groups], zero between launches
-    // epilogue
-    const float *residual;   // single matrix: y = residual + W xr
-    float *y;
-    float *g, *u, *h;        // two matrices: g, u (optional) and h = silu(a g) (a u)
-    const float *x_rms;      // RMS scale source (nullptr: a = 1)
-    int64_t d_rms;
-    float rms_eps;
 };
 
 // T[slot][b] for b in [32 BQ, 32 BQ + 32): with v = floor(243 b / 256) the
-// code of byte b and d_n its base-3 digits, T = ((d0-1) x0 + (d1-1) x1) +
-// ((d2-1) x2 + (d3-1) x3 + (d4-1) x4); the digits are compile-time constants
-// of the unrolled loop, so each entry is a few adds.
+// code of byte b and d_n its base-3 digits, T = A[d0][d1] + B[d2][d3][d4]
+// where A = (d0-1) x0 + (d1-1) x1 and B = ((d2-1) x2 + (d3-1) x3) + (d4-1) x4
+// are formed once per thread (9 + 27 sums); the digits are compile-time
+// constants of the unrolled loop, so each entry costs one add.
 template <int BQ>
 __device__ __forceinline__ void lut_build_range(float *tab, int slot, const float (&xv)[5])
 {
+    float A[9], B[27];
+#pragma unroll
+    for (int d0 = 0; d0 < 3; ++d0)
+#pragma unroll
+        for (int d1 = 0; d1 < 3; ++d1)
+            A[3 * d0 + d1] = static_cast<float>(d0 - 1) * xv[0] + static_cast<float>(d1 - 1) * xv[1];
+#pragma unroll
+    for (int d2 = 0; d2 < 3; ++d2)
+#pragma unroll
+        for (int d3 = 0; d3 < 3; ++d3) {
+            const float c = static_cast<float>(d2 - 1) * xv[2] + static_cast<float>(d3 - 1) * xv[3];
+#pragma unroll
+            for (int d4 = 0; d4 < 3; ++d4) B[9 * d2 + 3 * d3 + d4] = c + static_cast<float>(d4 - 1) * xv[4];
+        }
     const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int b = 32 * BQ + i;
         const int v = (243 * b) >> 8;
-        const float c0 = static_cast<float>(v / 81 - 1), c1 = static_cast<float>((v / 27) % 3 - 1);
-        const float c2 = static_cast<float>((v / 9) % 3 - 1), c3 = static_cast<float>((v / 3) % 3 - 1);
-        const float c4 = static_cast<float>(v % 3 - 1);
-        const float t = (c0 * xv[0] + c1 * xv[1]) + (c2 * xv[2] + c3 * xv[3] + c4 * xv[4]);
-        *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) = t;
+        *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
+            A[v / 27] + B[v % 27];
     }
 }
 
-// Split-K partials cross workgroups (and XCDs, whose L2s are not coherent
-// for plain accesses): they are written and read with device-scope relaxed
-// atomic accesses, which reach the coherence point themselves, instead of
-// device-scope fences, which would write back and invalidate a whole L2.
-__device__ __forceinline__ float lut_load_part(const float *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void lut_store_part(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // One unit = (slice s, matrix mat, 32-row group grp) = tile (grp, s) of
-// matrix mat.  Row counts are below 2^20 (checked by the caller), so
-// indices fit in int.
+// matrix mat; `un` indexes the units of one slice (matrix-major).  Row
+// counts are below 2^20 (checked by the caller), so indices fit in int.
 struct LutUnit {
-    int mat, grp, r;
-    bool live;
+    int mat, grp;
 };
 
-__device__ __forceinline__ LutUnit lut_unit(const LutArgs &a, int64_t un, int s, int64_t per_slice, int row_l,
-                                           int blk_l, int nblk)
+__device__ __forceinline__ LutUnit lut_unit(const LutArgs &a, int64_t un)
 {
     LutUnit u;
-    const int rem = static_cast<int>(un - static_cast<int64_t>(s) * per_slice);
+    const int rem = static_cast<int>(un);
     const int groups = static_cast<int>(a.groups);
     u.mat = rem >= groups ? 1 : 0;
     u.grp = rem - u.mat * groups;
-    u.r = u.grp * kLutRows + row_l;
-    u.live = (u.r < static_cast<int>(a.n)) && (blk_l < nblk);
     return u;
 }
 
-// A block's 7 dwords, read with two wide loads (16 + 12 bytes; blocks are
-// only dword-aligned, which gfx950 global loads accept).  The lanes of a wave
-// cover one 1792-byte tile.
 typedef uint32_t lut_u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t lut_u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 
-__device__ __forceinline__ void lut_load(const LutArgs &a, const LutUnit &u, int s, int lane,
-                                         uint32_t (&d)[kBlockDwords])
-{
-    // Unconditional loads (a branch around them would make the compiler wait
-    // for each load before the next): padding rows and blocks of the tiled
-    // layout exist (zero bytes) and their scale is zeroed by the caller.
-    // Wave-uniform matrix base + 32-bit per-lane byte offset (tiled matrices
-    // below 2 GiB, checked by the caller).
-    const uint8_t *wm = u.mat ? a.w1 : a.w0;
-    const uint32_t off = (static_cast<uint32_t>(u.grp) * static_cast<uint32_t>(a.nslices) +
-                          static_cast<uint32_t>(s)) * kTileBytes + static_cast<uint32_t>(lane) * kBlockBytes;
-    const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(wm + off);
-    const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(wm + off + 16);
-    d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
-    d[4] = hi.x; d[5] = hi.y; d[6] = hi.z;
-}
-
 // d[j] <- d[(j + rho) mod 7]: a three-stage rotate by 1, 2 and 4.  The
-// stages merge values with a lane mask (one v_bfi_b32 each); a select of
-// array elements would become a dynamically indexed (private-memory) array.
+// stages merge values with a lane mask; a select of array elements would
+// become a dynamically indexed (private-memory) array.
 __device__ __forceinline__ void lut_rotate(uint32_t (&d)[kBlockDwords], int rho)
 {
 #pragma unroll
@@ -183,113 +179,95 @@ __device__ __forceinline__ void lut_rotate(uint32_t (&d)[kBlockDwords], int rho)
     }
 }
 
-// Finish up to two completed row groups at once (one whole wave): lane =
-// (group of the batch, row of the group); each lane sums its row's partials
-// over all slices in slice order and applies the epilogue.  Every partial of
-// a round of 16 slices is requested before any is summed.
-__device__ void lut_finish(const LutArgs &a, const int (&grp)[2], int ngrp, int lane, float rms_a)
-{
-    constexpr int kPer = 16;
-    const int gi = lane >> 5;
-    const int64_t r_raw = gi < ngrp ? static_cast<int64_t>(grp[gi]) * kLutRows + (lane & (kLutRows - 1)) : a.n;
-    const bool ok = r_raw < a.n;
-    const int64_t r = ok ? r_raw : 0;  // clamped: every lane loads, no branch around the loads
-    const int64_t stride = static_cast<int64_t>(a.nmat) * a.n;  // floats between slices
-    const float *p0 = a.part + r;
-    const float *p1 = a.part + (a.nmat == 2 ? a.n : 0) + r;
-    float t0 = 0.0f, t1 = 0.0f;
-    for (int q0 = 0; q0 < a.nslices; q0 += kPer) {
-        float v0[kPer], v1[kPer];
-#pragma unroll
-        for (int c = 0; c < kPer; ++c) {
-            const int q = q0 + c < a.nslices ? q0 + c : a.nslices - 1;
-            v0[c] = lut_load_part(p0 + q * stride);
-            v1[c] = lut_load_part(p1 + q * stride);
-        }
-#pragma unroll
-        for (int c = 0; c < kPer; ++c) {
-            if (q0 + c < a.nslices) {
-                t0 += v0[c];
-                t1 += v1[c];
-            }
-        }
-    }
-    if (ok) {
-        if (a.nmat == 1) {
-            a.y[r] = a.residual ? a.residual[r] + t0 : t0;
-        } else {
-            const float gv = t0 * rms_a, uv = t1 * rms_a;
-            if (a.g) a.g[r] = gv;
-            if (a.u) a.u[r] = uv;
-            if (a.h) a.h[r] = gv / (1.0f + expf(-gv)) * uv;
-        }
-    }
-}
-
+// U: units per wave.
 template <int U>
-__global__ void __launch_bounds__(kLutThreads, 2) k_matvec_lut(LutArgs a)
+__global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 waves per SIMD: two workgroups per CU
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     float *tab = reinterpret_cast<float *>(lds);                 // 64 KB table
     float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 256 floats
-    float *red = xs + kLutSliceW;                               // 16 floats
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-    const int s = blockIdx.y;                                      // the slice
+    const int s = blockIdx.x;                                      // the slice
     const int64_t per_slice = static_cast<int64_t>(a.nmat) * a.groups;
-    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kLutWaves + wave) * U;  // this wave's first unit
+    const int64_t first = (static_cast<int64_t>(blockIdx.y) * kLutWaves + wave) * U;  // this wave's first unit
     const int64_t k0 = static_cast<int64_t>(s) * kLutSliceW;
     const int kw = static_cast<int>(a.k - k0 < kLutSliceW ? a.k - k0 : kLutSliceW);
     const int nblk = kw / kBlockWeights;
     const int row_l = lane >> 1;  // row of the unit (tile) this lane reads
     const int blk_l = lane & 1;   // block of the slice this lane reads
-    const int rho = kLutRho[lane & 31], sig = kLutSig[lane & 31];
+    const int rho = lut_rho(lane), sig = lut_sig(lane);
 
-    // ---- this wave's U units of weights, requested before anything else
+    // ---- 1. the table's input is requested before the weights: vector
+    // memory returns in order, so anything requested after the weights
+    // would wait for all of them.
+    const int64_t c0 = (k0 / kHadamard) * kHadamard;  // 1024-chunk holding the slice
+    float xv16[kRotPerLane], sv16[kRotPerLane];
+    if (wave == 0) {
+        if (a.signs != nullptr) {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane; ++j) {
+                xv16[j] = a.x[c0 + lane + kWave * j];
+                sv16[j] = a.signs[lane + kWave * j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane / 4; ++j) {
+                const int e = lane + kWave * j;
+                xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];  // clamped; zeroed below
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. weights of this wave's first kLutDepth units (the rest are
+    // requested one unit ahead of use during the lookups, so a wave never
+    // has more than kLutDepth units in flight and reaches the table barrier
+    // without waiting for the memory queue): the lane's 28-byte block with
+    // two wide loads (16 + 12 bytes; blocks are only dword-aligned, which
+    // gfx950 global loads accept) at a wave-uniform tile base.
     uint32_t dat[U][kBlockDwords];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
+    auto issue = [&](int i) {
         const int64_t un = first + i < per_slice ? first + i : per_slice - 1;  // clamped: no branch
-        lut_load(a, lut_unit(a, un + static_cast<int64_t>(s) * per_slice, s, per_slice, row_l, blk_l, nblk),
-                 s, lane, dat[i]);
-    }
+        const LutUnit u = lut_unit(a, un);
+        // tiled matrices are below 2 GiB (checked by the caller)
+        const uint8_t *blk = (u.mat ? a.w1 : a.w0) +
+                             (static_cast<uint32_t>(u.grp) * static_cast<uint32_t>(a.nslices) +
+                              static_cast<uint32_t>(s)) * static_cast<uint32_t>(kTileBytes) +
+                             static_cast<uint32_t>(lane * kBlockBytes);
+        const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(blk);
+        const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(blk + 16);
+        dat[i][0] = lo.x; dat[i][1] = lo.y; dat[i][2] = lo.z; dat[i][3] = lo.w;
+        dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z;
+    };
+#pragma unroll
+    for (int i = 0; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- RMS scale of the block input (gate/up epilogue only)
-    float rms_a = 1.0f;
-    if (a.x_rms != nullptr) {
-        float sq = 0.0f;
-        for (int64_t i = tid; i < a.d_rms; i += kLutThreads) sq = fmaf(a.x_rms[i], a.x_rms[i], sq);
+    // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
+    if (wave == 0) {
+        if (a.signs != nullptr) {
 #pragma unroll
-        for (int h = kWave / 2; h > 0; h >>= 1) sq += __shfl_xor(sq, h, kWave);
-        if (lane == 0) red[wave] = sq;
-    }
-    // ---- x for this slice (rotated when signs are given: k % 1024 == 0)
-    if (a.signs != nullptr) {
-        if (wave == 0) {
-            const int64_t c0 = (k0 / kHadamard) * kHadamard;
+            for (int j = 0; j < kRotPerLane; ++j) xv16[j] *= sv16[j];
+            fwht1024_wave(xv16);
             const int part = static_cast<int>(k0 - c0);  // 0, 256, 512 or 768
-            float v[kRotPerLane];
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j) v[j] = a.x[c0 + lane + kWave * j] * a.signs[lane + kWave * j];
-            fwht1024_wave(v);
 #pragma unroll
             for (int j = 0; j < kRotPerLane; ++j) {
                 const int e = lane + kWave * j - part;
-                if (e >= 0 && e < kLutSliceW) xs[e] = v[j] * (1.0f / 32.0f);
+                if (e >= 0 && e < kLutSliceW) xs[e] = xv16[j] * (1.0f / 32.0f);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane / 4; ++j) {
+                const int e = lane + kWave * j;
+                xs[e] = e < kw ? xv16[j] : 0.0f;
             }
         }
-    } else {
-        for (int i = tid; i < kLutSliceW; i += kLutThreads) xs[i] = i < kw ? a.x[k0 + i] : 0.0f;
     }
     __syncthreads();
-    if (a.x_rms != nullptr) {
-        float t = 0.0f;
-        for (int w = 0; w < kLutWaves; ++w) t += red[w];
-        rms_a = 1.0f / sqrtf(t / static_cast<float>(a.d_rms) + a.rms_eps);
-    }
-    // ---- table: thread = (slot, 32-value range of the byte)
+    // ---- 4. table: thread = (slot, 32-value range of the byte)
     {
         const int bq = tid >> 6;  // 0..7
         const int slot = tid & 63;
@@ -315,8 +293,9 @@ __global__ void __launch_bounds__(kLutThreads, 2) k_matvec_lut(LutArgs a)
     }
     __syncthreads();
 
-    // ---- per-lane lookup constants.  Address of the lookup for byte c of
-    // the lane's j-th dword: byte << 8 | slot << 2; the four slot bytes of a
+    // ---- 5. per-lane lookup constants.  After the rotation, register dword
+    // j holds dword (j + rho) mod 7 of the block; the address of the lookup
+    // for its byte c is byte << 8 | slot << 2; the four slot bytes of a
     // dword are packed in one register (byte c) and v_perm_b32 inserts the
     // data byte (selector: byte 0 <- P byte c, byte 1 <- data byte e, 0, 0).
     uint32_t P[kBlockDwords];
@@ -338,15 +317,17 @@ __global__ void __launch_bounds__(kLutThreads, 2) k_matvec_lut(LutArgs a)
         P[j] = packed;
     }
 
-    // ---- lookups, scale, 2-lane reduction, partial store
+    // ---- 6. lookups, scale, 2-lane reduction, partial store
     typedef __attribute__((address_space(3))) const float lds_f32;
-    int my_grp = 0;  // lane i records the group of unit i
 #pragma unroll
     for (int i = 0; i < U; ++i) {
+        if (i + kLutDepth < U) issue(i + kLutDepth);  // compile-time condition
         const bool unit_ok = first + i < per_slice;  // wave-uniform
         const int64_t un = unit_ok ? first + i : per_slice - 1;
-        const LutUnit u = lut_unit(a, un + static_cast<int64_t>(s) * per_slice, s, per_slice, row_l, blk_l, nblk);
-        const float scale = (u.live && unit_ok) ? half_bits_to_float(dat[i][kBlockDwords - 1] >> 16) : 0.0f;
+        const LutUnit u = lut_unit(a, un);
+        const int r = u.grp * kLutRows + row_l;
+        const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
+        const float scale = live ? half_bits_to_float(dat[i][kBlockDwords - 1] >> 16) : 0.0f;
         lut_rotate(dat[i], rho);
         float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
@@ -360,39 +341,10 @@ __global__ void __launch_bounds__(kLutThreads, 2) k_matvec_lut(LutArgs a)
         }
         float p = (acc0 + acc1) * scale;
         p += __shfl_xor(p, 1, kWave);
-        if (unit_ok && blk_l == 0 && u.r < a.n)
-            lut_store_part(a.part + (static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + u.r, p);
-        if (lane == i) my_grp = u.grp;
-    }
-
-    // ---- arrivals: all partial stores complete at the coherence point
-    // (s_waitcnt vmcnt(0); gfx9 encoding, expcnt/lgkmcnt not waited), then
-    // one atomic per lane counts unit `lane`; the last arrival of a row group
-    // sums that group's partials over all slices and finishes it.
-    const int nu = first < per_slice ? static_cast<int>(per_slice - first < U ? per_slice - first : U) : 0;
-    if (nu > 0) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        const uint32_t target = static_cast<uint32_t>(a.nslices * a.nmat);
-        uint32_t old = 0;
-        if (lane < nu) old = atomicInc(&a.cnt[my_grp], target - 1u);
-        uint64_t last = __ballot(lane < nu && old == target - 1u);
-        while (last) {
-            int grp2[2];
-            int ng = 0;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                grp2[q] = 0;
-                if (last) {
-                    const int i = __builtin_ctzll(last);
-                    last &= last - 1;
-                    grp2[q] = __shfl(my_grp, i, kWave);
-                    ng = q + 1;
-                }
-            }
-            lut_finish(a, grp2, ng, lane, rms_a);
-        }
+        if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r] = p;
     }
 }
+
 
 static int device_cus()
 {
@@ -408,34 +360,30 @@ static int device_cus()
     return cached[dev];
 }
 
-size_t lut_part_floats(int64_t n, int nmat, int64_t k)
-{
-    const int64_t nslices = (k + kLutSliceW - 1) / kLutSliceW;
-    return static_cast<size_t>(nslices * nmat * n);
-}
+int64_t lut_nslices(int64_t k) { return (k + kLutSliceW - 1) / kLutSliceW; }
 
-size_t lut_counter_words(int64_t n) { return static_cast<size_t>((n + kLutRows - 1) / kLutRows); }
+size_t lut_part_floats(int64_t n, int nmat, int64_t k) { return static_cast<size_t>(lut_nslices(k) * nmat * n); }
 
 template <int U>
 static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
 {
     static bool attr_done = false;
-    const size_t lds = kLutTableBytes + (kLutSliceW + kLutWaves) * sizeof(float);
+    const size_t lds = kLutTableBytes + kLutSliceW * sizeof(float);
     if (!attr_done) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_matvec_lut<U>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipLaunchKernelGGL(k_matvec_lut<U>, dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(a.nslices)),
+    // x = slice (fastest in dispatch order): the slices of a row band start
+    // together and read neighbouring tiles
+    hipLaunchKernelGGL(k_matvec_lut<U>, dim3(static_cast<unsigned>(a.nslices), static_cast<unsigned>(chunks)),
                        dim3(kLutThreads), lds, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, float *part, uint32_t *cnt,
-                             const float *residual, float *y, float *g, float *u, float *h,
-                             const float *x_rms, int64_t d_rms, float rms_eps, hipStream_t s)
+                             const float *x, const float *signs, float *part, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
     LutArgs a{};
@@ -444,21 +392,11 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.n = n;
     a.k = k;
     a.nmat = nmat;
-    a.nslices = static_cast<int>((k + kLutSliceW - 1) / kLutSliceW);
+    a.nslices = static_cast<int>(lut_nslices(k));
     a.groups = (n + kLutRows - 1) / kLutRows;
-    a.units = static_cast<int64_t>(a.nslices) * nmat * a.groups;
     a.x = x;
     a.signs = signs;
     a.part = part;
-    a.cnt = cnt;
-    a.residual = residual;
-    a.y = y;
-    a.g = g;
-    a.u = u;
-    a.h = h;
-    a.x_rms = x_rms;
-    a.d_rms = d_rms;
-    a.rms_eps = rms_eps;
     // units per wave: the smallest U whose grid (slices x chunks of 8U units)
     // fits two workgroups per CU in one round, else the largest U
     const int64_t per_slice = static_cast<int64_t>(nmat) * a.groups;
@@ -473,7 +411,6 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
         }
     }
     const int64_t chunks = (per_slice + kLutWaves * U - 1) / (kLutWaves * U);
-    a.units_per_wg = static_cast<int64_t>(kLutWaves) * U;
     switch (U) {
         case 1: return lut_launch<1>(a, chunks, s);
         case 2: return lut_launch<2>(a, chunks, s);
@@ -482,6 +419,167 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
         case 6: return lut_launch<6>(a, chunks, s);
         default: return lut_launch<8>(a, chunks, s);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K sums.  Every partial of a thread is requested before any is
+// added (clamped indices: no branch around the loads); rows are summed in
+// slice order, so results are deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kSumPer = 24;       // partials per thread per round
+constexpr int kSumThreads = 256;
+
+// y[r] = (residual ? residual[r] : 0) + sum_s part[s][r].  T threads per
+// row: lane = j * (64 / T) + i sums slices [j ns / T, (j + 1) ns / T) of row
+// i of the wave's 64 / T rows (consecutive lanes read consecutive rows), and
+// the T sums are combined in fixed order.
+template <int T>
+__global__ void __launch_bounds__(kSumThreads) k_lut_sum_rows(const float *__restrict__ part, int64_t n, int ns,
+                                                              const float *residual, float *y)
+{
+    constexpr int kRowsPerWave = kWave / T;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j = lane / kRowsPerWave;
+    const int64_t r = (static_cast<int64_t>(blockIdx.x) * (kSumThreads / kWave) + threadIdx.x / kWave) * kRowsPerWave +
+                      lane % kRowsPerWave;
+    const int64_t rc = r < n ? r : n - 1;
+    const int q_lo = static_cast<int>(static_cast<int64_t>(j) * ns / T);
+    const int q_hi = static_cast<int>(static_cast<int64_t>(j + 1) * ns / T);
+    float t = 0.0f;
+    for (int q0 = q_lo; q0 < q_hi; q0 += kSumPer) {
+        float v[kSumPer];
+#pragma unroll
+        for (int c = 0; c < kSumPer; ++c) {
+            const int q = q0 + c < q_hi ? q0 + c : q_hi - 1;
+            v[c] = part[static_cast<int64_t>(q) * n + rc];
+        }
+#pragma unroll
+        for (int c = 0; c < kSumPer; ++c)
+            if (q0 + c < q_hi) t += v[c];
+    }
+#pragma unroll
+    for (int h = kRowsPerWave; h < kWave; h <<= 1) {
+        const float o = __shfl_xor(t, h, kWave);
+        t = (lane & h) ? o + t : t + o;  // lower slice range first: the same order in every lane
+    }
+    if (j == 0 && r < n) y[r] = residual ? residual[r] + t : t;
+}
+
+hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
+                               hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    const int ns = static_cast<int>(lut_nslices(k));
+    const int T = ns <= kSumPer ? 1 : (ns <= 2 * kSumPer ? 2 : 4);
+    const int64_t rows_per_wg = static_cast<int64_t>(kSumThreads) / T;
+    const dim3 grid(static_cast<unsigned>((n + rows_per_wg - 1) / rows_per_wg));
+    switch (T) {
+        case 1: hipLaunchKernelGGL(k_lut_sum_rows<1>, grid, dim3(kSumThreads), 0, s, part, n, ns, residual, y); break;
+        case 2: hipLaunchKernelGGL(k_lut_sum_rows<2>, grid, dim3(kSumThreads), 0, s, part, n, ns, residual, y); break;
+        default: hipLaunchKernelGGL(k_lut_sum_rows<4>, grid, dim3(kSumThreads), 0, s, part, n, ns, residual, y); break;
+    }
+    return hipGetLastError();
+}
+
+// Gate/up epilogue, T threads per row as in k_lut_sum_rows (thread j sums
+// slices [j ns / T, (j + 1) ns / T) of both matrices):
+//   g, u = a * sum_s part[s][0][r], a * sum_s part[s][1][r]  (a = RMS scale
+//   of x_rms [d], or 1 when x_rms == nullptr), h = silu(g) * u; any of g, u,
+//   h may be nullptr.  Every workgroup computes a itself (d values from L2).
+template <int T>
+__global__ void __launch_bounds__(kSumThreads) k_lut_gate_up_sum(
+    const float *__restrict__ part, int64_t f, int ns, const float *__restrict__ x_rms, int64_t d, float rms_eps,
+    float *g, float *u, float *h)
+{
+    constexpr int kRowsPerWave = kWave / T;
+    constexpr int kRmsPer = 24;  // RMS inputs per thread requested up front (d <= 6144), any rest below
+    __shared__ float red[kSumThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int j = lane / kRowsPerWave;
+    const int64_t r = (static_cast<int64_t>(blockIdx.x) * (kSumThreads / kWave) + wave) * kRowsPerWave +
+                      lane % kRowsPerWave;
+    const int64_t rc = r < f ? r : f - 1;
+    float rv[kRmsPer];
+    if (x_rms != nullptr) {
+#pragma unroll
+        for (int c = 0; c < kRmsPer; ++c) {
+            const int64_t i = tid + static_cast<int64_t>(c) * kSumThreads;
+            rv[c] = x_rms[i < d ? i : d - 1];
+        }
+    }
+    const int q_lo = static_cast<int>(static_cast<int64_t>(j) * ns / T);
+    const int q_hi = static_cast<int>(static_cast<int64_t>(j + 1) * ns / T);
+    float tg = 0.0f, tu = 0.0f;
+    for (int q0 = q_lo; q0 < q_hi; q0 += kSumPer / 2) {
+        float vg[kSumPer / 2], vu[kSumPer / 2];
+#pragma unroll
+        for (int c = 0; c < kSumPer / 2; ++c) {
+            const int q = q0 + c < q_hi ? q0 + c : q_hi - 1;
+            vg[c] = part[(2 * static_cast<int64_t>(q)) * f + rc];
+            vu[c] = part[(2 * static_cast<int64_t>(q) + 1) * f + rc];
+        }
+#pragma unroll
+        for (int c = 0; c < kSumPer / 2; ++c) {
+            if (q0 + c < q_hi) {
+                tg += vg[c];
+                tu += vu[c];
+            }
+        }
+    }
+#pragma unroll
+    for (int hh = kRowsPerWave; hh < kWave; hh <<= 1) {
+        const float og = __shfl_xor(tg, hh, kWave), ou = __shfl_xor(tu, hh, kWave);
+        tg = (lane & hh) ? og + tg : tg + og;
+        tu = (lane & hh) ? ou + tu : tu + ou;
+    }
+    float a = 1.0f;
+    if (x_rms != nullptr) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kRmsPer; ++c)
+            if (tid + static_cast<int64_t>(c) * kSumThreads < d) sq = fmaf(rv[c], rv[c], sq);
+        for (int64_t i = tid + static_cast<int64_t>(kRmsPer) * kSumThreads; i < d; i += kSumThreads)
+            sq = fmaf(x_rms[i], x_rms[i], sq);
+#pragma unroll
+        for (int hh = kWave / 2; hh > 0; hh >>= 1) sq += __shfl_xor(sq, hh, kWave);
+        if (lane == 0) red[wave] = sq;
+        __syncthreads();
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSumThreads / kWave; ++w) t += red[w];
+        a = 1.0f / sqrtf(t / static_cast<float>(d) + rms_eps);
+    }
+    if (j == 0 && r < f) {
+        const float gv = tg * a, uv = tu * a;
+        if (g) g[r] = gv;
+        if (u) u[r] = uv;
+        if (h) h[r] = gv / (1.0f + expf(-gv)) * uv;
+    }
+}
+
+hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, const float *x_rms, int64_t d_rms,
+                                  float rms_eps, float *g, float *u, float *h, hipStream_t s)
+{
+    if (f == 0) return hipSuccess;
+    const int ns = static_cast<int>(lut_nslices(d_in));
+    const int T = ns <= kSumPer / 2 ? 1 : (ns <= kSumPer ? 2 : 4);
+    const int64_t rows_per_wg = static_cast<int64_t>(kSumThreads) / T;
+    const dim3 grid(static_cast<unsigned>((f + rows_per_wg - 1) / rows_per_wg));
+    switch (T) {
+        case 1:
+            hipLaunchKernelGGL(k_lut_gate_up_sum<1>, grid, dim3(kSumThreads), 0, s, part, f, ns, x_rms, d_rms, rms_eps,
+                               g, u, h);
+            break;
+        case 2:
+            hipLaunchKernelGGL(k_lut_gate_up_sum<2>, grid, dim3(kSumThreads), 0, s, part, f, ns, x_rms, d_rms, rms_eps,
+                               g, u, h);
+            break;
+        default:
+            hipLaunchKernelGGL(k_lut_gate_up_sum<4>, grid, dim3(kSumThreads), 0, s, part, f, ns, x_rms, d_rms, rms_eps,
+                               g, u, h);
+            break;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace ptq1

@@ -40,16 +40,21 @@ hipError_t launch_reduce_gate_up(const float *part, int64_t f, int64_t nseg, flo
                                  hipStream_t s);
 hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t s);
 
-// Lookup-table decode matvec (one launch) over tiled weights: one matrix
-// (nmat = 1: y = residual + W xr) or two (nmat = 2: g, u = a W0 xr, a W1 xr;
-// h = silu(g) u, a = RMS scale of x_rms or 1).  part: lut_part_floats
-// floats; cnt: lut_counter_words zero words (left zero on completion).
+// Lookup-table decode matvec over tiled weights, split over 256-wide
+// K-slices: part[slice][matrix][row] (lut_part_floats floats) for one matrix
+// (nmat = 1) or two sharing x (nmat = 2); x rotated per 1024-chunk when
+// signs != nullptr, else used as given.
+int64_t lut_nslices(int64_t k);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
-size_t lut_counter_words(int64_t n);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, float *part, uint32_t *cnt,
-                             const float *residual, float *y, float *g, float *u, float *h,
-                             const float *x_rms, int64_t d_rms, float rms_eps, hipStream_t s);
+                             const float *x, const float *signs, float *part, hipStream_t s);
+// y[r] = (residual ? residual[r] : 0) + sum over slices of part[s][r] (nmat = 1)
+hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
+                               hipStream_t s);
+// nmat = 2 epilogue: g, u = a * sums (a = RMS scale of x_rms [d_rms], or 1
+// when x_rms == nullptr), h = silu(g) u; any of g, u, h may be nullptr.
+hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, const float *x_rms, int64_t d_rms,
+                                  float rms_eps, float *g, float *u, float *h, hipStream_t s);
 
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
 // xb [m_pad][k] bf16 = bf16(R (a * x)); rows >= m zero.  a = RMS scale if

@@ -117,7 +117,7 @@ def test_unrotate_validation():
 
 def test_matvec_validation():
     ws_need = L().ptq1_matvec_workspace_bytes(5120, 17408)
-    assert ws_need >= 34 * 5120 * 4 + 320 * 4
+    assert ws_need >= 68 * 5120 * 4  # one partial per 256-wide K-slice and row
     B, X, Y, WS, S = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400, 500))
     rc, msg = _err(L().ptq1_matvec(B, 5120, 17408, X, S, None, Y, None, 0, None))
     assert rc == 6 and "ws" in msg
@@ -140,7 +140,7 @@ def test_gemm_and_ffn_validation():
     rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, -1, S, Y, WS, 1 << 40, None))
     assert rc == 2
     need = L().ptq1_gemm_workspace_bytes(256, 17408, 5120)
-    assert need == 256 * 1024 + 256 * 5120 * 2
+    assert need == 256 * 5120 * 2  # bf16 activations
     rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, 256, S, Y, WS, need - 1, None))
     assert rc == 6
     W2, W3 = C.c_void_p(FAKE * 600), C.c_void_p(FAKE * 700)

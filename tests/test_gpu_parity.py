@@ -269,13 +269,13 @@ def test_matvec_residual_and_special_cases(fn):
 
 
 def test_shared_workspace_across_calls():
-    """One zero-filled workspace reused by 60 calls of mixed shapes and entry
-    points: the per-group arrival counters must return to zero after every
-    call, or a later call would finish a row group early."""
+    """One workspace, filled with 0xFF bytes (NaN floats) before the first
+    call, reused by 60 calls of mixed shapes and entry points: each call
+    must write every scratch value it reads."""
     shapes = [(1024, 1024, True), (300, 384, False), (5120, 3072, True), (33, 1024, True), (2048, 512, False)]
     big = max(P.workspace_bytes("matvec", n, k) for n, k, _ in shapes)
     big = max(big, P.workspace_bytes("gate_up", 1040, 2048), P.workspace_bytes("gemm", 40, 1024, 1024))
-    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device=DEV)
     cases = []
     for i, (n, k, rot) in enumerate(shapes):
         t, s = host_matrix(20 + i, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
