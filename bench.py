@@ -10,18 +10,35 @@ Weights rotate over WEIGHT_SETS independent sets (936 MB, beyond the 256 MB
 Infinity Cache) so every step streams its 58.5 MB of PTQ1_0 blocks from HBM.
 value = algorithmic bytes per step / step time (decode matvec GB/s).
 
-Also reported (breakdown): cold gate+up alone, cold down alone, the hot
-1024 x 1024 matvec, the prefill GEMM at M = 128 / 256 / 512 (TFLOP/s), and
-the 64-layer FFN stack at batch 1 and 8 (layers/s); the fp64 oracle timed
-on the host's cores on a bounded sample (cpu_baseline).
+The timed steps replay HIP graphs of the step (the step is five dependent
+kernels of about 40 us in all, so eager launches leave the GPU waiting on
+the host).
+
+roofline: the dominant kernel, the table-lookup matvec over gate and up
+(one launch per step), timed in a second pass of the same K steps run
+eagerly, with HIP events attached to that kernel's dispatch by the library
+(ptq1_profile_arm -> hipExtLaunchKernel: the kernel's own start and end);
+algorithmic bytes per launch = its PTQ1_0 blocks + x.  `traffic` is the
+counter-measured HBM bytes per launch from the committed rocprofv3 summary
+profiles/lut_matvec_gate_up_decode_27b_traffic.md, or null when that
+kernel's source changed after the counters were taken.
+
+Also reported (breakdown): the down-projection lookup kernel inside the
+same steps, cold gate+up and down calls alone, the hot 1024 x 1024 matvec,
+the prefill GEMM at M = 128 / 256 / 512 (TFLOP/s, fraction of the bf16
+MFMA peak), and the 64-layer FFN stack at batch 1 and 8 (layers/s); the
+fp64 oracle timed on the host's cores on a bounded sample (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+                    [--copy-calibration]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,6 +69,32 @@ SWIGLU_BYTES = 3 * 4 * F                                      # g, u in, h out
 EMBED_BYTES = 2 * 4 * D                                       # one row in, one row out
 STEP_BYTES = GATE_UP_BYTES + SWIGLU_BYTES + DOWN_BYTES + EMBED_BYTES
 LAYER_WEIGHT_BYTES = 3 * packed(F, D)
+# the dominant kernel: the lookup-table matvec over gate and up reads both
+# matrices' blocks and x once per launch (its split-K partials are scratch)
+LUT_GATE_UP_BYTES = 2 * packed(F, D) + 4 * D
+LUT_DOWN_BYTES = packed(D, F) + 4 * F
+COPY_CAL_BYTES = 256 << 20     # plain device copy used to scale the byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lut_matvec_gate_up_decode_27b_traffic.md")
+LUT_SOURCE = os.path.join(ROOT, "ternary_weight_ptq1_amd", "csrc", "matvec_lut.hip")
+
+
+def lut_source_hash() -> str:
+    with open(LUT_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate+up lookup kernel from the committed
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_src = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    m_val = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not m_src or not m_val or m_src.group(1) != lut_source_hash():
+        return None
+    return int(m_val.group(1))
 
 
 def main() -> int:
@@ -61,6 +104,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--quick", action="store_true", help="headline only (no breakdown)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (scale for the byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded path is a "
@@ -124,19 +169,63 @@ def main() -> int:
         P.ptq1_ffn_block(emb, W[0], W[1], W[2], signs, D, F, rms_eps=1e-6, out=x_out, ws=ws)
 
     log("bench: headline step")
-    for i in range(args.warmup):
+    for i in range(args.warmup):  # eager warm-up (also settles per-kernel launch attributes)
         step(i)
+    torch.cuda.synchronize()
+    # The step is launch-bound (five dependent kernels, about 40 us), so the
+    # timed steps replay HIP graphs: one of WEIGHT_SETS steps (a pass over
+    # every weight set) and one of the remainder, so that exactly K steps run.
+    graphs = []
+    for count in (WEIGHT_SETS, args.steps % WEIGHT_SETS):
+        if count == 0:
+            graphs.append(None)
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    if graphs[0] is not None:
+        graphs[0].replay()  # first replay uploads the graph
+    if graphs[1] is not None:
+        graphs[1].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0, e1 = ev(), ev()
     e0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps // WEIGHT_SETS):
+        graphs[0].replay()
+    if graphs[1] is not None:
+        graphs[1].replay()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
+    del graphs
+
+    # roofline pass: the same K steps run eagerly with HIP events attached to
+    # the dispatches of the gate+up and down lookup kernels (ptq1_profile_arm)
+    log("bench: roofline pass")
+    t_gu = P.KernelTimer("lut_matvec_2", args.steps)
+    t_dn = P.KernelTimer("lut_matvec_1", args.steps)
+    e2, e3 = ev(), ev()
+    with t_gu, t_dn:
+        e2.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e3.record(stream)
+    torch.cuda.synchronize()
+    ms_step_eager_profiled = e2.elapsed_time(e3) / args.steps
+    d_gu, d_dn = t_gu.durations_ms(), t_dn.durations_ms()
+    t_gu.close()
+    t_dn.close()
+    assert len(d_gu) == args.steps and len(d_dn) == args.steps, "one gate+up and one down launch per step"
+    us_gu = 1e3 * sum(d_gu) / len(d_gu)
+    us_dn = 1e3 * sum(d_dn) / len(d_dn)
+    lut_gu_gbs = LUT_GATE_UP_BYTES / (us_gu * 1e-6) / 1e9
+    lut_dn_gbs = LUT_DOWN_BYTES / (us_dn * 1e-6) / 1e9
 
     # dominant kernel: the fused gate+up decode matvec (cold), timed alone on the same stream
     ws_gu = torch.zeros(P.workspace_bytes("gate_up", F, D), dtype=torch.uint8, device=dev)
@@ -151,7 +240,10 @@ def main() -> int:
     ms_gu = timed(gate_up, max(args.steps, 100), args.warmup)
     gu_gbs = GATE_UP_BYTES / (ms_gu * 1e-3) / 1e9
 
-    breakdown = {"gate_up_cold": {"us": ms_gu * 1e3, "GB/s": gu_gbs, "bytes": GATE_UP_BYTES}}
+    breakdown = {"step_eager_with_kernel_events_us": ms_step_eager_profiled * 1e3,
+                 "lut_kernel_gate_up_in_step": {"us": us_gu, "GB/s": lut_gu_gbs, "bytes": LUT_GATE_UP_BYTES},
+                 "lut_kernel_down_in_step": {"us": us_dn, "GB/s": lut_dn_gbs, "bytes": LUT_DOWN_BYTES},
+                 "gate_up_call_cold": {"us": ms_gu * 1e3, "GB/s": gu_gbs, "bytes": GATE_UP_BYTES}}
     if not args.quick:
         log("bench: breakdown")
         ws_dn = torch.zeros(P.workspace_bytes("matvec", D, F), dtype=torch.uint8, device=dev)
@@ -163,8 +255,8 @@ def main() -> int:
             P.ptq1_matvec(W[2], D, F, h, signs, residual=xg, out=y, ws=ws_dn)
 
         ms_dn = timed(down, 200, 20)
-        breakdown["down_cold"] = {"us": ms_dn * 1e3, "GB/s": DOWN_BYTES / (ms_dn * 1e-3) / 1e9,
-                                  "bytes": DOWN_BYTES}
+        breakdown["down_call_cold"] = {"us": ms_dn * 1e3, "GB/s": DOWN_BYTES / (ms_dn * 1e-3) / 1e9,
+                                       "bytes": DOWN_BYTES}
 
         def unrot(i):
             P.hadamard_unrotate_rows(table, signs, ids=ids[i % 4096:i % 4096 + 1], out=emb)
@@ -189,9 +281,16 @@ def main() -> int:
             xm = torch.from_numpy(synth.activations(3, m, D)).to(dev)
             ym = torch.empty((m, F), dtype=torch.float32, device=dev)
             wsm = torch.zeros(P.workspace_bytes("gemm", m, F, D), dtype=torch.uint8, device=dev)
-            ms = timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 5)
-            gemm[f"M{m}"] = {"us": ms * 1e3, "TFLOP/s": 2.0 * m * F * D / (ms * 1e-3) / 1e12,
-                             "mfma_frac": 2.0 * m * F * D / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 3, 0)  # warm-up
+            tg = P.KernelTimer("gemm", 50)
+            with tg:
+                ms = timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 0)
+            dg = tg.durations_ms()
+            tg.close()
+            us_k = 1e3 * sum(dg) / len(dg)
+            fl = 2.0 * m * F * D
+            gemm[f"M{m}"] = {"us_call": ms * 1e3, "us_kernel": us_k, "TFLOP/s": fl / (us_k * 1e-6) / 1e12,
+                             "mfma_frac": fl / (us_k * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
         breakdown["prefill_gemm"] = gemm
 
         # 64-layer FFN stack (configuration 4): 3.74 GB of weights, cold by construction
@@ -217,6 +316,15 @@ def main() -> int:
         breakdown["ffn_stack_64"] = stk
         del stack
 
+    if args.copy_calibration:
+        log("bench: copy calibration")
+        src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes COPY_CAL_BYTES
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = measured_traffic()
     cpu = None
     if not args.no_cpu:
         log("bench: oracle CPU baseline")
@@ -238,14 +346,15 @@ def main() -> int:
         "config": {"workload": "decode step: unrotate 1 row of a 248320x5120 fp32 table, then one "
                                "FFN block x[5120] -> rotate -> gate+up 5120->2x17408 (PTQ1_0) -> "
                                "SwiGLU -> rotate -> down 17408->5120 + residual, batch 1, RMS scale on, "
-                               f"{WEIGHT_SETS} rotating weight sets",
+                               f"{WEIGHT_SETS} rotating weight sets; steps replayed from HIP graphs",
                    "d": D, "f": F, "batch": 1, "weight_sets": WEIGHT_SETS,
                    "step_bytes": STEP_BYTES, "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                    "wall_s_timed": round(wall, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gate+up decode matvec (ptq1_gate_up, cold)",
-                     "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": GATE_UP_BYTES, "us_per_launch": round(ms_gu * 1e3, 3)},
+        "roofline": {"bound": "hbm", "kernel": "k_matvec_lut over gate+up (17408x5120 x 2, PTQ1_0), in the step",
+                     "achieved": round(lut_gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(lut_gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": LUT_GATE_UP_BYTES, "us_per_launch": round(us_gu, 3),
+                     "launches_timed": len(d_gu), "source_sha256_16": lut_source_hash()},
         "cpu_baseline": cpu,
         "breakdown": breakdown,
     }

@@ -223,6 +223,22 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
                            const float *signs1024, float rms_eps, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
+ * next `count` launches of one kernel family (hipExtLaunchKernel: they take
+ * the kernel's own start and end times on its stream), so a caller can time
+ * a kernel inside a composite call (ptq1_ffn_block) with events.  Families: "lut_matvec_2" (the
+ * table-lookup matvec over two matrices: gate and up), "lut_matvec_1" (over
+ * one matrix: ptq1_matvec, the down projection), "gemm" (the MFMA GEMM).
+ * Events are created and owned by the caller; both arrays must stay valid
+ * until `count` launches have happened or the family is re-armed.  count =
+ * 0 disarms.  Process-wide; not meant for concurrent use by several
+ * threads.  Errors: NULL, SHAPE (count < 0), UNSUPPORTED (unknown name). */
+ptq1_status ptq1_profile_arm(const char *kernel, hipEvent_t *start, hipEvent_t *stop, int32_t count);
+
+/* Launches of `kernel` bracketed since it was last armed; -1 for an unknown
+ * name. */
+int32_t ptq1_profile_count(const char *kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,8 @@ _SIGS = {
     "ptq1_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
     "ptq1_ffn_workspace_bytes": ([i64, i64, i64], sz),
     "ptq1_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, sz, p], C.c_int),
+    "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
+    "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
 
 
@@ -299,3 +301,72 @@ def workspace_bytes(kind: str, *shape) -> int:
     fn = {"matvec": "ptq1_matvec_workspace_bytes", "gate_up": "ptq1_gate_up_workspace_bytes",
           "gemm": "ptq1_gemm_workspace_bytes", "ffn": "ptq1_ffn_workspace_bytes"}[kind]
     return int(getattr(lib(), fn)(*shape))
+
+
+# -------------------------------------------------------------- profiling ----
+
+_hip = None
+
+
+def _hiprt():
+    """The HIP runtime (already loaded by torch), for raw events."""
+    global _hip
+    if _hip is None:
+        h = C.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        h.hipEventDestroy.argtypes = [C.c_void_p]
+        h.hipEventSynchronize.argtypes = [C.c_void_p]
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        _hip = h
+    return _hip
+
+
+class KernelTimer:
+    """Times the next `count` launches of one kernel family inside any call
+    (ptq1_profile_arm): HIP events recorded by the library on the stream of
+    each launch.  Use as a context manager around the timed calls, then read
+    `durations_ms()` after a device synchronisation."""
+
+    def __init__(self, kernel: str, count: int):
+        self.kernel = kernel.encode()
+        self.count = count
+        hip = _hiprt()
+        self._start = (C.c_void_p * count)()
+        self._stop = (C.c_void_p * count)()
+        for arr in (self._start, self._stop):
+            for i in range(count):
+                ev = C.c_void_p()
+                if hip.hipEventCreate(C.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev
+
+    def __enter__(self):
+        _check("ptq1_profile_arm", lib().ptq1_profile_arm(self.kernel, C.cast(self._start, p),
+                                                          C.cast(self._stop, p), self.count))
+        return self
+
+    def __exit__(self, *exc):
+        self.launches = lib().ptq1_profile_count(self.kernel)
+        _check("ptq1_profile_arm", lib().ptq1_profile_arm(self.kernel, None, None, 0))
+        return False
+
+    def durations_ms(self) -> list[float]:
+        hip = _hiprt()
+        out = []
+        for i in range(self.launches):
+            if hip.hipEventSynchronize(self._stop[i]) != 0:
+                raise RuntimeError("hipEventSynchronize failed")
+            ms = C.c_float()
+            if hip.hipEventElapsedTime(C.byref(ms), self._start[i], self._stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        hip = _hiprt()
+        for arr in (self._start, self._stop):
+            for i in range(self.count):
+                if arr[i]:
+                    hip.hipEventDestroy(arr[i])
+                    arr[i] = None
+

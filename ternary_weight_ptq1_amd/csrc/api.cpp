@@ -8,9 +8,12 @@
 // and sizes are computed with checked arithmetic.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/ptq1.h"
@@ -202,9 +205,84 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
     return L;
 }
 
+// ---- profiling hook ----------------------------------------------------------
+// Armed kernel families record caller events around their next launches.
+enum ProfKind { kProfLut2 = 0, kProfLut1 = 1, kProfGemm = 2, kProfKinds = 3 };
+const char *const kProfNames[kProfKinds] = {"lut_matvec_2", "lut_matvec_1", "gemm"};
+
+struct ProfArm {
+    hipEvent_t *start = nullptr, *stop = nullptr;
+    int32_t count = 0, next = 0;
+};
+
+std::mutex g_prof_mu;
+ProfArm g_prof[kProfKinds];
+std::atomic<bool> g_prof_any{false};
+
+int prof_kind(const char *name)
+{
+    for (int i = 0; i < kProfKinds; ++i)
+        if (std::strcmp(name, kProfNames[i]) == 0) return i;
+    return -1;
+}
+
+// Runs `launch` with the family's next pair of events attached to its
+// kernel dispatch, if the family is armed.
+template <class F>
+hipError_t profiled(int kind, hipStream_t s, F launch)
+{
+    (void)s;
+    if (!g_prof_any.load(std::memory_order_relaxed)) return launch();
+    ptq1::ProfEvents ev;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        ProfArm &p = g_prof[kind];
+        if (p.next < p.count) {
+            ev.start = p.start[p.next];
+            ev.stop = p.stop[p.next];
+            ++p.next;
+        }
+    }
+    ptq1::prof_events() = ev;
+    const hipError_t e = launch();
+    ptq1::prof_events() = ptq1::ProfEvents{};
+    return e;
+}
+
 }  // namespace
 
+namespace ptq1 {
+ProfEvents &prof_events()
+{
+    thread_local ProfEvents ev;
+    return ev;
+}
+}  // namespace ptq1
+
 extern "C" {
+
+ptq1_status ptq1_profile_arm(const char *kernel, hipEvent_t *start, hipEvent_t *stop, int32_t count)
+{
+    if (kernel == nullptr) return fail(PTQ1_ERR_NULL, "kernel is NULL");
+    const int kind = prof_kind(kernel);
+    if (kind < 0) return fail(PTQ1_ERR_UNSUPPORTED, "no kernel family named '%s'", kernel);
+    if (count < 0) return fail(PTQ1_ERR_SHAPE, "count = %d is negative", count);
+    if (count > 0 && (start == nullptr || stop == nullptr)) return fail(PTQ1_ERR_NULL, "start or stop is NULL");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof[kind] = ProfArm{count > 0 ? start : nullptr, count > 0 ? stop : nullptr, count, 0};
+    bool any = false;
+    for (const ProfArm &p : g_prof) any = any || p.count > 0;
+    g_prof_any.store(any, std::memory_order_relaxed);
+    return ok();
+}
+
+int32_t ptq1_profile_count(const char *kernel)
+{
+    const int kind = kernel ? prof_kind(kernel) : -1;
+    if (kind < 0) return -1;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    return g_prof[kind].next;
+}
 
 const char *ptq1_status_string(ptq1_status s)
 {
@@ -372,7 +450,9 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
     PTQ1_TRY(check_matvec(tiled, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec", true, &empty));
     if (empty) return ok();
     float *part = static_cast<float *>(ws);
-    hipError_t e = ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024, part, stream);
+    hipError_t e = profiled(kProfLut1, stream, [&] {
+        return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024, part, stream);
+    });
     if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
     return hip_status(e, "ptq1_matvec");
 }
@@ -420,7 +500,9 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
     if (f > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "f = %lld > %lld rows", (long long)f, (long long)kMaxLutRows);
     if (wgb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
     float *part = static_cast<float *>(ws);
-    hipError_t e = ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+    hipError_t e = profiled(kProfLut2, stream, [&] {
+        return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+    });
     if (e == hipSuccess)
         e = ptq1::launch_lut_gate_up_sum(part, f, d, nullptr, 0, 0.0f, g, u, nullptr, stream);
     return hip_status(e, "ptq1_gate_up");
@@ -468,7 +550,9 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
     uint16_t *xbf = static_cast<uint16_t *>(ws);
     hipError_t e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, k, signs1024, 0.0f, xbf, stream);
     if (e == hipSuccess)
-        e = ptq1::launch_gemm(xbf, m, m_pad, k, tiled, n, nullptr, 0, y, nullptr, nullptr, stream);
+        e = profiled(kProfGemm, stream, [&] {
+            return ptq1::launch_gemm(xbf, m, m_pad, k, tiled, n, nullptr, 0, y, nullptr, nullptr, stream);
+        });
     return hip_status(e, "ptq1_gemm");
 }
 
@@ -516,11 +600,16 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
         // gate/up partials -> RMS scale and SwiGLU -> down partials over R h -> + x
         float *part = reinterpret_cast<float *>(w + L.part);
         float *h = reinterpret_cast<float *>(w + L.hr);
-        e = ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+        e = profiled(kProfLut2, stream, [&] {
+            return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+        });
         if (e == hipSuccess)
             e = ptq1::launch_lut_gate_up_sum(part, f, d, rms_eps > 0.0f ? x : nullptr, d, rms_eps, nullptr, nullptr,
                                              h, stream);
-        if (e == hipSuccess) e = ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, part, stream);
+        if (e == hipSuccess)
+            e = profiled(kProfLut1, stream, [&] {
+                return ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, part, stream);
+            });
         if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, d, f, x, x_out, stream);
     } else {
         const int64_t m_pad = ptq1::gemm_m_pad(m);
@@ -528,10 +617,15 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
         float *g = reinterpret_cast<float *>(w + L.g);
         float *u = reinterpret_cast<float *>(w + L.u);
         e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, d, signs1024, rms_eps, xbf, stream);
-        if (e == hipSuccess) e = ptq1::launch_gemm(xbf, m, m_pad, d, w_gate, f, w_up, f, g, u, nullptr, stream);
+        if (e == hipSuccess)
+            e = profiled(kProfGemm, stream, [&] {
+                return ptq1::launch_gemm(xbf, m, m_pad, d, w_gate, f, w_up, f, g, u, nullptr, stream);
+            });
         if (e == hipSuccess) e = ptq1::launch_prep_bf16(nullptr, g, u, m, m_pad, f, signs1024, 0.0f, xbf, stream);
         if (e == hipSuccess)
-            e = ptq1::launch_gemm(xbf, m, m_pad, f, w_down, d, nullptr, 0, x_out, nullptr, x, stream);
+            e = profiled(kProfGemm, stream, [&] {
+                return ptq1::launch_gemm(xbf, m, m_pad, f, w_down, d, nullptr, 0, x_out, nullptr, x, stream);
+            });
     }
     return hip_status(e, "ptq1_ffn_block");
 }

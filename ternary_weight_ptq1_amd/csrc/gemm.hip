@@ -9,6 +9,8 @@
 // Each 128-weight block's MFMA partial sum is multiplied by that block's
 // scale in fp32 (never folded into bf16), so the only rounding beyond fp32
 // is the bf16 rounding of the rotated activations.
+#include <hip/hip_ext.h>
+
 #include "ptq1_device.h"
 #include "ptq1_launch.h"
 
@@ -229,6 +231,20 @@ hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int6
     return hipGetLastError();
 }
 
+// Launches one GEMM kernel instance, with the profiling events attached to
+// the dispatch when a caller armed them.
+template <class K, class... Args>
+static void gemm_dispatch(K kernel, dim3 grid, hipStream_t s, Args... args)
+{
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0u, s, pe.start, pe.stop, 0u, args...);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0, s, args...);
+    }
+}
+
 hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
                        int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
                        const float *residual, hipStream_t s)
@@ -238,13 +254,11 @@ hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, 
     if (m_pad == 32) {
         constexpr int BM = 32, BN = 128;
         const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), 1);
-        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, 1, 4>), grid, dim3(kGemmThreads), 0, s, xb, m, k, w0,
-                           n0, w1, n1, y0, y1, residual);
+        gemm_dispatch(k_gemm_mfma<BM, BN, 1, 4>, grid, s, xb, m, k, w0, n0, w1, n1, y0, y1, residual);
     } else {
         constexpr int BM = 128, BN = 64;
         const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), static_cast<unsigned>(m_pad / BM));
-        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, 2, 2>), grid, dim3(kGemmThreads), 0, s, xb, m, k, w0,
-                           n0, w1, n1, y0, y1, residual);
+        gemm_dispatch(k_gemm_mfma<BM, BN, 2, 2>, grid, s, xb, m, k, w0, n0, w1, n1, y0, y1, residual);
     }
     return hipGetLastError();
 }

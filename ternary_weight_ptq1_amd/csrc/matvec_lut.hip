@@ -49,6 +49,8 @@
 //     at once; finishing inside the matvec kernel instead (arrival counters
 //     and device-scope loads that bypass the L2) measured slower, its
 //     round trips to memory sitting at the end of the critical path.
+#include <hip/hip_ext.h>
+
 #include "ptq1_device.h"
 #include "ptq1_launch.h"
 
@@ -377,8 +379,15 @@ static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
     }
     // x = slice (fastest in dispatch order): the slices of a row band start
     // together and read neighbouring tiles
-    hipLaunchKernelGGL(k_matvec_lut<U>, dim3(static_cast<unsigned>(a.nslices), static_cast<unsigned>(chunks)),
-                       dim3(kLutThreads), lds, st, a);
+    const dim3 grid(static_cast<unsigned>(a.nslices), static_cast<unsigned>(chunks));
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
+                              pe.stop, 0u, a);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), lds, st, a);
+    }
     return hipGetLastError();
 }
 

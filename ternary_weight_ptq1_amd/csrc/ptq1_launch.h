@@ -8,6 +8,15 @@
 
 namespace ptq1 {
 
+// Events for the next profiled launch (set by the C ABI's profiling hook,
+// consumed and cleared by the launch it brackets): attached to that
+// dispatch with hipExtLaunchKernel, so they time the kernel's execution and
+// not the queue in front of it.
+struct ProfEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents &prof_events();  // per host thread
+
 hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
                        uint8_t *blocks, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s);

@@ -76,6 +76,16 @@ def test_tile_validation():
     assert L().ptq1_tile(None, 0, 128, None, None) == 0
 
 
+def test_profile_arm_validation():
+    assert _err(L().ptq1_profile_arm(b"no_such_kernel", None, None, 0))[0] == 5
+    assert _err(L().ptq1_profile_arm(None, None, None, 0))[0] == 1
+    assert _err(L().ptq1_profile_arm(b"gemm", None, None, -1))[0] == 2
+    assert _err(L().ptq1_profile_arm(b"gemm", None, None, 3))[0] == 1
+    assert L().ptq1_profile_arm(b"lut_matvec_2", None, None, 0) == 0  # disarm is always fine
+    assert L().ptq1_profile_count(b"lut_matvec_2") == 0
+    assert L().ptq1_profile_count(b"nope") == -1
+
+
 def _err(rc):
     return rc, L().ptq1_last_error().decode()
 

@@ -456,3 +456,59 @@ def test_ffn_block_full_shape(m):
                                 1e-6))
     ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
     assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+
+
+# -------------------------------------------------------------- profiling ----
+
+def test_kernel_timer_brackets_each_launch():
+    """ptq1_profile_arm: the events recorded around the lookup-table matvec
+    launches inside ptq1_ffn_block give one positive duration per launch,
+    for exactly the armed number of launches."""
+    d, f, seed = 1024, 2048, 6
+    wg, wu, wd = _ffn_host(seed, d, f)
+    tg, tu, td = tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f)
+    s = to_dev(synth.signs(seed))
+    x = to_dev(synth.activations(seed, 1, d))
+    t2, t1 = P.KernelTimer("lut_matvec_2", 3), P.KernelTimer("lut_matvec_1", 3)
+    with t2, t1:
+        for _ in range(4):  # the fourth call is beyond the armed count
+            P.ptq1_ffn_block(x, tg, tu, td, s, d, f, 1e-6)
+    torch.cuda.synchronize()
+    for t in (t2, t1):
+        ms = t.durations_ms()
+        assert len(ms) == 3 and all(0.0 < v < 100.0 for v in ms), ms
+        t.close()
+
+
+def test_ffn_block_graph_replay_matches_eager():
+    """The decode and batched FFN calls captured in a HIP graph (as the
+    benchmark replays them): every replay, with eager work and
+    synchronisations in between, reproduces the eager result bit for bit
+    (no memset nodes; every kernel is deterministic)."""
+    d, f, seed = 1024, 2048, 7
+    wg, wu, wd = _ffn_host(seed, d, f)
+    tg, tu, td = tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f)
+    s = to_dev(synth.signs(seed))
+    x1 = to_dev(synth.activations(seed, 1, d))
+    x4 = to_dev(synth.activations(seed + 1, 4, d))
+    o1, o4 = torch.empty_like(x1), torch.empty_like(x4)
+    ws = torch.empty(max(P.workspace_bytes("ffn", 1, d, f), P.workspace_bytes("ffn", 4, d, f)),
+                     dtype=torch.uint8, device=DEV)
+    ref1 = host(P.ptq1_ffn_block(x1, tg, tu, td, s, d, f, 1e-6, ws=ws))
+    ref4 = host(P.ptq1_ffn_block(x4, tg, tu, td, s, d, f, 1e-6, ws=ws))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.ptq1_ffn_block(x1, tg, tu, td, s, d, f, 1e-6, out=o1, ws=ws)
+        P.ptq1_ffn_block(x4, tg, tu, td, s, d, f, 1e-6, out=o4, ws=ws)
+    other = to_dev(synth.activations(seed + 2, 1, d))
+    for rep in range(3):
+        o1.fill_(float("nan"))
+        o4.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(o1), ref1, err_msg=f"replay {rep}, m = 1")
+        np.testing.assert_array_equal(host(o4), ref4, err_msg=f"replay {rep}, m = 4")
+        P.ptq1_ffn_block(other, tg, tu, td, s, d, f, 1e-6, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
+
