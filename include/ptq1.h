@@ -24,10 +24,11 @@
  *
  * Tiled layout (this library's device layout, not part of the format): the
  * same 28-byte blocks reordered so that each tile of 32 rows x 2 blocks
- * (256 weights of K) is 1792 contiguous bytes.  With T = ceil(k/256) tiles
- * per 32-row band, tile (g, t) starts at byte (g*T + t) * 1792 and holds
- * block j = 2t + b of row r = 32g + i at byte (2i + b) * 28 of the tile;
- * places past the matrix (r >= n or j >= k/128) hold zero bytes.  The
+ * (256 weights of K) is 1792 contiguous bytes, K-slices outermost.  With
+ * G = ceil(n/32) row bands, tile (g, t) -- rows 32g.., K-slice t -- starts at
+ * byte (t*G + g) * 1792 and holds block j = 2t + b of row r = 32g + i at
+ * byte (2i + b) * 28 of the tile; places past the matrix (r >= n or
+ * j >= k/128) hold zero bytes.  The
  * matvec, gate/up, GEMM and feed-forward calls read weights in this layout
  * (ptq1_tile makes it from a packed matrix, once, at load time); pack,
  * dequant and the float-peel matvec use the packed layout.

@@ -64,17 +64,18 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ blo
 }
 
 // Packed -> tiled reorder: one thread per 28-byte place of the tiled output
-// (tiles of kTileRows rows x kTileBlocks blocks, row bands outermost, rows
-// then blocks inside a tile); places past the matrix get zero bytes.
+// (tiles of kTileRows rows x kTileBlocks blocks, K-slices outermost, then
+// row bands; rows then blocks inside a tile); places past the matrix get
+// zero bytes.
 __global__ void __launch_bounds__(256) k_tile(const uint8_t *__restrict__ blocks, int64_t n, int64_t nb,
-                                              int64_t tiles_k, int64_t total, uint8_t *__restrict__ tiled)
+                                              int64_t bands, int64_t total, uint8_t *__restrict__ tiled)
 {
     for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
          o += (int64_t)gridDim.x * blockDim.x) {
         const int64_t tile = o / kTileSlots;
         const int pos = static_cast<int>(o - tile * kTileSlots);
-        const int64_t band = tile / tiles_k;
-        const int64_t t = tile - band * tiles_k;
+        const int64_t t = tile / bands;
+        const int64_t band = tile - t * bands;
         const int64_t r = band * kTileRows + pos / kTileBlocks;
         const int64_t j = t * kTileBlocks + pos % kTileBlocks;
         uint32_t d[kBlockDwords];
@@ -127,7 +128,7 @@ hipError_t launch_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *til
     const int64_t bands = (n + kTileRows - 1) / kTileRows;
     const int64_t total = bands * tiles_k * kTileSlots;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_tile, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks, n, nb, tiles_k, total,
+    hipLaunchKernelGGL(k_tile, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks, n, nb, bands, total,
                        tiled);
     return hipGetLastError();
 }

@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
     const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t tile_m = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t nb = k / kBlockWeights;
-    const int64_t tiles_k = (nb + kTileBlocks - 1) / kTileBlocks;
+    const int64_t bands0 = (n0 + kTileRows - 1) / kTileRows, bands1 = (n1 + kTileRows - 1) / kTileRows;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -139,8 +139,9 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
             uint32_t dw = 0x80808080u;  // byte 128 = code 121 = all digits 1 = zero weights
             if (rv < rows) {
                 const int64_t rr = (rv < n0) ? rv : rv - n0;  // row of its own (tiled) matrix
+                const int64_t bands = (rv < n0) ? bands0 : bands1;
                 const uint8_t *tile = ((rv < n0) ? w0 : w1) +
-                                      ((rr / kTileRows) * tiles_k + kb / kTileBlocks) * kTileBytes;
+                                      ((kb / kTileBlocks) * bands + rr / kTileRows) * kTileBytes;
                 const int pos = static_cast<int>(rr % kTileRows) * kTileBlocks + static_cast<int>(kb % kTileBlocks);
                 dw = reinterpret_cast<const uint32_t *>(tile + pos * kBlockBytes)[q];
             }

@@ -30,11 +30,14 @@
 //     are one contiguous 1792-byte tile, lane 2i + b holding block b of row
 //     i, so a wave's loads are fully used 128-byte lines (a row-major matrix
 //     would give each workgroup 56-byte pieces at the row pitch, which
-//     measured at well under half the bandwidth);
+//     measured at well under half the bandwidth); tiles are K-slice-major,
+//     so the units a workgroup walks (consecutive row bands of one slice)
+//     are one contiguous run of memory, and so are its neighbours';
 //   - a workgroup (512 threads) owns one slice and a run of (matrix, 32-row
-//     group) units of it; wave 0 rotates the slice's 1024-chunk of x in
-//     registers (its loads requested before any weights: vector-memory loads
-//     return in order), all threads build the table, and each of the 8 waves
+//     group) units of it; wave 0 rotates x for the slice in registers (its
+//     loads requested before any weights: vector-memory loads return in
+//     order; only the slice's 256 outputs of the 1024-chunk's transform are
+//     formed, see lut_fwht256), all threads build the table, and each of the 8 waves
 //     processes U units (U is a template parameter chosen per launch so the
 //     grid fits two workgroups per CU) with kLutDepth units of weights in
 //     flight; a lane reads its 28-byte block with two wide loads and rotates
@@ -42,7 +45,7 @@
 //     amount so the 32 lanes of a half-wave (16 rows x 2 blocks) spread over
 //     LDS banks;
 //   - a unit's 2 block partials (times their fp16 scales) are summed across
-//     lanes with one xor-shuffle and stored as split-K partials
+//     neighbouring lanes (one DPP move) and stored as split-K partials
 //     part[slice][matrix][row]; a second kernel sums each row's partials in
 //     slice order and applies the epilogue (+ residual, or RMS scale and
 //     SwiGLU).  The kernel boundary makes the partials visible across XCDs
@@ -59,8 +62,14 @@ namespace ptq1 {
 constexpr int kLutBlocks = 2;                          // blocks per K-slice
 constexpr int kLutSliceW = kLutBlocks * kBlockWeights;  // 256 weights
 constexpr int kLutSlots = kLutBlocks * kBlockBytes;    // 56 byte slots
-constexpr int kLutThreads = 512;
-constexpr int kLutWaves = kLutThreads / kWave;         // 8
+#ifndef PTQ1_LUT_THREADS
+#define PTQ1_LUT_THREADS 512
+#endif
+constexpr int kLutThreads = PTQ1_LUT_THREADS;          // one workgroup: kLutWgPerCu per CU
+constexpr int kLutWaves = kLutThreads / kWave;
+constexpr int kLutWgPerCu = 1024 / kLutThreads;        // 64 KB of LDS each
+constexpr int kLutBuildRanges = kLutThreads / kWave;   // table build: threads = (slot, byte range)
+constexpr int kLutBuildPer = 256 / kLutBuildRanges;    // byte values per thread
 constexpr int kLutRows = 32;                           // rows per unit
 constexpr int kLutTableBytes = 65536;                  // 256 byte values x 64 slot columns x fp32
 constexpr int kLutDepth = 3;                           // units of weights in flight per wave
@@ -113,13 +122,79 @@ struct LutArgs {
     float *part;             // [nslices][nmat][n]
 };
 
+// ---------------------------------------------------------------------------
+// Rotation of one slice's 256 activations.  In natural order H_1024 =
+// H_4 (x) H_256 (the top two index bits are the H_4 factor), so outputs
+// 256 p .. 256 p + 255 of a 1024-chunk are the 256-point transform of
+// z_d = sum_c (-1)^popcount(p & c) s[256 c + d] x[256 c + d]: one wave, four
+// values per lane (d = lane + 64 k), butterflies across lanes by DPP and the
+// gfx950 lane-swap instructions (no LDS traffic), the two in-lane stages in
+// registers.  A butterfly leaves x_i + x_(i^h) at the lane whose bit h is 0
+// and x_(i^h) - x_i at the other: partner + sgn * own, sgn = +-1.
+// ---------------------------------------------------------------------------
+template <int kRowShl, int kRowShr>
+__device__ __forceinline__ float lut_dpp(float v, bool upper)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    const int lo = __builtin_amdgcn_update_dpp(iv, iv, kRowShl, 0xF, 0xF, false);  // lane + h
+    const int hi = __builtin_amdgcn_update_dpp(iv, iv, kRowShr, 0xF, 0xF, false);  // lane - h
+    return __builtin_bit_cast(float, upper ? hi : lo);
+}
+
+__device__ __forceinline__ void lut_fwht256(float (&v)[4], int lane)
+{
+    // lane bits 0, 1: quad permutations
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int iv = __builtin_bit_cast(int, v[k]);
+        const float p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false));
+        v[k] = fmaf((lane & 1) ? -1.0f : 1.0f, v[k], p);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int iv = __builtin_bit_cast(int, v[k]);
+        const float p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false));
+        v[k] = fmaf((lane & 2) ? -1.0f : 1.0f, v[k], p);
+    }
+    // lane bits 2, 3: row shifts by 4 and 8 (within 16-lane rows)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = fmaf((lane & 4) ? -1.0f : 1.0f, v[k], lut_dpp<0x104, 0x114>(v[k], lane & 4));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = fmaf((lane & 8) ? -1.0f : 1.0f, v[k], lut_dpp<0x108, 0x118>(v[k], lane & 8));
+    // lane bits 4, 5: swaps of 16-lane rows and of 32-lane halves between
+    // two copies of the value; result [0] holds the own value in the lower
+    // part and the partner's above, result [1] the partner's below and the
+    // own value above.  (The elements are copied to scalars before the bit
+    // cast: a bit cast of an element of the returned pair reads element 0.)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v[k]);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        v[k] = fmaf((lane & 16) ? -1.0f : 1.0f, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v[k]);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        v[k] = fmaf((lane & 32) ? -1.0f : 1.0f, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
+    }
+    // value bits 0, 1 (d bits 6, 7): in registers
+    float t0 = v[0] + v[1], t1 = v[0] - v[1], t2 = v[2] + v[3], t3 = v[2] - v[3];
+    v[0] = t0 + t2;
+    v[1] = t1 + t3;
+    v[2] = t0 - t2;
+    v[3] = t1 - t3;
+}
+
 // T[slot][b] for b in [32 BQ, 32 BQ + 32): with v = floor(243 b / 256) the
 // code of byte b and d_n its base-3 digits, T = A[d0][d1] + B[d2][d3][d4]
 // where A = (d0-1) x0 + (d1-1) x1 and B = ((d2-1) x2 + (d3-1) x3) + (d4-1) x4
 // are formed once per thread (9 + 27 sums); the digits are compile-time
 // constants of the unrolled loop, so each entry costs one add.
 template <int BQ>
-__device__ __forceinline__ void lut_build_range(float *tab, int slot, const float (&xv)[5])
+__device__ __forceinline__ void lut_build_range(float *tab, int slot, const float (&xv)[5])  // bytes kLutBuildPer * BQ ..
 {
     float A[9], B[27];
 #pragma unroll
@@ -137,11 +212,24 @@ __device__ __forceinline__ void lut_build_range(float *tab, int slot, const floa
         }
     const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int b = 32 * BQ + i;
+    for (int i = 0; i < kLutBuildPer; ++i) {
+        const int b = kLutBuildPer * BQ + i;
         const int v = (243 * b) >> 8;
         *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
             A[v / 27] + B[v % 27];
+    }
+}
+
+// bq (wave-uniform) -> lut_build_range<bq>: the digits of each entry stay
+// compile-time constants.
+template <int BQ>
+__device__ __forceinline__ void lut_build_dispatch(int bq, float *tab, int slot, const float (&xv)[5])
+{
+    if constexpr (BQ < kLutBuildRanges) {
+        if (bq == BQ)
+            lut_build_range<BQ>(tab, slot, xv);
+        else
+            lut_build_dispatch<BQ + 1>(bq, tab, slot, xv);
     }
 }
 
@@ -182,19 +270,14 @@ __device__ __forceinline__ void lut_rotate(uint32_t (&d)[kBlockDwords], int rho)
 }
 
 // U: units per wave.
+// One segment of a workgroup's work: units [u0, u1) of slice s, unit
+// u0 + w + 8 i going to wave w (i < U).
 template <int U>
-__global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 waves per SIMD: two workgroups per CU
+__device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float *xs, int s, int64_t u0, int64_t u1)
 {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    float *tab = reinterpret_cast<float *>(lds);                 // 64 KB table
-    float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 256 floats
-
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-    const int s = blockIdx.x;                                      // the slice
-    const int64_t per_slice = static_cast<int64_t>(a.nmat) * a.groups;
-    const int64_t first = (static_cast<int64_t>(blockIdx.y) * kLutWaves + wave) * U;  // this wave's first unit
     const int64_t k0 = static_cast<int64_t>(s) * kLutSliceW;
     const int kw = static_cast<int>(a.k - k0 < kLutSliceW ? a.k - k0 : kLutSliceW);
     const int nblk = kw / kBlockWeights;
@@ -206,13 +289,14 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     // memory returns in order, so anything requested after the weights
     // would wait for all of them.
     const int64_t c0 = (k0 / kHadamard) * kHadamard;  // 1024-chunk holding the slice
-    float xv16[kRotPerLane], sv16[kRotPerLane];
+    float xv16[kRotPerLane], sv16[kRotPerLane];        // [4 c + k]: element 256 c + lane + 64 k of the chunk
     if (wave == 0) {
         if (a.signs != nullptr) {
 #pragma unroll
             for (int j = 0; j < kRotPerLane; ++j) {
-                xv16[j] = a.x[c0 + lane + kWave * j];
-                sv16[j] = a.signs[lane + kWave * j];
+                const int e = kLutSliceW * (j >> 2) + lane + kWave * (j & 3);
+                xv16[j] = a.x[c0 + e];
+                sv16[j] = a.signs[e];
             }
         } else {
 #pragma unroll
@@ -231,13 +315,14 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     // two wide loads (16 + 12 bytes; blocks are only dword-aligned, which
     // gfx950 global loads accept) at a wave-uniform tile base.
     uint32_t dat[U][kBlockDwords];
+    auto unit_of = [&](int i) { return u0 + wave + static_cast<int64_t>(kLutWaves) * i; };
     auto issue = [&](int i) {
-        const int64_t un = first + i < per_slice ? first + i : per_slice - 1;  // clamped: no branch
+        const int64_t un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
         const LutUnit u = lut_unit(a, un);
         // tiled matrices are below 2 GiB (checked by the caller)
         const uint8_t *blk = (u.mat ? a.w1 : a.w0) +
-                             (static_cast<uint32_t>(u.grp) * static_cast<uint32_t>(a.nslices) +
-                              static_cast<uint32_t>(s)) * static_cast<uint32_t>(kTileBytes) +
+                             (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
+                              static_cast<uint32_t>(u.grp)) * static_cast<uint32_t>(kTileBytes) +
                              static_cast<uint32_t>(lane * kBlockBytes);
         const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(blk);
         const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(blk + 16);
@@ -251,15 +336,18 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
     if (wave == 0) {
         if (a.signs != nullptr) {
+            const int part = static_cast<int>((k0 - c0) / kLutSliceW);  // 0..3: this slice's quarter
+            const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
+            float z[4];
 #pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j) xv16[j] *= sv16[j];
-            fwht1024_wave(xv16);
-            const int part = static_cast<int>(k0 - c0);  // 0, 256, 512 or 768
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j) {
-                const int e = lane + kWave * j - part;
-                if (e >= 0 && e < kLutSliceW) xs[e] = xv16[j] * (1.0f / 32.0f);
+            for (int k = 0; k < 4; ++k) {
+                const float t0 = xv16[k] * sv16[k], t1 = xv16[4 + k] * sv16[4 + k];
+                const float t2 = xv16[8 + k] * sv16[8 + k], t3 = xv16[12 + k] * sv16[12 + k];
+                z[k] = fmaf(sa, t1, t0) + sb * fmaf(sa, t3, t2);  // row `part` of H_4
             }
+            lut_fwht256(z, lane);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xs[lane + kWave * k] = z[k] * (1.0f / 32.0f);
         } else {
 #pragma unroll
             for (int j = 0; j < kRotPerLane / 4; ++j) {
@@ -271,7 +359,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     __syncthreads();
     // ---- 4. table: thread = (slot, 32-value range of the byte)
     {
-        const int bq = tid >> 6;  // 0..7
+        const int bq = tid >> 6;  // 0 .. kLutBuildRanges - 1
         const int slot = tid & 63;
         if (slot < kLutSlots) {
             const int blk = slot / kBlockBytes, i = slot % kBlockBytes;
@@ -281,16 +369,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
                 const int j = kTritsPerByte * i + n;  // weight index in the block
                 xv[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
             }
-            switch (bq) {
-                case 0: lut_build_range<0>(tab, slot, xv); break;
-                case 1: lut_build_range<1>(tab, slot, xv); break;
-                case 2: lut_build_range<2>(tab, slot, xv); break;
-                case 3: lut_build_range<3>(tab, slot, xv); break;
-                case 4: lut_build_range<4>(tab, slot, xv); break;
-                case 5: lut_build_range<5>(tab, slot, xv); break;
-                case 6: lut_build_range<6>(tab, slot, xv); break;
-                default: lut_build_range<7>(tab, slot, xv); break;
-            }
+            lut_build_dispatch<0>(bq, tab, slot, xv);
         }
     }
     __syncthreads();
@@ -324,8 +403,8 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         if (i + kLutDepth < U) issue(i + kLutDepth);  // compile-time condition
-        const bool unit_ok = first + i < per_slice;  // wave-uniform
-        const int64_t un = unit_ok ? first + i : per_slice - 1;
+        const bool unit_ok = unit_of(i) < u1;  // wave-uniform
+        const int64_t un = unit_ok ? unit_of(i) : u1 - 1;
         const LutUnit u = lut_unit(a, un);
         const int r = u.grp * kLutRows + row_l;
         const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
@@ -342,11 +421,30 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
             }
         }
         float p = (acc0 + acc1) * scale;
-        p += __shfl_xor(p, 1, kWave);
+        const int ip = __builtin_bit_cast(int, p);
+        p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
         if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r] = p;
     }
 }
 
+// Slice s owns workgroups [floor(s G / ns), floor((s + 1) G / ns)) of the
+// G launched (two per CU, G >= ns), so every workgroup has one slice and
+// one table, and each takes an equal part of that slice's units: no CU holds
+// twice the work of another, and no workgroup builds two tables.
+template <int U>
+__global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 waves per SIMD (1024 threads per CU)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float *tab = reinterpret_cast<float *>(lds);                 // 64 KB table
+    float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 256 floats
+    const int64_t per_slice = static_cast<int64_t>(a.nmat) * a.groups;
+    const int64_t G = gridDim.x, ns = a.nslices, w = blockIdx.x;
+    const int s = static_cast<int>(((w + 1) * ns - 1) / G);
+    const int64_t c_lo = static_cast<int64_t>(s) * G / ns, c_hi = (static_cast<int64_t>(s) + 1) * G / ns;
+    const int64_t c = w - c_lo, cs = c_hi - c_lo;
+    const int64_t u0 = c * per_slice / cs, u1 = (c + 1) * per_slice / cs;
+    if (u0 < u1) lut_segment<U>(a, tab, xs, s, u0, u1);  // workgroup-uniform
+}
 
 static int device_cus()
 {
@@ -377,9 +475,7 @@ static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    // x = slice (fastest in dispatch order): the slices of a row band start
-    // together and read neighbouring tiles
-    const dim3 grid(static_cast<unsigned>(a.nslices), static_cast<unsigned>(chunks));
+    const dim3 grid(static_cast<unsigned>(chunks));
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
         hipExtLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
@@ -406,20 +502,30 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.x = x;
     a.signs = signs;
     a.part = part;
-    // units per wave: the smallest U whose grid (slices x chunks of 8U units)
-    // fits two workgroups per CU in one round, else the largest U
+    // two workgroups per CU (at least one per slice and at most one per 8
+    // units), each slice's units split evenly over its workgroups; U = units
+    // per wave of the largest part
     const int64_t per_slice = static_cast<int64_t>(nmat) * a.groups;
+    const int64_t total = per_slice * a.nslices;
     const int cus = device_cus();
+    int64_t wgs = kLutWgPerCu * static_cast<int64_t>(cus);
+    if (wgs > total / kLutWaves) wgs = total / kLutWaves;
+    if (wgs < a.nslices) wgs = a.nslices;
     static const int kUs[] = {1, 2, 3, 4, 6, 8};
-    int U = 8;
-    for (int cand : kUs) {
-        const int64_t chunks = (per_slice + kLutWaves * cand - 1) / (kLutWaves * cand);
-        if (chunks * a.nslices <= 2 * static_cast<int64_t>(cus)) {
-            U = cand;
-            break;
-        }
+    int U = 0;
+    for (;;) {
+        const int64_t fewest = wgs / a.nslices;                        // workgroups of the poorest slice
+        const int64_t part = (per_slice + fewest - 1) / fewest;        // its units per workgroup
+        const int64_t need = (part + kLutWaves - 1) / kLutWaves;
+        for (int cand : kUs)
+            if (cand >= need) {
+                U = cand;
+                break;
+            }
+        if (U != 0) break;
+        wgs += a.nslices;  // parts above 64 units: more workgroups per slice
     }
-    const int64_t chunks = (per_slice + kLutWaves * U - 1) / (kLutWaves * U);
+    const int64_t chunks = wgs;
     switch (U) {
         case 1: return lut_launch<1>(a, chunks, s);
         case 2: return lut_launch<2>(a, chunks, s);

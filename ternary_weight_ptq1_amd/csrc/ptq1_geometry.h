@@ -30,6 +30,8 @@ static_assert(kBlockBytes == kTritBytes + 2 && kBlockBytes % 4 == 0, "block is w
 // The blocks of a matrix reordered into tiles of 32 rows x 2 blocks: one tile
 // is 64 whole blocks = 1792 contiguous bytes, so a wave that needs 32 rows x
 // 256 weights of K reads one contiguous run instead of 32 strided pieces.
+// Tiles are stored K-slice-major (tile of band g, slice t at t * G + g), the
+// order in which the decode matvec walks them.
 constexpr int kTileRows = 32;
 constexpr int kTileBlocks = 2;
 constexpr int kTileSlots = kTileRows * kTileBlocks;   // 64 blocks

@@ -56,13 +56,13 @@ def tiled(b, n, k):
 
 def tile_host(blocks, n, k):
     """The tiled layout written out from its definition in include/ptq1.h:
-    tiles of 32 rows x 2 blocks, row bands outermost, block (32g + i, 2t + b)
-    at byte (2i + b) * 28 of tile g * T + t, zero bytes past the matrix."""
+    tiles of 32 rows x 2 blocks, K-slices outermost, block (32g + i, 2t + b)
+    at byte (2i + b) * 28 of tile t * G + g, zero bytes past the matrix."""
     nb = k // 128
     bands, tk = -(-n // 32), -(-nb // 2)
     full = np.zeros((bands * 32, tk * 2, 28), np.uint8)
     full[:n, :nb] = np.asarray(blocks).reshape(n, nb, 28)
-    return full.reshape(bands, 32, tk, 2, 28).transpose(0, 2, 1, 3, 4).reshape(-1)
+    return full.reshape(bands, 32, tk, 2, 28).transpose(2, 0, 1, 3, 4).reshape(-1)
 
 
 def dev_matrix(seed, tr, sc, n, k):
