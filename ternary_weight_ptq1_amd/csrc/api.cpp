@@ -176,14 +176,23 @@ size_t lut_ws(int64_t n, int nmat, int64_t k)
     return round_up(ptq1::lut_part_floats(n, nmat, k) * sizeof(float), kWsAlign);
 }
 
-// GEMM: bf16 activations [m_pad][k]
-size_t gemm_ws(int64_t m, int64_t k)
+// GEMM: bf16 activation fragments, then split-K partials
+struct GemmWs {
+    size_t frag = 0, part = 0, total = 0;  // byte offsets
+};
+
+GemmWs gemm_layout(const ptq1::GemmPlan &p, int64_t m, int64_t rows, int64_t k)
 {
-    return round_up(static_cast<size_t>(ptq1::gemm_m_pad(m)) * static_cast<size_t>(k) * 2, kWsAlign);
+    GemmWs L;
+    L.frag = 0;
+    L.part = round_up(ptq1::gemm_frag_elems(p, k) * 2, kWsAlign);
+    L.total = L.part + round_up(ptq1::gemm_part_floats(p, m, rows) * sizeof(float), kWsAlign);
+    return L;
 }
 
 struct FfnWs {
     size_t part = 0, hr = 0, g = 0, u = 0, xb = 0, total = 0;  // byte offsets (hr: h at m = 1)
+    ptq1::GemmPlan gu, dn;                                      // m >= 2: gate+up and down GEMMs
 };
 
 FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
@@ -196,10 +205,14 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
         off += part_a > part_b ? part_a : part_b;
         L.hr = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
     } else {
-        L.xb = off;
-        off += gemm_ws(m, d > f ? d : f);
+        L.gu = ptq1::gemm_plan(m, 2 * f, d);
+        L.dn = ptq1::gemm_plan(m, d, f);
+        const size_t fa = ptq1::gemm_frag_elems(L.gu, d), fb = ptq1::gemm_frag_elems(L.dn, f);
+        const size_t pa = ptq1::gemm_part_floats(L.gu, m, 2 * f), pb = ptq1::gemm_part_floats(L.dn, m, d);
+        L.xb = off; off += round_up((fa > fb ? fa : fb) * 2, kWsAlign);
         L.g = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
         L.u = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
+        L.part = off; off += round_up((pa > pb ? pa : pb) * sizeof(float), kWsAlign);
     }
     L.total = off;
     return L;
@@ -524,7 +537,7 @@ size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
     if (m == 0) return 0;
-    return gemm_ws(m, k);
+    return gemm_layout(ptq1::gemm_plan(m, n, k), m, n, k).total;
 }
 
 ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m,
@@ -539,19 +552,22 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
     if (mn == 0) return ok();
     PTQ1_TRY(check_floats(x, "x", mk, &xb));
     PTQ1_TRY(check_signs(signs1024, false));
-    const size_t need = gemm_ws(m, k);
+    const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k);
+    const GemmWs L = gemm_layout(plan, m, n, k);
+    const size_t need = L.total;
     PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm"));
     if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
     if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps tiled");
     if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
         overlaps(ws, (int64_t)need, tiled, wb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
-    const int64_t m_pad = ptq1::gemm_m_pad(m);
-    uint16_t *xbf = static_cast<uint16_t *>(ws);
-    hipError_t e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, k, signs1024, 0.0f, xbf, stream);
+    char *w = static_cast<char *>(ws);
+    uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
+    float *part = reinterpret_cast<float *>(w + L.part);
+    hipError_t e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, k, signs1024, 0.0f, xf, stream);
     if (e == hipSuccess)
         e = profiled(kProfGemm, stream, [&] {
-            return ptq1::launch_gemm(xbf, m, m_pad, k, tiled, n, nullptr, 0, y, nullptr, nullptr, stream);
+            return ptq1::launch_gemm(plan, xf, m, tiled, n, nullptr, 0, y, nullptr, nullptr, part, stream);
         });
     return hip_status(e, "ptq1_gemm");
 }
@@ -612,19 +628,19 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
             });
         if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, d, f, x, x_out, stream);
     } else {
-        const int64_t m_pad = ptq1::gemm_m_pad(m);
-        uint16_t *xbf = reinterpret_cast<uint16_t *>(w + L.xb);
+        uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.xb);
         float *g = reinterpret_cast<float *>(w + L.g);
         float *u = reinterpret_cast<float *>(w + L.u);
-        e = ptq1::launch_prep_bf16(x, nullptr, nullptr, m, m_pad, d, signs1024, rms_eps, xbf, stream);
+        float *part = reinterpret_cast<float *>(w + L.part);
+        e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, d, signs1024, rms_eps, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
-                return ptq1::launch_gemm(xbf, m, m_pad, d, w_gate, f, w_up, f, g, u, nullptr, stream);
+                return ptq1::launch_gemm(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream);
             });
-        if (e == hipSuccess) e = ptq1::launch_prep_bf16(nullptr, g, u, m, m_pad, f, signs1024, 0.0f, xbf, stream);
+        if (e == hipSuccess) e = ptq1::launch_prep_frag(nullptr, g, u, m, f, signs1024, 0.0f, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
-                return ptq1::launch_gemm(xbf, m, m_pad, f, w_down, d, nullptr, 0, x_out, nullptr, x, stream);
+                return ptq1::launch_gemm(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);
             });
     }
     return hip_status(e, "ptq1_ffn_block");

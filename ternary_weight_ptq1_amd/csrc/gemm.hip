@@ -3,12 +3,22 @@
 // accumulation and the per-block scale applied in fp32.
 //
 // "A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally":
-//   - "What Ferrox does with it": a GEMM for prefill, trits read with the
-//     float-pipeline peel;
+//   - "What Ferrox does with it": a GEMM for prefill whose weight tiles are
+//     decoded from the packed trits;
 //   - "What Bonsai is": activations rotated before every folded matmul.
 // Each 128-weight block's MFMA partial sum is multiplied by that block's
 // scale in fp32 (never folded into bf16), so the only rounding beyond fp32
 // is the bf16 rounding of the rotated activations.
+//
+// K order inside a block.  A dot product does not depend on the order in
+// which K is summed, so both operands are stored in one fixed permutation of
+// the block's 128 positions that makes the trit decode cheap: MFMA K
+// position kappa = 8 f + j (fragment f = 0..15, element j = 0..7) carries
+//   f < 15:  digit d = f % 5 of byte 8 (f / 5) + j   (weight 5 byte + d),
+//   f = 15:  weight 120 + j   (bytes 24 and 25 in natural order).
+// One fragment is then "digit d of eight consecutive bytes", which a table
+// read per byte and one v_perm per pair of bytes produce directly.  The
+// activation side is written in the same order by the prep kernel.
 #include <hip/hip_ext.h>
 
 #include "ptq1_device.h"
@@ -18,30 +28,38 @@ namespace ptq1 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t gm_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t gm_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gm_u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t gm_u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+
+// Weight index (0..127 inside the block) held at MFMA K position kappa.
+__host__ __device__ constexpr int gemm_kperm(int kappa)
+{
+    return (kappa >> 3) == 15 ? kappa : 5 * (8 * ((kappa >> 3) / 5) + (kappa & 7)) + (kappa >> 3) % 5;
+}
 
 // ---------------------------------------------------------------------------
 // Activation prep: one wavefront per (row, 1024-chunk).
 //   input  = x (times the row's RMS scale when rms_eps > 0), or silu(g) * u
-//   output = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
-// Rows in [m, m_pad) are written as zeros so MFMA tiles need no row guard.
+//   value  = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
+// Output: MFMA A fragments.  For 32-row group mt, block kb, step s (0..7)
+// and lane l the 16 bytes at element offset (((mt nb + kb) 8 + s) 64 + l) 8
+// hold A[32 mt + l % 32][128 kb + gemm_kperm(16 s + 8 (l / 32) + j)],
+// j = 0..7 -- the operand of v_mfma_f32_32x32x16_bf16 for that step.
+// Rows >= m are never written: an output row of the MFMA depends only on
+// its own A row, so whatever they hold only reaches outputs nobody stores.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kRotThreads) k_prep_bf16(
+__global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
-    int64_t m, int64_t k, const float *__restrict__ signs, float rms_eps,
-    uint16_t *__restrict__ xb)
+    int64_t k, const float *__restrict__ signs, float rms_eps, uint16_t *__restrict__ xf)
 {
+    __shared__ float st[kHadamard];
     const int64_t cpr = (k + kHadamard - 1) / kHadamard;  // == k / 1024 when signs are given
     const int64_t row = blockIdx.x / cpr;
     const int64_t ch = blockIdx.x - row * cpr;
     const int lane = threadIdx.x;
     const int64_t e0 = ch * kHadamard;  // first element of this chunk in the row
-    uint16_t *dst = xb + row * k + e0;
-    if (row >= m) {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j)
-            if (e0 + lane + kWave * j < k) dst[lane + kWave * j] = 0;
-        return;
-    }
     float a = 1.0f;
     if (x != nullptr && rms_eps > 0.0f) {
         const float *xr = x + row * k;
@@ -73,194 +91,507 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_bf16(
         for (int j = 0; j < kRotPerLane; ++j) v[j] *= (1.0f / 32.0f);
     }
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j)
-        if (e0 + lane + kWave * j < k) dst[lane + kWave * j] = f32_to_bf16_rne(v[j]);
+    for (int j = 0; j < kRotPerLane; ++j) st[lane + kWave * j] = v[j];
+    __syncthreads();
+
+    const int64_t nb = k / kBlockWeights;
+    const int64_t mt = row / 32;
+    const int rl = static_cast<int>(row % 32);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const int p = lane + kWave * pp;  // fragment piece: block kbl of the chunk, fragment f
+        const int kbl = p >> 4, f = p & 15;
+        const int64_t kb = ch * (kHadamard / kBlockWeights) + kbl;
+        if (kb >= nb) continue;
+        const float *src = st + kBlockWeights * kbl;
+        gm_u32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t lo = f32_to_bf16_rne(src[gemm_kperm(8 * f + 2 * jj)]);
+            const uint32_t hi = f32_to_bf16_rne(src[gemm_kperm(8 * f + 2 * jj + 1)]);
+            o[jj] = lo | (hi << 16);
+        }
+        const int64_t off = (((mt * nb + kb) * 8 + (f >> 1)) * kWave + rl + 32 * (f & 1)) * 8;
+        *reinterpret_cast<gm_u32x4 *>(xf + off) = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// MFMA GEMM.  Workgroup tile BM (tokens) x BN (weight rows); 4 waves in a
-// WM x WN grid, each owning TM x TN 32x32 output tiles of
-// v_mfma_f32_32x32x16_bf16.  K advances one PTQ1_0 block (128) per step:
-//   A: the bf16 activation tile [BM][128] is copied to LDS;
-//   B: the weight tile's 28-byte blocks (tiled layout) are read once, trits
-//      peeled on the float pipeline and written to LDS as exact bf16
-//      -1/0/+1; the scale goes to LDS as fp32;
-//   16 x K=16 MFMAs accumulate the block's partial product from zero, then
-//   acc += partial * scale[column] in fp32.
+// MFMA GEMM.  A workgroup (4 waves) owns 128 output columns (weight rows)
+// and BM = 32 WM output rows; the waves form a WM x WN grid, each owning
+// one 32-row group and TN 32x32 tiles of v_mfma_f32_32x32x16_bf16
+// (WN TN = 4).  K advances one PTQ1_0 block per iteration:
+//   B: every thread decodes part of one column's 28-byte block (its first
+//      12 bytes, or the last 16 with the scale) through a byte -> 5 trits
+//      table into LDS fragments, double-buffered, one barrier per block;
+//   A: each wave loads its 16-byte activation fragments from global memory
+//      one block ahead;
+//   8 MFMA steps accumulate the block's partial product from zero, then
+//      acc += partial * scale[column] in fp32.
+// Trits are stored as bf16 -2 / 0 / +2 (low byte always zero, so a table
+// entry is just the five high bytes) and the scale is halved to match.
+// A split-K grid (blockIdx.z) writes fp32 partial sums instead; a second
+// kernel adds them in a fixed order.
 // Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
 // and B[8(l/32)+j][l%32], j = 0..7; result register r of lane l is
 // D[8(r/4) + 4(l/32) + r%4][l%32].
 // ---------------------------------------------------------------------------
-constexpr int kLdsK = kGemmKB + 8;  // padded row (bf16 elements): 272 B, conflict-free b128 reads
+constexpr int kFragsPerBlock = 16;                             // per column, 16 B each
+constexpr int kBufBytes = kFragsPerBlock * kGemmBN * 16;        // 32 KB per decoded block
+constexpr int kTabCopies = 32;                                  // one per lane of a 32-lane LDS phase
+constexpr int kTabBytes = 256 * kTabCopies * 8;                 // 64 KB
+// Two decoded blocks (16 fragments x 128 columns each), then one spare
+// fragment row for the role that has no fragment 15, then the scales
+// [real / spare][buffer][column].
+constexpr int kGemmLds = kTabBytes + 2 * kBufBytes + kGemmBN * 16 + 4 * kGemmBN * 4;
+static_assert(kGemmLds <= 160 * 1024, "LDS");
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(
-    const uint16_t *__restrict__ xb, int64_t m, int64_t k, const uint8_t *__restrict__ w0,
-    int64_t n0, const uint8_t *__restrict__ w1, int64_t n1, float *__restrict__ y0,
-    float *__restrict__ y1, const float *residual)
+// bf16 high byte of 2 * (digit - 1): digit 0 -> -2 (0xC0), 1 -> 0, 2 -> +2 (0x40)
+__device__ __forceinline__ uint32_t trit_hi(uint32_t d) { return d == 0 ? 0xC0u : (d == 1 ? 0x00u : 0x40u); }
+
+// v_perm selector: fragment dword of digit d for bytes (x, y) taken from the
+// table entries' dword (d < 4 ? 0 : 1): [0, H_d(x), 0, H_d(y)].
+__device__ __forceinline__ constexpr uint32_t dsel(int d)
 {
-    static_assert(WM * WN * kWave == kGemmThreads, "4 waves");
-    constexpr int TM = BM / WM / 32;
-    constexpr int TN = BN / WN / 32;
-    static_assert(TM >= 1 && TN >= 1, "tile");
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM][kLdsK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][kLdsK];
-    __shared__ float ssc[BN];
+    return 0x000c000cu | (static_cast<uint32_t>(d & 3) << 8) | (static_cast<uint32_t>(4 + (d & 3)) << 24);
+}
+
+struct GemmArgs {
+    const uint16_t *xf;      // A fragments (k_prep_frag layout)
+    const uint8_t *w0;       // tiled matrix 0 (rows [0, n0) of the virtual matrix)
+    const uint8_t *w1;       // tiled matrix 1 (rows [n0, n0 + n1)), may be null
+    int64_t n0, n1, bands0, bands1;
+    float *y0, *y1;          // outputs [m][n0], [m][n1] (split == 1)
+    const float *residual;   // [m][n0] or null (split == 1)
+    float *part;             // [split][m][n0 + n1] partial sums (split > 1), else null
+    int64_t m, nb;           // activation rows, K blocks
+    int32_t bps;             // K blocks per split
+};
+
+template <int WM, int WN, int TM, int TN, int PD>
+__global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
+{
+    static_assert(WM * WN == 4 && WN * TN * 32 == kGemmBN, "4 waves x 128 columns");
+    static_assert(PD >= 2 && PD % 2 == 0, "weight prefetch depth");
+    constexpr int kBq = TM * TN >= 8 ? 2 : 3;  // B-fragment prefetch depth in MFMA steps
+    constexpr int kAr = 4;                     // activation-fragment ring, in MFMA steps
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *tab = lds;
+    char *bsm = lds + kTabBytes;
+    float *ssc = reinterpret_cast<float *>(lds + kTabBytes + 2 * kBufBytes + kGemmBN * 16);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t rows = n0 + n1;
-    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * BN;
-    const int64_t tile_m = static_cast<int64_t>(blockIdx.y) * BM;
-    const int64_t nb = k / kBlockWeights;
-    const int64_t bands0 = (n0 + kTileRows - 1) / kTileRows, bands1 = (n1 + kTileRows - 1) / kTileRows;
+    const int64_t rows = a.n0 + a.n1;
+    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * kGemmBN;
+    const int64_t mt0 = (static_cast<int64_t>(blockIdx.y) * WM + wm) * TM;  // this wave's first 32-row group
+    const bool active = mt0 * 32 < a.m;
+    const int64_t kb0 = static_cast<int64_t>(blockIdx.z) * a.bps;
+    const int nblk = static_cast<int>((a.nb - kb0 < a.bps) ? a.nb - kb0 : a.bps);
 
-    f32x16 acc[TM][TN];
+    // ---- byte -> trit table: entry b, copy c at b * 256 + c * 8
+    {
+        const uint32_t b = static_cast<uint32_t>(tid);
+        uint32_t r = b, h[5];
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    for (int64_t kb = 0; kb < nb; ++kb) {
-        // ---- A tile: BM rows x 128 bf16, 16 B per copy
-        for (int c = tid; c < BM * (kGemmKB / 8); c += kGemmThreads) {
-            const int r = c / (kGemmKB / 8), p = c % (kGemmKB / 8);
-            const uint4 v = *reinterpret_cast<const uint4 *>(xb + (tile_m + r) * k + kb * kGemmKB + p * 8);
-            *reinterpret_cast<uint4 *>(&As[r][p * 8]) = v;
+        for (int n = 0; n < 5; ++n) {
+            const uint32_t t = 3u * r;
+            h[n] = trit_hi(t >> 8);
+            r = t & 0xffu;
         }
-        // ---- B tile: BN rows x 7 dwords; peel 4 (or 2) trit bytes per dword
-        for (int c = tid; c < BN * kBlockDwords; c += kGemmThreads) {
-            const int r = c / kBlockDwords, q = c % kBlockDwords;
-            const int64_t rv = tile_n + r;
-            uint32_t dw = 0x80808080u;  // byte 128 = code 121 = all digits 1 = zero weights
-            if (rv < rows) {
-                const int64_t rr = (rv < n0) ? rv : rv - n0;  // row of its own (tiled) matrix
-                const int64_t bands = (rv < n0) ? bands0 : bands1;
-                const uint8_t *tile = ((rv < n0) ? w0 : w1) +
-                                      ((kb / kTileBlocks) * bands + rr / kTileRows) * kTileBytes;
-                const int pos = static_cast<int>(rr % kTileRows) * kTileBlocks + static_cast<int>(kb % kTileBlocks);
-                dw = reinterpret_cast<const uint32_t *>(tile + pos * kBlockBytes)[q];
-            }
-            const int nbytes = (q == kBlockDwords - 1) ? 2 : 4;
-            for (int t = 0; t < nbytes; ++t) {
-                const int i = 4 * q + t;
-                const Peel5 p = peel5(static_cast<float>((dw >> (8 * t)) & 0xffu));
-                const float dg[5] = {p.d0, p.d1, p.d2, p.d3, p.d4};
-#pragma unroll
-                for (int n = 0; n < kTritsPerByte; ++n) {
-                    const int j = kTritsPerByte * i + n;
-                    if (j < kBlockWeights)
-                        Bs[r][j] = static_cast<uint16_t>(__builtin_bit_cast(uint32_t, dg[n] - 1.0f) >> 16);
-                }
-            }
-            if (q == kBlockDwords - 1) ssc[r] = (rv < rows) ? half_bits_to_float(dw >> 16) : 0.0f;
-        }
-        __syncthreads();
-
-        f32x16 part[TM][TN];
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int b = 0; b < TN; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) part[a][b][r] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < kGemmKB / 16; ++ks) {
-            const int kof = ks * 16 + 8 * (lane / 32);
-            bf16x8 av[TM], bv[TN];
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-                av[a] = *reinterpret_cast<const bf16x8 *>(&As[wm * (BM / WM) + a * 32 + (lane & 31)][kof]);
-#pragma unroll
-            for (int b = 0; b < TN; ++b)
-                bv[b] = *reinterpret_cast<const bf16x8 *>(&Bs[wn * (BN / WN) + b * 32 + (lane & 31)][kof]);
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], part[a][b], 0, 0, 0);
-        }
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const float sc = ssc[wn * (BN / WN) + b * 32 + (lane & 31)];
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[a][b][r] = fmaf(part[a][b][r], sc, acc[a][b][r]);
-        }
-        __syncthreads();
+        const gm_u32x2 e = {h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), h[4]};
+#pragma unroll 8
+        for (int i = 0; i < kTabCopies; ++i)
+            *reinterpret_cast<gm_u32x2 *>(tab + b * 256 + ((b + i) & (kTabCopies - 1)) * 8) = e;
     }
 
+    // ---- this thread's share of the decode: column dn, bytes [0,12) (role 0)
+    //      or [12,28) (role 1)
+    const int dn = tid & (kGemmBN - 1);
+    const int role = tid >> 7;
+    const int64_t gcol = tile_n + dn;
+    const uint8_t *wcol = a.w0;
+    int64_t sstride = 0;
+    if (gcol < rows) {
+        const bool first = gcol < a.n0;
+        const int64_t rr = first ? gcol : gcol - a.n0;
+        wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+        sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+    }
+    wcol += role * 12;
+    const uint32_t lc = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+
+    // Loads are unconditional (callers clamp kb to the split) so that the
+    // compiler's in-order load counting never has to merge two paths.
+    auto load_w = [&](gm_u32x4 &r, int64_t kb) {  // role 0 uses 3 of the 4 dwords
+        r = *reinterpret_cast<const gm_u32x4a *>(wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes);
+    };
+    // The table sits at LDS address 0 (the kernel has no static LDS), so the
+    // v_perm result is the complete LDS address.
+    typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
+    auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
+        const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
+        return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
+    };
+    // Both roles run one branch-free sequence over their own bytes:
+    //   an 8-byte group  -> 5 whole fragments (role 0: bytes 0-7 -> fragments
+    //                       0-4; role 1: bytes 16-23 -> fragments 10-14),
+    //   a 4-byte half    -> half of fragments 5-9 (role 0: bytes 8-11, low
+    //                       8 bytes; role 1: bytes 12-15, high 8 bytes),
+    //   fragment 15 and the scale from bytes 24-27 (role 1; role 0 writes
+    //   its copy to a spare slot that nothing reads).
+    const int grp_frag = role ? 10 : 0;
+    const int half_off = role ? 8 : 0;
+    const int sc_slot = role ? 0 : 1;  // scale row: real (role 1) or spare (role 0)
+    struct TabRegs {
+        gm_u32x2 tg[8], th[4], tt[2];
+        uint32_t tw;
+    };
+    auto decode_read = [&](const gm_u32x4 &r, TabRegs &q, int part_no) {
+        if (part_no == 0) {
+            const uint32_t g0 = role ? r[1] : r[0], g1 = role ? r[2] : r[1];
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+            for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(g0, i);
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const int64_t col = tile_n + wn * (BN / WN) + b * 32 + (lane & 31);
+            for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(g1, i);
+        } else {
+            const uint32_t hw = role ? r[0] : r[2];
+            q.tw = r[3];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q.th[i] = tab_read(hw, i);
+            q.tt[0] = tab_read(q.tw, 0);
+            q.tt[1] = tab_read(q.tw, 1);
+        }
+    };
+    // fragment group d (0..4) of the decoded block, or (d == 5) fragment 15
+    // and the scale
+    auto decode_write = [&](const TabRegs &q, int buf, int d) {
+        char *bw = bsm + buf * kBufBytes;
+        if (d < 5) {
+            const int c = d >> 2;
+            const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
+                                __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
+                                __builtin_amdgcn_perm(q.tg[5][c], q.tg[4][c], dsel(d)),
+                                __builtin_amdgcn_perm(q.tg[7][c], q.tg[6][c], dsel(d))};
+            *reinterpret_cast<gm_u32x4 *>(bw + ((grp_frag + d) * kGemmBN + dn) * 16) = o;
+            const gm_u32x2 h = {__builtin_amdgcn_perm(q.th[1][c], q.th[0][c], dsel(d)),
+                                __builtin_amdgcn_perm(q.th[3][c], q.th[2][c], dsel(d))};
+            *reinterpret_cast<gm_u32x2 *>(bw + ((5 + d) * kGemmBN + dn) * 16 + half_off) = h;
+        } else {
+            // fragment 15: digits 0..4 of byte 24, digits 0..2 of byte 25
+            const gm_u32x4 o = {__builtin_amdgcn_perm(q.tt[0][0], q.tt[0][0], 0x010c000cu),
+                                __builtin_amdgcn_perm(q.tt[0][0], q.tt[0][0], 0x030c020cu),
+                                __builtin_amdgcn_perm(q.tt[1][0], q.tt[0][1], 0x040c000cu),
+                                __builtin_amdgcn_perm(q.tt[1][0], q.tt[1][0], 0x020c010cu)};
+            char *f15 = role ? bw + (15 * kGemmBN + dn) * 16 : bsm + 2 * kBufBytes + dn * 16;
+            *reinterpret_cast<gm_u32x4 *>(f15) = o;
+            ssc[(sc_slot * 2 + buf) * kGemmBN + dn] = 0.5f * half_bits_to_float(q.tw >> 16);
+        }
+    };
+
+    // activation fragments: this wave's 32-row groups mt0 .. mt0 + TM - 1
+    const uint16_t *xw = a.xf + (mt0 * a.nb * 8 * kWave + lane) * 8;
+    const int64_t tm_stride = a.nb * 8 * kWave * 8;
+    auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int s) {
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+            f[m] = *reinterpret_cast<const gm_u32x4 *>(xw + m * tm_stride + (kb * 8 + s) * kWave * 8);
+    };
+
+    f32x16 acc[TM][TN], part[TM][TN];
+    float scl[2][TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        scl[0][t] = scl[1][t] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][t][r] = part[m][t][r] = 0.0f;
+    }
+    const int scol = wn * 32 * TN + (lane & 31);
+    const char *bsr = bsm + ((lane >> 5) * kGemmBN + scol) * 16;
+
+    // One block of K, as eight MFMA steps.  Each step also carries part of
+    // the surrounding work, in a fixed order (sched_barrier keeps it): the
+    // B fragments kBq steps ahead, the activation fragments kAr steps ahead
+    // and a slice of the next block's decode (table reads in steps 0-1,
+    // fragment groups in steps 2-6, fragment 15 and the scale in 7).  Step 0
+    // first folds the previous block's partial into acc (acc += part *
+    // scale), tile by tile, just before that tile's MFMA chain restarts.
+    gm_u32x4 afr[kAr][TM];
+    auto iteration = [&](int buf, const float (&sp)[TN], float (&sc)[TN], gm_u32x4 &rslot, int64_t kb_cur,
+                         int64_t kb_next, int64_t kb_w) {
+        const char *bs = bsr + buf * kBufBytes;
+        bf16x8 bq[kBq + 1][TN];
+#pragma unroll
+        for (int p = 0; p < kBq; ++p)
+#pragma unroll
+            for (int t = 0; t < TN; ++t) bq[p][t] = *reinterpret_cast<const bf16x8 *>(bs + (2 * p * kGemmBN + 32 * t) * 16);
+        TabRegs q;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s + kBq < 8) {
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    bq[(s + kBq) % (kBq + 1)][t] =
+                        *reinterpret_cast<const bf16x8 *>(bs + (2 * (s + kBq) * kGemmBN + 32 * t) * 16);
+            }
+            // activation fragments for step s + kAr (this block or the next)
+            {
+                gm_u32x4 (&dst)[TM] = afr[(s + kAr) % kAr];
+                const gm_u32x4 (&cur)[TM] = afr[s % kAr];
+                bf16x8 av[TM];
+#pragma unroll
+                for (int m = 0; m < TM; ++m) av[m] = __builtin_bit_cast(bf16x8, cur[m]);
+#pragma unroll
+                for (int m = 0; m < TM; ++m)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t) {
+                        if (s == 0) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], sp[t], acc[m][t][r]);
+                            const f32x16 z = {};
+                            part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[0][t], z, 0, 0, 0);
+                        } else {
+                            part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[s % (kBq + 1)][t],
+                                                                                  part[m][t], 0, 0, 0);
+                        }
+                    }
+                if (s + kAr < 8)
+                    load_a(dst, kb_cur, s + kAr);
+                else
+                    load_a(dst, kb_next, s + kAr - 8);
+            }
+            if (s < 2) {
+                decode_read(rslot, q, s);
+                if (s == 1) load_w(rslot, kb_w);
+            } else {
+                decode_write(q, buf ^ 1, s - 2);
+            }
+            if (s == 7) {
+#pragma unroll
+                for (int t = 0; t < TN; ++t) sc[t] = ssc[buf * kGemmBN + scol + 32 * t];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: PD blocks of weights and kAr steps of activations in
+    // flight, block 0 decoded
+    const int last = nblk - 1;
+    gm_u32x4 ring[PD];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_w(ring[p], kb0 + (p < last ? p : last));
+#pragma unroll
+    for (int s = 0; s < kAr; ++s) load_a(afr[s], kb0, s);
+    __syncthreads();  // table
+    {
+        TabRegs q;
+        decode_read(ring[0], q, 0);
+        decode_read(ring[0], q, 1);
+#pragma unroll
+        for (int d = 0; d < 6; ++d) decode_write(q, 0, d);
+    }
+    load_w(ring[0], kb0 + (PD < last ? PD : last));
+    __syncthreads();
+
+    for (int base = 0; base < nblk; base += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int i = base + u;
+            if (i >= nblk) break;
+            // kb_next: the block whose first activation steps are fetched
+            // (clamped; its contents are unused past the split)
+            iteration(u & 1, scl[(u + 1) & 1], scl[u & 1], ring[(u + 1) % PD], kb0 + i,
+                      kb0 + (i + 1 < last ? i + 1 : last), kb0 + (i + 1 + PD < last ? i + 1 + PD : last));
+            __syncthreads();
+        }
+    }
+    // the last block's partial is not scaled yet (static indices only: a
+    // runtime index would force the arrays out of registers)
+    auto flush = [&](const float (&sp)[TN]) {
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], sp[t], acc[m][t][r]);
+    };
+    if ((nblk - 1) & 1)
+        flush(scl[1]);
+    else
+        flush(scl[0]);
+
+    if (!active) return;
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int64_t col = tile_n + wn * 32 * TN + 32 * t + (lane & 31);
             if (col >= rows) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = tile_m + wm * (BM / WM) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row >= m) continue;
-                if (col < n0) {
-                    const int64_t o = row * n0 + col;
-                    y0[o] = residual ? residual[o] + acc[a][b][r] : acc[a][b][r];
+                const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                if (row >= a.m) continue;
+                const float v = acc[m][t][r];
+                if (a.part != nullptr) {
+                    a.part[(static_cast<int64_t>(blockIdx.z) * a.m + row) * rows + col] = v;
+                } else if (col < a.n0) {
+                    const int64_t o = row * a.n0 + col;
+                    a.y0[o] = a.residual ? a.residual[o] + v : v;
                 } else {
-                    y1[row * n1 + (col - n0)] = acc[a][b][r];
+                    a.y1[row * a.n1 + (col - a.n0)] = v;
                 }
             }
         }
 }
 
-int64_t gemm_m_pad(int64_t m)
+// Sum of the split-K partials in split order (+ residual), routed to y0 / y1.
+__global__ void __launch_bounds__(kEwThreads) k_gemm_reduce(const float *__restrict__ part, int32_t splits,
+                                                             int64_t m, int64_t n0, int64_t n1, float *y0, float *y1,
+                                                             const float *residual)
 {
-    if (m <= 32) return 32;
-    return (m + 127) / 128 * 128;
+    const int64_t rows = n0 + n1;
+    const int64_t total = m * rows;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEwThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kEwThreads) {
+        float v = 0.0f;
+        for (int32_t z = 0; z < splits; ++z) v += part[z * total + i];
+        const int64_t row = i / rows, col = i - row * rows;
+        if (col < n0) {
+            const int64_t o = row * n0 + col;
+            y0[o] = residual ? residual[o] + v : v;
+        } else {
+            y1[row * n1 + (col - n0)] = v;
+        }
+    }
 }
 
-hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int64_t m,
-                            int64_t m_pad, int64_t k, const float *signs, float rms_eps,
-                            uint16_t *xb, hipStream_t s)
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kPlanCus = 256;      // compute units the split heuristic plans for
+constexpr int kMaxSplits = 32;
+}  // namespace
+
+GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
 {
-    const int64_t nchunks = m_pad * ((k + kHadamard - 1) / kHadamard);
+    // workgroup rows per configuration, and the time one workgroup spends
+    // on one block (microseconds, measured order of magnitude)
+    static const int64_t kBm[3] = {32, 64, 128};
+    static const double kTblk[3] = {0.25, 0.35, 0.6};
+    GemmPlan p;
+    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
+    const int64_t bm = kBm[p.cfg];
+    p.m_pad = (m + bm - 1) / bm * bm;
+    p.nb = k / kBlockWeights;
+    p.tiles_n = (rows + kGemmBN - 1) / kGemmBN;
+    p.tiles_m = p.m_pad / bm;
+    p.splits = 1;
+    p.bps = static_cast<int32_t>(p.nb);
+    if (m == 0 || rows == 0 || p.nb == 0) return p;
+    // Time model: rounds of one workgroup per CU, each block costing t_blk,
+    // plus a fixed start per round; splits add their fp32 partials
+    // (written and read back) and a launch.
+    const double t_blk = kTblk[p.cfg];
+    double best = 0.0;
+    for (int64_t s = 1; s <= kMaxSplits && s <= p.nb; ++s) {
+        const int64_t bps = (p.nb + s - 1) / s;
+        const int64_t se = (p.nb + bps - 1) / bps;
+        if (se != s) continue;
+        const int64_t wgs = p.tiles_n * p.tiles_m * s;
+        const int64_t rounds = (wgs + kPlanCus - 1) / kPlanCus;
+        double t = static_cast<double>(rounds) * (static_cast<double>(bps) * t_blk + 1.0);
+        if (s > 1) t += 2.0 * static_cast<double>(s * m * rows) * 4.0 / 5.0e6 + 3.0;
+        if (s == 1 || t < best) {
+            best = t;
+            p.splits = static_cast<int32_t>(s);
+            p.bps = static_cast<int32_t>(bps);
+        }
+    }
+    return p;
+}
+
+size_t gemm_frag_elems(const GemmPlan &p, int64_t k) { return static_cast<size_t>(p.m_pad) * static_cast<size_t>(k); }
+
+size_t gemm_part_floats(const GemmPlan &p, int64_t m, int64_t rows)
+{
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(rows) : 0;
+}
+
+hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
+                            const float *signs, float rms_eps, uint16_t *xf, hipStream_t s)
+{
+    const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prep_bf16, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
-                       g, u, m, k, signs, rms_eps, xb);
+    hipLaunchKernelGGL(k_prep_frag, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u, k,
+                       signs, rms_eps, xf);
     return hipGetLastError();
 }
 
-// Launches one GEMM kernel instance, with the profiling events attached to
-// the dispatch when a caller armed them.
-template <class K, class... Args>
-static void gemm_dispatch(K kernel, dim3 grid, hipStream_t s, Args... args)
+// Launches one GEMM kernel instance (dynamic LDS above the 64 KB default is
+// enabled once per instance), with the profiling events attached to the
+// dispatch when a caller armed them.
+template <int WM, int WN, int TM, int TN, int PD>
+static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 {
+    static bool attr_set = false;
+    const auto kernel = k_gemm_mfma<WM, WN, TM, TN, PD>;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
-        hipExtLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0u, s, pe.start, pe.stop, 0u, args...);
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), static_cast<uint32_t>(kGemmLds), s, pe.start, pe.stop,
+                              0u, args);
         pe = ProfEvents{};
     } else {
-        hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0, s, args...);
+        hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), kGemmLds, s, args);
     }
+    return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
-                       int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
-                       const float *residual, hipStream_t s)
+hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                       const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
+                       hipStream_t s)
 {
     const int64_t rows = n0 + n1;
-    if (rows == 0 || m == 0) return hipSuccess;
-    if (m_pad == 32) {
-        constexpr int BM = 32, BN = 128;
-        const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), 1);
-        gemm_dispatch(k_gemm_mfma<BM, BN, 1, 4>, grid, s, xb, m, k, w0, n0, w1, n1, y0, y1, residual);
-    } else {
-        constexpr int BM = 128, BN = 64;
-        const dim3 grid(static_cast<unsigned>((rows + BN - 1) / BN), static_cast<unsigned>(m_pad / BM));
-        gemm_dispatch(k_gemm_mfma<BM, BN, 2, 2>, grid, s, xb, m, k, w0, n0, w1, n1, y0, y1, residual);
-    }
+    if (rows == 0 || m == 0 || p.nb == 0) return hipSuccess;
+    GemmArgs a;
+    a.xf = xf;
+    a.w0 = w0;
+    a.w1 = w1;
+    a.n0 = n0;
+    a.n1 = n1;
+    a.bands0 = (n0 + kTileRows - 1) / kTileRows;
+    a.bands1 = (n1 + kTileRows - 1) / kTileRows;
+    a.y0 = y0;
+    a.y1 = y1;
+    a.residual = residual;
+    a.part = p.splits > 1 ? part : nullptr;
+    a.m = m;
+    a.nb = p.nb;
+    a.bps = p.bps;
+    const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m), static_cast<unsigned>(p.splits));
+    hipError_t e;
+    if (p.cfg == 0)
+        e = gemm_dispatch<1, 4, 1, 1, 4>(grid, s, a);
+    else if (p.cfg == 1)
+        e = gemm_dispatch<2, 2, 1, 2, 4>(grid, s, a);
+    else
+        e = gemm_dispatch<2, 2, 2, 2, 4>(grid, s, a);
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int64_t total = m * rows;
+    int64_t blocks = (total + kEwThreads - 1) / kEwThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>(blocks)), dim3(kEwThreads), 0, s, part, p.splits, m,
+                       n0, n1, y0, y1, residual);
     return hipGetLastError();
 }
 

@@ -54,8 +54,7 @@ constexpr int kMvRowsPerWg = kMvThreads;
 constexpr int kEwThreads = 256;
 
 // MFMA GEMM tile (bf16 32x32x16 MFMA, fp32 accumulate)
-constexpr int kGemmBN = 64;                     // weight rows per workgroup
-constexpr int kGemmKB = kBlockWeights;          // one PTQ1_0 block of K per step
+constexpr int kGemmBN = 128;                    // weight rows (output columns) per workgroup
 constexpr int kGemmThreads = 256;
 
 }  // namespace ptq1

@@ -66,17 +66,25 @@ hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, co
                                   float rms_eps, float *g, float *u, float *h, hipStream_t s);
 
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
-// xb [m_pad][k] bf16 = bf16(R (a * x)); rows >= m zero.  a = RMS scale if
+// Shape of one GEMM launch: tile configuration (cfg 0/1/2 = 32/64/128 rows
+// per workgroup), padded activation rows, grid and K split.
+struct GemmPlan {
+    int cfg = 0;
+    int64_t m_pad = 0, tiles_n = 0, tiles_m = 0, nb = 0;
+    int32_t splits = 1, bps = 0;  // K split count and blocks per split
+};
+GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k);
+size_t gemm_frag_elems(const GemmPlan &p, int64_t k);                // bf16 A fragments
+size_t gemm_part_floats(const GemmPlan &p, int64_t m, int64_t rows);  // split-K partials
+// xf = bf16 MFMA A fragments of R (a * x) (rows < m only); a = RMS scale if
 // rms_eps > 0.  When g/u are given instead of x, the input is silu(g) * u.
-int64_t gemm_m_pad(int64_t m);
-hipError_t launch_prep_bf16(const float *x, const float *g, const float *u, int64_t m,
-                            int64_t m_pad, int64_t k, const float *signs, float rms_eps,
-                            uint16_t *xb, hipStream_t s);
-// y [m][rows] (ldy) = xb . W^T (+ residual [m][rows] if given), W tiled;
-// rows of the virtual matrix as in launch_matvec_part; the second matrix's
-// outputs go to y1 (same ld) when n1 > 0.
-hipError_t launch_gemm(const uint16_t *xb, int64_t m, int64_t m_pad, int64_t k, const uint8_t *w0,
-                       int64_t n0, const uint8_t *w1, int64_t n1, float *y0, float *y1,
-                       const float *residual, hipStream_t s);
+hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
+                            const float *signs, float rms_eps, uint16_t *xf, hipStream_t s);
+// y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; rows of the
+// virtual matrix as in launch_matvec_part, the second matrix's outputs in
+// y1 [m][n1].  part: gemm_part_floats(p, m, n0 + n1) floats of scratch.
+hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                       const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
+                       hipStream_t s);
 
 }  // namespace ptq1
