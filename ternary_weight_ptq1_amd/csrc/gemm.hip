@@ -30,7 +30,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t gm_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t gm_u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t gm_u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t gm_u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t gm_u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
 // Weight index (0..127 inside the block) held at MFMA K position kappa.
@@ -60,30 +60,50 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const int64_t ch = blockIdx.x - row * cpr;
     const int lane = threadIdx.x;
     const int64_t e0 = ch * kHadamard;  // first element of this chunk in the row
-    float a = 1.0f;
-    if (x != nullptr && rms_eps > 0.0f) {
-        const float *xr = x + row * k;
-        float s = 0.0f;
-        for (int64_t i = lane; i < k; i += kWave) s = fmaf(xr[i], xr[i], s);
-#pragma unroll
-        for (int h = kWave / 2; h > 0; h >>= 1) s += __shfl_xor(s, h, kWave);
-        a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
-    }
+    // chunk values first (clamped addresses, no branches around the loads)
     float v[kRotPerLane];
+    const float *src0 = x != nullptr ? x : g;
 #pragma unroll
     for (int j = 0; j < kRotPerLane; ++j) {
         const int64_t e = e0 + lane + kWave * j;
-        float in = 0.0f;
-        if (e < k) {
-            const int64_t i = row * k + e;
-            if (x != nullptr) {
-                in = x[i] * a;
-            } else {
-                const float gv = g[i];
-                in = gv / (1.0f + expf(-gv)) * u[i];
+        v[j] = src0[row * k + (e < k ? e : k - 1)];
+    }
+    if (x == nullptr) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) {
+            const int64_t e = e0 + lane + kWave * j;
+            const float uv = u[row * k + (e < k ? e : k - 1)];
+            v[j] = v[j] / (1.0f + expf(-v[j])) * uv;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j)
+        if (e0 + lane + kWave * j >= k) v[j] = 0.0f;
+    if (x != nullptr && rms_eps > 0.0f) {
+        // the row's mean square: 16-byte loads (k is a multiple of 128),
+        // eight in flight per lane
+        const float4 *xr = reinterpret_cast<const float4 *>(x + row * k);
+        const int64_t k4 = k / 4;
+        float s8[8] = {};
+        for (int64_t i0 = 0; i0 < k4; i0 += 8 * kWave) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t i = i0 + q * kWave + lane;
+                const float4 xv = xr[i < k4 ? i : k4 - 1];
+                const float w = i < k4 ? 1.0f : 0.0f;
+                s8[q] = fmaf(w * xv.x, xv.x, fmaf(w * xv.y, xv.y, fmaf(w * xv.z, xv.z, fmaf(w * xv.w, xv.w, s8[q]))));
             }
         }
-        v[j] = signs ? in * signs[lane + kWave * j] : in;
+        float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+#pragma unroll
+        for (int h = kWave / 2; h > 0; h >>= 1) s += __shfl_xor(s, h, kWave);
+        const float a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] *= a;
+    }
+    if (signs != nullptr) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] *= signs[lane + kWave * j];
     }
     if (signs != nullptr) {
         fwht1024_wave(v);
@@ -117,15 +137,17 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 }
 
 // ---------------------------------------------------------------------------
-// MFMA GEMM.  A workgroup (4 waves) owns 128 output columns (weight rows)
-// and BM = 32 WM output rows; the waves form a WM x WN grid, each owning
-// one 32-row group and TN 32x32 tiles of v_mfma_f32_32x32x16_bf16
-// (WN TN = 4).  K advances one PTQ1_0 block per iteration:
-//   B: every thread decodes part of one column's 28-byte block (its first
-//      12 bytes, or the last 16 with the scale) through a byte -> 5 trits
-//      table into LDS fragments, double-buffered, one barrier per block;
+// MFMA GEMM.  A workgroup (4 or 8 waves) owns 128 output columns (weight
+// rows) and BM = 32 TM WM output rows; the waves form a WM x WN grid, each
+// owning TM x TN 32x32 tiles of v_mfma_f32_32x32x16_bf16.  K advances one
+// PTQ1_0 block per iteration:
+//   B: every thread decodes part of one column's 28-byte block through a
+//      byte -> 5 trits table into LDS fragments.  Three buffers rotate:
+//      while block i is multiplied, block i + 2 is decoded and the first
+//      fragments of block i + 1 are already being read, so the MFMA
+//      pipeline runs on across the one barrier per block;
 //   A: each wave loads its 16-byte activation fragments from global memory
-//      one block ahead;
+//      a few MFMA steps ahead;
 //   8 MFMA steps accumulate the block's partial product from zero, then
 //      acc += partial * scale[column] in fp32.
 // Trits are stored as bf16 -2 / 0 / +2 (low byte always zero, so a table
@@ -135,16 +157,27 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 // Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
 // and B[8(l/32)+j][l%32], j = 0..7; result register r of lane l is
 // D[8(r/4) + 4(l/32) + r%4][l%32].
+//
+// LDS (160 KB): [0, 64 KB) holds 256 rows of 256 bytes, row b for byte
+// value b: 16 copies of its 8-byte table entry in the first half (lane l
+// reads copy l % 16), and in the second half of rows 0..11 the block
+// scales [buffer][column]; [64 KB, 160 KB) holds the three decoded blocks.
 // ---------------------------------------------------------------------------
 constexpr int kFragsPerBlock = 16;                             // per column, 16 B each
 constexpr int kBufBytes = kFragsPerBlock * kGemmBN * 16;        // 32 KB per decoded block
-constexpr int kTabCopies = 32;                                  // one per lane of a 32-lane LDS phase
-constexpr int kTabBytes = 256 * kTabCopies * 8;                 // 64 KB
-// Two decoded blocks (16 fragments x 128 columns each), then one spare
-// fragment row for the role that has no fragment 15, then the scales
-// [real / spare][buffer][column].
-constexpr int kGemmLds = kTabBytes + 2 * kBufBytes + kGemmBN * 16 + 4 * kGemmBN * 4;
+constexpr int kNumBufs = 3;
+constexpr int kTabCopies = 16;
+constexpr int kTabBytes = 256 * 256;
+constexpr int kGemmLds = kTabBytes + kNumBufs * kBufBytes;
 static_assert(kGemmLds <= 160 * 1024, "LDS");
+static_assert(kNumBufs * kGemmBN <= 12 * 32, "scales fit in the free halves of rows 0..11");
+
+// LDS byte offset of the scale of (buffer, column)
+__device__ __forceinline__ uint32_t gemm_scale_addr(int buf, int col)
+{
+    const uint32_t i = static_cast<uint32_t>(buf * kGemmBN + col);
+    return (i >> 5) * 256u + 128u + (i & 31u) * 4u;
+}
 
 // bf16 high byte of 2 * (digit - 1): digit 0 -> -2 (0xC0), 1 -> 0, 2 -> +2 (0x40)
 __device__ __forceinline__ uint32_t trit_hi(uint32_t d) { return d == 0 ? 0xC0u : (d == 1 ? 0x00u : 0x40u); }
@@ -169,16 +202,17 @@ struct GemmArgs {
 };
 
 template <int WM, int WN, int TM, int TN, int PD>
-__global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
+__global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
 {
-    static_assert(WM * WN == 4 && WN * TN * 32 == kGemmBN, "4 waves x 128 columns");
-    static_assert(PD >= 2 && PD % 2 == 0, "weight prefetch depth");
-    constexpr int kBq = TM * TN >= 8 ? 2 : 3;  // B-fragment prefetch depth in MFMA steps
-    constexpr int kAr = 4;                     // activation-fragment ring, in MFMA steps
+    constexpr int kNT = 64 * WM * WN;  // 256 or 512 threads
+    static_assert((kNT == 256 || kNT == 512) && WN * TN * 32 == kGemmBN, "4 or 8 waves x 128 columns");
+    static_assert(PD % kNumBufs == 0, "weight ring: a multiple of the B buffers");
+    constexpr int kBq = 3;  // B-fragment prefetch, MFMA steps (ring of 4)
+    constexpr int kAr = 4;  // activation-fragment ring, MFMA steps
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char *tab = lds;
     char *bsm = lds + kTabBytes;
-    float *ssc = reinterpret_cast<float *>(lds + kTabBytes + 2 * kBufBytes + kGemmBN * 16);
+    typedef __attribute__((address_space(3))) float lds_f32;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -190,10 +224,12 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
     const bool active = mt0 * 32 < a.m;
     const int64_t kb0 = static_cast<int64_t>(blockIdx.z) * a.bps;
     const int nblk = static_cast<int>((a.nb - kb0 < a.bps) ? a.nb - kb0 : a.bps);
+    const int last = nblk - 1;
+    auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };  // clamped block index
 
     // ---- byte -> trit table: entry b, copy c at b * 256 + c * 8
     {
-        const uint32_t b = static_cast<uint32_t>(tid);
+        const uint32_t b = static_cast<uint32_t>(tid & 255);
         uint32_t r = b, h[5];
 #pragma unroll
         for (int n = 0; n < 5; ++n) {
@@ -202,13 +238,17 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
             r = t & 0xffu;
         }
         const gm_u32x2 e = {h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), h[4]};
-#pragma unroll 8
-        for (int i = 0; i < kTabCopies; ++i)
-            *reinterpret_cast<gm_u32x2 *>(tab + b * 256 + ((b + i) & (kTabCopies - 1)) * 8) = e;
+        constexpr int kCopiesPerThread = kTabCopies * 256 / kNT;
+        const int c0 = (tid >> 8) * kCopiesPerThread;
+#pragma unroll
+        for (int i = 0; i < kCopiesPerThread; ++i)
+            *reinterpret_cast<gm_u32x2 *>(tab + b * 256 + ((b + c0 + i) & (kTabCopies - 1)) * 8) = e;
     }
 
-    // ---- this thread's share of the decode: column dn, bytes [0,12) (role 0)
-    //      or [12,28) (role 1)
+    // ---- this thread's share of the decode: column dn and a byte range of
+    //      its block.  256 threads: bytes [0,12) (role 0) or [12,28) (role 1);
+    //      512 threads: bytes [0,8), [8,16), [16,24) (roles 0-2, five whole
+    //      fragments each) or [20,28) (role 3: fragment 15 and the scale).
     const int dn = tid & (kGemmBN - 1);
     const int role = tid >> 7;
     const int64_t gcol = tile_n + dn;
@@ -220,13 +260,19 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
         wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
         sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
     }
-    wcol += role * 12;
+    wcol += kNT == 256 ? role * 12 : (role < 3 ? 8 * role : 20);
     const uint32_t lc = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
 
-    // Loads are unconditional (callers clamp kb to the split) so that the
+    // Loads are unconditional (callers clamp the block) so that the
     // compiler's in-order load counting never has to merge two paths.
-    auto load_w = [&](gm_u32x4 &r, int64_t kb) {  // role 0 uses 3 of the 4 dwords
-        r = *reinterpret_cast<const gm_u32x4a *>(wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes);
+    auto load_w = [&](gm_u32x4 &r, int64_t kb) {  // 256 threads: role 0 uses 3 of the 4 dwords
+        const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+        if constexpr (kNT == 256) {
+            r = *reinterpret_cast<const gm_u32x4a *>(p);
+        } else {
+            const gm_u32x2a v = *reinterpret_cast<const gm_u32x2a *>(p);
+            r = gm_u32x4{v[0], v[1], 0u, 0u};
+        }
     };
     // The table sits at LDS address 0 (the kernel has no static LDS), so the
     // v_perm result is the complete LDS address.
@@ -235,22 +281,28 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
         const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
         return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
     };
-    // Both roles run one branch-free sequence over their own bytes:
+    // 256 threads, both roles in one branch-free sequence over their bytes:
     //   an 8-byte group  -> 5 whole fragments (role 0: bytes 0-7 -> fragments
     //                       0-4; role 1: bytes 16-23 -> fragments 10-14),
     //   a 4-byte half    -> half of fragments 5-9 (role 0: bytes 8-11, low
     //                       8 bytes; role 1: bytes 12-15, high 8 bytes),
-    //   fragment 15 and the scale from bytes 24-27 (role 1; role 0 writes
-    //   its copy to a spare slot that nothing reads).
+    //   fragment 15 and the scale from bytes 24-27 (role 1 only).
     const int grp_frag = role ? 10 : 0;
     const int half_off = role ? 8 : 0;
-    const int sc_slot = role ? 0 : 1;  // scale row: real (role 1) or spare (role 0)
     struct TabRegs {
         gm_u32x2 tg[8], th[4], tt[2];
         uint32_t tw;
     };
     auto decode_read = [&](const gm_u32x4 &r, TabRegs &q, int part_no) {
-        if (part_no == 0) {
+        if constexpr (kNT == 512) {
+            if (part_no == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(r[0], i);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(r[1], i);
+                q.tw = r[1];
+            }
+        } else if (part_no == 0) {
             const uint32_t g0 = role ? r[1] : r[0], g1 = role ? r[2] : r[1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(g0, i);
@@ -265,11 +317,35 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
             q.tt[1] = tab_read(q.tw, 1);
         }
     };
+    // fragment fifteen from the table entries of bytes 24 and 25
+    auto frag15 = [&](gm_u32x2 t24, gm_u32x2 t25) -> gm_u32x4 {
+        return gm_u32x4{__builtin_amdgcn_perm(t24[0], t24[0], 0x010c000cu),
+                        __builtin_amdgcn_perm(t24[0], t24[0], 0x030c020cu),
+                        __builtin_amdgcn_perm(t25[0], t24[1], 0x040c000cu),
+                        __builtin_amdgcn_perm(t25[0], t25[0], 0x020c010cu)};
+    };
+    auto put_scale = [&](int buf, uint32_t tw) {
+        *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(gemm_scale_addr(buf, dn))) =
+            0.5f * half_bits_to_float(tw >> 16);
+    };
     // fragment group d (0..4) of the decoded block, or (d == 5) fragment 15
     // and the scale
     auto decode_write = [&](const TabRegs &q, int buf, int d) {
         char *bw = bsm + buf * kBufBytes;
-        if (d < 5) {
+        if constexpr (kNT == 512) {
+            if (d >= 5) return;
+            if (role < 3) {  // wave-uniform
+                const int c = d >> 2;
+                const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
+                                    __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
+                                    __builtin_amdgcn_perm(q.tg[5][c], q.tg[4][c], dsel(d)),
+                                    __builtin_amdgcn_perm(q.tg[7][c], q.tg[6][c], dsel(d))};
+                *reinterpret_cast<gm_u32x4 *>(bw + ((5 * role + d) * kGemmBN + dn) * 16) = o;
+            } else if (d == 0) {  // bytes 20..27: 24 and 25 are entries 4 and 5
+                *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tg[4], q.tg[5]);
+                put_scale(buf, q.tw);
+            }
+        } else if (d < 5) {
             const int c = d >> 2;
             const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
                                 __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
@@ -279,16 +355,17 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
             const gm_u32x2 h = {__builtin_amdgcn_perm(q.th[1][c], q.th[0][c], dsel(d)),
                                 __builtin_amdgcn_perm(q.th[3][c], q.th[2][c], dsel(d))};
             *reinterpret_cast<gm_u32x2 *>(bw + ((5 + d) * kGemmBN + dn) * 16 + half_off) = h;
-        } else {
-            // fragment 15: digits 0..4 of byte 24, digits 0..2 of byte 25
-            const gm_u32x4 o = {__builtin_amdgcn_perm(q.tt[0][0], q.tt[0][0], 0x010c000cu),
-                                __builtin_amdgcn_perm(q.tt[0][0], q.tt[0][0], 0x030c020cu),
-                                __builtin_amdgcn_perm(q.tt[1][0], q.tt[0][1], 0x040c000cu),
-                                __builtin_amdgcn_perm(q.tt[1][0], q.tt[1][0], 0x020c010cu)};
-            char *f15 = role ? bw + (15 * kGemmBN + dn) * 16 : bsm + 2 * kBufBytes + dn * 16;
-            *reinterpret_cast<gm_u32x4 *>(f15) = o;
-            ssc[(sc_slot * 2 + buf) * kGemmBN + dn] = 0.5f * half_bits_to_float(q.tw >> 16);
+        } else if (role == 1) {  // wave-uniform
+            *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tt[0], q.tt[1]);
+            put_scale(buf, q.tw);
         }
+    };
+    auto decode_all = [&](const gm_u32x4 &r, int buf) {
+        TabRegs q;
+        decode_read(r, q, 0);
+        decode_read(r, q, 1);
+#pragma unroll
+        for (int d = 0; d < 6; ++d) decode_write(q, buf, d);
     };
 
     // activation fragments: this wave's 32-row groups mt0 .. mt0 + TM - 1
@@ -301,10 +378,10 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
     };
 
     f32x16 acc[TM][TN], part[TM][TN];
-    float scl[2][TN];
+    float scl[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-        scl[0][t] = scl[1][t] = 0.0f;
+        scl[t] = 0.0f;
 #pragma unroll
         for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -312,46 +389,61 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
     }
     const int scol = wn * 32 * TN + (lane & 31);
     const char *bsr = bsm + ((lane >> 5) * kGemmBN + scol) * 16;
+    auto read_b = [&](bf16x8 (&dst)[TN], int buf, int step) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            dst[t] = *reinterpret_cast<const bf16x8 *>(bsr + buf * kBufBytes + (2 * step * kGemmBN + 32 * t) * 16);
+    };
+
+    // ---- prologue: blocks 0 and 1 decoded, block 2 .. of weights, the first
+    //      activation steps and the first B fragments in flight
+    gm_u32x4 afr[kAr][TM];
+    bf16x8 bq[kBq + 1][TN];
+    gm_u32x4 ring[PD];  // weights of blocks i + 2 .. i + 1 + PD at iteration i
+    {
+        gm_u32x4 w_first, w_second;
+        load_w(w_first, blk(0));
+        load_w(w_second, blk(1));
+#pragma unroll
+        for (int p = 0; p < PD; ++p) load_w(ring[(2 + p) % PD], blk(2 + p));
+#pragma unroll
+        for (int s = 0; s < kAr; ++s) load_a(afr[s], blk(0), s);
+        __syncthreads();  // table
+        decode_all(w_first, 0);
+        decode_all(w_second, 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kBq; ++p) read_b(bq[p], 0, p);
 
     // One block of K, as eight MFMA steps.  Each step also carries part of
     // the surrounding work, in a fixed order (sched_barrier keeps it): the
-    // B fragments kBq steps ahead, the activation fragments kAr steps ahead
-    // and a slice of the next block's decode (table reads in steps 0-1,
-    // fragment groups in steps 2-6, fragment 15 and the scale in 7).  Step 0
-    // first folds the previous block's partial into acc (acc += part *
-    // scale), tile by tile, just before that tile's MFMA chain restarts.
-    gm_u32x4 afr[kAr][TM];
-    auto iteration = [&](int buf, const float (&sp)[TN], float (&sc)[TN], gm_u32x4 &rslot, int64_t kb_cur,
-                         int64_t kb_next, int64_t kb_w) {
-        const char *bs = bsr + buf * kBufBytes;
-        bf16x8 bq[kBq + 1][TN];
-#pragma unroll
-        for (int p = 0; p < kBq; ++p)
-#pragma unroll
-            for (int t = 0; t < TN; ++t) bq[p][t] = *reinterpret_cast<const bf16x8 *>(bs + (2 * p * kGemmBN + 32 * t) * 16);
+    // B fragments kBq steps ahead (into the next block's buffer at the end),
+    // the activation fragments kAr steps ahead and a slice of the decode of
+    // block i + 2 (table reads in steps 0-1, fragment groups in steps 2-7).
+    // Step 0 first folds the previous block's partial into acc (acc += part
+    // * scale), tile by tile, just before that tile's MFMA chain restarts.
+    auto iteration = [&](int buf, int i, gm_u32x4 &rslot) {
+        const int nbuf = (buf + 1) % kNumBufs, dbuf = (buf + 2) % kNumBufs;
         TabRegs q;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            if (s + kBq < 8) {
-#pragma unroll
-                for (int t = 0; t < TN; ++t)
-                    bq[(s + kBq) % (kBq + 1)][t] =
-                        *reinterpret_cast<const bf16x8 *>(bs + (2 * (s + kBq) * kGemmBN + 32 * t) * 16);
-            }
-            // activation fragments for step s + kAr (this block or the next)
+            if (s + kBq < 8)
+                read_b(bq[(s + kBq) % (kBq + 1)], buf, s + kBq);
+            else
+                read_b(bq[(s + kBq) % (kBq + 1)], nbuf, s + kBq - 8);
             {
-                gm_u32x4 (&dst)[TM] = afr[(s + kAr) % kAr];
-                const gm_u32x4 (&cur)[TM] = afr[s % kAr];
+                gm_u32x4 (&ar)[TM] = afr[s % kAr];
                 bf16x8 av[TM];
 #pragma unroll
-                for (int m = 0; m < TM; ++m) av[m] = __builtin_bit_cast(bf16x8, cur[m]);
+                for (int m = 0; m < TM; ++m) av[m] = __builtin_bit_cast(bf16x8, ar[m]);
 #pragma unroll
                 for (int m = 0; m < TM; ++m)
 #pragma unroll
                     for (int t = 0; t < TN; ++t) {
                         if (s == 0) {
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], sp[t], acc[m][t][r]);
+                            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
                             const f32x16 z = {};
                             part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[0][t], z, 0, 0, 0);
                         } else {
@@ -360,69 +452,42 @@ __global__ void __launch_bounds__(kGemmThreads) k_gemm_mfma(GemmArgs a)
                         }
                     }
                 if (s + kAr < 8)
-                    load_a(dst, kb_cur, s + kAr);
+                    load_a(ar, blk(i), s + kAr);
                 else
-                    load_a(dst, kb_next, s + kAr - 8);
+                    load_a(ar, blk(i + 1), s + kAr - 8);
             }
             if (s < 2) {
                 decode_read(rslot, q, s);
-                if (s == 1) load_w(rslot, kb_w);
+                if (s == 1) load_w(rslot, blk(i + 2 + PD));
             } else {
-                decode_write(q, buf ^ 1, s - 2);
+                decode_write(q, dbuf, s - 2);
             }
             if (s == 7) {
 #pragma unroll
-                for (int t = 0; t < TN; ++t) sc[t] = ssc[buf * kGemmBN + scol + 32 * t];
+                for (int t = 0; t < TN; ++t)
+                    scl[t] = *reinterpret_cast<const lds_f32 *>(
+                        static_cast<uintptr_t>(gemm_scale_addr(buf, scol + 32 * t)));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-
-    // ---- prologue: PD blocks of weights and kAr steps of activations in
-    // flight, block 0 decoded
-    const int last = nblk - 1;
-    gm_u32x4 ring[PD];
-#pragma unroll
-    for (int p = 0; p < PD; ++p) load_w(ring[p], kb0 + (p < last ? p : last));
-#pragma unroll
-    for (int s = 0; s < kAr; ++s) load_a(afr[s], kb0, s);
-    __syncthreads();  // table
-    {
-        TabRegs q;
-        decode_read(ring[0], q, 0);
-        decode_read(ring[0], q, 1);
-#pragma unroll
-        for (int d = 0; d < 6; ++d) decode_write(q, 0, d);
-    }
-    load_w(ring[0], kb0 + (PD < last ? PD : last));
-    __syncthreads();
 
     for (int base = 0; base < nblk; base += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u) {
             const int i = base + u;
             if (i >= nblk) break;
-            // kb_next: the block whose first activation steps are fetched
-            // (clamped; its contents are unused past the split)
-            iteration(u & 1, scl[(u + 1) & 1], scl[u & 1], ring[(u + 1) % PD], kb0 + i,
-                      kb0 + (i + 1 < last ? i + 1 : last), kb0 + (i + 1 + PD < last ? i + 1 + PD : last));
+            iteration(u % kNumBufs, i, ring[(u + 2) % PD]);
             __syncthreads();
         }
     }
-    // the last block's partial is not scaled yet (static indices only: a
-    // runtime index would force the arrays out of registers)
-    auto flush = [&](const float (&sp)[TN]) {
+    // the last block's partial is not scaled yet
 #pragma unroll
-        for (int m = 0; m < TM; ++m)
+    for (int m = 0; m < TM; ++m)
 #pragma unroll
-            for (int t = 0; t < TN; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], sp[t], acc[m][t][r]);
-    };
-    if ((nblk - 1) & 1)
-        flush(scl[1]);
-    else
-        flush(scl[0]);
+            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
 
     if (!active) return;
 #pragma unroll
@@ -481,10 +546,10 @@ GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
 {
     // workgroup rows per configuration, and the time one workgroup spends
     // on one block (microseconds, measured order of magnitude)
-    static const int64_t kBm[3] = {32, 64, 128};
-    static const double kTblk[3] = {0.25, 0.35, 0.6};
+    static const int64_t kBm[4] = {32, 64, 128, 128};
+    static const double kTblk[4] = {0.25, 0.35, 0.6, 0.6};
     GemmPlan p;
-    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
+    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 3);
     const int64_t bm = kBm[p.cfg];
     p.m_pad = (m + bm - 1) / bm * bm;
     p.nb = k / kBlockWeights;
@@ -548,11 +613,11 @@ static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
     }
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
-        hipExtLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), static_cast<uint32_t>(kGemmLds), s, pe.start, pe.stop,
-                              0u, args);
+        hipExtLaunchKernelGGL(kernel, grid, dim3(64 * WM * WN), static_cast<uint32_t>(kGemmLds), s, pe.start,
+                              pe.stop, 0u, args);
         pe = ProfEvents{};
     } else {
-        hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), kGemmLds, s, args);
+        hipLaunchKernelGGL(kernel, grid, dim3(64 * WM * WN), kGemmLds, s, args);
     }
     return hipGetLastError();
 }
@@ -581,11 +646,13 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m), static_cast<unsigned>(p.splits));
     hipError_t e;
     if (p.cfg == 0)
-        e = gemm_dispatch<1, 4, 1, 1, 4>(grid, s, a);
+        e = gemm_dispatch<1, 4, 1, 1, 3>(grid, s, a);
     else if (p.cfg == 1)
-        e = gemm_dispatch<2, 2, 1, 2, 4>(grid, s, a);
+        e = gemm_dispatch<2, 2, 1, 2, 3>(grid, s, a);
+    else if (p.cfg == 2)
+        e = gemm_dispatch<2, 2, 2, 2, 3>(grid, s, a);
     else
-        e = gemm_dispatch<2, 2, 2, 2, 4>(grid, s, a);
+        e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t total = m * rows;
     int64_t blocks = (total + kEwThreads - 1) / kEwThreads;
