@@ -97,6 +97,32 @@ def measured_traffic():
     return int(m_val.group(1))
 
 
+def gemm_only(args, torch, synth, sdev, P, dev) -> int:
+    """The prefill GEMM alone (for counter runs): M x 5120 activations against
+    one 17408 x 5120 PTQ1_0 matrix, --steps calls after --warmup."""
+    m, n, k = args.gemm_only, F, D
+    w = P.ptq1_tile(P.ptq1_pack(sdev.trits(1, 1, n, k), sdev.scales(1, 2, n, k // 128)), n, k)
+    x = torch.from_numpy(synth.activations(1, m, k)).to(dev)
+    sg = torch.from_numpy(synth.signs(1)).to(dev)
+    y = torch.empty(m, n, device=dev)
+    ws = torch.empty(P.workspace_bytes("gemm", m, n, k), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
+    torch.cuda.synchronize()
+    kt = P.KernelTimer("gemm", args.steps)
+    with kt:
+        for _ in range(args.steps):
+            P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
+    torch.cuda.synchronize()
+    ms = sorted(kt.durations_ms())
+    kt.close()
+    us = ms[len(ms) // 2] * 1e3
+    fl = 2.0 * m * n * k
+    print(json.dumps({"workload": f"prefill GEMM {m}x{k} -> {n}", "us_kernel_median": us,
+                      "TFLOP/s": fl / (us * 1e-6) / 1e12, "mfma_frac": fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +132,9 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline only (no breakdown)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (scale for the byte counters)")
+    ap.add_argument("--gemm-only", type=int, default=0, metavar="M",
+                    help="profiling aid: run the prefill GEMM (M x 5120 -> 17408) --steps times, print its "
+                         "kernel time, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded path is a "
@@ -124,6 +153,8 @@ def main() -> int:
     P.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.gemm_only > 0:
+        return gemm_only(args, torch, synth, sdev, P, dev)
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
