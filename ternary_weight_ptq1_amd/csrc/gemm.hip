@@ -17,8 +17,12 @@
 //   f < 15:  digit d = f % 5 of byte 8 (f / 5) + j   (weight 5 byte + d),
 //   f = 15:  weight 120 + j   (bytes 24 and 25 in natural order).
 // One fragment is then "digit d of eight consecutive bytes", which a table
-// read per byte and one v_perm per pair of bytes produce directly.  The
-// activation side is written in the same order by the prep kernel.
+// read per byte and one v_perm per pair of bytes produce directly.  MFMA
+// step s (0..7) takes fragment s in lanes 0-31 and fragment
+// kHiFrag[s] = 10, 11, 12, 13, 14, 8, 9, 15 in lanes 32-63: then a half-wave
+// only ever needs 16-20 bytes of a block (lanes 0-31 bytes 0-15, lanes
+// 32-63 bytes 8-27) and both halves read the same digit position in steps
+// 0-4.  The activation side is written in the same order by the prep kernel.
 #include <hip/hip_ext.h>
 
 #include "ptq1_device.h"
@@ -33,6 +37,11 @@ typedef uint32_t gm_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t gm_u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t gm_u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
+__host__ __device__ constexpr int gemm_hi_frag(int step)
+{
+    return step < 5 ? 10 + step : (step == 5 ? 8 : (step == 6 ? 9 : 15));
+}
+
 // Weight index (0..127 inside the block) held at MFMA K position kappa.
 __host__ __device__ constexpr int gemm_kperm(int kappa)
 {
@@ -45,8 +54,9 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 //   value  = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
 // Output: MFMA A fragments.  For 32-row group mt, block kb, step s (0..7)
 // and lane l the 16 bytes at element offset (((mt nb + kb) 8 + s) 64 + l) 8
-// hold A[32 mt + l % 32][128 kb + gemm_kperm(16 s + 8 (l / 32) + j)],
-// j = 0..7 -- the operand of v_mfma_f32_32x32x16_bf16 for that step.
+// hold A[32 mt + l % 32][128 kb + gemm_kperm(8 f + j)], j = 0..7, with
+// f = s (l < 32) or gemm_hi_frag(s) (l >= 32) -- the operand of
+// v_mfma_f32_32x32x16_bf16 for that step.
 // Rows >= m are never written: an output row of the MFMA depends only on
 // its own A row, so whatever they hold only reaches outputs nobody stores.
 // ---------------------------------------------------------------------------
@@ -131,7 +141,10 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
             const uint32_t hi = f32_to_bf16_rne(src[gemm_kperm(8 * f + 2 * jj + 1)]);
             o[jj] = lo | (hi << 16);
         }
-        const int64_t off = (((mt * nb + kb) * 8 + (f >> 1)) * kWave + rl + 32 * (f & 1)) * 8;
+        // (step, half) that carries fragment f
+        const int fs = f < 8 ? f : (f < 10 ? f - 3 : (f < 15 ? f - 10 : 7));
+        const int fh = f < 8 ? 0 : 1;
+        const int64_t off = (((mt * nb + kb) * 8 + fs) * kWave + rl + 32 * fh) * 8;
         *reinterpret_cast<gm_u32x4 *>(xf + off) = o;
     }
 }
@@ -388,11 +401,18 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
             for (int r = 0; r < 16; ++r) acc[m][t][r] = part[m][t][r] = 0.0f;
     }
     const int scol = wn * 32 * TN + (lane & 31);
-    const char *bsr = bsm + ((lane >> 5) * kGemmBN + scol) * 16;
+    // B fragment of step s: fragment s (lanes 0-31) or gemm_hi_frag(s)
+    // (lanes 32-63); the difference takes three values, folded into three
+    // per-lane bases
+    const int hi = lane >> 5;
+    const char *bsr0 = bsm + scol * 16 + hi * (10 * kGemmBN * 16);
+    const char *bsr1 = bsm + scol * 16 + hi * (3 * kGemmBN * 16);
+    const char *bsr2 = bsm + scol * 16 + hi * (8 * kGemmBN * 16);
     auto read_b = [&](bf16x8 (&dst)[TN], int buf, int step) {
+        const char *b = step < 5 ? bsr0 : (step < 7 ? bsr1 : bsr2);
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-            dst[t] = *reinterpret_cast<const bf16x8 *>(bsr + buf * kBufBytes + (2 * step * kGemmBN + 32 * t) * 16);
+            dst[t] = *reinterpret_cast<const bf16x8 *>(b + buf * kBufBytes + (step * kGemmBN + 32 * t) * 16);
     };
 
     // ---- prologue: blocks 0 and 1 decoded, block 2 .. of weights, the first
@@ -513,6 +533,240 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
         }
 }
 
+// ---------------------------------------------------------------------------
+// Small-batch GEMM (M <= 64): every wave decodes the B fragments of its own
+// 32 columns straight into registers, so no decoded block goes through LDS
+// and the loop has no barrier; only the byte -> trit table (read-only after
+// its build) sits in LDS, and two workgroups share a CU.
+//
+// A workgroup (4 waves) owns 128 columns and 32 TM rows; wave w owns columns
+// 32 w .. 32 w + 31, all TM row groups.  Lane l (column l % 32, half
+// h = l / 32) loads 16 bytes of its column's block at byte 8 h and the dword
+// at byte 24 (the scale, and bytes 24-25 for lanes 32-63), looks up the 18
+// table entries it needs and builds, for MFMA step s, the fragment of the
+// step/half mapping above: steps 0-4 take digit s of its first 8 bytes
+// (bytes 0-7 in lanes 0-31, 16-23 in lanes 32-63), steps 5-7 digits of
+// bytes 8-15 (0, 1, 2 in lanes 0-31; 3, 4 and fragment 15 in lanes 32-63).
+// Table entries here are [H0 H1 H2 H3 | H4 H1 H2 H3] so that the two halves'
+// digits of steps 5 and 6 sit in the same dword.
+// ---------------------------------------------------------------------------
+constexpr int kRdThreads = 256;
+constexpr int kRdTabCopies = 32;                    // conflict-free 8-byte reads
+constexpr int kRdLds = 256 * kRdTabCopies * 8;      // 64 KB: two workgroups per CU
+
+// v_perm selector: [0, byte b of x's entry, 0, byte b of y's entry]
+__device__ __forceinline__ constexpr uint32_t rd_sel(int b)
+{
+    return 0x000c000cu | (static_cast<uint32_t>(b) << 8) | (static_cast<uint32_t>(4 + b) << 24);
+}
+
+template <int TM, int PD>
+__global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
+{
+    constexpr int kAr = 4;  // activation-fragment ring, MFMA steps
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int hi = lane >> 5;
+    const int64_t rows = a.n0 + a.n1;
+    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * kGemmBN;
+    const int64_t mt0 = static_cast<int64_t>(blockIdx.y) * TM;
+    const int64_t kb0 = static_cast<int64_t>(blockIdx.z) * a.bps;
+    const int nblk = static_cast<int>((a.nb - kb0 < a.bps) ? a.nb - kb0 : a.bps);
+    const int last = nblk - 1;
+    auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };
+
+    // ---- table: entry b, copy c at b * 256 + c * 8
+    {
+        const uint32_t b = static_cast<uint32_t>(tid);
+        uint32_t r = b, h[5];
+#pragma unroll
+        for (int n = 0; n < 5; ++n) {
+            const uint32_t t = 3u * r;
+            h[n] = trit_hi(t >> 8);
+            r = t & 0xffu;
+        }
+        const gm_u32x2 e = {h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24),
+                            h[4] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24)};
+#pragma unroll 8
+        for (int i = 0; i < kRdTabCopies; ++i)
+            *reinterpret_cast<gm_u32x2 *>(lds + b * 256 + ((b + i) & (kRdTabCopies - 1)) * 8) = e;
+    }
+
+    // ---- this lane's column
+    const int64_t gcol = tile_n + wave * 32 + (lane & 31);
+    const uint8_t *wcol = a.w0;
+    int64_t sstride = 0;
+    if (gcol < rows) {
+        const bool first = gcol < a.n0;
+        const int64_t rr = first ? gcol : gcol - a.n0;
+        wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+        sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+    }
+    const uint32_t lc = static_cast<uint32_t>(lane & (kRdTabCopies - 1)) << 3;
+
+    struct WRegs {
+        gm_u32x4 v;  // bytes 8 h .. 8 h + 15
+        uint32_t w;  // bytes 24..27
+    };
+    auto load_w = [&](WRegs &r, int64_t kb) {
+        const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+        const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 8 * hi);
+        r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
+        r.w = *reinterpret_cast<const uint32_t *>(p + 24);
+    };
+    auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
+        const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
+        return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
+    };
+    struct Ent {
+        gm_u32x2 g[8];  // "first" bytes: 0-7 (lanes 0-31) or 16-23 (lanes 32-63)
+        gm_u32x2 m[8];  // bytes 8-15
+        gm_u32x2 t[2];  // bytes 24, 25
+        float scale;    // the block's scale, halved (trits are stored as +-2)
+    };
+    auto tab_reads = [&](const WRegs &r, Ent &e) {
+        const uint32_t g0 = hi ? r.v[2] : r.v[0], g1 = hi ? r.v[3] : r.v[1];
+        const uint32_t m0 = hi ? r.v[0] : r.v[2], m1 = hi ? r.v[1] : r.v[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e.g[i] = tab_read(g0, i);
+            e.g[4 + i] = tab_read(g1, i);
+            e.m[i] = tab_read(m0, i);
+            e.m[4 + i] = tab_read(m1, i);
+        }
+        e.t[0] = tab_read(r.w, 0);
+        e.t[1] = tab_read(r.w, 1);
+        e.scale = 0.5f * half_bits_to_float(r.w >> 16);
+    };
+    // per-lane selectors of steps 5 and 6 (digit 0 / 3 and 1 / 4 of bytes 8-15)
+    const uint32_t sel5 = hi ? rd_sel(3) : rd_sel(0);
+    const uint32_t sel6 = hi ? rd_sel(0) : rd_sel(1);
+    auto bfrag = [&](const Ent &e, int st) -> bf16x8 {
+        gm_u32x4 o;
+        if (st < 5) {
+            const int c = st == 4 ? 1 : 0;
+            const uint32_t sl = rd_sel(st == 4 ? 0 : st);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.g[2 * q + 1][c], e.g[2 * q][c], sl);
+        } else if (st < 7) {
+            const int c = st == 6 ? 1 : 0;
+            const uint32_t sl = st == 5 ? sel5 : sel6;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][c], e.m[2 * q][c], sl);
+        } else {
+            gm_u32x4 lo, f15;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lo[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][0], e.m[2 * q][0], rd_sel(2));
+            f15[0] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x010c000cu);
+            f15[1] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x030c020cu);
+            f15[2] = __builtin_amdgcn_perm(e.t[1][0], e.t[0][1], 0x040c000cu);
+            f15[3] = __builtin_amdgcn_perm(e.t[1][0], e.t[1][0], 0x020c010cu);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = hi ? f15[q] : lo[q];
+        }
+        return __builtin_bit_cast(bf16x8, o);
+    };
+
+    const uint16_t *xw = a.xf + (mt0 * a.nb * 8 * kWave + lane) * 8;
+    const int64_t tm_stride = a.nb * 8 * kWave * 8;
+    auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int st) {
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+            f[m] = *reinterpret_cast<const gm_u32x4 *>(xw + m * tm_stride + (kb * 8 + st) * kWave * 8);
+    };
+
+    f32x16 acc[TM], part[TM];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] = part[m][r] = 0.0f;
+    float sc_prev = 0.0f;
+
+    // ---- prologue: PD blocks of weights, the table entries of block 0 and
+    //      kAr steps of activations in flight
+    WRegs ring[PD];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_w(ring[p], blk(p));
+    gm_u32x4 afr[kAr][TM];
+#pragma unroll
+    for (int st = 0; st < kAr; ++st) load_a(afr[st], blk(0), st);
+    __syncthreads();  // table built
+    Ent ent[2];
+    tab_reads(ring[0], ent[0]);
+    load_w(ring[0], blk(PD));
+
+    // One block: eight MFMA steps on the fragments of ent[cur]; step 1 also
+    // issues the table reads of the next block (into ent[cur ^ 1]) and
+    // refills its weight slot; step 0 first folds the previous block's
+    // partial into acc.
+    auto iteration = [&](int i, Ent &cur, Ent &nxt, WRegs &rslot) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const bf16x8 bv = bfrag(cur, st);
+            gm_u32x4 (&ar)[TM] = afr[st % kAr];
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, ar[m]);
+                if (st == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
+                    const f32x16 z = {};
+                    part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, z, 0, 0, 0);
+                } else {
+                    part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, part[m], 0, 0, 0);
+                }
+            }
+            if (st + kAr < 8)
+                load_a(ar, blk(i), st + kAr);
+            else
+                load_a(ar, blk(i + 1), st + kAr - 8);
+            if (st == 1) {
+                tab_reads(rslot, nxt);
+                load_w(rslot, blk(i + 1 + PD));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        sc_prev = cur.scale;
+    };
+
+    for (int base = 0; base < nblk; base += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int i = base + u;
+            if (i >= nblk) break;
+            iteration(i, ent[u & 1], ent[(u + 1) & 1], ring[(u + 1) % PD]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
+
+    const int64_t col = gcol;
+    if (col >= rows) return;
+#pragma unroll
+    for (int m = 0; m < TM; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+            if (row >= a.m) continue;
+            const float v = acc[m][r];
+            if (a.part != nullptr) {
+                a.part[(static_cast<int64_t>(blockIdx.z) * a.m + row) * rows + col] = v;
+            } else if (col < a.n0) {
+                const int64_t o = row * a.n0 + col;
+                a.y0[o] = a.residual ? a.residual[o] + v : v;
+            } else {
+                a.y1[row * a.n1 + (col - a.n0)] = v;
+            }
+        }
+    }
+}
+
 // Sum of the split-K partials in split order (+ residual), routed to y0 / y1.
 __global__ void __launch_bounds__(kEwThreads) k_gemm_reduce(const float *__restrict__ part, int32_t splits,
                                                              int64_t m, int64_t n0, int64_t n1, float *y0, float *y1,
@@ -544,12 +798,15 @@ constexpr int kMaxSplits = 32;
 
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
 {
-    // workgroup rows per configuration, and the time one workgroup spends
-    // on one block (microseconds, measured order of magnitude)
-    static const int64_t kBm[4] = {32, 64, 128, 128};
-    static const double kTblk[4] = {0.25, 0.35, 0.6, 0.6};
+    // cfg 0 / 1: register-decode kernel, 32 / 64 rows, two workgroups per
+    // CU; cfg 2: LDS-decode kernel, 128 rows with 8 waves, one per CU.
+    // t_blk: time of one workgroup on one block (microseconds, measured
+    // order of magnitude).
+    static const int64_t kBm[3] = {32, 64, 128};
+    static const int64_t kPerCu[3] = {2, 2, 1};
+    static const double kTblk[3] = {0.35, 0.45, 0.6};
     GemmPlan p;
-    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 3);
+    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
     const int64_t bm = kBm[p.cfg];
     p.m_pad = (m + bm - 1) / bm * bm;
     p.nb = k / kBlockWeights;
@@ -558,17 +815,18 @@ GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
     p.splits = 1;
     p.bps = static_cast<int32_t>(p.nb);
     if (m == 0 || rows == 0 || p.nb == 0) return p;
-    // Time model: rounds of one workgroup per CU, each block costing t_blk,
-    // plus a fixed start per round; splits add their fp32 partials
+    // Time model: rounds of workgroups over the CUs, each block costing
+    // t_blk, plus a fixed start per round; splits add their fp32 partials
     // (written and read back) and a launch.
     const double t_blk = kTblk[p.cfg];
+    const int64_t slots = kPlanCus * kPerCu[p.cfg];
     double best = 0.0;
     for (int64_t s = 1; s <= kMaxSplits && s <= p.nb; ++s) {
         const int64_t bps = (p.nb + s - 1) / s;
         const int64_t se = (p.nb + bps - 1) / bps;
         if (se != s) continue;
         const int64_t wgs = p.tiles_n * p.tiles_m * s;
-        const int64_t rounds = (wgs + kPlanCus - 1) / kPlanCus;
+        const int64_t rounds = (wgs + slots - 1) / slots;
         double t = static_cast<double>(rounds) * (static_cast<double>(bps) * t_blk + 1.0);
         if (s > 1) t += 2.0 * static_cast<double>(s * m * rows) * 4.0 / 5.0e6 + 3.0;
         if (s == 1 || t < best) {
@@ -622,6 +880,28 @@ static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
     return hipGetLastError();
 }
 
+template <int TM, int PD>
+static hipError_t gemm_rd_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
+{
+    static bool attr_set = false;
+    const auto kernel = k_gemm_rd<TM, PD>;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kRdLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kRdThreads), static_cast<uint32_t>(kRdLds), s, pe.start, pe.stop, 0u,
+                              args);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, dim3(kRdThreads), kRdLds, s, args);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
                        hipStream_t s)
@@ -646,11 +926,9 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m), static_cast<unsigned>(p.splits));
     hipError_t e;
     if (p.cfg == 0)
-        e = gemm_dispatch<1, 4, 1, 1, 3>(grid, s, a);
+        e = gemm_rd_dispatch<1, 4>(grid, s, a);
     else if (p.cfg == 1)
-        e = gemm_dispatch<2, 2, 1, 2, 3>(grid, s, a);
-    else if (p.cfg == 2)
-        e = gemm_dispatch<2, 2, 2, 2, 3>(grid, s, a);
+        e = gemm_rd_dispatch<2, 4>(grid, s, a);
     else
         e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     if (e != hipSuccess || p.splits == 1) return e;

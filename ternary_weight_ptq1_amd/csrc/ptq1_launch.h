@@ -66,8 +66,8 @@ hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, co
                                   float rms_eps, float *g, float *u, float *h, hipStream_t s);
 
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
-// Shape of one GEMM launch: tile configuration (cfg 0/1/2 = 32/64/128 rows
-// per workgroup with 4 waves, cfg 3 = 128 rows with 8 waves), padded activation rows, grid and K split.
+// Shape of one GEMM launch: tile configuration (cfg 0/1 = 32/64 rows
+// per workgroup, register decode; cfg 2 = 128 rows, LDS decode), padded activation rows, grid and K split.
 struct GemmPlan {
     int cfg = 0;
     int64_t m_pad = 0, tiles_n = 0, tiles_m = 0, nb = 0;
