@@ -209,9 +209,11 @@ struct GemmArgs {
     int64_t n0, n1, bands0, bands1;
     float *y0, *y1;          // outputs [m][n0], [m][n1] (split == 1)
     const float *residual;   // [m][n0] or null (split == 1)
-    float *part;             // [split][m][n0 + n1] partial sums (split > 1), else null
+    float *part;             // [split][m][n0 + n1] partial sums (split > 1), else null; register
+                             // decode: [workgroup][first / last][m][128]
     int64_t m, nb;           // activation rows, K blocks
-    int32_t bps;             // K blocks per split
+    int32_t bps;             // K blocks per split (LDS-decode kernel)
+    int64_t units, wgs;      // tiles x K blocks, and the workgroups sharing them (register-decode kernel)
 };
 
 template <int WM, int WN, int TM, int TN, int PD>
@@ -560,9 +562,12 @@ __device__ __forceinline__ constexpr uint32_t rd_sel(int b)
     return 0x000c000cu | (static_cast<uint32_t>(b) << 8) | (static_cast<uint32_t>(4 + b) << 24);
 }
 
-template <int TM, int PD>
+// LR: 8-row groups of the last row tile that hold activation rows (the
+// others are zero padding and are neither scaled nor stored).
+template <int TM, int PD, int LR>
 __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
 {
+    static_assert(LR >= 1 && LR <= 4, "8-row groups of a 32-row tile");
     constexpr int kAr = 4;  // activation-fragment ring, MFMA steps
     extern __shared__ __attribute__((aligned(16))) char lds[];
     typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
@@ -572,12 +577,7 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     const int wave = tid / kWave;
     const int hi = lane >> 5;
     const int64_t rows = a.n0 + a.n1;
-    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * kGemmBN;
     const int64_t mt0 = static_cast<int64_t>(blockIdx.y) * TM;
-    const int64_t kb0 = static_cast<int64_t>(blockIdx.z) * a.bps;
-    const int nblk = static_cast<int>((a.nb - kb0 < a.bps) ? a.nb - kb0 : a.bps);
-    const int last = nblk - 1;
-    auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };
 
     // ---- table: entry b, copy c at b * 256 + c * 8
     {
@@ -596,174 +596,246 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
             *reinterpret_cast<gm_u32x2 *>(lds + b * 256 + ((b + i) & (kRdTabCopies - 1)) * 8) = e;
     }
 
-    // ---- this lane's column
-    const int64_t gcol = tile_n + wave * 32 + (lane & 31);
-    const uint8_t *wcol = a.w0;
-    int64_t sstride = 0;
-    if (gcol < rows) {
-        const bool first = gcol < a.n0;
-        const int64_t rr = first ? gcol : gcol - a.n0;
-        wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
-        sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
-    }
+    __syncthreads();  // table built
     const uint32_t lc = static_cast<uint32_t>(lane & (kRdTabCopies - 1)) << 3;
 
-    struct WRegs {
-        gm_u32x4 v;  // bytes 8 h .. 8 h + 15
-        uint32_t w;  // bytes 24..27
-    };
-    auto load_w = [&](WRegs &r, int64_t kb) {
-        const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
-        const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 8 * hi);
-        r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
-        r.w = *reinterpret_cast<const uint32_t *>(p + 24);
-    };
-    auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
-        const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
-        return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
-    };
-    struct Ent {
-        gm_u32x2 g[8];  // "first" bytes: 0-7 (lanes 0-31) or 16-23 (lanes 32-63)
-        gm_u32x2 m[8];  // bytes 8-15
-        gm_u32x2 t[2];  // bytes 24, 25
-        float scale;    // the block's scale, halved (trits are stored as +-2)
-    };
-    auto tab_reads = [&](const WRegs &r, Ent &e) {
-        const uint32_t g0 = hi ? r.v[2] : r.v[0], g1 = hi ? r.v[3] : r.v[1];
-        const uint32_t m0 = hi ? r.v[0] : r.v[2], m1 = hi ? r.v[1] : r.v[3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            e.g[i] = tab_read(g0, i);
-            e.g[4 + i] = tab_read(g1, i);
-            e.m[i] = tab_read(m0, i);
-            e.m[4 + i] = tab_read(m1, i);
-        }
-        e.t[0] = tab_read(r.w, 0);
-        e.t[1] = tab_read(r.w, 1);
-        e.scale = 0.5f * half_bits_to_float(r.w >> 16);
-    };
-    // per-lane selectors of steps 5 and 6 (digit 0 / 3 and 1 / 4 of bytes 8-15)
-    const uint32_t sel5 = hi ? rd_sel(3) : rd_sel(0);
-    const uint32_t sel6 = hi ? rd_sel(0) : rd_sel(1);
-    auto bfrag = [&](const Ent &e, int st) -> bf16x8 {
-        gm_u32x4 o;
-        if (st < 5) {
-            const int c = st == 4 ? 1 : 0;
-            const uint32_t sl = rd_sel(st == 4 ? 0 : st);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.g[2 * q + 1][c], e.g[2 * q][c], sl);
-        } else if (st < 7) {
-            const int c = st == 6 ? 1 : 0;
-            const uint32_t sl = st == 5 ? sel5 : sel6;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][c], e.m[2 * q][c], sl);
-        } else {
-            gm_u32x4 lo, f15;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) lo[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][0], e.m[2 * q][0], rd_sel(2));
-            f15[0] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x010c000cu);
-            f15[1] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x030c020cu);
-            f15[2] = __builtin_amdgcn_perm(e.t[1][0], e.t[0][1], 0x040c000cu);
-            f15[3] = __builtin_amdgcn_perm(e.t[1][0], e.t[1][0], 0x020c010cu);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = hi ? f15[q] : lo[q];
-        }
-        return __builtin_bit_cast(bf16x8, o);
-    };
+    // ---- stream-K: workgroup w takes units [w U / G, (w + 1) U / G) of the
+    // U = tiles x blocks (tile-major) and runs them as one segment per tile
+    // it touches.
+    const int64_t G = gridDim.x, wg = blockIdx.x;
+    const int64_t u_lo = wg * a.units / G, u_hi = (wg + 1) * a.units / G;
+    for (int64_t useg = u_lo; useg < u_hi;) {
+        const int64_t tile = useg / a.nb;
+        const int64_t kb0 = useg - tile * a.nb;
+        const int64_t uend = (tile + 1) * a.nb < u_hi ? (tile + 1) * a.nb : u_hi;
+        const int nblk = static_cast<int>(uend - useg);
+        const int last = nblk - 1;
+        auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };
+        const int64_t tile_n = tile * kGemmBN;
 
-    const uint16_t *xw = a.xf + (mt0 * a.nb * 8 * kWave + lane) * 8;
-    const int64_t tm_stride = a.nb * 8 * kWave * 8;
-    auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int st) {
+        // ---- this lane's column
+        const int64_t gcol = tile_n + wave * 32 + (lane & 31);
+        const uint8_t *wcol = a.w0;
+        int64_t sstride = 0;
+        if (gcol < rows) {
+            const bool first = gcol < a.n0;
+            const int64_t rr = first ? gcol : gcol - a.n0;
+            wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+            sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+        }
+
+        struct WRegs {
+            gm_u32x4 v;  // bytes 8 h .. 8 h + 15
+            uint32_t w;  // bytes 24..27
+        };
+        auto load_w = [&](WRegs &r, int64_t kb) {
+            const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+            const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 8 * hi);
+            r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
+            r.w = *reinterpret_cast<const uint32_t *>(p + 24);
+        };
+        auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
+            const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
+            return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
+        };
+        struct Ent {
+            gm_u32x2 g[8];  // "first" bytes: 0-7 (lanes 0-31) or 16-23 (lanes 32-63)
+            gm_u32x2 m[8];  // bytes 8-15
+            gm_u32x2 t[2];  // bytes 24, 25
+            float scale;    // the block's scale, halved (trits are stored as +-2)
+        };
+        auto tab_reads = [&](const WRegs &r, Ent &e) {
+            const uint32_t g0 = hi ? r.v[2] : r.v[0], g1 = hi ? r.v[3] : r.v[1];
+            const uint32_t m0 = hi ? r.v[0] : r.v[2], m1 = hi ? r.v[1] : r.v[3];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e.g[i] = tab_read(g0, i);
+                e.g[4 + i] = tab_read(g1, i);
+                e.m[i] = tab_read(m0, i);
+                e.m[4 + i] = tab_read(m1, i);
+            }
+            e.t[0] = tab_read(r.w, 0);
+            e.t[1] = tab_read(r.w, 1);
+            e.scale = 0.5f * half_bits_to_float(r.w >> 16);
+        };
+        // per-lane selectors of steps 5 and 6 (digit 0 / 3 and 1 / 4 of bytes 8-15)
+        const uint32_t sel5 = hi ? rd_sel(3) : rd_sel(0);
+        const uint32_t sel6 = hi ? rd_sel(0) : rd_sel(1);
+        auto bfrag = [&](const Ent &e, int st) -> bf16x8 {
+            gm_u32x4 o;
+            if (st < 5) {
+                const int c = st == 4 ? 1 : 0;
+                const uint32_t sl = rd_sel(st == 4 ? 0 : st);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.g[2 * q + 1][c], e.g[2 * q][c], sl);
+            } else if (st < 7) {
+                const int c = st == 6 ? 1 : 0;
+                const uint32_t sl = st == 5 ? sel5 : sel6;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][c], e.m[2 * q][c], sl);
+            } else {
+                gm_u32x4 lo, f15;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) lo[q] = __builtin_amdgcn_perm(e.m[2 * q + 1][0], e.m[2 * q][0], rd_sel(2));
+                f15[0] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x010c000cu);
+                f15[1] = __builtin_amdgcn_perm(e.t[0][0], e.t[0][0], 0x030c020cu);
+                f15[2] = __builtin_amdgcn_perm(e.t[1][0], e.t[0][1], 0x040c000cu);
+                f15[3] = __builtin_amdgcn_perm(e.t[1][0], e.t[1][0], 0x020c010cu);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = hi ? f15[q] : lo[q];
+            }
+            return __builtin_bit_cast(bf16x8, o);
+        };
+
+        // A lane whose row is padding (row >= m) reads the fragment of row 0
+        // of its tile instead: its MFMA output row is never stored, and the
+        // read shares the live lanes' cache lines (no traffic for padding).
+        const uint16_t *xw[TM];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const bool live_row = (mt0 + m) * 32 + (lane & 31) < a.m;
+            xw[m] = a.xf + (((mt0 + m) * a.nb * 8 * kWave) + (live_row ? lane : (lane & 32))) * 8;
+        }
+        auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int st) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+                f[m] = *reinterpret_cast<const gm_u32x4 *>(xw[m] + (kb * 8 + st) * kWave * 8);
+        };
+
+        f32x16 acc[TM], part[TM];
 #pragma unroll
         for (int m = 0; m < TM; ++m)
-            f[m] = *reinterpret_cast<const gm_u32x4 *>(xw + m * tm_stride + (kb * 8 + st) * kWave * 8);
-    };
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][r] = part[m][r] = 0.0f;
+        float sc_prev = 0.0f;
 
-    f32x16 acc[TM], part[TM];
+        // ---- prologue: PD blocks of weights, the table entries of block 0 and
+        //      kAr steps of activations in flight
+        WRegs ring[PD];
 #pragma unroll
-    for (int m = 0; m < TM; ++m)
+        for (int p = 0; p < PD; ++p) load_w(ring[p], blk(p));
+        gm_u32x4 afr[kAr][TM];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][r] = part[m][r] = 0.0f;
-    float sc_prev = 0.0f;
+        for (int st = 0; st < kAr; ++st) load_a(afr[st], blk(0), st);
+        Ent ent[2];
+        tab_reads(ring[0], ent[0]);
+        load_w(ring[0], blk(PD));
 
-    // ---- prologue: PD blocks of weights, the table entries of block 0 and
-    //      kAr steps of activations in flight
-    WRegs ring[PD];
+        // One block: eight MFMA steps on the fragments of ent[cur]; step 1 also
+        // issues the table reads of the next block (into ent[cur ^ 1]) and
+        // refills its weight slot; step 0 first folds the previous block's
+        // partial into acc.
+        auto iteration = [&](int i, Ent &cur, Ent &nxt, WRegs &rslot) {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) load_w(ring[p], blk(p));
-    gm_u32x4 afr[kAr][TM];
+            for (int st = 0; st < 8; ++st) {
+                const bf16x8 bv = bfrag(cur, st);
+                gm_u32x4 (&ar)[TM] = afr[st % kAr];
 #pragma unroll
-    for (int st = 0; st < kAr; ++st) load_a(afr[st], blk(0), st);
-    __syncthreads();  // table built
-    Ent ent[2];
-    tab_reads(ring[0], ent[0]);
-    load_w(ring[0], blk(PD));
+                for (int m = 0; m < TM; ++m) {
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, ar[m]);
+                    if (st == 0) {
+#pragma unroll
+                        for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r)
+                            acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
+                        const f32x16 z = {};
+                        part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, z, 0, 0, 0);
+                    } else {
+                        part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, part[m], 0, 0, 0);
+                    }
+                }
+                if (st + kAr < 8)
+                    load_a(ar, blk(i), st + kAr);
+                else
+                    load_a(ar, blk(i + 1), st + kAr - 8);
+                if (st == 1) {
+                    tab_reads(rslot, nxt);
+                    load_w(rslot, blk(i + 1 + PD));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sc_prev = cur.scale;
+        };
 
-    // One block: eight MFMA steps on the fragments of ent[cur]; step 1 also
-    // issues the table reads of the next block (into ent[cur ^ 1]) and
-    // refills its weight slot; step 0 first folds the previous block's
-    // partial into acc.
-    auto iteration = [&](int i, Ent &cur, Ent &nxt, WRegs &rslot) {
+        for (int base = 0; base < nblk; base += PD) {
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const bf16x8 bv = bfrag(cur, st);
-            gm_u32x4 (&ar)[TM] = afr[st % kAr];
+            for (int u = 0; u < PD; ++u) {
+                const int i = base + u;
+                if (i >= nblk) break;
+                iteration(i, ent[u & 1], ent[(u + 1) & 1], ring[(u + 1) % PD]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
+
+        // a segment over all blocks of its tile is final; any other is stored
+        // as this workgroup's first (0) or last (1) partial for k_gemm_rd_fix
+        const bool full = kb0 == 0 && nblk == a.nb;
+        float *pp = a.part + (wg * 2 + (useg == u_lo ? 0 : 1)) * a.m * kGemmBN;
+        const int64_t col = gcol;
+        // the row offsets below are the same in every segment; an opaque lane
+        // index keeps the compiler from hoisting them (16 rows x 64-bit
+        // offsets) out of the segment loop into live registers
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        if (col < rows) {
 #pragma unroll
             for (int m = 0; m < TM; ++m) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, ar[m]);
-                if (st == 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
-                    const f32x16 z = {};
-                    part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, z, 0, 0, 0);
-                } else {
-                    part[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, part[m], 0, 0, 0);
+                for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r) {
+                    const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane_e / 32) + (r % 4);
+                    if (row >= a.m) continue;
+                    const float v = acc[m][r];
+                    if (!full) {
+                        pp[row * kGemmBN + (col - tile_n)] = v;
+                    } else if (col < a.n0) {
+                        const int64_t o = row * a.n0 + col;
+                        a.y0[o] = a.residual ? a.residual[o] + v : v;
+                    } else {
+                        a.y1[row * a.n1 + (col - a.n0)] = v;
+                    }
                 }
             }
-            if (st + kAr < 8)
-                load_a(ar, blk(i), st + kAr);
-            else
-                load_a(ar, blk(i + 1), st + kAr - 8);
-            if (st == 1) {
-                tab_reads(rslot, nxt);
-                load_w(rslot, blk(i + 1 + PD));
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        sc_prev = cur.scale;
-    };
+        useg = uend;
+    }  // segments
+}
 
-    for (int base = 0; base < nblk; base += PD) {
-#pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int i = base + u;
-            if (i >= nblk) break;
-            iteration(i, ent[u & 1], ent[(u + 1) & 1], ring[(u + 1) % PD]);
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
+// Workgroup of the stream-K range holding unit u: the largest w with
+// floor(w U / G) <= u.
+__device__ __forceinline__ int64_t rd_owner(int64_t u, int64_t units, int64_t G)
+{
+    int64_t w = u * G / units;
+    while (w + 1 < G && (w + 1) * units / G <= u) ++w;
+    return w;
+}
 
-    const int64_t col = gcol;
-    if (col >= rows) return;
-#pragma unroll
-    for (int m = 0; m < TM; ++m) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-            if (row >= a.m) continue;
-            const float v = acc[m][r];
-            if (a.part != nullptr) {
-                a.part[(static_cast<int64_t>(blockIdx.z) * a.m + row) * rows + col] = v;
-            } else if (col < a.n0) {
-                const int64_t o = row * a.n0 + col;
-                a.y0[o] = a.residual ? a.residual[o] + v : v;
-            } else {
-                a.y1[row * a.n1 + (col - a.n0)] = v;
-            }
-        }
+// Tiles that more than one workgroup touched: the sum of their partials in
+// workgroup order (+ residual), routed to y0 / y1.  Grid: tiles x ceil(m 128
+// / 256), one output per thread.
+__global__ void __launch_bounds__(kEwThreads) k_gemm_rd_fix(GemmArgs a)
+{
+    const int64_t G = a.wgs, t = blockIdx.x;
+    const int64_t rows = a.n0 + a.n1;
+    const int64_t first_u = t * a.nb;
+    const int64_t w_lo = rd_owner(first_u, a.units, G), w_hi = rd_owner(first_u + a.nb - 1, a.units, G);
+    if (w_lo == w_hi) return;  // stored final by its one workgroup
+    const int64_t e = static_cast<int64_t>(blockIdx.y) * kEwThreads + threadIdx.x;
+    const int64_t row = e / kGemmBN, c = e - row * kGemmBN;
+    const int64_t col = t * kGemmBN + c;
+    if (row >= a.m || col >= rows) return;
+    // w_lo's segment of this tile is its first unless its range began in an
+    // earlier tile; every later workgroup's range begins inside this tile
+    const int64_t k_lo = (w_lo * a.units / G < first_u) ? 1 : 0;
+    float v = a.part[((w_lo * 2 + k_lo) * a.m + row) * kGemmBN + c];
+#pragma unroll 4
+    for (int64_t w = w_lo + 1; w <= w_hi; ++w) v += a.part[(w * 2 * a.m + row) * kGemmBN + c];
+    if (col < a.n0) {
+        const int64_t o = row * a.n0 + col;
+        a.y0[o] = a.residual ? a.residual[o] + v : v;
+    } else {
+        a.y1[row * a.n1 + (col - a.n0)] = v;
     }
 }
 
@@ -792,19 +864,19 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_reduce(const float *__restr
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kPlanCus = 256;      // compute units the split heuristic plans for
+constexpr int kPlanCus = 256;      // compute units the grid and split heuristics plan for
 constexpr int kMaxSplits = 32;
+constexpr int kRdWgsPerCu = 2;     // register-decode workgroups resident per CU
+constexpr int kRdMinBlocks = 4;    // fewest units a register-decode workgroup takes
 }  // namespace
 
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
 {
     // cfg 0 / 1: register-decode kernel, 32 / 64 rows, two workgroups per
-    // CU; cfg 2: LDS-decode kernel, 128 rows with 8 waves, one per CU.
-    // t_blk: time of one workgroup on one block (microseconds, measured
-    // order of magnitude).
+    // CU sharing the tiles x blocks units evenly (stream-K); cfg 2:
+    // LDS-decode kernel, 128 rows with 8 waves, one per CU, K split chosen
+    // from a time model.
     static const int64_t kBm[3] = {32, 64, 128};
-    static const int64_t kPerCu[3] = {2, 2, 1};
-    static const double kTblk[3] = {0.35, 0.45, 0.6};
     GemmPlan p;
     p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
     const int64_t bm = kBm[p.cfg];
@@ -815,11 +887,19 @@ GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
     p.splits = 1;
     p.bps = static_cast<int32_t>(p.nb);
     if (m == 0 || rows == 0 || p.nb == 0) return p;
+    if (p.cfg < 2) {
+        const int64_t units = p.tiles_n * p.nb;
+        int64_t g = kRdWgsPerCu * kPlanCus;
+        if (g > units / kRdMinBlocks) g = units / kRdMinBlocks;
+        p.wgs = g < 1 ? 1 : g;
+        return p;
+    }
     // Time model: rounds of workgroups over the CUs, each block costing
-    // t_blk, plus a fixed start per round; splits add their fp32 partials
-    // (written and read back) and a launch.
-    const double t_blk = kTblk[p.cfg];
-    const int64_t slots = kPlanCus * kPerCu[p.cfg];
+    // t_blk (microseconds, measured order of magnitude), plus a fixed start
+    // per round; splits add their fp32 partials (written and read back) and
+    // a launch.
+    const double t_blk = 0.6;
+    const int64_t slots = kPlanCus;
     double best = 0.0;
     for (int64_t s = 1; s <= kMaxSplits && s <= p.nb; ++s) {
         const int64_t bps = (p.nb + s - 1) / s;
@@ -842,6 +922,7 @@ size_t gemm_frag_elems(const GemmPlan &p, int64_t k) { return static_cast<size_t
 
 size_t gemm_part_floats(const GemmPlan &p, int64_t m, int64_t rows)
 {
+    if (p.cfg < 2) return static_cast<size_t>(2 * p.wgs) * static_cast<size_t>(m) * kGemmBN;
     return p.splits > 1 ? static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(rows) : 0;
 }
 
@@ -880,11 +961,11 @@ static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
     return hipGetLastError();
 }
 
-template <int TM, int PD>
+template <int TM, int PD, int LR>
 static hipError_t gemm_rd_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 {
     static bool attr_set = false;
-    const auto kernel = k_gemm_rd<TM, PD>;
+    const auto kernel = k_gemm_rd<TM, PD, LR>;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kRdLds);
@@ -923,14 +1004,29 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     a.m = m;
     a.nb = p.nb;
     a.bps = p.bps;
-    const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m), static_cast<unsigned>(p.splits));
+    a.units = p.tiles_n * p.nb;
+    a.wgs = p.wgs;
     hipError_t e;
-    if (p.cfg == 0)
-        e = gemm_rd_dispatch<1, 4>(grid, s, a);
-    else if (p.cfg == 1)
-        e = gemm_rd_dispatch<2, 4>(grid, s, a);
-    else
-        e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
+    if (p.cfg < 2) {
+        a.part = part;
+        const dim3 grid(static_cast<unsigned>(p.wgs), static_cast<unsigned>(p.tiles_m), 1);
+        const int64_t live = m - (p.tiles_m - 1) * (p.cfg == 0 ? 32 : 64);  // rows of the last row tile
+        if (p.cfg == 1)
+            e = gemm_rd_dispatch<2, 4, 4>(grid, s, a);
+        else if (live <= 8)
+            e = gemm_rd_dispatch<1, 4, 1>(grid, s, a);
+        else if (live <= 16)
+            e = gemm_rd_dispatch<1, 4, 2>(grid, s, a);
+        else
+            e = gemm_rd_dispatch<1, 4, 4>(grid, s, a);
+        if (e != hipSuccess) return e;
+        const unsigned ey = static_cast<unsigned>((m * kGemmBN + kEwThreads - 1) / kEwThreads);
+        hipLaunchKernelGGL(k_gemm_rd_fix, dim3(static_cast<unsigned>(p.tiles_n), ey), dim3(kEwThreads), 0, s, a);
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m),
+                    static_cast<unsigned>(p.splits));
+    e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t total = m * rows;
     int64_t blocks = (total + kEwThreads - 1) / kEwThreads;

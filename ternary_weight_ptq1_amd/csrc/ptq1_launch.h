@@ -67,11 +67,14 @@ hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, co
 
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
 // Shape of one GEMM launch: tile configuration (cfg 0/1 = 32/64 rows
-// per workgroup, register decode; cfg 2 = 128 rows, LDS decode), padded activation rows, grid and K split.
+// per workgroup, register decode, `wgs` workgroups sharing the tiles x
+// blocks evenly; cfg 2 = 128 rows, LDS decode, a grid of tiles x K
+// splits), padded activation rows.
 struct GemmPlan {
     int cfg = 0;
     int64_t m_pad = 0, tiles_n = 0, tiles_m = 0, nb = 0;
-    int32_t splits = 1, bps = 0;  // K split count and blocks per split
+    int32_t splits = 1, bps = 0;  // K split count and blocks per split (cfg 2)
+    int64_t wgs = 0;              // workgroups (cfg 0 / 1)
 };
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k);
 size_t gemm_frag_elems(const GemmPlan &p, int64_t k);                // bf16 A fragments
