@@ -181,12 +181,12 @@ struct GemmWs {
     size_t frag = 0, part = 0, total = 0;  // byte offsets
 };
 
-GemmWs gemm_layout(const ptq1::GemmPlan &p, int64_t m, int64_t rows, int64_t k)
+GemmWs gemm_layout(const ptq1::GemmPlan &p, int64_t k)
 {
     GemmWs L;
     L.frag = 0;
     L.part = round_up(ptq1::gemm_frag_elems(p, k) * 2, kWsAlign);
-    L.total = L.part + round_up(ptq1::gemm_part_floats(p, m, rows) * sizeof(float), kWsAlign);
+    L.total = L.part + round_up(ptq1::gemm_part_floats(p) * sizeof(float), kWsAlign);
     return L;
 }
 
@@ -208,7 +208,7 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
         L.gu = ptq1::gemm_plan(m, 2 * f, d);
         L.dn = ptq1::gemm_plan(m, d, f);
         const size_t fa = ptq1::gemm_frag_elems(L.gu, d), fb = ptq1::gemm_frag_elems(L.dn, f);
-        const size_t pa = ptq1::gemm_part_floats(L.gu, m, 2 * f), pb = ptq1::gemm_part_floats(L.dn, m, d);
+        const size_t pa = ptq1::gemm_part_floats(L.gu), pb = ptq1::gemm_part_floats(L.dn);
         L.xb = off; off += round_up((fa > fb ? fa : fb) * 2, kWsAlign);
         L.g = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
         L.u = off; off += round_up(static_cast<size_t>(m) * f * 4, kWsAlign);
@@ -537,7 +537,7 @@ size_t ptq1_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
     if (m == 0) return 0;
-    return gemm_layout(ptq1::gemm_plan(m, n, k), m, n, k).total;
+    return gemm_layout(ptq1::gemm_plan(m, n, k), k).total;
 }
 
 ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m,
@@ -553,7 +553,7 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
     PTQ1_TRY(check_floats(x, "x", mk, &xb));
     PTQ1_TRY(check_signs(signs1024, false));
     const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k);
-    const GemmWs L = gemm_layout(plan, m, n, k);
+    const GemmWs L = gemm_layout(plan, k);
     const size_t need = L.total;
     PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm"));
     if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");

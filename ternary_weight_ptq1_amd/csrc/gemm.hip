@@ -165,8 +165,11 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 //      acc += partial * scale[column] in fp32.
 // Trits are stored as bf16 -2 / 0 / +2 (low byte always zero, so a table
 // entry is just the five high bytes) and the scale is halved to match.
-// A split-K grid (blockIdx.z) writes fp32 partial sums instead; a second
-// kernel adds them in a fixed order.
+// Work split (stream-K): the grid is one workgroup per CU, and workgroup w
+// takes an equal run of the (tile, K block) units in tile order, as one
+// segment per tile it touches.  A segment covering all blocks of its tile
+// stores the result; any other stores an fp32 partial, and k_gemm_fix adds
+// the partials of each shared tile in workgroup order.
 // Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
 // and B[8(l/32)+j][l%32], j = 0..7; result register r of lane l is
 // D[8(r/4) + 4(l/32) + r%4][l%32].
@@ -207,13 +210,16 @@ struct GemmArgs {
     const uint8_t *w0;       // tiled matrix 0 (rows [0, n0) of the virtual matrix)
     const uint8_t *w1;       // tiled matrix 1 (rows [n0, n0 + n1)), may be null
     int64_t n0, n1, bands0, bands1;
-    float *y0, *y1;          // outputs [m][n0], [m][n1] (split == 1)
-    const float *residual;   // [m][n0] or null (split == 1)
-    float *part;             // [split][m][n0 + n1] partial sums (split > 1), else null; register
-                             // decode: [workgroup][first / last][m][128]
+    float *y0, *y1;          // outputs [m][n0], [m][n1]
+    const float *residual;   // [m][n0] or null
+    float *part;             // partial tiles [workgroup][first / last][prow][128]
     int64_t m, nb;           // activation rows, K blocks
-    int32_t bps;             // K blocks per split (LDS-decode kernel)
-    int64_t units, wgs;      // tiles x K blocks, and the workgroups sharing them (register-decode kernel)
+    int64_t tiles_m, prow;   // row tiles; rows of a row tile (= m with one row tile)
+    int64_t wgs;             // workgroups
+    int64_t dp_rounds;       // rounds of whole tiles per workgroup (tiles [0, dp_tiles))
+    int64_t dp_tiles;        // dp_rounds x wgs
+    int64_t sk_units;        // (tiles - dp_tiles) x K blocks, shared evenly by
+    int64_t sk_wgs;          // workgroups [0, sk_wgs), sk_wgs = min(wgs, sk_units)
 };
 
 template <int WM, int WN, int TM, int TN, int PD>
@@ -234,13 +240,6 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
     const int wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
     const int64_t rows = a.n0 + a.n1;
-    const int64_t tile_n = static_cast<int64_t>(blockIdx.x) * kGemmBN;
-    const int64_t mt0 = (static_cast<int64_t>(blockIdx.y) * WM + wm) * TM;  // this wave's first 32-row group
-    const bool active = mt0 * 32 < a.m;
-    const int64_t kb0 = static_cast<int64_t>(blockIdx.z) * a.bps;
-    const int nblk = static_cast<int>((a.nb - kb0 < a.bps) ? a.nb - kb0 : a.bps);
-    const int last = nblk - 1;
-    auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };  // clamped block index
 
     // ---- byte -> trit table: entry b, copy c at b * 256 + c * 8
     {
@@ -260,280 +259,326 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
             *reinterpret_cast<gm_u32x2 *>(tab + b * 256 + ((b + c0 + i) & (kTabCopies - 1)) * 8) = e;
     }
 
-    // ---- this thread's share of the decode: column dn and a byte range of
-    //      its block.  256 threads: bytes [0,12) (role 0) or [12,28) (role 1);
-    //      512 threads: bytes [0,8), [8,16), [16,24) (roles 0-2, five whole
-    //      fragments each) or [20,28) (role 3: fragment 15 and the scale).
-    const int dn = tid & (kGemmBN - 1);
-    const int role = tid >> 7;
-    const int64_t gcol = tile_n + dn;
-    const uint8_t *wcol = a.w0;
-    int64_t sstride = 0;
-    if (gcol < rows) {
-        const bool first = gcol < a.n0;
-        const int64_t rr = first ? gcol : gcol - a.n0;
-        wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
-        sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
-    }
-    wcol += kNT == 256 ? role * 12 : (role < 3 ? 8 * role : 20);
-    const uint32_t lc = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+    // ---- work split: whole tiles wg, wg + G, ... for the first dp_rounds
+    // rounds, then units [w U / G, (w + 1) U / G) of the U = (remaining
+    // tiles) x blocks, one segment per tile touched (tile t = column tile
+    // t / tiles_m, row tile t % tiles_m).
+    const int64_t G = gridDim.x, wg = blockIdx.x;
+    const int64_t Gs = a.sk_wgs;  // workgroups [0, Gs) share the stream-K units
+    const int64_t sk_lo = wg < Gs ? wg * a.sk_units / Gs : 0, sk_hi = wg < Gs ? (wg + 1) * a.sk_units / Gs : 0;
+    int64_t jdp = 0, useg = sk_lo;
+    while (jdp < a.dp_rounds || useg < sk_hi) {
+        int64_t tile, kb0;
+        int nblk, kslot = 0;
+        bool full;
+        if (jdp < a.dp_rounds) {  // whole tile wg + jdp G
+            tile = wg + jdp * G;
+            kb0 = 0;
+            nblk = static_cast<int>(a.nb);
+            full = true;
+            ++jdp;
+        } else {  // units [useg, uend) of stream-K tile t2
+            const int64_t t2 = useg / a.nb;
+            kb0 = useg - t2 * a.nb;
+            const int64_t uend = (t2 + 1) * a.nb < sk_hi ? (t2 + 1) * a.nb : sk_hi;
+            nblk = static_cast<int>(uend - useg);
+            tile = a.dp_tiles + t2;
+            full = kb0 == 0 && nblk == a.nb;
+            kslot = useg == sk_lo ? 0 : 1;
+            useg = uend;
+        }
+        const int last = nblk - 1;
+        auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };  // clamped block index
+        const int64_t tn = tile / a.tiles_m, tm = tile - tn * a.tiles_m;
+        const int64_t tile_n = tn * kGemmBN;
+        const int64_t mt0 = (tm * WM + wm) * TM;  // this wave's first 32-row group
+        const bool active = mt0 * 32 < a.m;
 
-    // Loads are unconditional (callers clamp the block) so that the
-    // compiler's in-order load counting never has to merge two paths.
-    auto load_w = [&](gm_u32x4 &r, int64_t kb) {  // 256 threads: role 0 uses 3 of the 4 dwords
-        const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
-        if constexpr (kNT == 256) {
-            r = *reinterpret_cast<const gm_u32x4a *>(p);
-        } else {
-            const gm_u32x2a v = *reinterpret_cast<const gm_u32x2a *>(p);
-            r = gm_u32x4{v[0], v[1], 0u, 0u};
+        // ---- this thread's share of the decode: column dn and a byte range of
+        //      its block.  256 threads: bytes [0,12) (role 0) or [12,28) (role 1);
+        //      512 threads: bytes [0,8), [8,16), [16,24) (roles 0-2, five whole
+        //      fragments each) or [20,28) (role 3: fragment 15 and the scale).
+        const int dn = tid & (kGemmBN - 1);
+        const int role = tid >> 7;
+        const int64_t gcol = tile_n + dn;
+        const uint8_t *wcol = a.w0;
+        int64_t sstride = 0;
+        if (gcol < rows) {
+            const bool first = gcol < a.n0;
+            const int64_t rr = first ? gcol : gcol - a.n0;
+            wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+            sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
         }
-    };
-    // The table sits at LDS address 0 (the kernel has no static LDS), so the
-    // v_perm result is the complete LDS address.
-    typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
-    auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
-        const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
-        return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
-    };
-    // 256 threads, both roles in one branch-free sequence over their bytes:
-    //   an 8-byte group  -> 5 whole fragments (role 0: bytes 0-7 -> fragments
-    //                       0-4; role 1: bytes 16-23 -> fragments 10-14),
-    //   a 4-byte half    -> half of fragments 5-9 (role 0: bytes 8-11, low
-    //                       8 bytes; role 1: bytes 12-15, high 8 bytes),
-    //   fragment 15 and the scale from bytes 24-27 (role 1 only).
-    const int grp_frag = role ? 10 : 0;
-    const int half_off = role ? 8 : 0;
-    struct TabRegs {
-        gm_u32x2 tg[8], th[4], tt[2];
-        uint32_t tw;
-    };
-    auto decode_read = [&](const gm_u32x4 &r, TabRegs &q, int part_no) {
-        if constexpr (kNT == 512) {
-            if (part_no == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(r[0], i);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(r[1], i);
-                q.tw = r[1];
+        wcol += kNT == 256 ? role * 12 : (role < 3 ? 8 * role : 20);
+        const uint32_t lc = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+
+        // Loads are unconditional (callers clamp the block) so that the
+        // compiler's in-order load counting never has to merge two paths.
+        auto load_w = [&](gm_u32x4 &r, int64_t kb) {  // 256 threads: role 0 uses 3 of the 4 dwords
+            const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+            if constexpr (kNT == 256) {
+                r = *reinterpret_cast<const gm_u32x4a *>(p);
+            } else {
+                const gm_u32x2a v = *reinterpret_cast<const gm_u32x2a *>(p);
+                r = gm_u32x4{v[0], v[1], 0u, 0u};
             }
-        } else if (part_no == 0) {
-            const uint32_t g0 = role ? r[1] : r[0], g1 = role ? r[2] : r[1];
+        };
+        // The table sits at LDS address 0 (the kernel has no static LDS), so the
+        // v_perm result is the complete LDS address.
+        typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
+        auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
+            const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
+            return *reinterpret_cast<lds_u32x2 *>(static_cast<uintptr_t>(addr));
+        };
+        // 256 threads, both roles in one branch-free sequence over their bytes:
+        //   an 8-byte group  -> 5 whole fragments (role 0: bytes 0-7 -> fragments
+        //                       0-4; role 1: bytes 16-23 -> fragments 10-14),
+        //   a 4-byte half    -> half of fragments 5-9 (role 0: bytes 8-11, low
+        //                       8 bytes; role 1: bytes 12-15, high 8 bytes),
+        //   fragment 15 and the scale from bytes 24-27 (role 1 only).
+        const int grp_frag = role ? 10 : 0;
+        const int half_off = role ? 8 : 0;
+        struct TabRegs {
+            gm_u32x2 tg[8], th[4], tt[2];
+            uint32_t tw;
+        };
+        auto decode_read = [&](const gm_u32x4 &r, TabRegs &q, int part_no) {
+            if constexpr (kNT == 512) {
+                if (part_no == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(g0, i);
+                    for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(r[0], i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(g1, i);
-        } else {
-            const uint32_t hw = role ? r[0] : r[2];
-            q.tw = r[3];
+                    for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(r[1], i);
+                    q.tw = r[1];
+                }
+            } else if (part_no == 0) {
+                const uint32_t g0 = role ? r[1] : r[0], g1 = role ? r[2] : r[1];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q.th[i] = tab_read(hw, i);
-            q.tt[0] = tab_read(q.tw, 0);
-            q.tt[1] = tab_read(q.tw, 1);
-        }
-    };
-    // fragment fifteen from the table entries of bytes 24 and 25
-    auto frag15 = [&](gm_u32x2 t24, gm_u32x2 t25) -> gm_u32x4 {
-        return gm_u32x4{__builtin_amdgcn_perm(t24[0], t24[0], 0x010c000cu),
-                        __builtin_amdgcn_perm(t24[0], t24[0], 0x030c020cu),
-                        __builtin_amdgcn_perm(t25[0], t24[1], 0x040c000cu),
-                        __builtin_amdgcn_perm(t25[0], t25[0], 0x020c010cu)};
-    };
-    auto put_scale = [&](int buf, uint32_t tw) {
-        *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(gemm_scale_addr(buf, dn))) =
-            0.5f * half_bits_to_float(tw >> 16);
-    };
-    // fragment group d (0..4) of the decoded block, or (d == 5) fragment 15
-    // and the scale
-    auto decode_write = [&](const TabRegs &q, int buf, int d) {
-        char *bw = bsm + buf * kBufBytes;
-        if constexpr (kNT == 512) {
-            if (d >= 5) return;
-            if (role < 3) {  // wave-uniform
+                for (int i = 0; i < 4; ++i) q.tg[i] = tab_read(g0, i);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q.tg[4 + i] = tab_read(g1, i);
+            } else {
+                const uint32_t hw = role ? r[0] : r[2];
+                q.tw = r[3];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q.th[i] = tab_read(hw, i);
+                q.tt[0] = tab_read(q.tw, 0);
+                q.tt[1] = tab_read(q.tw, 1);
+            }
+        };
+        // fragment fifteen from the table entries of bytes 24 and 25
+        auto frag15 = [&](gm_u32x2 t24, gm_u32x2 t25) -> gm_u32x4 {
+            return gm_u32x4{__builtin_amdgcn_perm(t24[0], t24[0], 0x010c000cu),
+                            __builtin_amdgcn_perm(t24[0], t24[0], 0x030c020cu),
+                            __builtin_amdgcn_perm(t25[0], t24[1], 0x040c000cu),
+                            __builtin_amdgcn_perm(t25[0], t25[0], 0x020c010cu)};
+        };
+        auto put_scale = [&](int buf, uint32_t tw) {
+            *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(gemm_scale_addr(buf, dn))) =
+                0.5f * half_bits_to_float(tw >> 16);
+        };
+        // fragment group d (0..4) of the decoded block, or (d == 5) fragment 15
+        // and the scale
+        auto decode_write = [&](const TabRegs &q, int buf, int d) {
+            char *bw = bsm + buf * kBufBytes;
+            if constexpr (kNT == 512) {
+                if (d >= 5) return;
+                if (role < 3) {  // wave-uniform
+                    const int c = d >> 2;
+                    const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
+                                        __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
+                                        __builtin_amdgcn_perm(q.tg[5][c], q.tg[4][c], dsel(d)),
+                                        __builtin_amdgcn_perm(q.tg[7][c], q.tg[6][c], dsel(d))};
+                    *reinterpret_cast<gm_u32x4 *>(bw + ((5 * role + d) * kGemmBN + dn) * 16) = o;
+                } else if (d == 0) {  // bytes 20..27: 24 and 25 are entries 4 and 5
+                    *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tg[4], q.tg[5]);
+                    put_scale(buf, q.tw);
+                }
+            } else if (d < 5) {
                 const int c = d >> 2;
                 const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
                                     __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
                                     __builtin_amdgcn_perm(q.tg[5][c], q.tg[4][c], dsel(d)),
                                     __builtin_amdgcn_perm(q.tg[7][c], q.tg[6][c], dsel(d))};
-                *reinterpret_cast<gm_u32x4 *>(bw + ((5 * role + d) * kGemmBN + dn) * 16) = o;
-            } else if (d == 0) {  // bytes 20..27: 24 and 25 are entries 4 and 5
-                *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tg[4], q.tg[5]);
+                *reinterpret_cast<gm_u32x4 *>(bw + ((grp_frag + d) * kGemmBN + dn) * 16) = o;
+                const gm_u32x2 h = {__builtin_amdgcn_perm(q.th[1][c], q.th[0][c], dsel(d)),
+                                    __builtin_amdgcn_perm(q.th[3][c], q.th[2][c], dsel(d))};
+                *reinterpret_cast<gm_u32x2 *>(bw + ((5 + d) * kGemmBN + dn) * 16 + half_off) = h;
+            } else if (role == 1) {  // wave-uniform
+                *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tt[0], q.tt[1]);
                 put_scale(buf, q.tw);
             }
-        } else if (d < 5) {
-            const int c = d >> 2;
-            const gm_u32x4 o = {__builtin_amdgcn_perm(q.tg[1][c], q.tg[0][c], dsel(d)),
-                                __builtin_amdgcn_perm(q.tg[3][c], q.tg[2][c], dsel(d)),
-                                __builtin_amdgcn_perm(q.tg[5][c], q.tg[4][c], dsel(d)),
-                                __builtin_amdgcn_perm(q.tg[7][c], q.tg[6][c], dsel(d))};
-            *reinterpret_cast<gm_u32x4 *>(bw + ((grp_frag + d) * kGemmBN + dn) * 16) = o;
-            const gm_u32x2 h = {__builtin_amdgcn_perm(q.th[1][c], q.th[0][c], dsel(d)),
-                                __builtin_amdgcn_perm(q.th[3][c], q.th[2][c], dsel(d))};
-            *reinterpret_cast<gm_u32x2 *>(bw + ((5 + d) * kGemmBN + dn) * 16 + half_off) = h;
-        } else if (role == 1) {  // wave-uniform
-            *reinterpret_cast<gm_u32x4 *>(bw + (15 * kGemmBN + dn) * 16) = frag15(q.tt[0], q.tt[1]);
-            put_scale(buf, q.tw);
-        }
-    };
-    auto decode_all = [&](const gm_u32x4 &r, int buf) {
-        TabRegs q;
-        decode_read(r, q, 0);
-        decode_read(r, q, 1);
+        };
+        auto decode_all = [&](const gm_u32x4 &r, int buf) {
+            TabRegs q;
+            decode_read(r, q, 0);
+            decode_read(r, q, 1);
 #pragma unroll
-        for (int d = 0; d < 6; ++d) decode_write(q, buf, d);
-    };
+            for (int d = 0; d < 6; ++d) decode_write(q, buf, d);
+        };
 
-    // activation fragments: this wave's 32-row groups mt0 .. mt0 + TM - 1
-    const uint16_t *xw = a.xf + (mt0 * a.nb * 8 * kWave + lane) * 8;
-    const int64_t tm_stride = a.nb * 8 * kWave * 8;
-    auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int s) {
+        // activation fragments: this wave's 32-row groups mt0 .. mt0 + TM - 1
+        const uint16_t *xw = a.xf + (mt0 * a.nb * 8 * kWave + lane) * 8;
+        const int64_t tm_stride = a.nb * 8 * kWave * 8;
+        auto load_a = [&](gm_u32x4 (&f)[TM], int64_t kb, int s) {
 #pragma unroll
-        for (int m = 0; m < TM; ++m)
-            f[m] = *reinterpret_cast<const gm_u32x4 *>(xw + m * tm_stride + (kb * 8 + s) * kWave * 8);
-    };
+            for (int m = 0; m < TM; ++m)
+                f[m] = *reinterpret_cast<const gm_u32x4 *>(xw + m * tm_stride + (kb * 8 + s) * kWave * 8);
+        };
 
-    f32x16 acc[TM][TN], part[TM][TN];
-    float scl[TN];
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-        scl[t] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < TM; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][t][r] = part[m][t][r] = 0.0f;
-    }
-    const int scol = wn * 32 * TN + (lane & 31);
-    // B fragment of step s: fragment s (lanes 0-31) or gemm_hi_frag(s)
-    // (lanes 32-63); the difference takes three values, folded into three
-    // per-lane bases
-    const int hi = lane >> 5;
-    const char *bsr0 = bsm + scol * 16 + hi * (10 * kGemmBN * 16);
-    const char *bsr1 = bsm + scol * 16 + hi * (3 * kGemmBN * 16);
-    const char *bsr2 = bsm + scol * 16 + hi * (8 * kGemmBN * 16);
-    auto read_b = [&](bf16x8 (&dst)[TN], int buf, int step) {
-        const char *b = step < 5 ? bsr0 : (step < 7 ? bsr1 : bsr2);
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-            dst[t] = *reinterpret_cast<const bf16x8 *>(b + buf * kBufBytes + (step * kGemmBN + 32 * t) * 16);
-    };
-
-    // ---- prologue: blocks 0 and 1 decoded, block 2 .. of weights, the first
-    //      activation steps and the first B fragments in flight
-    gm_u32x4 afr[kAr][TM];
-    bf16x8 bq[kBq + 1][TN];
-    gm_u32x4 ring[PD];  // weights of blocks i + 2 .. i + 1 + PD at iteration i
-    {
-        gm_u32x4 w_first, w_second;
-        load_w(w_first, blk(0));
-        load_w(w_second, blk(1));
-#pragma unroll
-        for (int p = 0; p < PD; ++p) load_w(ring[(2 + p) % PD], blk(2 + p));
-#pragma unroll
-        for (int s = 0; s < kAr; ++s) load_a(afr[s], blk(0), s);
-        __syncthreads();  // table
-        decode_all(w_first, 0);
-        decode_all(w_second, 1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kBq; ++p) read_b(bq[p], 0, p);
-
-    // One block of K, as eight MFMA steps.  Each step also carries part of
-    // the surrounding work, in a fixed order (sched_barrier keeps it): the
-    // B fragments kBq steps ahead (into the next block's buffer at the end),
-    // the activation fragments kAr steps ahead and a slice of the decode of
-    // block i + 2 (table reads in steps 0-1, fragment groups in steps 2-7).
-    // Step 0 first folds the previous block's partial into acc (acc += part
-    // * scale), tile by tile, just before that tile's MFMA chain restarts.
-    auto iteration = [&](int buf, int i, gm_u32x4 &rslot) {
-        const int nbuf = (buf + 1) % kNumBufs, dbuf = (buf + 2) % kNumBufs;
-        TabRegs q;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if (s + kBq < 8)
-                read_b(bq[(s + kBq) % (kBq + 1)], buf, s + kBq);
-            else
-                read_b(bq[(s + kBq) % (kBq + 1)], nbuf, s + kBq - 8);
-            {
-                gm_u32x4 (&ar)[TM] = afr[s % kAr];
-                bf16x8 av[TM];
-#pragma unroll
-                for (int m = 0; m < TM; ++m) av[m] = __builtin_bit_cast(bf16x8, ar[m]);
-#pragma unroll
-                for (int m = 0; m < TM; ++m)
-#pragma unroll
-                    for (int t = 0; t < TN; ++t) {
-                        if (s == 0) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
-                            const f32x16 z = {};
-                            part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[0][t], z, 0, 0, 0);
-                        } else {
-                            part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[s % (kBq + 1)][t],
-                                                                                  part[m][t], 0, 0, 0);
-                        }
-                    }
-                if (s + kAr < 8)
-                    load_a(ar, blk(i), s + kAr);
-                else
-                    load_a(ar, blk(i + 1), s + kAr - 8);
-            }
-            if (s < 2) {
-                decode_read(rslot, q, s);
-                if (s == 1) load_w(rslot, blk(i + 2 + PD));
-            } else {
-                decode_write(q, dbuf, s - 2);
-            }
-            if (s == 7) {
-#pragma unroll
-                for (int t = 0; t < TN; ++t)
-                    scl[t] = *reinterpret_cast<const lds_f32 *>(
-                        static_cast<uintptr_t>(gemm_scale_addr(buf, scol + 32 * t)));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    for (int base = 0; base < nblk; base += PD) {
-#pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int i = base + u;
-            if (i >= nblk) break;
-            iteration(u % kNumBufs, i, ring[(u + 2) % PD]);
-            __syncthreads();
-        }
-    }
-    // the last block's partial is not scaled yet
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
-
-    if (!active) return;
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
+        f32x16 acc[TM][TN], part[TM][TN];
+        float scl[TN];
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
-            const int64_t col = tile_n + wn * 32 * TN + 32 * t + (lane & 31);
-            if (col >= rows) continue;
+            scl[t] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row >= a.m) continue;
-                const float v = acc[m][t][r];
-                if (a.part != nullptr) {
-                    a.part[(static_cast<int64_t>(blockIdx.z) * a.m + row) * rows + col] = v;
-                } else if (col < a.n0) {
-                    const int64_t o = row * a.n0 + col;
-                    a.y0[o] = a.residual ? a.residual[o] + v : v;
-                } else {
-                    a.y1[row * a.n1 + (col - a.n0)] = v;
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[m][t][r] = part[m][t][r] = 0.0f;
+        }
+        const int scol = wn * 32 * TN + (lane & 31);
+        // B fragment of step s: fragment s (lanes 0-31) or gemm_hi_frag(s)
+        // (lanes 32-63); the difference takes three values, folded into three
+        // per-lane bases
+        const int hi = lane >> 5;
+        const char *bsr0 = bsm + scol * 16 + hi * (10 * kGemmBN * 16);
+        const char *bsr1 = bsm + scol * 16 + hi * (3 * kGemmBN * 16);
+        const char *bsr2 = bsm + scol * 16 + hi * (8 * kGemmBN * 16);
+        auto read_b = [&](bf16x8 (&dst)[TN], int buf, int step) {
+            const char *b = step < 5 ? bsr0 : (step < 7 ? bsr1 : bsr2);
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                dst[t] = *reinterpret_cast<const bf16x8 *>(b + buf * kBufBytes + (step * kGemmBN + 32 * t) * 16);
+        };
+
+        // ---- prologue: blocks 0 and 1 decoded, block 2 .. of weights, the first
+        //      activation steps and the first B fragments in flight
+        gm_u32x4 afr[kAr][TM];
+        bf16x8 bq[kBq + 1][TN];
+        gm_u32x4 ring[PD];  // weights of blocks i + 2 .. i + 1 + PD at iteration i
+        {
+            gm_u32x4 w_first, w_second;
+            load_w(w_first, blk(0));
+            load_w(w_second, blk(1));
+#pragma unroll
+            for (int p = 0; p < PD; ++p) load_w(ring[(2 + p) % PD], blk(2 + p));
+#pragma unroll
+            for (int s = 0; s < kAr; ++s) load_a(afr[s], blk(0), s);
+            __syncthreads();  // table
+            decode_all(w_first, 0);
+            decode_all(w_second, 1);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kBq; ++p) read_b(bq[p], 0, p);
+
+        // One block of K, as eight MFMA steps.  Each step also carries part of
+        // the surrounding work, in a fixed order (sched_barrier keeps it): the
+        // B fragments kBq steps ahead (into the next block's buffer at the end),
+        // the activation fragments kAr steps ahead and a slice of the decode of
+        // block i + 2 (table reads in steps 0-1, fragment groups in steps 2-7).
+        // Step 0 first folds the previous block's partial into acc (acc += part
+        // * scale), tile by tile, just before that tile's MFMA chain restarts.
+        auto iteration = [&](int buf, int i, gm_u32x4 &rslot) {
+            const int nbuf = (buf + 1) % kNumBufs, dbuf = (buf + 2) % kNumBufs;
+            TabRegs q;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                if (s + kBq < 8)
+                    read_b(bq[(s + kBq) % (kBq + 1)], buf, s + kBq);
+                else
+                    read_b(bq[(s + kBq) % (kBq + 1)], nbuf, s + kBq - 8);
+                {
+                    gm_u32x4 (&ar)[TM] = afr[s % kAr];
+                    bf16x8 av[TM];
+#pragma unroll
+                    for (int m = 0; m < TM; ++m) av[m] = __builtin_bit_cast(bf16x8, ar[m]);
+#pragma unroll
+                    for (int m = 0; m < TM; ++m)
+#pragma unroll
+                        for (int t = 0; t < TN; ++t) {
+                            if (s == 0) {
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
+                                const f32x16 z = {};
+                                part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[0][t], z, 0, 0, 0);
+                            } else {
+                                part[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bq[s % (kBq + 1)][t],
+                                                                                      part[m][t], 0, 0, 0);
+                            }
+                        }
+                    if (s + kAr < 8)
+                        load_a(ar, blk(i), s + kAr);
+                    else
+                        load_a(ar, blk(i + 1), s + kAr - 8);
                 }
+                if (s < 2) {
+                    decode_read(rslot, q, s);
+                    if (s == 1) load_w(rslot, blk(i + 2 + PD));
+                } else {
+                    decode_write(q, dbuf, s - 2);
+                }
+                if (s == 7) {
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        scl[t] = *reinterpret_cast<const lds_f32 *>(
+                            static_cast<uintptr_t>(gemm_scale_addr(buf, scol + 32 * t)));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        for (int base = 0; base < nblk; base += PD) {
+#pragma unroll
+            for (int u = 0; u < PD; ++u) {
+                const int i = base + u;
+                if (i >= nblk) break;
+                iteration(u % kNumBufs, i, ring[(u + 2) % PD]);
+                __syncthreads();
             }
         }
+        // the last block's partial is not scaled yet
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[m][t][r] = fmaf(part[m][t][r], scl[t], acc[m][t][r]);
+
+        // a segment over all blocks of its tile is final; any other is stored
+        // as this workgroup's first (0) or last (1) partial for k_gemm_fix
+        float *pp = a.part + (wg * 2 + kslot) * a.prow * kGemmBN;
+        const int64_t row0 = tm * a.prow;  // first row of the tile
+        // the row offsets below are the same in every segment; an opaque lane
+        // index keeps the compiler from hoisting them out of the segment loop
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        if (active) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    const int64_t col = tile_n + wn * 32 * TN + 32 * t + (lane_e & 31);
+                    if (col >= rows) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane_e / 32) + (r % 4);
+                        if (row >= a.m) continue;
+                        const float v = acc[m][t][r];
+                        if (!full) {
+                            pp[(row - row0) * kGemmBN + (col - tile_n)] = v;
+                        } else if (col < a.n0) {
+                            const int64_t o = row * a.n0 + col;
+                            a.y0[o] = a.residual ? a.residual[o] + v : v;
+                        } else {
+                            a.y1[row * a.n1 + (col - a.n0)] = v;
+                        }
+                    }
+                }
+        }
+    }  // segments
 }
+
 
 // ---------------------------------------------------------------------------
 // Small-batch GEMM (M <= 64): every wave decodes the B fragments of its own
@@ -577,7 +622,6 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     const int wave = tid / kWave;
     const int hi = lane >> 5;
     const int64_t rows = a.n0 + a.n1;
-    const int64_t mt0 = static_cast<int64_t>(blockIdx.y) * TM;
 
     // ---- table: entry b, copy c at b * 256 + c * 8
     {
@@ -599,19 +643,39 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     __syncthreads();  // table built
     const uint32_t lc = static_cast<uint32_t>(lane & (kRdTabCopies - 1)) << 3;
 
-    // ---- stream-K: workgroup w takes units [w U / G, (w + 1) U / G) of the
-    // U = tiles x blocks (tile-major) and runs them as one segment per tile
-    // it touches.
+    // ---- work split as in k_gemm_mfma: whole tiles first, then an equal
+    // run of the remaining tiles' (tile, block) units, one segment per tile
+    // touched.
     const int64_t G = gridDim.x, wg = blockIdx.x;
-    const int64_t u_lo = wg * a.units / G, u_hi = (wg + 1) * a.units / G;
-    for (int64_t useg = u_lo; useg < u_hi;) {
-        const int64_t tile = useg / a.nb;
-        const int64_t kb0 = useg - tile * a.nb;
-        const int64_t uend = (tile + 1) * a.nb < u_hi ? (tile + 1) * a.nb : u_hi;
-        const int nblk = static_cast<int>(uend - useg);
+    const int64_t Gs = a.sk_wgs;  // workgroups [0, Gs) share the stream-K units
+    const int64_t sk_lo = wg < Gs ? wg * a.sk_units / Gs : 0, sk_hi = wg < Gs ? (wg + 1) * a.sk_units / Gs : 0;
+    int64_t jdp = 0, useg = sk_lo;
+    while (jdp < a.dp_rounds || useg < sk_hi) {
+        int64_t tile, kb0;
+        int nblk, kslot = 0;
+        bool full;
+        if (jdp < a.dp_rounds) {  // whole tile wg + jdp G
+            tile = wg + jdp * G;
+            kb0 = 0;
+            nblk = static_cast<int>(a.nb);
+            full = true;
+            ++jdp;
+        } else {  // units [useg, uend) of stream-K tile t2
+            const int64_t t2 = useg / a.nb;
+            kb0 = useg - t2 * a.nb;
+            const int64_t uend = (t2 + 1) * a.nb < sk_hi ? (t2 + 1) * a.nb : sk_hi;
+            nblk = static_cast<int>(uend - useg);
+            tile = a.dp_tiles + t2;
+            full = kb0 == 0 && nblk == a.nb;
+            kslot = useg == sk_lo ? 0 : 1;
+            useg = uend;
+        }
         const int last = nblk - 1;
         auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };
-        const int64_t tile_n = tile * kGemmBN;
+        const int64_t tn = tile / a.tiles_m, tm = tile - tn * a.tiles_m;
+        const int64_t tile_n = tn * kGemmBN;
+        const int64_t mt0 = tm * TM;
+        const int64_t row0 = tm * a.prow;  // first row of the tile
 
         // ---- this lane's column
         const int64_t gcol = tile_n + wave * 32 + (lane & 31);
@@ -770,9 +834,8 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
             for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r) acc[m][r] = fmaf(part[m][r], sc_prev, acc[m][r]);
 
         // a segment over all blocks of its tile is final; any other is stored
-        // as this workgroup's first (0) or last (1) partial for k_gemm_rd_fix
-        const bool full = kb0 == 0 && nblk == a.nb;
-        float *pp = a.part + (wg * 2 + (useg == u_lo ? 0 : 1)) * a.m * kGemmBN;
+        // as this workgroup's first (0) or last (1) partial for k_gemm_fix
+        float *pp = a.part + (wg * 2 + kslot) * a.prow * kGemmBN;
         const int64_t col = gcol;
         // the row offsets below are the same in every segment; an opaque lane
         // index keeps the compiler from hoisting them (16 rows x 64-bit
@@ -788,7 +851,7 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
                     if (row >= a.m) continue;
                     const float v = acc[m][r];
                     if (!full) {
-                        pp[row * kGemmBN + (col - tile_n)] = v;
+                        pp[(row - row0) * kGemmBN + (col - tile_n)] = v;
                     } else if (col < a.n0) {
                         const int64_t o = row * a.n0 + col;
                         a.y0[o] = a.residual ? a.residual[o] + v : v;
@@ -798,64 +861,55 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
                 }
             }
         }
-        useg = uend;
     }  // segments
 }
 
 // Workgroup of the stream-K range holding unit u: the largest w with
 // floor(w U / G) <= u.
-__device__ __forceinline__ int64_t rd_owner(int64_t u, int64_t units, int64_t G)
+__device__ __forceinline__ int64_t gemm_owner(int64_t u, int64_t units, int64_t G)
 {
     int64_t w = u * G / units;
     while (w + 1 < G && (w + 1) * units / G <= u) ++w;
     return w;
 }
 
-// Tiles that more than one workgroup touched: the sum of their partials in
-// workgroup order (+ residual), routed to y0 / y1.  Grid: tiles x ceil(m 128
-// / 256), one output per thread.
-__global__ void __launch_bounds__(kEwThreads) k_gemm_rd_fix(GemmArgs a)
+// Stream-K tiles that more than one workgroup touched: the sum of their
+// partials in workgroup order (+ residual), routed to y0 / y1.  Grid:
+// (tiles - dp_tiles) x ceil(prow / kFixRows); a thread adds 4 adjacent
+// columns of one row.
+constexpr int kFixRows = kEwThreads / (kGemmBN / 4);  // rows per workgroup: 8
+
+__global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
 {
-    const int64_t G = a.wgs, t = blockIdx.x;
-    const int64_t rows = a.n0 + a.n1;
-    const int64_t first_u = t * a.nb;
-    const int64_t w_lo = rd_owner(first_u, a.units, G), w_hi = rd_owner(first_u + a.nb - 1, a.units, G);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // workgroup-uniform: which workgroups hold partials of this tile
+    const int64_t G = a.sk_wgs, t = a.dp_tiles + blockIdx.x;
+    const int64_t first_u = static_cast<int64_t>(blockIdx.x) * a.nb;
+    const int64_t w_lo = gemm_owner(first_u, a.sk_units, G), w_hi = gemm_owner(first_u + a.nb - 1, a.sk_units, G);
     if (w_lo == w_hi) return;  // stored final by its one workgroup
-    const int64_t e = static_cast<int64_t>(blockIdx.y) * kEwThreads + threadIdx.x;
-    const int64_t row = e / kGemmBN, c = e - row * kGemmBN;
-    const int64_t col = t * kGemmBN + c;
-    if (row >= a.m || col >= rows) return;
     // w_lo's segment of this tile is its first unless its range began in an
     // earlier tile; every later workgroup's range begins inside this tile
-    const int64_t k_lo = (w_lo * a.units / G < first_u) ? 1 : 0;
-    float v = a.part[((w_lo * 2 + k_lo) * a.m + row) * kGemmBN + c];
+    const int64_t k_lo = (w_lo * a.sk_units / G < first_u) ? 1 : 0;
+    const int64_t tn = t / a.tiles_m, tm = t - tn * a.tiles_m;
+    const int64_t rows = a.n0 + a.n1;
+    const int64_t r = static_cast<int64_t>(blockIdx.y) * kFixRows + threadIdx.x / (kGemmBN / 4);
+    const int64_t c = 4 * (threadIdx.x % (kGemmBN / 4));
+    const int64_t row = tm * a.prow + r, col = tn * kGemmBN + c;
+    if (r >= a.prow || row >= a.m || col >= rows) return;
+    const float *p0 = a.part + r * kGemmBN + c;
+    const int64_t seg = 2 * a.prow * kGemmBN;  // floats per workgroup (first and last partial)
+    f32x4 v = *reinterpret_cast<const f32x4 *>(p0 + w_lo * seg + k_lo * a.prow * kGemmBN);
 #pragma unroll 4
-    for (int64_t w = w_lo + 1; w <= w_hi; ++w) v += a.part[(w * 2 * a.m + row) * kGemmBN + c];
-    if (col < a.n0) {
-        const int64_t o = row * a.n0 + col;
-        a.y0[o] = a.residual ? a.residual[o] + v : v;
-    } else {
-        a.y1[row * a.n1 + (col - a.n0)] = v;
-    }
-}
-
-// Sum of the split-K partials in split order (+ residual), routed to y0 / y1.
-__global__ void __launch_bounds__(kEwThreads) k_gemm_reduce(const float *__restrict__ part, int32_t splits,
-                                                             int64_t m, int64_t n0, int64_t n1, float *y0, float *y1,
-                                                             const float *residual)
-{
-    const int64_t rows = n0 + n1;
-    const int64_t total = m * rows;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEwThreads + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * kEwThreads) {
-        float v = 0.0f;
-        for (int32_t z = 0; z < splits; ++z) v += part[z * total + i];
-        const int64_t row = i / rows, col = i - row * rows;
-        if (col < n0) {
-            const int64_t o = row * n0 + col;
-            y0[o] = residual ? residual[o] + v : v;
+    for (int64_t w = w_lo + 1; w <= w_hi; ++w) v += *reinterpret_cast<const f32x4 *>(p0 + w * seg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t cj = col + j;
+        if (cj >= rows) break;
+        if (cj < a.n0) {
+            const int64_t o = row * a.n0 + cj;
+            a.y0[o] = a.residual ? a.residual[o] + v[j] : v[j];
         } else {
-            y1[row * n1 + (col - n0)] = v;
+            a.y1[row * a.n1 + (cj - a.n0)] = v[j];
         }
     }
 }
@@ -864,19 +918,19 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_reduce(const float *__restr
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kPlanCus = 256;      // compute units the grid and split heuristics plan for
-constexpr int kMaxSplits = 32;
-constexpr int kRdWgsPerCu = 2;     // register-decode workgroups resident per CU
-constexpr int kRdMinBlocks = 4;    // fewest units a register-decode workgroup takes
+constexpr int kPlanCus = 256;   // compute units the grid is sized for
+constexpr int kMinBlocks = 4;   // fewest units a workgroup takes
 }  // namespace
 
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
 {
     // cfg 0 / 1: register-decode kernel, 32 / 64 rows, two workgroups per
-    // CU sharing the tiles x blocks units evenly (stream-K); cfg 2:
-    // LDS-decode kernel, 128 rows with 8 waves, one per CU, K split chosen
-    // from a time model.
+    // CU; cfg 2: LDS-decode kernel, 128 rows with 8 waves, one per CU.
+    // Either way the grid fills the CUs once: each workgroup takes whole
+    // tiles for the full rounds there are, then an equal run of the rest's
+    // (tile, K block) units.
     static const int64_t kBm[3] = {32, 64, 128};
+    static const int64_t kPerCu[3] = {2, 2, 1};
     GemmPlan p;
     p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
     const int64_t bm = kBm[p.cfg];
@@ -884,46 +938,23 @@ GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
     p.nb = k / kBlockWeights;
     p.tiles_n = (rows + kGemmBN - 1) / kGemmBN;
     p.tiles_m = p.m_pad / bm;
-    p.splits = 1;
-    p.bps = static_cast<int32_t>(p.nb);
+    p.prow = p.tiles_m == 1 ? m : bm;
     if (m == 0 || rows == 0 || p.nb == 0) return p;
-    if (p.cfg < 2) {
-        const int64_t units = p.tiles_n * p.nb;
-        int64_t g = kRdWgsPerCu * kPlanCus;
-        if (g > units / kRdMinBlocks) g = units / kRdMinBlocks;
-        p.wgs = g < 1 ? 1 : g;
-        return p;
-    }
-    // Time model: rounds of workgroups over the CUs, each block costing
-    // t_blk (microseconds, measured order of magnitude), plus a fixed start
-    // per round; splits add their fp32 partials (written and read back) and
-    // a launch.
-    const double t_blk = 0.6;
-    const int64_t slots = kPlanCus;
-    double best = 0.0;
-    for (int64_t s = 1; s <= kMaxSplits && s <= p.nb; ++s) {
-        const int64_t bps = (p.nb + s - 1) / s;
-        const int64_t se = (p.nb + bps - 1) / bps;
-        if (se != s) continue;
-        const int64_t wgs = p.tiles_n * p.tiles_m * s;
-        const int64_t rounds = (wgs + slots - 1) / slots;
-        double t = static_cast<double>(rounds) * (static_cast<double>(bps) * t_blk + 1.0);
-        if (s > 1) t += 2.0 * static_cast<double>(s * m * rows) * 4.0 / 5.0e6 + 3.0;
-        if (s == 1 || t < best) {
-            best = t;
-            p.splits = static_cast<int32_t>(s);
-            p.bps = static_cast<int32_t>(bps);
-        }
-    }
+    const int64_t tiles = p.tiles_n * p.tiles_m;
+    int64_t g = kPerCu[p.cfg] * kPlanCus;
+    if (g > tiles * p.nb / kMinBlocks) g = tiles * p.nb / kMinBlocks;
+    p.wgs = g < 1 ? 1 : g;
+    // whole tiles for as many full rounds as there are, the rest shared
+    p.dp_rounds = tiles / p.wgs;
+    p.sk_tiles = tiles - p.dp_rounds * p.wgs;
     return p;
 }
 
 size_t gemm_frag_elems(const GemmPlan &p, int64_t k) { return static_cast<size_t>(p.m_pad) * static_cast<size_t>(k); }
 
-size_t gemm_part_floats(const GemmPlan &p, int64_t m, int64_t rows)
+size_t gemm_part_floats(const GemmPlan &p)
 {
-    if (p.cfg < 2) return static_cast<size_t>(2 * p.wgs) * static_cast<size_t>(m) * kGemmBN;
-    return p.splits > 1 ? static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(rows) : 0;
+    return static_cast<size_t>(2 * p.wgs) * static_cast<size_t>(p.prow) * kGemmBN;
 }
 
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
@@ -1000,39 +1031,34 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     a.y0 = y0;
     a.y1 = y1;
     a.residual = residual;
-    a.part = p.splits > 1 ? part : nullptr;
+    a.part = part;
     a.m = m;
     a.nb = p.nb;
-    a.bps = p.bps;
-    a.units = p.tiles_n * p.nb;
+    a.tiles_m = p.tiles_m;
+    a.prow = p.prow;
     a.wgs = p.wgs;
+    a.dp_rounds = p.dp_rounds;
+    a.dp_tiles = p.dp_rounds * p.wgs;
+    a.sk_units = p.sk_tiles * p.nb;
+    a.sk_wgs = a.sk_units < p.wgs ? a.sk_units : p.wgs;
+    const dim3 grid(static_cast<unsigned>(p.wgs));
     hipError_t e;
-    if (p.cfg < 2) {
-        a.part = part;
-        const dim3 grid(static_cast<unsigned>(p.wgs), static_cast<unsigned>(p.tiles_m), 1);
-        const int64_t live = m - (p.tiles_m - 1) * (p.cfg == 0 ? 32 : 64);  // rows of the last row tile
-        if (p.cfg == 1)
-            e = gemm_rd_dispatch<2, 4, 4>(grid, s, a);
-        else if (live <= 8)
+    if (p.cfg == 0) {
+        if (m <= 8)
             e = gemm_rd_dispatch<1, 4, 1>(grid, s, a);
-        else if (live <= 16)
+        else if (m <= 16)
             e = gemm_rd_dispatch<1, 4, 2>(grid, s, a);
         else
             e = gemm_rd_dispatch<1, 4, 4>(grid, s, a);
-        if (e != hipSuccess) return e;
-        const unsigned ey = static_cast<unsigned>((m * kGemmBN + kEwThreads - 1) / kEwThreads);
-        hipLaunchKernelGGL(k_gemm_rd_fix, dim3(static_cast<unsigned>(p.tiles_n), ey), dim3(kEwThreads), 0, s, a);
-        return hipGetLastError();
+    } else if (p.cfg == 1) {
+        e = gemm_rd_dispatch<2, 4, 4>(grid, s, a);
+    } else {
+        e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     }
-    const dim3 grid(static_cast<unsigned>(p.tiles_n), static_cast<unsigned>(p.tiles_m),
-                    static_cast<unsigned>(p.splits));
-    e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
-    if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t total = m * rows;
-    int64_t blocks = (total + kEwThreads - 1) / kEwThreads;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_gemm_reduce, dim3(static_cast<unsigned>(blocks)), dim3(kEwThreads), 0, s, part, p.splits, m,
-                       n0, n1, y0, y1, residual);
+    if (e != hipSuccess) return e;
+    if (p.sk_tiles == 0) return hipSuccess;
+    const unsigned ey = static_cast<unsigned>((p.prow + kFixRows - 1) / kFixRows);
+    hipLaunchKernelGGL(k_gemm_fix, dim3(static_cast<unsigned>(p.sk_tiles), ey), dim3(kEwThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -67,25 +67,25 @@ hipError_t launch_lut_gate_up_sum(const float *part, int64_t f, int64_t d_in, co
 
 // ---- prefill (m >= 1, bf16 MFMA) --------------------------------------------
 // Shape of one GEMM launch: tile configuration (cfg 0/1 = 32/64 rows
-// per workgroup, register decode, `wgs` workgroups sharing the tiles x
-// blocks evenly; cfg 2 = 128 rows, LDS decode, a grid of tiles x K
-// splits), padded activation rows.
+// per workgroup, register decode; cfg 2 = 128 rows, LDS decode), padded
+// activation rows, tiles, and the workgroups sharing the tiles x K blocks.
 struct GemmPlan {
     int cfg = 0;
     int64_t m_pad = 0, tiles_n = 0, tiles_m = 0, nb = 0;
-    int32_t splits = 1, bps = 0;  // K split count and blocks per split (cfg 2)
-    int64_t wgs = 0;              // workgroups (cfg 0 / 1)
+    int64_t prow = 0;  // rows of one row tile's partial (m when there is one row tile)
+    int64_t wgs = 0;   // workgroups
+    int64_t dp_rounds = 0, sk_tiles = 0;  // whole-tile rounds; tiles shared by (tile, block) units
 };
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k);
-size_t gemm_frag_elems(const GemmPlan &p, int64_t k);                // bf16 A fragments
-size_t gemm_part_floats(const GemmPlan &p, int64_t m, int64_t rows);  // split-K partials
+size_t gemm_frag_elems(const GemmPlan &p, int64_t k);  // bf16 A fragments
+size_t gemm_part_floats(const GemmPlan &p);            // partial tiles of the work split
 // xf = bf16 MFMA A fragments of R (a * x) (rows < m only); a = RMS scale if
 // rms_eps > 0.  When g/u are given instead of x, the input is silu(g) * u.
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
                             const float *signs, float rms_eps, uint16_t *xf, hipStream_t s);
 // y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; rows of the
 // virtual matrix as in launch_matvec_part, the second matrix's outputs in
-// y1 [m][n1].  part: gemm_part_floats(p, m, n0 + n1) floats of scratch.
+// y1 [m][n1].  part: gemm_part_floats(p) floats of scratch.
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
                        hipStream_t s);

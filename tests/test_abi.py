@@ -150,7 +150,9 @@ def test_gemm_and_ffn_validation():
     rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, -1, S, Y, WS, 1 << 40, None))
     assert rc == 2
     need = L().ptq1_gemm_workspace_bytes(256, 17408, 5120)
-    assert need == 256 * 5120 * 2  # bf16 activations
+    # bf16 activations, then two fp32 partial tiles (128 x 128) for each of
+    # the 256 workgroups (one per CU) that share the tiles x K blocks
+    assert need == 256 * 5120 * 2 + 256 * 2 * 128 * 128 * 4
     rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, 256, S, Y, WS, need - 1, None))
     assert rc == 6
     W2, W3 = C.c_void_p(FAKE * 600), C.c_void_p(FAKE * 700)

@@ -374,9 +374,12 @@ def test_swiglu():
 
 @pytest.mark.parametrize("m,n,k,rot", [(1, 300, 1024, True), (2, 300, 1024, True), (8, 300, 2048, True),
                                        (37, 300, 1024, True), (129, 200, 1024, True), (5, 130, 384, False),
-                                       # long K over few column tiles: split-K partials and their reduction
+                                       # long K over few column tiles: partial tiles and their fix-up
                                        (4, 256, 8192, True), (40, 300, 8192, True), (130, 256, 8192, True),
-                                       (3, 100, 3200, False)])
+                                       (3, 100, 3200, False),
+                                       # more tiles than workgroups: a round of whole tiles, then the
+                                       # remaining tiles shared as (tile, block) units
+                                       (130, 16512, 1024, True), (8, 65664, 512, False)])
 def test_gemm_small(m, n, k, rot):
     seed = 3
     t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
