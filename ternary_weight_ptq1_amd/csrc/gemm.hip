@@ -91,20 +91,30 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
         if (e0 + lane + kWave * j >= k) v[j] = 0.0f;
     if (x != nullptr && rms_eps > 0.0f) {
         // the row's mean square: 16-byte loads (k is a multiple of 128),
-        // eight in flight per lane
+        // 24 in flight per lane (one round trip for k <= 6144)
+        constexpr int kQ = 24;
         const float4 *xr = reinterpret_cast<const float4 *>(x + row * k);
         const int64_t k4 = k / 4;
-        float s8[8] = {};
-        for (int64_t i0 = 0; i0 < k4; i0 += 8 * kWave) {
+        float sq[kQ] = {};
+        for (int64_t i0 = 0; i0 < k4; i0 += kQ * kWave) {
+            float4 xv[kQ];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < kQ; ++q) {
                 const int64_t i = i0 + q * kWave + lane;
-                const float4 xv = xr[i < k4 ? i : k4 - 1];
-                const float w = i < k4 ? 1.0f : 0.0f;
-                s8[q] = fmaf(w * xv.x, xv.x, fmaf(w * xv.y, xv.y, fmaf(w * xv.z, xv.z, fmaf(w * xv.w, xv.w, s8[q]))));
+                xv[q] = xr[i < k4 ? i : k4 - 1];
+            }
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                const float w = i0 + q * kWave + lane < k4 ? 1.0f : 0.0f;
+                sq[q] = fmaf(w * xv[q].x, xv[q].x,
+                             fmaf(w * xv[q].y, xv[q].y, fmaf(w * xv[q].z, xv[q].z, fmaf(w * xv[q].w, xv[q].w, sq[q]))));
             }
         }
-        float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+#pragma unroll
+        for (int h = kQ / 2; h >= 3; h /= 2)
+#pragma unroll
+            for (int q = 0; q < h; ++q) sq[q] += sq[q + h];
+        float s = (sq[0] + sq[1]) + sq[2];
 #pragma unroll
         for (int h = kWave / 2; h > 0; h >>= 1) s += __shfl_xor(s, h, kWave);
         const float a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
@@ -865,12 +875,10 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
 }
 
 // Workgroup of the stream-K range holding unit u: the largest w with
-// floor(w U / G) <= u.
+// floor(w U / G) <= u, that is with w U < (u + 1) G.
 __device__ __forceinline__ int64_t gemm_owner(int64_t u, int64_t units, int64_t G)
 {
-    int64_t w = u * G / units;
-    while (w + 1 < G && (w + 1) * units / G <= u) ++w;
-    return w;
+    return ((u + 1) * G + units - 1) / units - 1;
 }
 
 // Stream-K tiles that more than one workgroup touched: the sum of their
@@ -889,7 +897,7 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
     if (w_lo == w_hi) return;  // stored final by its one workgroup
     // w_lo's segment of this tile is its first unless its range began in an
     // earlier tile; every later workgroup's range begins inside this tile
-    const int64_t k_lo = (w_lo * a.sk_units / G < first_u) ? 1 : 0;
+    const int64_t k_lo = (w_lo * a.sk_units < first_u * G) ? 1 : 0;
     const int64_t tn = t / a.tiles_m, tm = t - tn * a.tiles_m;
     const int64_t rows = a.n0 + a.n1;
     const int64_t r = static_cast<int64_t>(blockIdx.y) * kFixRows + threadIdx.x / (kGemmBN / 4);
@@ -899,8 +907,17 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
     const float *p0 = a.part + r * kGemmBN + c;
     const int64_t seg = 2 * a.prow * kGemmBN;  // floats per workgroup (first and last partial)
     f32x4 v = *reinterpret_cast<const f32x4 *>(p0 + w_lo * seg + k_lo * a.prow * kGemmBN);
-#pragma unroll 4
-    for (int64_t w = w_lo + 1; w <= w_hi; ++w) v += *reinterpret_cast<const f32x4 *>(p0 + w * seg);
+    // the later workgroups' first partials, eight requests in flight at a
+    // time (clamped indices, no branch around the loads), added in order
+    for (int64_t base = w_lo + 1; base <= w_hi; base += 8) {
+        f32x4 q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            q[j] = *reinterpret_cast<const f32x4 *>(p0 + (base + j <= w_hi ? base + j : w_hi) * seg);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (base + j <= w_hi) v += q[j];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t cj = col + j;
