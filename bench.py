@@ -339,10 +339,19 @@ def main() -> int:
                     W = stack[L]
                     P.ptq1_ffn_block(xa, W[0], W[1], W[2], signs, D, F, rms_eps=1e-6, out=xa, ws=wss)
 
-            ms = timed(run_stack, 5, 1)
+            ms_eager = timed(run_stack, 3, 1)
+            # the stack replayed from one HIP graph of its 64 layers (no host
+            # launch gaps between the dependent kernels), as the decode step
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_stack(0)
+            torch.cuda.synchronize()
+            ms = timed(lambda i: g.replay(), 5, 1)
+            del g
             stk[f"M{m}"] = {"ms_per_stack": ms, "us_per_layer": ms * 1e3 / LAYERS,
                             "layers_per_s": LAYERS / (ms * 1e-3),
                             "weight_GB/s": LAYERS * LAYER_WEIGHT_BYTES / (ms * 1e-3) / 1e9,
+                            "us_per_layer_eager": ms_eager * 1e3 / LAYERS,
                             "finite": bool(torch.isfinite(xa).all().item())}
         breakdown["ffn_stack_64"] = stk
         del stack
