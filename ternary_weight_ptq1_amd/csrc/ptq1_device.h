@@ -62,19 +62,54 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 // lane l holds elements l + 64 j in v[j], j = 0..15.  Natural-order
 // (Sylvester) H: the butterfly pairs element i with i ^ h for h = 1 .. 512.
 // Pairs with h >= 64 sit in one lane (index j ^ (h/64)); pairs with h < 64
-// are in lanes l and l ^ h.  Unnormalised: returns H v.
+// are in lanes l and l ^ h, exchanged without LDS traffic: DPP quad
+// permutations (h = 1, 2), row shifts (h = 4), a half-row rotation (h = 8)
+// and the gfx950 lane swaps (h = 16, 32).  A butterfly leaves v + o at the
+// lane whose bit h is 0 and o - v at the other.  Unnormalised: returns H v.
 // ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float fwht_dpp(float v)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, kCtrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
 {
     const int lane = threadIdx.x & (kWave - 1);
+    const float s1 = (lane & 1) ? -1.0f : 1.0f, s2 = (lane & 2) ? -1.0f : 1.0f;
+    const float s4 = (lane & 4) ? -1.0f : 1.0f, s8 = (lane & 8) ? -1.0f : 1.0f;
+    const float s16 = (lane & 16) ? -1.0f : 1.0f, s32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int h = 1; h < kWave; h <<= 1) {
-        const float sgn = (lane & h) ? -1.0f : 1.0f;
+    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s1, v[j], fwht_dpp<0xB1>(v[j]));  // quad_perm [1,0,3,2]
 #pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) {
-            const float o = __shfl_xor(v[j], h, kWave);
-            v[j] = fmaf(sgn, v[j], o);  // low index: v + o; high index: o - v
-        }
+    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s2, v[j], fwht_dpp<0x4E>(v[j]));  // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) {
+        // lane + 4 (row_shl:4) or lane - 4 (row_shr:4): both are read by
+        // every lane before the select (a DPP read inside a branch would see
+        // the inactive lanes' old values)
+        const float up = fwht_dpp<0x104>(v[j]);
+        const float dn = fwht_dpp<0x114>(v[j]);
+        v[j] = fmaf(s4, v[j], (lane & 4) ? dn : up);
+    }
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s8, v[j], fwht_dpp<0x128>(v[j]));  // row_ror:8
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) {
+        // element [0] of the swap holds the own value in lanes 0-15 of each
+        // 32 and the partner's in 16-31; element [1] the other way round
+        const uint32_t u = __builtin_bit_cast(uint32_t, v[j]);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        v[j] = fmaf(s16, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
+    }
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v[j]);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        v[j] = fmaf(s32, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
     }
 #pragma unroll
     for (int hj = 1; hj < kRotPerLane; hj <<= 1) {
