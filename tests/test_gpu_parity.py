@@ -373,7 +373,8 @@ def test_swiglu():
 # ----------------------------------------------------------------- GEMM ----
 
 @pytest.mark.parametrize("m,n,k,rot", [(1, 300, 1024, True), (2, 300, 1024, True), (8, 300, 2048, True),
-                                       (12, 300, 2048, True), (32, 520, 1024, False),
+                                       (12, 300, 2048, True), (32, 520, 1024, False), (33, 260, 1024, True),
+                                       (64, 200, 1024, True), (100, 300, 1024, False),
                                        (37, 300, 1024, True), (129, 200, 1024, True), (5, 130, 384, False),
                                        # long K over few column tiles: partial tiles and their fix-up
                                        (4, 256, 8192, True), (40, 300, 8192, True), (130, 256, 8192, True),
