@@ -176,7 +176,8 @@ size_t lut_ws(int64_t n, int nmat, int64_t k)
     return round_up(ptq1::lut_part_floats(n, nmat, k) * sizeof(float), kWsAlign);
 }
 
-// GEMM: bf16 activation fragments, then split-K partials
+// GEMM: bf16 activation fragments, then the partial tiles of tiles that
+// several workgroups share (two per workgroup at most)
 struct GemmWs {
     size_t frag = 0, part = 0, total = 0;  // byte offsets
 };

@@ -175,11 +175,12 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 //      acc += partial * scale[column] in fp32.
 // Trits are stored as bf16 -2 / 0 / +2 (low byte always zero, so a table
 // entry is just the five high bytes) and the scale is halved to match.
-// Work split (stream-K): the grid is one workgroup per CU, and workgroup w
-// takes an equal run of the (tile, K block) units in tile order, as one
-// segment per tile it touches.  A segment covering all blocks of its tile
-// stores the result; any other stores an fp32 partial, and k_gemm_fix adds
-// the partials of each shared tile in workgroup order.
+// Work split: the grid fills the CUs once; each workgroup takes whole tiles
+// for as many full rounds as there are, then (stream-K) an equal run of the
+// remaining tiles' (tile, K block) units in tile order, as one segment per
+// tile it touches.  A segment covering all blocks of its tile stores the
+// result; any other stores an fp32 partial, and k_gemm_fix adds the
+// partials of each shared tile in workgroup order.
 // Operand layouts (gfx950, 32x32x16 bf16): lane l supplies A[l%32][8(l/32)+j]
 // and B[8(l/32)+j][l%32], j = 0..7; result register r of lane l is
 // D[8(r/4) + 4(l/32) + r%4][l%32].
