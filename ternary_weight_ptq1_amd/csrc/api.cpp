@@ -271,6 +271,18 @@ ProfEvents &prof_events()
     thread_local ProfEvents ev;
     return ev;
 }
+
+hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<uint64_t> &done_mask)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+    if (bit != 0 && (done_mask.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done_mask.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 }  // namespace ptq1
 
 extern "C" {

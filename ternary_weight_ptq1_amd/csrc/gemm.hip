@@ -986,19 +986,15 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 }
 
 // Launches one GEMM kernel instance (dynamic LDS above the 64 KB default is
-// enabled once per instance), with the profiling events attached to the
-// dispatch when a caller armed them.
+// enabled once per instance and device), with the profiling events attached
+// to the dispatch when a caller armed them.
 template <int WM, int WN, int TM, int TN, int PD>
 static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 {
-    static bool attr_set = false;
+    static std::atomic<uint64_t> lds_done{0};
     const auto kernel = k_gemm_mfma<WM, WN, TM, TN, PD>;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), kGemmLds, lds_done);
+    if (e != hipSuccess) return e;
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
         hipExtLaunchKernelGGL(kernel, grid, dim3(64 * WM * WN), static_cast<uint32_t>(kGemmLds), s, pe.start,
@@ -1013,14 +1009,10 @@ static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 template <int TM, int PD, int LR>
 static hipError_t gemm_rd_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 {
-    static bool attr_set = false;
+    static std::atomic<uint64_t> lds_done{0};
     const auto kernel = k_gemm_rd<TM, PD, LR>;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kRdLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), kRdLds, lds_done);
+    if (e != hipSuccess) return e;
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
         hipExtLaunchKernelGGL(kernel, grid, dim3(kRdThreads), static_cast<uint32_t>(kRdLds), s, pe.start, pe.stop, 0u,

@@ -467,14 +467,11 @@ size_t lut_part_floats(int64_t n, int nmat, int64_t k) { return static_cast<size
 template <int U>
 static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
 {
-    static bool attr_done = false;
+    static std::atomic<uint64_t> lds_done{0};
     const size_t lds = kLutTableBytes + kLutSliceW * sizeof(float);
-    if (!attr_done) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_matvec_lut<U>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    const hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&k_matvec_lut<U>), static_cast<int>(lds), lds_done);
+    if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(chunks));
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {

@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstddef>
+#include <atomic>
 #include <cstdint>
 
 namespace ptq1 {
@@ -16,6 +17,10 @@ struct ProfEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 ProfEvents &prof_events();  // per host thread
+
+// Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once
+// per device (bit d of done_mask; calls that race set the same value).
+hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<uint64_t> &done_mask);
 
 hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
                        uint8_t *blocks, hipStream_t s);
