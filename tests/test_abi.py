@@ -173,3 +173,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         P.lib()
+
+
+def test_empty_calls_enqueue_nothing():
+    """Zero rows or tokens: every entry point returns PTQ1_OK without touching
+    the (fake) device pointers and without a workspace."""
+    B, X, Y, WS, S = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400, 500))
+    assert L().ptq1_gemm(B, 17408, 5120, X, 0, S, Y, WS, 0, None) == 0
+    assert L().ptq1_matvec(B, 0, 5120, X, S, None, Y, WS, 0, None) == 0
+    assert L().ptq1_gate_up(B, B, 0, 5120, X, S, Y, Y, WS, 0, None) == 0
+    assert L().ptq1_ffn_block(X, Y, 0, 5120, 17408, B, B, B, S, 0.0, WS, 0, None) == 0
+    assert L().hadamard_unrotate_rows(X, 100, 1024, None, 0, S, Y, None) == 0
+    assert L().ptq1_swiglu(X, X, Y, 0, None) == 0
+    assert L().ptq1_dequant(B, 0, 128, Y, None) == 0
