@@ -123,6 +123,43 @@ def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     return 0
 
 
+def ffn_only(args, torch, synth, sdev, P, dev) -> int:
+    """One 27B-shaped FFN block at batch M alone (for kernel traces): --steps
+    calls replayed from a HIP graph after --warmup eager ones."""
+    m = args.ffn_only
+    w = [P.ptq1_tile(P.ptq1_pack(sdev.trits(4, tr, n, k), sdev.scales(4, sc, n, k // 128)), n, k)
+         for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
+                              (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
+                              (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F))]
+    x = torch.from_numpy(synth.activations(4, m, D)).to(dev)
+    sg = torch.from_numpy(synth.signs(4)).to(dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(P.workspace_bytes("ffn", m, D, F), dtype=torch.uint8, device=dev)
+
+    def call():
+        P.ptq1_ffn_block(x, w[0], w[1], w[2], sg, D, F, rms_eps=1e-6, out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    print(json.dumps({"workload": f"FFN block {m} x {D} -> {F} -> {D} (PTQ1_0), HIP graph", "us_per_layer": us,
+                      "weight_GB/s": LAYER_WEIGHT_BYTES / (us * 1e-6) / 1e9}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +172,9 @@ def main() -> int:
     ap.add_argument("--gemm-only", type=int, default=0, metavar="M",
                     help="profiling aid: run the prefill GEMM (M x 5120 -> 17408) --steps times, print its "
                          "kernel time, and exit")
+    ap.add_argument("--ffn-only", type=int, default=0, metavar="M",
+                    help="profiling aid: replay one FFN block at batch M --steps times from a HIP graph, print "
+                         "its time per layer, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded path is a "
@@ -155,6 +195,8 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     if args.gemm_only > 0:
         return gemm_only(args, torch, synth, sdev, P, dev)
+    if args.ffn_only > 0:
+        return ffn_only(args, torch, synth, sdev, P, dev)
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
