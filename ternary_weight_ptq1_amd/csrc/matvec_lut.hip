@@ -40,10 +40,16 @@
 //     formed, see lut_fwht256), all threads build the table, and each of the 8 waves
 //     processes U units (U is a template parameter chosen per launch so the
 //     grid fits two workgroups per CU) with kLutDepth units of weights in
-//     flight; a lane reads its 28-byte block with two wide loads and rotates
-//     its 7 dwords (and the byte order within a dword) by a lane-dependent
-//     amount so the 32 lanes of a half-wave (16 rows x 2 blocks) spread over
-//     LDS banks;
+//     flight (one requested before x, so that x is not queued behind a
+//     chip-wide burst of weight requests); a lane reads its 28-byte block
+//     with two wide loads and rotates its 7 dwords (and the byte order within
+//     a dword) by a lane-dependent amount so the 32 lanes of a half-wave
+//     (16 rows x 2 blocks) spread over LDS banks.  With per-lane dword
+//     rotations every lookup still meets a 2-way bank conflict (at most one
+//     of a lane's seven dword positions can be conflict-free: the two
+//     blocks' 56 slots share 32 banks); general per-lane permutations would
+//     avoid a third of the conflicts but cost more in loads or VALU moves
+//     than they save, so rotations stay;
 //   - a unit's 2 block partials (times their fp16 scales) are summed across
 //     neighbouring lanes (one DPP move) and stored as split-K partials
 //     part[slice][matrix][row]; a second kernel sums each row's partials in
@@ -73,6 +79,7 @@ constexpr int kLutBuildPer = 256 / kLutBuildRanges;    // byte values per thread
 constexpr int kLutRows = 32;                           // rows per unit
 constexpr int kLutTableBytes = 65536;                  // 256 byte values x 64 slot columns x fp32
 constexpr int kLutDepth = 3;                           // units of weights in flight per wave
+constexpr int kLutEarly = 1;                           // of which requested before x arrives
 static_assert(kLutRows == kTileRows && kLutBlocks == kTileBlocks, "a unit is one tile");
 static_assert(kLutRows * kLutBlocks == kWave, "one block per lane");
 
@@ -308,12 +315,17 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 2. weights of this wave's first kLutDepth units (the rest are
-    // requested one unit ahead of use during the lookups, so a wave never
-    // has more than kLutDepth units in flight and reaches the table barrier
-    // without waiting for the memory queue): the lane's 28-byte block with
-    // two wide loads (16 + 12 bytes; blocks are only dword-aligned, which
-    // gfx950 global loads accept) at a wave-uniform tile base.
+    // ---- 2. weights of this wave's first kLutEarly units; units up to
+    // kLutDepth follow once x has arrived (after the first barrier) and the
+    // rest one unit ahead of use during the lookups, so a wave never has more
+    // than kLutDepth units in flight and reaches each barrier without waiting
+    // for the memory queue.  Requests are served roughly in arrival order:
+    // with all kLutDepth units requested at entry (22 MB over the chip at
+    // 17408 x 5120 x 2), x's loads queued behind them and arrived about
+    // 0.7 us later; one unit per wave (7 MB) still keeps HBM busy meanwhile.
+    // A lane reads its 28-byte block with two wide loads (16 + 12 bytes;
+    // blocks are only dword-aligned, which gfx950 global loads accept) at a
+    // wave-uniform tile base.
     uint32_t dat[U][kBlockDwords];
     auto unit_of = [&](int i) { return u0 + wave + static_cast<int64_t>(kLutWaves) * i; };
     auto issue = [&](int i) {
@@ -330,7 +342,7 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z;
     };
 #pragma unroll
-    for (int i = 0; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);
+    for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
@@ -357,6 +369,10 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         }
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = kLutEarly; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);  // in flight during the build
+    __builtin_amdgcn_sched_barrier(0);
     // ---- 4. table: thread = (slot, 32-value range of the byte)
     {
         const int bq = tid >> 6;  // 0 .. kLutBuildRanges - 1
