@@ -125,6 +125,7 @@ struct LutArgs {
     int64_t n, k;            // rows per matrix, K
     int nmat, nslices;
     int64_t groups;          // ceil(n / 32)
+    int per_wg;              // units of a slice per workgroup (the last workgroup of a slice may get fewer)
     const float *x, *signs;  // x [k], rotated here when signs != nullptr
     float *part;             // [nslices][nmat][n]
 };
@@ -443,23 +444,22 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     }
 }
 
-// Slice s owns workgroups [floor(s G / ns), floor((s + 1) G / ns)) of the
-// G launched (two per CU, G >= ns), so every workgroup has one slice and
-// one table, and each takes an equal part of that slice's units: no CU holds
-// twice the work of another, and no workgroup builds two tables.
+// Grid (workgroups per slice, slices): workgroup (c, s) owns slice s and
+// its units [c per_wg, min((c + 1) per_wg, units per slice)), so every
+// workgroup has one slice and one table and none holds more than per_wg
+// units.  The grid shape carries the partition: no division at entry (the
+// 64-bit divisions of an even split cost a dependent chain of scalar and
+// reciprocal steps before the first load could be issued).
 template <int U>
 __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 waves per SIMD (1024 threads per CU)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     float *tab = reinterpret_cast<float *>(lds);                 // 64 KB table
     float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);  // 256 floats
-    const int64_t per_slice = static_cast<int64_t>(a.nmat) * a.groups;
-    const int64_t G = gridDim.x, ns = a.nslices, w = blockIdx.x;
-    const int s = static_cast<int>(((w + 1) * ns - 1) / G);
-    const int64_t c_lo = static_cast<int64_t>(s) * G / ns, c_hi = (static_cast<int64_t>(s) + 1) * G / ns;
-    const int64_t c = w - c_lo, cs = c_hi - c_lo;
-    const int64_t u0 = c * per_slice / cs, u1 = (c + 1) * per_slice / cs;
-    if (u0 < u1) lut_segment<U>(a, tab, xs, s, u0, u1);  // workgroup-uniform
+    const int per_slice = a.nmat * static_cast<int>(a.groups);  // rows < 2^20 (checked by the caller)
+    const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
+    const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
+    if (u0 < u1) lut_segment<U>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);  // workgroup-uniform
 }
 
 static int device_cus()
@@ -488,7 +488,7 @@ static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
     const hipError_t e =
         allow_dynamic_lds(reinterpret_cast<const void *>(&k_matvec_lut<U>), static_cast<int>(lds), lds_done);
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(chunks));
+    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.nslices));
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
         hipExtLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
@@ -515,30 +515,32 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.x = x;
     a.signs = signs;
     a.part = part;
-    // two workgroups per CU (at least one per slice and at most one per 8
-    // units), each slice's units split evenly over its workgroups; U = units
-    // per wave of the largest part
+    // up to two workgroups per CU (at most one per 8 units), the same number
+    // cs of workgroups for every slice, each taking per_wg = ceil(units / cs)
+    // consecutive units; U = units per wave of a full workgroup
     const int64_t per_slice = static_cast<int64_t>(nmat) * a.groups;
     const int64_t total = per_slice * a.nslices;
     const int cus = device_cus();
     int64_t wgs = kLutWgPerCu * static_cast<int64_t>(cus);
     if (wgs > total / kLutWaves) wgs = total / kLutWaves;
-    if (wgs < a.nslices) wgs = a.nslices;
+    int64_t cs = wgs / a.nslices;
+    if (cs < 1) cs = 1;
     static const int kUs[] = {1, 2, 3, 4, 6, 8};
     int U = 0;
+    int64_t per_wg = 0;
     for (;;) {
-        const int64_t fewest = wgs / a.nslices;                        // workgroups of the poorest slice
-        const int64_t part = (per_slice + fewest - 1) / fewest;        // its units per workgroup
-        const int64_t need = (part + kLutWaves - 1) / kLutWaves;
+        per_wg = (per_slice + cs - 1) / cs;
+        const int64_t need = (per_wg + kLutWaves - 1) / kLutWaves;
         for (int cand : kUs)
             if (cand >= need) {
                 U = cand;
                 break;
             }
         if (U != 0) break;
-        wgs += a.nslices;  // parts above 64 units: more workgroups per slice
+        ++cs;  // parts above 64 units: more workgroups per slice
     }
-    const int64_t chunks = wgs;
+    a.per_wg = static_cast<int>(per_wg);
+    const int64_t chunks = (per_slice + per_wg - 1) / per_wg;  // workgroups per slice that get units
     switch (U) {
         case 1: return lut_launch<1>(a, chunks, s);
         case 2: return lut_launch<2>(a, chunks, s);
