@@ -346,6 +346,40 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- per-lane lookup constants, formed while x is in flight (they
+    // depend on neither x nor the table; formed after the table barrier they
+    // held every wave of a SIMD for ~150 VALU operations while the LDS
+    // idled).  After the rotation, register dword j holds dword
+    // (j + rho) mod 7 of the block; the address of the lookup for its byte c
+    // is byte << 8 | slot << 2 with slot = 28 blk + 4 ((j + rho) mod 7) +
+    // ((c + sig) & 3); the four slot bytes of a dword are packed in one
+    // register (byte c) and v_perm_b32 inserts the data byte (selector:
+    // byte 0 <- P byte c, byte 1 <- data byte (c + sig) & 3, 0, 0).  The
+    // packed form is the dword's base slot replicated into four bytes plus
+    // the per-lane byte offsets (no carries: slot << 2 < 256).
+    uint32_t P[kBlockDwords];
+    uint32_t S[4];
+    uint32_t boff = 0;  // byte c: ((c + sig) & 3) << 2
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t e = static_cast<uint32_t>((c + sig) & 3);
+        S[c] = 0x0C0C0000u | (e << 8) | static_cast<uint32_t>(4 + c);
+        boff |= (e << 2) << (8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < kBlockDwords; ++j) {
+        const int q = j + rho < kBlockDwords ? j + rho : j + rho - kBlockDwords;
+        const uint32_t base = static_cast<uint32_t>(kBlockBytes * blk_l + 4 * q) << 2;
+        P[j] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;  // base in all four bytes
+    }
+    // opaque from here on: otherwise the compiler recomputes them next to
+    // their uses, after the table barrier
+#pragma unroll
+    for (int j = 0; j < kBlockDwords; ++j) asm volatile("" : "+v"(P[j]));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
     if (wave == 0) {
         if (a.signs != nullptr) {
@@ -389,33 +423,14 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
             lut_build_dispatch<0>(bq, tab, slot, xv);
         }
     }
+    // unit 0 (requested at entry, long arrived) is rotated before the
+    // barrier, so the lookups start right after it; its scale dword is kept
+    // from before the rotation
+    const uint32_t scale_w0 = dat[0][kBlockDwords - 1];
+    lut_rotate(dat[0], rho);
     __syncthreads();
 
-    // ---- 5. per-lane lookup constants.  After the rotation, register dword
-    // j holds dword (j + rho) mod 7 of the block; the address of the lookup
-    // for its byte c is byte << 8 | slot << 2; the four slot bytes of a
-    // dword are packed in one register (byte c) and v_perm_b32 inserts the
-    // data byte (selector: byte 0 <- P byte c, byte 1 <- data byte e, 0, 0).
-    uint32_t P[kBlockDwords];
-    uint32_t S[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t e = static_cast<uint32_t>((c + sig) & 3);
-        S[c] = 0x0C0C0000u | (e << 8) | static_cast<uint32_t>(4 + c);
-    }
-#pragma unroll
-    for (int j = 0; j < kBlockDwords; ++j) {
-        const int q = (j + rho) % kBlockDwords;
-        uint32_t packed = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int slot = kBlockBytes * blk_l + 4 * q + ((c + sig) & 3);
-            packed |= (static_cast<uint32_t>(slot) << 2) << (8 * c);
-        }
-        P[j] = packed;
-    }
-
-    // ---- 6. lookups, scale, 2-lane reduction, partial store
+    // ---- 5. lookups, scale, 2-lane reduction, partial store
     typedef __attribute__((address_space(3))) const float lds_f32;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -425,8 +440,9 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         const LutUnit u = lut_unit(a, un);
         const int r = u.grp * kLutRows + row_l;
         const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
-        const float scale = live ? half_bits_to_float(dat[i][kBlockDwords - 1] >> 16) : 0.0f;
-        lut_rotate(dat[i], rho);
+        const uint32_t scale_w = i == 0 ? scale_w0 : dat[i][kBlockDwords - 1];  // compile-time choice
+        const float scale = live ? half_bits_to_float(scale_w >> 16) : 0.0f;
+        if (i > 0) lut_rotate(dat[i], rho);
         float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
         for (int j = 0; j < kBlockDwords; ++j) {
