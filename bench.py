@@ -346,6 +346,19 @@ def main() -> int:
         ms0 = timed(lambda i: P.ptq1_matvec(w0, 1024, 1024, x0, s0, out=y0, ws=ws0), 500, 50)
         breakdown["matvec_1024_hot"] = {"us": ms0 * 1e3}
 
+        # measured streaming-read rate of this GPU, for context beside the
+        # 8 TB/s published peak: torch row sums over 2 GiB of fp32 (8x the
+        # Infinity Cache) viewed as [2^19, 1024], a read-only kernel with one
+        # output per 4 KB row (the fastest of the plain torch reductions and
+        # copies tried: a full sum reads at about 4 TB/s, a copy at 4.9)
+        big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        ms_rd = timed(lambda i: big.view(-1, 1024).sum(dim=1), 20, 3)
+        rd_gbs = big.numel() * 4 / (ms_rd * 1e-3) / 1e9
+        breakdown["hbm_read_measured"] = {"GB/s": rd_gbs, "how": "torch row sums over [2^19, 1024] fp32 (2 GiB), 20 calls",
+                                          "lut_gate_up_frac_of_it": lut_gu_gbs / rd_gbs}
+        del big
+        torch.cuda.empty_cache()
+
         # prefill GEMM (configuration 3)
         wq = P.ptq1_tile(P.ptq1_pack(sdev.trits(3, synth.S_W_TRITS, F, D),
                                      sdev.scales(3, synth.S_W_SCALES, F, D // 128)), F, D)
