@@ -70,9 +70,18 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const int64_t ch = blockIdx.x - row * cpr;
     const int lane = threadIdx.x;
     const int64_t e0 = ch * kHadamard;  // first element of this chunk in the row
-    // chunk values first (clamped addresses, no branches around the loads)
-    float v[kRotPerLane];
+    // Every load is requested before any arithmetic (clamped addresses, no
+    // branches around the loads but wave-uniform ones): the chunk of x or of
+    // g and u, the signs and the first batch of the row for its mean square.
+    // Requested one after another's use, they cost a dependent round trip to
+    // memory each.
+    constexpr int kQ = 24;  // 16-byte loads of the row per lane per batch (one batch for k <= 6144)
+    float v[kRotPerLane], uw[kRotPerLane], sg[kRotPerLane];
+    float4 xv[kQ];
     const float *src0 = x != nullptr ? x : g;
+    const bool rms = x != nullptr && rms_eps > 0.0f;
+    const float4 *xr = reinterpret_cast<const float4 *>(src0 + row * k);
+    const int64_t k4 = k / 4;  // k is a multiple of 128
 #pragma unroll
     for (int j = 0; j < kRotPerLane; ++j) {
         const int64_t e = e0 + lane + kWave * j;
@@ -82,26 +91,41 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) {
             const int64_t e = e0 + lane + kWave * j;
-            const float uv = u[row * k + (e < k ? e : k - 1)];
-            v[j] = v[j] / (1.0f + expf(-v[j])) * uv;
+            uw[j] = u[row * k + (e < k ? e : k - 1)];
         }
+    }
+    if (signs != nullptr) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) sg[j] = signs[lane + kWave * j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) sg[j] = 1.0f;
+    }
+    if (rms) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int64_t i = q * kWave + lane;
+            xv[q] = xr[i < k4 ? i : k4 - 1];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (x == nullptr) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] = v[j] / (1.0f + expf(-v[j])) * uw[j];
     }
 #pragma unroll
     for (int j = 0; j < kRotPerLane; ++j)
         if (e0 + lane + kWave * j >= k) v[j] = 0.0f;
-    if (x != nullptr && rms_eps > 0.0f) {
-        // the row's mean square: 16-byte loads (k is a multiple of 128),
-        // 24 in flight per lane (one round trip for k <= 6144)
-        constexpr int kQ = 24;
-        const float4 *xr = reinterpret_cast<const float4 *>(x + row * k);
-        const int64_t k4 = k / 4;
+    if (rms) {
+        // the row's mean square, batch by batch (the first one requested above)
         float sq[kQ] = {};
         for (int64_t i0 = 0; i0 < k4; i0 += kQ * kWave) {
-            float4 xv[kQ];
+            if (i0 > 0) {
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-                const int64_t i = i0 + q * kWave + lane;
-                xv[q] = xr[i < k4 ? i : k4 - 1];
+                for (int q = 0; q < kQ; ++q) {
+                    const int64_t i = i0 + q * kWave + lane;
+                    xv[q] = xr[i < k4 ? i : k4 - 1];
+                }
             }
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
@@ -123,9 +147,7 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     }
     if (signs != nullptr) {
 #pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] *= signs[lane + kWave * j];
-    }
-    if (signs != nullptr) {
+        for (int j = 0; j < kRotPerLane; ++j) v[j] *= sg[j];
         fwht1024_wave(v);
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) v[j] *= (1.0f / 32.0f);
