@@ -929,6 +929,17 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
     if (r >= a.prow || row >= a.m || col >= rows) return;
     const float *p0 = a.part + r * kGemmBN + c;
     const int64_t seg = 2 * a.prow * kGemmBN;  // floats per workgroup (first and last partial)
+    // the residual of the four columns is requested with the partials
+    // (clamped indices; used only for columns of y0): requested after the
+    // sum it would add dependent round trips to memory
+    float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.residual != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t cj = col + j < a.n0 ? col + j : a.n0 - 1;
+            res[j] = a.residual[row * a.n0 + cj];
+        }
+    }
     f32x4 v = *reinterpret_cast<const f32x4 *>(p0 + w_lo * seg + k_lo * a.prow * kGemmBN);
     // the later workgroups' first partials, eight requests in flight at a
     // time (clamped indices, no branch around the loads), added in order
@@ -946,8 +957,7 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
         const int64_t cj = col + j;
         if (cj >= rows) break;
         if (cj < a.n0) {
-            const int64_t o = row * a.n0 + cj;
-            a.y0[o] = a.residual ? a.residual[o] + v[j] : v[j];
+            a.y0[row * a.n0 + cj] = a.residual ? res[j] + v[j] : v[j];
         } else {
             a.y1[row * a.n1 + (cj - a.n0)] = v[j];
         }

@@ -591,6 +591,9 @@ __global__ void __launch_bounds__(kSumThreads) k_lut_sum_rows(const float *__res
     const int64_t rc = r < n ? r : n - 1;
     const int q_lo = static_cast<int>(static_cast<int64_t>(j) * ns / T);
     const int q_hi = static_cast<int>(static_cast<int64_t>(j + 1) * ns / T);
+    // the residual is requested with the partials (after the sum it would
+    // cost a second round trip to memory)
+    const float res = residual != nullptr ? residual[rc] : 0.0f;
     float t = 0.0f;
     for (int q0 = q_lo; q0 < q_hi; q0 += kSumPer) {
         float v[kSumPer];
@@ -608,7 +611,7 @@ __global__ void __launch_bounds__(kSumThreads) k_lut_sum_rows(const float *__res
         const float o = __shfl_xor(t, h, kWave);
         t = (lane & h) ? o + t : t + o;  // lower slice range first: the same order in every lane
     }
-    if (j == 0 && r < n) y[r] = residual ? residual[r] + t : t;
+    if (j == 0 && r < n) y[r] = residual ? res + t : t;
 }
 
 hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
