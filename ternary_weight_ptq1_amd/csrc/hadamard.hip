@@ -40,6 +40,11 @@ __global__ void __launch_bounds__(kRotThreads) k_unrotate_rows(const float *__re
     const int64_t row = blockIdx.x / cpr;
     const int64_t ch = blockIdx.x - row * cpr;
     const int lane = threadIdx.x;
+    // the signs are requested before the id (the row's address waits for
+    // the id; loaded after the rotation they cost a third round trip)
+    float sg[kRotPerLane];
+#pragma unroll
+    for (int j = 0; j < kRotPerLane; ++j) sg[j] = signs[lane + kWave * j];
     const int64_t id = ids ? static_cast<int64_t>(ids[row]) : row;
     float *dst = out + row * d + ch * kHadamard;
     if (id < 0 || id >= n_table) {  // out-of-range id: a NaN row, no access
@@ -54,7 +59,7 @@ __global__ void __launch_bounds__(kRotThreads) k_unrotate_rows(const float *__re
     fwht1024_wave(v);
 #pragma unroll
     for (int j = 0; j < kRotPerLane; ++j)
-        dst[lane + kWave * j] = v[j] * (1.0f / 32.0f) * signs[lane + kWave * j];
+        dst[lane + kWave * j] = v[j] * (1.0f / 32.0f) * sg[j];
 }
 
 hipError_t launch_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs,
