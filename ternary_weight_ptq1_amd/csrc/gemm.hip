@@ -657,7 +657,8 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     const int64_t rows = a.n0 + a.n1;
 
     // ---- table: entry b, copy c at b * 256 + c * 8
-    {
+    // (built in the first segment, once its first loads are in flight)
+    auto build_table = [&]() {
         const uint32_t b = static_cast<uint32_t>(tid);
         uint32_t r = b, h[5];
 #pragma unroll
@@ -671,9 +672,8 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
 #pragma unroll 8
         for (int i = 0; i < kRdTabCopies; ++i)
             *reinterpret_cast<gm_u32x2 *>(lds + b * 256 + ((b + i) & (kRdTabCopies - 1)) * 8) = e;
-    }
-
-    __syncthreads();  // table built
+    };
+    bool table_built = false;  // workgroup-uniform
     const uint32_t lc = static_cast<uint32_t>(lane & (kRdTabCopies - 1)) << 3;
 
     // ---- work split as in k_gemm_mfma: whole tiles first, then an equal
@@ -814,6 +814,11 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
         gm_u32x4 afr[kAr][TM];
 #pragma unroll
         for (int st = 0; st < kAr; ++st) load_a(afr[st], blk(0), st);
+        if (!table_built) {  // first segment: the table is built while its loads are in flight
+            build_table();
+            __syncthreads();
+            table_built = true;
+        }
         Ent ent[2];
         tab_reads(ring[0], ent[0]);
         load_w(ring[0], blk(PD));
