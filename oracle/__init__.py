@@ -66,7 +66,7 @@ def lib():
         L.orc_gemm.argtypes = [p, i64, i64, p, i64, p]
         L.orc_swiglu.argtypes = [p, p, i64, p]
         L.orc_rms_scale.argtypes = [p, i64, i64, C.c_double, p]
-        L.orc_ffn_block.argtypes = [p, i64, i64, i64, p, p, p, p, C.c_double, p]
+        L.orc_ffn_block.argtypes = [p, i64, i64, i64, p, p, p, p, C.c_double, p, p]
         L.orc_set_threads.argtypes = [C.c_int]
         for fn in ("orc_pack", "orc_unpack", "orc_dequant", "orc_rotate", "orc_unrotate",
                    "orc_gemm_rows", "orc_gemm", "orc_ffn_block", "orc_threads",
@@ -199,13 +199,17 @@ def rms_scale(x: np.ndarray, eps: float) -> np.ndarray:
 
 
 def ffn_block(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
-              signs: np.ndarray, d: int, f: int, rms_eps: float) -> np.ndarray:
+              signs: np.ndarray, d: int, f: int, rms_eps: float, gain: np.ndarray | None = None) -> np.ndarray:
+    """x + Wd R(silu(Wg R(a gain x)) * (Wu R(a gain x))): a = RMS scale of x (1 when rms_eps <= 0),
+    gain [d] the norm's per-channel weight (None: all ones)."""
     x2 = _f64(x).reshape(-1, d)
     m = x2.shape[0]
     out = np.zeros_like(x2)
     args = [np.ascontiguousarray(w, dtype=np.uint8) for w in (wg, wu, wd)]
+    gv = None if gain is None else _f64(gain).reshape(d)
     _check(lib().orc_ffn_block(_ptr(x2), m, d, f, _ptr(args[0]), _ptr(args[1]), _ptr(args[2]),
-                               _ptr(_f64(signs)), float(rms_eps), _ptr(out)), "ffn_block")
+                               _ptr(_f64(signs)), float(rms_eps), _ptr(gv) if gv is not None else None,
+                               _ptr(out)), "ffn_block")
     return out
 
 

@@ -296,14 +296,15 @@ void orc_rms_scale(const double *x, int64_t m, int64_t d, double eps, double *a)
 }
 
 /* One feed-forward block on x [m][d] (tokens in rows):
- *   a  = RMS scale of x (or 1)
- *   xr = rotate(a * x);  g = Wg xr;  u = Wu xr   (Wg, Wu: [f][d] packed)
+ *   a  = RMS scale of x (or 1); gain [d] the norm's per-channel weight (NULL: 1)
+ *   xr = rotate(a * gain * x);  g = Wg xr;  u = Wu xr   (Wg, Wu: [f][d] packed)
  *   h  = silu(g) * u;    hr = rotate(h)
  *   x_out = x + Wd hr                            (Wd: [d][f] packed)
- * [B] rotate before every folded matmul; [S] gate, SwiGLU, down; [G] add. */
+ * [B] rotate before every folded matmul; [S] gate, SwiGLU, down; [G] add,
+ * and the layer's norm with its own weight ahead of the rotation (Level 4). */
 int orc_ffn_block(const double *x, int64_t m, int64_t d, int64_t f,
                   const uint8_t *wg, const uint8_t *wu, const uint8_t *wd,
-                  const double *signs, double rms_eps, double *x_out)
+                  const double *signs, double rms_eps, const double *gain, double *x_out)
 {
     if (m < 0 || d % ORC_HAD || f % ORC_HAD) return -1;
     double *a = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
@@ -317,7 +318,7 @@ int orc_ffn_block(const double *x, int64_t m, int64_t d, int64_t f,
     int rc = 0;
     orc_rms_scale(x, m, d, rms_eps, a);
     for (int64_t i = 0; i < m; ++i)
-        for (int64_t q = 0; q < d; ++q) xa[i * d + q] = a[i] * x[i * d + q];
+        for (int64_t q = 0; q < d; ++q) xa[i * d + q] = a[i] * (gain ? gain[q] : 1.0) * x[i * d + q];
     rc |= orc_rotate(xa, m, d, signs, xr);
     rc |= orc_gemm(wg, f, d, xr, m, g);
     rc |= orc_gemm(wu, f, d, xr, m, u);

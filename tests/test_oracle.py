@@ -313,28 +313,40 @@ def _ffn_weights(seed, d, f):
 
 def test_ffn_block_composition():
     """[page 1, "What Bonsai is" + "Speed, and where it goes"; page 2, Level 4]:
-    x + Wd R(silu(Wg R(a x)) * (Wu R(a x))), composed here from numpy matmuls
-    on dequantised weights and the textbook FWHT."""
+    x + Wd R(silu(Wg R(a gain x)) * (Wu R(a gain x))), composed here from numpy
+    matmuls on dequantised weights and the textbook FWHT; the RMS scale a
+    comes from x itself, the per-channel gain (the layer's norm weight) scales
+    the input of the rotation."""
     from scipy.special import expit
 
     d, f, m = 1024, 2048, 2
     wg, wu, wd = _ffn_weights(3, d, f)
     s = synth.signs(3)
     x = synth.activations(3, m, d).astype(np.float64)
-    for eps in (0.0, 1e-6):
-        out = oracle.ffn_block(x, wg, wu, wd, s, d, f, eps)
+    gain = 0.5 + synth.gauss(3, 7, d).astype(np.float64) ** 2
+    for eps, gv in ((0.0, None), (1e-6, None), (1e-6, gain), (0.0, gain)):
+        out = oracle.ffn_block(x, wg, wu, wd, s, d, f, eps, gain=gv)
         a = np.ones(m) if eps <= 0 else 1.0 / np.sqrt((x * x).mean(axis=1) + eps)
 
         def rot(v):
             return np.stack([np.concatenate([_fwht_textbook(s * c) / 32.0
                                              for c in row.reshape(-1, 1024)]) for row in v])
 
-        xr = rot(a[:, None] * x)
+        xr = rot(a[:, None] * (np.ones(d) if gv is None else gv)[None, :] * x)
         g = xr @ oracle.dequant(wg, f, d).T
         u = xr @ oracle.dequant(wu, f, d).T
         h = g * expit(g) * u
         ref = x + rot(h) @ oracle.dequant(wd, d, f).T
         np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-9)
+
+
+def test_ffn_block_unit_gain_is_no_gain():
+    d, f = 1024, 1024
+    wg, wu, wd = _ffn_weights(5, d, f)
+    x = synth.activations(5, 2, d).astype(np.float64)
+    s = synth.signs(5)
+    np.testing.assert_array_equal(oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6, gain=np.ones(d)),
+                                  oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6))
 
 
 def test_ffn_block_zero_down_is_identity():
