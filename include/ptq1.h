@@ -210,19 +210,23 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
                       hipStream_t stream);
 
 /* One feed-forward block on m tokens ("Speed, and where it goes": the whole
- * block -- rotation, gate, SwiGLU, down -- enqueued as one sequence):
+ * block -- rotation, gate, SwiGLU, down -- enqueued as one sequence; "Why I
+ * Am Building Another Inference Engine", Level 4: the layer's norm, with its
+ * own weight, ahead of the rotation):
  *   a     = (mean(x^2) + rms_eps)^(-1/2) per token if rms_eps > 0, else 1
- *   g, u  = a * (W_gate R x), a * (W_up R x)      (W_gate, W_up tiled [f][d])
+ *   xn    = a * rms_gain * x                      (rms_gain fp32 [d], NULL: 1)
+ *   g, u  = W_gate R xn, W_up R xn                (W_gate, W_up tiled [f][d])
  *   h     = silu(g) * u
  *   x_out = x + W_down R h                        (W_down tiled [d][f])
  * m == 1 runs the fp32 matvec path, m >= 2 the bf16-MFMA GEMM path.
- * d % 1024 == 0, f % 1024 == 0; x_out may equal x.
+ * d % 1024 == 0, f % 1024 == 0; x_out may equal x; rms_gain, if given, is
+ * 16-byte aligned and overlaps neither x_out nor ws.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED. */
 size_t ptq1_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
 ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
                            const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
-                           const float *signs1024, float rms_eps, void *ws, size_t ws_bytes,
-                           hipStream_t stream);
+                           const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
  * next `count` launches of one kernel family (hipExtLaunchKernel: they take

@@ -61,7 +61,7 @@ _SIGS = {
     "ptq1_gemm_workspace_bytes": ([i64, i64, i64], sz),
     "ptq1_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
     "ptq1_ffn_workspace_bytes": ([i64, i64, i64], sz),
-    "ptq1_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, sz, p], C.c_int),
+    "ptq1_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
@@ -281,9 +281,12 @@ def ptq1_gemm(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: 
 def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                    signs1024: torch.Tensor, d: int, f: int, rms_eps: float = 0.0,
                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                   stream=None) -> torch.Tensor:
-    """x [m, d] -> x + W_down R(silu(a W_gate R x) * (a W_up R x)); out may be x."""
+                   stream=None, rms_gain: torch.Tensor | None = None) -> torch.Tensor:
+    """x [m, d] -> x + W_down R(silu(W_gate R xn) * (W_up R xn)), xn = a * rms_gain * x (a = RMS
+    scale of x when rms_eps > 0; rms_gain [d] or None); out may be x."""
     _dev(x, "x", torch.float32)
+    if rms_gain is not None:
+        _dev(rms_gain, "rms_gain", torch.float32)
     for w, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
         _dev(w, nm, torch.uint8)
     m = x.numel() // d if d else 0
@@ -292,7 +295,8 @@ def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_
     _dev(out, "x_out", torch.float32)
     ws, wsb = _ws(lib().ptq1_ffn_workspace_bytes(m, d, f), x.device, ws)
     _check("ptq1_ffn_block", lib().ptq1_ffn_block(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up),
-                                                  _ptr(w_down), _ptr(signs1024), float(rms_eps), _ptr(ws),
+                                                  _ptr(w_down), _ptr(signs1024), float(rms_eps),
+                                                  _ptr(rms_gain) if rms_gain is not None else None, _ptr(ws),
                                                   wsb, _stream(stream)))
     return out
 

@@ -477,7 +477,7 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
     if (empty) return ok();
     float *part = static_cast<float *>(ws);
     hipError_t e = profiled(kProfLut1, stream, [&] {
-        return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024, part, stream);
+        return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, signs1024, nullptr, part, stream);
     });
     if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
     return hip_status(e, "ptq1_matvec");
@@ -527,7 +527,7 @@ ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, 
     if (wgb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
     float *part = static_cast<float *>(ws);
     hipError_t e = profiled(kProfLut2, stream, [&] {
-        return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+        return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, nullptr, part, stream);
     });
     if (e == hipSuccess)
         e = ptq1::launch_lut_gate_up_sum(part, f, d, nullptr, 0, 0.0f, g, u, nullptr, stream);
@@ -577,7 +577,7 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
     char *w = static_cast<char *>(ws);
     uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
     float *part = reinterpret_cast<float *>(w + L.part);
-    hipError_t e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, k, signs1024, 0.0f, xf, stream);
+    hipError_t e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, k, signs1024, 0.0f, nullptr, xf, stream);
     if (e == hipSuccess)
         e = profiled(kProfGemm, stream, [&] {
             return ptq1::launch_gemm(plan, xf, m, tiled, n, nullptr, 0, y, nullptr, nullptr, part, stream);
@@ -595,8 +595,8 @@ size_t ptq1_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
 
 ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
                            const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
-                           const float *signs1024, float rms_eps, void *ws, size_t ws_bytes,
-                           hipStream_t stream)
+                           const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
+                           size_t ws_bytes, hipStream_t stream)
 {
     int64_t wgb, wub, wdb, md, xb, ob;
     if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
@@ -609,6 +609,11 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
     if (md == 0) return ok();
     PTQ1_TRY(check_floats(x, "x", md, &xb));
     PTQ1_TRY(check_signs(signs1024, true));
+    int64_t gb = 0;
+    if (rms_gain != nullptr) {
+        PTQ1_TRY(check_floats(rms_gain, "rms_gain", d, &gb));
+        if (overlaps(x_out, ob, rms_gain, gb)) return fail(PTQ1_ERR_ALIAS, "x_out overlaps rms_gain");
+    }
     if (x_out != x && overlaps(x_out, ob, x, xb)) return fail(PTQ1_ERR_ALIAS, "x_out partially overlaps x");
     if (overlaps(x_out, ob, w_gate, wgb) || overlaps(x_out, ob, w_up, wub) || overlaps(x_out, ob, w_down, wdb))
         return fail(PTQ1_ERR_ALIAS, "x_out overlaps a weight matrix");
@@ -617,6 +622,8 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
     PTQ1_TRY(check_ws(ws, ws_bytes, L.total, "ptq1_ffn_block"));
     if (overlaps(ws, (int64_t)L.total, x, xb) || overlaps(ws, (int64_t)L.total, x_out, ob))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps x or x_out");
+    if (rms_gain != nullptr && overlaps(ws, (int64_t)L.total, rms_gain, gb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps rms_gain");
     if (nseg_of(f) * 4 > kMaxGridY || nseg_of(d) * 4 > kMaxGridY)
         return fail(PTQ1_ERR_UNSUPPORTED, "d or f too large");
     if (m == 1 && (f > kMaxLutRows || d > kMaxLutRows))
@@ -630,14 +637,14 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
         float *part = reinterpret_cast<float *>(w + L.part);
         float *h = reinterpret_cast<float *>(w + L.hr);
         e = profiled(kProfLut2, stream, [&] {
-            return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, part, stream);
+            return ptq1::launch_matvec_lut(w_gate, w_up, 2, f, d, x, signs1024, rms_gain, part, stream);
         });
         if (e == hipSuccess)
             e = ptq1::launch_lut_gate_up_sum(part, f, d, rms_eps > 0.0f ? x : nullptr, d, rms_eps, nullptr, nullptr,
                                              h, stream);
         if (e == hipSuccess)
             e = profiled(kProfLut1, stream, [&] {
-                return ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, part, stream);
+                return ptq1::launch_matvec_lut(w_down, nullptr, 1, d, f, h, signs1024, nullptr, part, stream);
             });
         if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, d, f, x, x_out, stream);
     } else {
@@ -645,12 +652,12 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
         float *g = reinterpret_cast<float *>(w + L.g);
         float *u = reinterpret_cast<float *>(w + L.u);
         float *part = reinterpret_cast<float *>(w + L.part);
-        e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, d, signs1024, rms_eps, xf, stream);
+        e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, d, signs1024, rms_eps, rms_gain, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
                 return ptq1::launch_gemm(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream);
             });
-        if (e == hipSuccess) e = ptq1::launch_prep_frag(nullptr, g, u, m, f, signs1024, 0.0f, xf, stream);
+        if (e == hipSuccess) e = ptq1::launch_prep_frag(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
                 return ptq1::launch_gemm(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);

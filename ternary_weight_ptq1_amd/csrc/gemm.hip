@@ -50,7 +50,8 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 
 // ---------------------------------------------------------------------------
 // Activation prep: one wavefront per (row, 1024-chunk).
-//   input  = x (times the row's RMS scale when rms_eps > 0), or silu(g) * u
+//   input  = x (times the row's RMS scale when rms_eps > 0 and the per-channel
+//            gain when given), or silu(g) * u
 //   value  = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
 // Output: MFMA A fragments.  For 32-row group mt, block kb, step s (0..7)
 // and lane l the 16 bytes at element offset (((mt nb + kb) 8 + s) 64 + l) 8
@@ -62,7 +63,8 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
-    int64_t k, const float *__restrict__ signs, float rms_eps, uint16_t *__restrict__ xf)
+    int64_t k, const float *__restrict__ signs, float rms_eps, const float *__restrict__ gain,
+    uint16_t *__restrict__ xf)
 {
     __shared__ float st[kHadamard];
     const int64_t cpr = (k + kHadamard - 1) / kHadamard;  // == k / 1024 when signs are given
@@ -93,6 +95,12 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
             const int64_t e = e0 + lane + kWave * j;
             uw[j] = u[row * k + (e < k ? e : k - 1)];
         }
+    } else if (gain != nullptr) {  // the norm's per-channel weight (uw holds it on this path)
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) {
+            const int64_t e = e0 + lane + kWave * j;
+            uw[j] = gain[e < k ? e : k - 1];
+        }
     }
     if (signs != nullptr) {
 #pragma unroll
@@ -112,6 +120,9 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     if (x == nullptr) {
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) v[j] = v[j] / (1.0f + expf(-v[j])) * uw[j];
+    } else if (gain != nullptr) {
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] *= uw[j];
     }
 #pragma unroll
     for (int j = 0; j < kRotPerLane; ++j)
@@ -1013,12 +1024,12 @@ size_t gemm_part_floats(const GemmPlan &p)
 }
 
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                            const float *signs, float rms_eps, uint16_t *xf, hipStream_t s)
+                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s)
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
     hipLaunchKernelGGL(k_prep_frag, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u, k,
-                       signs, rms_eps, xf);
+                       signs, rms_eps, gain, xf);
     return hipGetLastError();
 }
 

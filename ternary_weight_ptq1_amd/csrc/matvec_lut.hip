@@ -127,6 +127,7 @@ struct LutArgs {
     int64_t groups;          // ceil(n / 32)
     int per_wg;              // units of a slice per workgroup (the last workgroup of a slice may get fewer)
     const float *x, *signs;  // x [k], rotated here when signs != nullptr
+    const float *gain;       // [k] or nullptr: x is used as gain * x (a norm's per-channel weight)
     float *part;             // [nslices][nmat][n]
 };
 
@@ -298,6 +299,7 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     // would wait for all of them.
     const int64_t c0 = (k0 / kHadamard) * kHadamard;  // 1024-chunk holding the slice
     float xv16[kRotPerLane], sv16[kRotPerLane];        // [4 c + k]: element 256 c + lane + 64 k of the chunk
+    float gv16[kRotPerLane];                           // the gain at the same elements (when given)
     if (wave == 0) {
         if (a.signs != nullptr) {
 #pragma unroll
@@ -306,11 +308,22 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
                 xv16[j] = a.x[c0 + e];
                 sv16[j] = a.signs[e];
             }
+            if (a.gain != nullptr) {
+#pragma unroll
+                for (int j = 0; j < kRotPerLane; ++j) gv16[j] = a.gain[c0 + kLutSliceW * (j >> 2) + lane + kWave * (j & 3)];
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < kRotPerLane / 4; ++j) {
                 const int e = lane + kWave * j;
                 xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];  // clamped; zeroed below
+            }
+            if (a.gain != nullptr) {
+#pragma unroll
+                for (int j = 0; j < kRotPerLane / 4; ++j) {
+                    const int e = lane + kWave * j;
+                    gv16[j] = a.gain[k0 + (e < kw ? e : kw - 1)];
+                }
             }
         }
     }
@@ -382,6 +395,11 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
 
     // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
     if (wave == 0) {
+        if (a.gain != nullptr) {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane; ++j)
+                if (a.signs != nullptr || j < kRotPerLane / 4) xv16[j] *= gv16[j];
+        }
         if (a.signs != nullptr) {
             const int part = static_cast<int>((k0 - c0) / kLutSliceW);  // 0..3: this slice's quarter
             const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
@@ -517,7 +535,7 @@ static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
 }
 
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, float *part, hipStream_t s)
+                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
     LutArgs a{};
@@ -530,6 +548,7 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.groups = (n + kLutRows - 1) / kLutRows;
     a.x = x;
     a.signs = signs;
+    a.gain = gain;
     a.part = part;
     // up to two workgroups per CU (at most one per 8 units), the same number
     // cs of workgroups for every slice, each taking per_wg = ceil(units / cs)

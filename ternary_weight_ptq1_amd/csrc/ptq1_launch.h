@@ -56,12 +56,12 @@ hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, 
 
 // Lookup-table decode matvec over tiled weights, split over 256-wide
 // K-slices: part[slice][matrix][row] (lut_part_floats floats) for one matrix
-// (nmat = 1) or two sharing x (nmat = 2); x rotated per 1024-chunk when
-// signs != nullptr, else used as given.
+// (nmat = 1) or two sharing x (nmat = 2); x (times gain [k], if given)
+// rotated per 1024-chunk when signs != nullptr, else used as given.
 int64_t lut_nslices(int64_t k);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, float *part, hipStream_t s);
+                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
 // y[r] = (residual ? residual[r] : 0) + sum over slices of part[s][r] (nmat = 1)
 hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
                                hipStream_t s);
@@ -84,10 +84,11 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k);
 size_t gemm_frag_elems(const GemmPlan &p, int64_t k);  // bf16 A fragments
 size_t gemm_part_floats(const GemmPlan &p);            // partial tiles of the work split
-// xf = bf16 MFMA A fragments of R (a * x) (rows < m only); a = RMS scale if
-// rms_eps > 0.  When g/u are given instead of x, the input is silu(g) * u.
+// xf = bf16 MFMA A fragments of R (a * gain * x) (rows < m only); a = RMS
+// scale of x if rms_eps > 0, gain [k] or nullptr (1).  When g/u are given
+// instead of x, the input is silu(g) * u (gain unused).
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                            const float *signs, float rms_eps, uint16_t *xf, hipStream_t s);
+                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s);
 // y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; rows of the
 // virtual matrix as in launch_matvec_part, the second matrix's outputs in
 // y1 [m][n1].  part: gemm_part_floats(p) floats of scratch.

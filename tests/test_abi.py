@@ -156,13 +156,20 @@ def test_gemm_and_ffn_validation():
     rc, _ = _err(L().ptq1_gemm(B, 17408, 5120, X, 256, S, Y, WS, need - 1, None))
     assert rc == 6
     W2, W3 = C.c_void_p(FAKE * 600), C.c_void_p(FAKE * 700)
-    rc, msg = _err(L().ptq1_ffn_block(X, Y, 1, 5120, 17408, B, W2, W3, None, 0.0, WS, 1 << 40, None))
+    rc, msg = _err(L().ptq1_ffn_block(X, Y, 1, 5120, 17408, B, W2, W3, None, 0.0, None, WS, 1 << 40, None))
     assert rc == 1 and "signs" in msg
-    rc, _ = _err(L().ptq1_ffn_block(X, Y, 1, 5000, 17408, B, W2, W3, S, 0.0, WS, 1 << 40, None))
+    rc, _ = _err(L().ptq1_ffn_block(X, Y, 1, 5000, 17408, B, W2, W3, S, 0.0, None, WS, 1 << 40, None))
     assert rc == 2
-    rc, _ = _err(L().ptq1_ffn_block(X, C.c_void_p(FAKE * 200 + 16), 2, 5120, 17408, B, W2, W3, S, 0.0, WS,
-                                    1 << 40, None))
+    rc, _ = _err(L().ptq1_ffn_block(X, C.c_void_p(FAKE * 200 + 16), 2, 5120, 17408, B, W2, W3, S, 0.0, None,
+                                    WS, 1 << 40, None))
     assert rc == 7
+    # the norm's gain: 16-byte aligned, disjoint from x_out and the workspace
+    rc, msg = _err(L().ptq1_ffn_block(X, Y, 1, 5120, 17408, B, W2, W3, S, 1e-6, C.c_void_p(FAKE * 800 + 4), WS,
+                                      1 << 40, None))
+    assert rc == 3 and "rms_gain" in msg
+    rc, msg = _err(L().ptq1_ffn_block(X, Y, 1, 5120, 17408, B, W2, W3, S, 1e-6, C.c_void_p(FAKE * 300 + 64), WS,
+                                      1 << 40, None))
+    assert rc == 7 and "rms_gain" in msg
     assert L().ptq1_ffn_workspace_bytes(1, 5120, 17408) > 0
     assert L().ptq1_ffn_workspace_bytes(8, 5120, 17408) >= 32 * 17408 * 2
     assert L().ptq1_ffn_workspace_bytes(1, 5120, 17400) == 0
@@ -182,7 +189,7 @@ def test_empty_calls_enqueue_nothing():
     assert L().ptq1_gemm(B, 17408, 5120, X, 0, S, Y, WS, 0, None) == 0
     assert L().ptq1_matvec(B, 0, 5120, X, S, None, Y, WS, 0, None) == 0
     assert L().ptq1_gate_up(B, B, 0, 5120, X, S, Y, Y, WS, 0, None) == 0
-    assert L().ptq1_ffn_block(X, Y, 0, 5120, 17408, B, B, B, S, 0.0, WS, 0, None) == 0
+    assert L().ptq1_ffn_block(X, Y, 0, 5120, 17408, B, B, B, S, 0.0, None, WS, 0, None) == 0
     assert L().hadamard_unrotate_rows(X, 100, 1024, None, 0, S, Y, None) == 0
     assert L().ptq1_swiglu(X, X, Y, 0, None) == 0
     assert L().ptq1_dequant(B, 0, 128, Y, None) == 0

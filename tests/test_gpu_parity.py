@@ -466,6 +466,47 @@ def test_ffn_block_full_shape(m):
     assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
 
 
+def _gain(seed, d):
+    # a positive per-channel norm weight around 1 (0.5 + z^2)
+    return (0.5 + synth.gauss(seed, 7, d).astype(np.float64) ** 2).astype(np.float32)
+
+
+@pytest.mark.parametrize("m,d,f,eps", [(1, 1024, 2048, 1e-6), (1, 2048, 1024, 0.0), (2, 1024, 2048, 1e-6),
+                                       (8, 2048, 1024, 0.0), (5, 1024, 3072, 1e-6)])
+def test_ffn_block_rms_gain(m, d, f, eps):
+    """The norm's per-channel weight: the gate/up input is a * gain * x, on
+    the fp32 lookup path (m = 1) and the bf16 prep path (m >= 2)."""
+    seed = 9
+    wg, wu, wd = _ffn_host(seed, d, f)
+    x = synth.activations(seed, m, d)
+    s = synth.signs(seed)
+    gv = _gain(seed, d)
+    got = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f, eps,
+                                rms_gain=to_dev(gv)))
+    ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, eps, gain=gv)
+    assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+    # a gain of ones is no gain
+    ones = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f,
+                                 eps, rms_gain=to_dev(np.ones(d, np.float32))))
+    plain = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f,
+                                  eps))
+    np.testing.assert_array_equal(ones, plain)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_ffn_block_full_shape_rms_gain(m):
+    """A 27B-shaped block (d = 5120, f = 17408) with the RMS scale and a gain."""
+    d, f, seed = 5120, 17408, 4
+    wg, wu, wd = _ffn_host(seed, d, f)
+    x = synth.activations(seed, m, d)
+    s = synth.signs(seed)
+    gv = _gain(seed, d)
+    got = host(P.ptq1_ffn_block(to_dev(x), tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f), to_dev(s), d, f,
+                                1e-6, rms_gain=to_dev(gv)))
+    ref = oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6, gain=gv)
+    assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+
+
 # -------------------------------------------------------------- profiling ----
 
 def test_kernel_timer_brackets_each_launch():
