@@ -336,6 +336,42 @@ def main() -> int:
 
         breakdown["embed_unrotate_row"] = {"us": timed(unrot, 200, 20) * 1e3}
 
+        # prefill embedding gather: 256 rows of the table un-rotated in one call
+        emb256 = torch.empty((256, D), dtype=torch.float32, device=dev)
+        breakdown["embed_unrotate_256_rows"] = {
+            "us": timed(lambda i: P.hadamard_unrotate_rows(table, signs, ids=ids[(i % 16) * 256:(i % 16 + 1) * 256],
+                                                           out=emb256), 100, 10) * 1e3}
+        del emb256
+
+        # other folded projections at synthetic shapes (the pages give no
+        # attention shapes): the same kernels, a wide and a narrow matrix,
+        # decode (32 weight sets, beyond the Infinity Cache) and M = 256 prefill
+        proj = {}
+        for n_p, k_p in ((8192, D), (D, 8192)):
+            psets = [P.ptq1_tile(P.ptq1_pack(sdev.trits(5, synth.layer_stream(synth.S_W_TRITS, j), n_p, k_p, device=dev),
+                                             sdev.scales(5, synth.layer_stream(synth.S_W_SCALES, j), n_p, k_p // 128,
+                                                         device=dev)), n_p, k_p) for j in range(32)]
+            xp = torch.from_numpy(synth.activations(5, 256, k_p)).to(dev)
+            yp = torch.empty(n_p, dtype=torch.float32, device=dev)
+            wsp = torch.zeros(P.workspace_bytes("matvec", n_p, k_p), dtype=torch.uint8, device=dev)
+            ms_p = timed(lambda i: P.ptq1_matvec(psets[i % 32], n_p, k_p, xp[0], signs, out=yp, ws=wsp), 200, 20)
+            yg = torch.empty((256, n_p), dtype=torch.float32, device=dev)
+            wsg = torch.zeros(P.workspace_bytes("gemm", 256, n_p, k_p), dtype=torch.uint8, device=dev)
+            timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 3, 0)  # warm-up
+            tg = P.KernelTimer("gemm", 30)
+            with tg:
+                timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 30, 0)
+            dg = tg.durations_ms()
+            tg.close()
+            us_gk = 1e3 * sum(dg) / len(dg)
+            mv_bytes = packed(n_p, k_p) + 4 * (n_p + k_p)
+            proj[f"{n_p}x{k_p}"] = {"matvec_us": ms_p * 1e3, "matvec_GB/s": mv_bytes / (ms_p * 1e-3) / 1e9,
+                                    "gemm_M256_us_kernel": us_gk,
+                                    "gemm_M256_TFLOP/s": 2.0 * 256 * n_p * k_p / (us_gk * 1e-6) / 1e12}
+            del psets, xp, yp, wsp, yg, wsg
+        breakdown["projections_synthetic_shapes"] = proj
+        torch.cuda.empty_cache()
+
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
         w0 = P.ptq1_tile(P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024),
                                      sdev.scales(0, synth.S_W_SCALES, 1024, 8)), 1024, 1024)

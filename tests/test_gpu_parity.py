@@ -205,17 +205,24 @@ def test_unrotate_rows_small():
 
 def test_unrotate_rows_full_table():
     """A 248320 x 5120 fp32 table (5.09 GB) generated on the device; rows 0,
-    248319 and seeded rows restored and compared with the oracle."""
+    248319 and seeded rows restored and compared with the oracle, then a
+    prefill-style gather of 256 token rows (with repeats) in one call."""
     V, d, seed = 248320, 5120, 2
     s = synth.signs(seed)
     table = sdev.gauss(seed, synth.S_TABLE, V * d).view(V, d)
     ids = np.concatenate([[0, V - 1], synth.token_ids(seed, 6, V)]).astype(np.int32)
     got = host(P.hadamard_unrotate_rows(table, to_dev(s), ids=to_dev(ids)))
+    ids256 = synth.token_ids(seed + 1, 256, V).astype(np.int32)
+    ids256[7] = ids256[3]  # a repeated token
+    got256 = host(P.hadamard_unrotate_rows(table, to_dev(s), ids=to_dev(ids256)))
     del table
     torch.cuda.empty_cache()
     ref = oracle.unrotate(synth.table_rows(seed, synth.S_TABLE, ids, d), s)
     for i in range(len(ids)):
         assert rel_l2(got[i], ref[i]) <= TOL_FP32, f"row {ids[i]}"
+    ref256 = oracle.unrotate(synth.table_rows(seed, synth.S_TABLE, ids256, d), s)
+    assert rel_l2(got256, ref256) <= TOL_FP32
+    np.testing.assert_array_equal(got256[7], got256[3])
 
 
 # --------------------------------------------------------------- matvec ----
@@ -414,6 +421,31 @@ def test_gemm_prefill_full_shape(m, prefill_weights):
     assert np.all(np.isfinite(got))
     rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed + m, 158, n)])).astype(np.int64)
     ref = oracle.gemm(b, n, k, oracle.rotate(x, sg), rows=rows)
+    assert rel_l2(got[:, rows], ref) <= TOL_BF16
+
+
+# ------------------------------------ other folded projections (synthetic) ----
+# The pages fold the rotation into every weight matrix but give no attention
+# shapes; a wide and a narrow projection stand in for them (seeded like the
+# layer configurations), on the decode matvec and the M = 256 prefill GEMM.
+
+PROJ_SHAPES = [(8192, 5120), (5120, 8192)]
+
+
+@pytest.mark.parametrize("n,k", PROJ_SHAPES)
+def test_projection_shapes(n, k):
+    seed = 5
+    t, sc = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, sc)
+    del t
+    bd = tiled(b, n, k)
+    s = synth.signs(seed)
+    x = synth.activations(seed, 256, k)
+    y = host(P.ptq1_matvec(bd, n, k, to_dev(x[0]), to_dev(s)))
+    assert rel_l2(y, oracle.matvec(b, n, k, oracle.rotate(x[0], s))) <= TOL_FP32
+    got = host(P.ptq1_gemm(bd, n, k, to_dev(x), to_dev(s)))
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed + n, 126, n)])).astype(np.int64)
+    ref = oracle.gemm(b, n, k, oracle.rotate(x, s), rows=rows)
     assert rel_l2(got[:, rows], ref) <= TOL_BF16
 
 
