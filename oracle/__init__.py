@@ -58,6 +58,9 @@ def lib():
         L.orc_pack.argtypes = [p, p, i64, i64, p]
         L.orc_unpack.argtypes = [p, i64, i64, p, p]
         L.orc_dequant.argtypes = [p, i64, i64, p]
+        L.orc_pq2_pack.argtypes = [p, p, i64, i64, p]
+        L.orc_pq2_unpack.argtypes = [p, i64, i64, p, p]
+        L.orc_pq2_dequant.argtypes = [p, i64, i64, p]
         L.orc_hadamard_entry.argtypes = [C.c_int, C.c_int]
         L.orc_hadamard_entry.restype = C.c_double
         L.orc_rotate.argtypes = [p, i64, i64, p, p]
@@ -71,7 +74,8 @@ def lib():
         for fn in ("orc_pack", "orc_unpack", "orc_dequant", "orc_rotate", "orc_unrotate",
                    "orc_gemm_rows", "orc_gemm", "orc_ffn_block", "orc_threads",
                    "orc_block_weights", "orc_block_bytes", "orc_block_trit_bytes",
-                   "orc_hadamard_width"):
+                   "orc_hadamard_width", "orc_pq2_pack", "orc_pq2_unpack", "orc_pq2_dequant",
+                   "orc_pq2_block_bytes"):
             getattr(L, fn).restype = C.c_int
         _lib = L
     return _lib
@@ -139,6 +143,41 @@ def dequant(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
     w = np.zeros((n, k), dtype=np.float64)
     _check(lib().orc_dequant(_ptr(b), n, k, _ptr(w)), "dequant")
     return w
+
+
+# ---- PQ2_0: 2-bit codes, 4 per byte, then the fp16 scale (34 bytes per 128 weights)
+
+def pq2_pack(trits: np.ndarray, scales_f16_bits: np.ndarray) -> np.ndarray:
+    """int8 trits [n, k], uint16 fp16 scale bits [n, k/128] -> uint8 blocks [n, k/128*34]."""
+    t = np.ascontiguousarray(trits, dtype=np.int8)
+    s = np.ascontiguousarray(scales_f16_bits, dtype=np.uint16)
+    n, k = t.shape
+    out = np.zeros((n, (k // BLOCK_W) * lib().orc_pq2_block_bytes()), dtype=np.uint8)
+    _check(lib().orc_pq2_pack(_ptr(t), _ptr(s), n, k, _ptr(out)), "pq2_pack")
+    return out
+
+
+def pq2_unpack(blocks: np.ndarray, n: int, k: int):
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    t = np.zeros((n, k), dtype=np.int8)
+    s = np.zeros((n, k // BLOCK_W), dtype=np.uint16)
+    _check(lib().orc_pq2_unpack(_ptr(b), n, k, _ptr(t), _ptr(s)), "pq2_unpack")
+    return t, s
+
+
+def pq2_dequant(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    w = np.zeros((n, k), dtype=np.float64)
+    _check(lib().orc_pq2_dequant(_ptr(b), n, k, _ptr(w)), "pq2_dequant")
+    return w
+
+
+def pq2_matvec(blocks: np.ndarray, n: int, k: int, xr: np.ndarray, rows=None) -> np.ndarray:
+    """W xr for a PQ2_0 matrix: the dequantised rows (fp64) times the already rotated x."""
+    w = pq2_dequant(blocks, n, k)
+    if rows is not None:
+        w = w[np.asarray(rows, dtype=np.int64)]
+    return w @ _f64(xr).reshape(k)
 
 
 def hadamard_entry(i: int, j: int) -> float:

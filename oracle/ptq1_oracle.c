@@ -196,6 +196,86 @@ int orc_dequant(const uint8_t *blocks, int64_t n, int64_t k, double *w)
     return 0;
 }
 
+/* ---- PQ2_0: the 2-bit ternary format of "Why I Am Building Another
+ * Inference Engine", Level 2 ("each ternary weight in 2 bits plus one
+ * 16-bit scale per 128 weights, 2.125 bits per weight").  Readings (the
+ * page gives neither field order nor code map): weight 4i+n of a block is
+ * the 2-bit field n (n = 0 least significant) of byte i; code q in {0,1,2}
+ * is the weight q - 1; code 3 (never written) decodes as weight 0; the 32
+ * code bytes are followed by the fp16 scale, little-endian: 34 bytes. */
+#define ORC_PQ2_CODE_BYTES 32
+#define ORC_PQ2_BLOCK_BYTES 34
+
+int orc_pq2_block_bytes(void) { return ORC_PQ2_BLOCK_BYTES; }
+
+/* Weight of 2-bit code q. */
+static int pq2_weight(int q) { return q == 3 ? 0 : q - 1; }
+
+/* trits int8 [n][k] in {-1,0,1}, scales fp16 bits [n][k/128] -> blocks
+ * [n][k/128][34].  Returns 0, or -1 on a bad shape or a trit outside
+ * {-1, 0, 1}. */
+int orc_pq2_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k, uint8_t *blocks)
+{
+    if (bad_shape(n, k)) return -1;
+    int64_t nb = k / ORC_BLOCK_W;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const int8_t *t = trits + r * k + b * ORC_BLOCK_W;
+            uint8_t *out = blocks + (r * nb + b) * ORC_PQ2_BLOCK_BYTES;
+            for (int i = 0; i < ORC_PQ2_CODE_BYTES; ++i) {
+                int byte = 0;
+                for (int f = 0; f < 4; ++f) {
+                    int tv = t[4 * i + f];
+                    if (tv < -1 || tv > 1) return -1;
+                    byte += (tv + 1) << (2 * f);
+                }
+                out[i] = (uint8_t)byte;
+            }
+            uint16_t s = scales[r * nb + b];
+            out[ORC_PQ2_CODE_BYTES] = (uint8_t)(s & 0xff);
+            out[ORC_PQ2_CODE_BYTES + 1] = (uint8_t)(s >> 8);
+        }
+    return 0;
+}
+
+static int pq2_block_trit(const uint8_t *blk, int j) { return pq2_weight((blk[j / 4] >> (2 * (j % 4))) & 3); }
+
+static uint16_t pq2_scale_bits(const uint8_t *blk)
+{
+    return (uint16_t)(blk[ORC_PQ2_CODE_BYTES] | (blk[ORC_PQ2_CODE_BYTES + 1] << 8));
+}
+
+/* blocks -> trits int8 [n][k] and scales fp16 bits [n][k/128]. */
+int orc_pq2_unpack(const uint8_t *blocks, int64_t n, int64_t k, int8_t *trits, uint16_t *scales)
+{
+    if (bad_shape(n, k)) return -1;
+    int64_t nb = k / ORC_BLOCK_W;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (r * nb + b) * ORC_PQ2_BLOCK_BYTES;
+            for (int j = 0; j < ORC_BLOCK_W; ++j)
+                trits[r * k + b * ORC_BLOCK_W + j] = (int8_t)pq2_block_trit(blk, j);
+            scales[r * nb + b] = pq2_scale_bits(blk);
+        }
+    return 0;
+}
+
+/* w[r][k] = fp16(scale of its block) * weight, in fp64. */
+int orc_pq2_dequant(const uint8_t *blocks, int64_t n, int64_t k, double *w)
+{
+    if (bad_shape(n, k)) return -1;
+    int64_t nb = k / ORC_BLOCK_W;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = blocks + (r * nb + b) * ORC_PQ2_BLOCK_BYTES;
+            double s = orc_f16_to_f64(pq2_scale_bits(blk));
+            for (int j = 0; j < ORC_BLOCK_W; ++j)
+                w[r * k + b * ORC_BLOCK_W + j] = s * (double)pq2_block_trit(blk, j);
+        }
+    return 0;
+}
+
 /* Sylvester Hadamard entry, natural order: (-1)^popcount(i & j). */
 double orc_hadamard_entry(int i, int j)
 {

@@ -311,6 +311,59 @@ def _ffn_weights(seed, d, f):
     return mats
 
 
+# --------------------------------------------------------------- PQ2_0 ----
+
+def test_pq2_worked_block_and_accounting():
+    """[page 2, Level 2]: 2 bits per weight + one 16-bit scale per 128 weights
+    = 2.125 bits per weight, 7.2 GB for 27e9 weights; the block in the fixture
+    is worked out by hand."""
+    g = _golden("pq2_worked_block.txt")
+    assert int(g["block_bytes"]) * 8 / 128 == float(g["bits_per_weight"])
+    assert int(27e9) * int(g["block_bytes"]) // 128 == int(g["bytes_27e9_weights"])
+    assert round(int(g["bytes_27e9_weights"]) / 1e9, 1) == 7.2
+    t = np.zeros((1, 128), np.int8)
+    t[0, :4] = [-1, 0, 1, 0]
+    t[0, 124:] = [1, 1, -1, 0]
+    b = oracle.pq2_pack(t, np.array([[0x4000]], np.uint16))[0]
+    assert b.size == int(g["block_bytes"])
+    assert b[0] == int(g["first_byte"]) and np.all(b[1:31] == int(g["middle_byte"]))
+    assert b[31] == int(g["last_code_byte"])
+    assert b[32:34].tolist() == [int(v) for v in g["scale_bytes"].split()]
+    w = oracle.pq2_dequant(b[None, :], 1, 128)[0]
+    assert w @ np.arange(1, 129, dtype=np.float64) == float(g["dot_with_k_plus_1"])
+
+
+def test_pq2_all_codes_round_trip():
+    """Every group of four trits maps to the byte sum (t_n + 1) 4^n and back;
+    code 3 (never written) decodes as weight 0."""
+    groups = np.array(np.meshgrid(*[[-1, 0, 1]] * 4, indexing="ij")).reshape(4, -1).T  # 81 x 4
+    groups = np.concatenate([groups, groups[:15]])  # 96 groups: three whole blocks
+    t = groups.reshape(-1, 128).astype(np.int8)
+    sc = np.full((t.shape[0], 1), 0x3C00, np.uint16)
+    b = oracle.pq2_pack(t, sc)
+    codes = b.reshape(t.shape[0], 34)[:, :32].reshape(-1)
+    want = ((groups[: codes.size] + 1) * (4 ** np.arange(4))).sum(axis=1)
+    np.testing.assert_array_equal(codes, want)
+    t2, sc2 = oracle.pq2_unpack(b, t.shape[0], 128)
+    np.testing.assert_array_equal(t2, t)
+    np.testing.assert_array_equal(sc2, sc)
+    # every byte decodes; fields equal to 3 give 0
+    blk = np.zeros((1, 34), np.uint8)
+    blk[0, :32] = [0xFF, 0x3F, 0xC0, 0x1B] * 8  # fields low to high: 3333, 3330, 0003, 3210
+    blk[0, 33] = 0x3C
+    tb, _ = oracle.pq2_unpack(blk, 1, 128)
+    np.testing.assert_array_equal(tb[0, :16], [0, 0, 0, 0, 0, 0, 0, -1, -1, -1, -1, 0, 0, 1, 0, -1])
+
+
+def test_pq2_dequant_is_scale_times_trit():
+    rng = np.random.default_rng(3)
+    t = rng.integers(-1, 2, size=(5, 384)).astype(np.int8)
+    sc = rng.integers(0x1000, 0x5000, size=(5, 3)).astype(np.uint16)
+    w = oracle.pq2_dequant(oracle.pq2_pack(t, sc), 5, 384)
+    ref = t.astype(np.float64) * np.repeat(sc.view(np.float16).astype(np.float64), 128, axis=1)
+    np.testing.assert_array_equal(w, ref)
+
+
 def test_ffn_block_composition():
     """[page 1, "What Bonsai is" + "Speed, and where it goes"; page 2, Level 4]:
     x + Wd R(silu(Wg R(a gain x)) * (Wu R(a gain x))), composed here from numpy
