@@ -372,6 +372,29 @@ def main() -> int:
         breakdown["projections_synthetic_shapes"] = proj
         torch.cuda.empty_cache()
 
+        # the same gate+up decode in the PQ2_0 format (2.125 bits per weight):
+        # the two matrices stacked as one [2F, D] matrix, 32 weight sets, the
+        # lookup kernel timed alone, against the PTQ1_0 kernel's figure above
+        n2 = 2 * F
+        q2sets = [P.pq2_tile(P.pq2_pack(sdev.trits(seed, synth.layer_stream(synth.S_W_TRITS, j), n2, D, device=dev),
+                                        sdev.scales(seed, synth.layer_stream(synth.S_W_SCALES, j), n2, D // 128,
+                                                    device=dev)), n2, D) for j in range(32)]
+        y2 = torch.empty(n2, dtype=torch.float32, device=dev)
+        ws2 = torch.zeros(P.workspace_bytes("pq2_matvec", n2, D), dtype=torch.uint8, device=dev)
+        timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 20, 0)  # warm-up
+        t2 = P.KernelTimer("pq2_matvec", 200)
+        with t2:
+            ms_q2 = timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 200, 0)
+        d2 = t2.durations_ms()
+        t2.close()
+        us_q2 = 1e3 * sum(d2) / len(d2)
+        q2_bytes = P.pq2_tiled_bytes(n2, D) + 4 * D
+        breakdown["pq2_gate_up_decode"] = {"us_kernel": us_q2, "GB/s": q2_bytes / (us_q2 * 1e-6) / 1e9,
+                                           "bytes": q2_bytes, "call_us": ms_q2 * 1e3,
+                                           "ptq1_kernel_us": us_gu}
+        del q2sets, y2, ws2
+        torch.cuda.empty_cache()
+
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
         w0 = P.ptq1_tile(P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024),
                                      sdev.scales(0, synth.S_W_SCALES, 1024, 8)), 1024, 1024)

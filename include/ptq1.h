@@ -228,12 +228,58 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
                            const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
                            size_t ws_bytes, hipStream_t stream);
 
+/* ---- PQ2_0: the two-bit ternary format ("Why I Am Building Another
+ * Inference Engine", Level 2: two bits per weight and one 16-bit scale per
+ * 128 weights, 2.125 bits per weight).  A block is 32 code bytes, weight
+ * 4i + f in bits 2f..2f+1 of byte i (code q is the trit q - 1; code 3, never
+ * written, reads as 0), then the binary16 scale, little-endian: 34 bytes.
+ * The device layout for the matvec is tiled like PTQ1_0's (32 rows x 2
+ * blocks per tile, tiles K-slice-major) with each tile holding its 64 code
+ * records of 32 bytes first and then its 64 scales: 2176 bytes per tile. */
+
+/* Bytes of a packed [n][k] PQ2_0 matrix: n * (k/128) * 34, or -1 if n < 0,
+ * k < 0, k % 128 != 0 or the product overflows. */
+int64_t pq2_packed_bytes(int64_t n, int64_t k);
+
+/* Encode.  trits int8 [n][k] ({-1, 0, +1}; others clamped), scales_f16
+ * binary16 bit patterns [n][k/128] (copied verbatim), blocks output of
+ * pq2_packed_bytes(n, k) bytes, 16-byte aligned.
+ * Errors: NULL, SHAPE (k % 128), ALIGN, ALIAS, OVERFLOW. */
+ptq1_status pq2_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k, uint8_t *blocks,
+                     hipStream_t stream);
+
+/* Decode: w [n][k] fp32 = binary16 scale * trit, exact.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW. */
+ptq1_status pq2_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t stream);
+
+/* Bytes of the PQ2_0 tiled layout: ceil(n/32) * ceil(k/256) * 2176, or -1 on
+ * a bad shape or overflow. */
+int64_t pq2_tiled_bytes(int64_t n, int64_t k);
+
+/* Packed -> tiled reorder (code bytes and scales copied unchanged, padding
+ * written as zeros).  Both pointers 16-byte aligned, not overlapping.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW. */
+ptq1_status pq2_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t stream);
+
+/* Batch-1 decode matvec over a PQ2_0 tiled matrix, with the arguments,
+ * results, workspace rule and errors of ptq1_matvec:
+ *   y[r] = (residual ? residual[r] : 0) + sum_c W[r][c] * xr[c],
+ *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
+ * Codes are decoded through a per-slice table of (code byte, byte value)
+ * partial dot products, fp32 throughout; split-K partials over 256-wide
+ * slices, then their sum in slice order.  The tiled matrix must be below
+ * 2 GiB (UNSUPPORTED otherwise). */
+size_t pq2_matvec_workspace_bytes(int64_t n, int64_t k);
+ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *signs1024,
+                       const float *residual, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
  * next `count` launches of one kernel family (hipExtLaunchKernel: they take
  * the kernel's own start and end times on its stream), so a caller can time
  * a kernel inside a composite call (ptq1_ffn_block) with events.  Families: "lut_matvec_2" (the
  * table-lookup matvec over two matrices: gate and up), "lut_matvec_1" (over
- * one matrix: ptq1_matvec, the down projection), "gemm" (the MFMA GEMM).
+ * one matrix: ptq1_matvec, the down projection), "gemm" (the MFMA GEMM),
+ * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec).
  * Events are created and owned by the caller; both arrays must stay valid
  * until `count` launches have happened or the family is re-armed.  count =
  * 0 disarms.  Process-wide; not meant for concurrent use by several

@@ -62,6 +62,13 @@ _SIGS = {
     "ptq1_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
     "ptq1_ffn_workspace_bytes": ([i64, i64, i64], sz),
     "ptq1_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
+    "pq2_packed_bytes": ([i64, i64], i64),
+    "pq2_pack": ([p, p, i64, i64, p, p], C.c_int),
+    "pq2_dequant": ([p, i64, i64, p, p], C.c_int),
+    "pq2_tiled_bytes": ([i64, i64], i64),
+    "pq2_tile": ([p, i64, i64, p, p], C.c_int),
+    "pq2_matvec_workspace_bytes": ([i64, i64], sz),
+    "pq2_matvec": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
@@ -301,9 +308,75 @@ def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_
     return out
 
 
+# ------------------------------------------------------------------ PQ2_0 ----
+
+PQ2_BLOCK_BYTES = 34
+
+
+def pq2_packed_bytes(n: int, k: int) -> int:
+    return lib().pq2_packed_bytes(n, k)
+
+
+def pq2_pack(trits: torch.Tensor, scales_f16: torch.Tensor, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """int8 trits [n, k] + binary16 bit patterns [n, k/128] -> uint8 [n, k/128*34]."""
+    _dev(trits, "trits", torch.int8)
+    _dev(scales_f16, "scales_f16", (torch.int16, torch.float16, torch.uint16))
+    n, k = trits.shape
+    if out is None:
+        out = torch.empty((n, (k // BLOCK_WEIGHTS) * PQ2_BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
+    _dev(out, "blocks", torch.uint8)
+    _check("pq2_pack", lib().pq2_pack(_ptr(trits), _ptr(scales_f16), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def pq2_dequant(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    _dev(blocks, "blocks", torch.uint8)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
+    _dev(out, "w", torch.float32)
+    _check("pq2_dequant", lib().pq2_dequant(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def pq2_tiled_bytes(n: int, k: int) -> int:
+    return lib().pq2_tiled_bytes(n, k)
+
+
+def pq2_tile(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """Packed PQ2_0 [n, k/128*34] uint8 -> the tiled layout pq2_matvec reads (flat uint8)."""
+    _dev(blocks, "blocks", torch.uint8)
+    nbytes = pq2_tiled_bytes(n, k)
+    if nbytes < 0:
+        raise ValueError(f"bad shape [{n}][{k}]")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
+    _dev(out, "tiled", torch.uint8)
+    _check("pq2_tile", lib().pq2_tile(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def pq2_matvec(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
+               residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = residual + W R x over a PQ2_0 tiled matrix (pq2_tile)."""
+    _dev(tiled, "tiled", torch.uint8)
+    _dev(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev(out, "y", torch.float32)
+    ws, wsb = _ws(lib().pq2_matvec_workspace_bytes(n, k), x.device, ws)
+    _check("pq2_matvec", lib().pq2_matvec(_ptr(tiled), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
+                                          _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
 def workspace_bytes(kind: str, *shape) -> int:
     fn = {"matvec": "ptq1_matvec_workspace_bytes", "gate_up": "ptq1_gate_up_workspace_bytes",
-          "gemm": "ptq1_gemm_workspace_bytes", "ffn": "ptq1_ffn_workspace_bytes"}[kind]
+          "gemm": "ptq1_gemm_workspace_bytes", "ffn": "ptq1_ffn_workspace_bytes",
+          "pq2_matvec": "pq2_matvec_workspace_bytes"}[kind]
     return int(getattr(lib(), fn)(*shape))
 
 

@@ -124,6 +124,48 @@ ptq1_status check_matrix(const uint8_t *blocks, const char *name, int64_t n, int
     return PTQ1_OK;
 }
 
+// PQ2_0 sizes (34-byte blocks; tiles of 32 rows x 2 blocks, 2176 bytes):
+// -1 on a bad shape or overflow.
+int64_t pq2_packed(int64_t n, int64_t k)
+{
+    if (n < 0 || k < 0 || k % ptq1::kBlockWeights != 0) return -1;
+    int64_t nb_bytes, total;
+    if (!mul_ok(k / ptq1::kBlockWeights, ptq1::kPq2BlockBytes, &nb_bytes)) return -1;
+    if (!mul_ok(n, nb_bytes, &total)) return -1;
+    return total;
+}
+
+int64_t pq2_tiled(int64_t n, int64_t k)
+{
+    if (pq2_packed(n, k) < 0) return -1;
+    const int64_t bands = n / ptq1::kTileRows + (n % ptq1::kTileRows != 0);
+    const int64_t nb = k / ptq1::kBlockWeights;
+    const int64_t tiles_k = nb / ptq1::kTileBlocks + (nb % ptq1::kTileBlocks != 0);
+    int64_t tiles, total;
+    if (!mul_ok(bands, tiles_k, &tiles)) return -1;
+    if (!mul_ok(tiles, ptq1::kPq2TileBytes, &total)) return -1;
+    return total;
+}
+
+ptq1_status check_pq2(const uint8_t *blocks, const char *name, int64_t n, int64_t k, bool need_1024,
+                      int64_t *bytes, bool tiled)
+{
+    if (n < 0) return fail(PTQ1_ERR_SHAPE, "%s: n = %lld is negative", name, (long long)n);
+    if (k < 0) return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is negative", name, (long long)k);
+    if (k % ptq1::kBlockWeights != 0)
+        return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is not a multiple of %d", name, (long long)k,
+                    ptq1::kBlockWeights);
+    if (need_1024 && k % ptq1::kHadamard != 0)
+        return fail(PTQ1_ERR_SHAPE, "%s: k = %lld is not a multiple of %d (rotation chunks)", name,
+                    (long long)k, ptq1::kHadamard);
+    const int64_t b = tiled ? pq2_tiled(n, k) : pq2_packed(n, k);
+    if (b < 0) return fail(PTQ1_ERR_OVERFLOW, "%s: size of [%lld][%lld] overflows", name, (long long)n, (long long)k);
+    if (b > 0 && blocks == nullptr) return fail(PTQ1_ERR_NULL, "%s is NULL", name);
+    if (b > 0 && !aligned(blocks, kAlign)) return fail(PTQ1_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    *bytes = b;
+    return PTQ1_OK;
+}
+
 ptq1_status check_floats(const void *p, const char *name, int64_t count, int64_t *bytes)
 {
     int64_t b;
@@ -221,8 +263,8 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
 
 // ---- profiling hook ----------------------------------------------------------
 // Armed kernel families record caller events around their next launches.
-enum ProfKind { kProfLut2 = 0, kProfLut1 = 1, kProfGemm = 2, kProfKinds = 3 };
-const char *const kProfNames[kProfKinds] = {"lut_matvec_2", "lut_matvec_1", "gemm"};
+enum ProfKind { kProfLut2 = 0, kProfLut1 = 1, kProfGemm = 2, kProfPq2 = 3, kProfKinds = 4 };
+const char *const kProfNames[kProfKinds] = {"lut_matvec_2", "lut_matvec_1", "gemm", "pq2_matvec"};
 
 struct ProfArm {
     hipEvent_t *start = nullptr, *stop = nullptr;
@@ -664,6 +706,89 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
             });
     }
     return hip_status(e, "ptq1_ffn_block");
+}
+
+// ---- PQ2_0 ------------------------------------------------------------------
+
+int64_t pq2_packed_bytes(int64_t n, int64_t k) { return pq2_packed(n, k); }
+
+int64_t pq2_tiled_bytes(int64_t n, int64_t k) { return pq2_tiled(n, k); }
+
+ptq1_status pq2_pack(const int8_t *trits, const uint16_t *scales_f16, int64_t n, int64_t k, uint8_t *blocks,
+                     hipStream_t stream)
+{
+    int64_t bytes;
+    PTQ1_TRY(check_pq2(blocks, "blocks", n, k, false, &bytes, false));
+    if (bytes == 0) return ok();
+    int64_t nt;
+    if (!mul_ok(n, k, &nt)) return fail(PTQ1_ERR_OVERFLOW, "trits: n * k overflows");
+    if (trits == nullptr) return fail(PTQ1_ERR_NULL, "trits is NULL");
+    if (scales_f16 == nullptr) return fail(PTQ1_ERR_NULL, "scales_f16 is NULL");
+    if (!aligned(scales_f16, 2)) return fail(PTQ1_ERR_ALIGN, "scales_f16 is not 2-byte aligned");
+    const int64_t ns = n * (k / ptq1::kBlockWeights);
+    if (overlaps(blocks, bytes, trits, nt) || overlaps(blocks, bytes, scales_f16, 2 * ns))
+        return fail(PTQ1_ERR_ALIAS, "blocks overlaps an input");
+    return hip_status(ptq1::launch_pq2_pack(trits, scales_f16, n, k, blocks, stream), "pq2_pack");
+}
+
+ptq1_status pq2_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t stream)
+{
+    int64_t bytes, wb, nk;
+    PTQ1_TRY(check_pq2(blocks, "blocks", n, k, false, &bytes, false));
+    if (!mul_ok(n, k, &nk)) return fail(PTQ1_ERR_OVERFLOW, "w: n * k overflows");
+    PTQ1_TRY(check_floats(w, "w", nk, &wb));
+    if (nk == 0) return ok();
+    if (overlaps(w, wb, blocks, bytes)) return fail(PTQ1_ERR_ALIAS, "w overlaps blocks");
+    return hip_status(ptq1::launch_pq2_dequant(blocks, n, k, w, stream), "pq2_dequant");
+}
+
+ptq1_status pq2_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t stream)
+{
+    int64_t pb, tb;
+    PTQ1_TRY(check_pq2(blocks, "blocks", n, k, false, &pb, false));
+    PTQ1_TRY(check_pq2(tiled, "tiled", n, k, false, &tb, true));
+    if (tb == 0) return ok();
+    if (overlaps(tiled, tb, blocks, pb)) return fail(PTQ1_ERR_ALIAS, "tiled overlaps blocks");
+    return hip_status(ptq1::launch_pq2_tile(blocks, n, k, tiled, stream), "pq2_tile");
+}
+
+size_t pq2_matvec_workspace_bytes(int64_t n, int64_t k)
+{
+    if (pq2_packed(n, k) < 0) return 0;
+    return lut_ws(n, 1, k);
+}
+
+ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *signs1024,
+                       const float *residual, float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, xb, yb;
+    PTQ1_TRY(check_pq2(tiled, "tiled", n, k, signs1024 != nullptr, &wb, true));
+    PTQ1_TRY(check_floats(y, "y", n, &yb));
+    if (n == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", k, &xb));
+    PTQ1_TRY(check_signs(signs1024, false));
+    if (residual != nullptr) {
+        int64_t rb;
+        PTQ1_TRY(check_floats(residual, "residual", n, &rb));
+        if (residual != y && overlaps(residual, rb, y, yb))
+            return fail(PTQ1_ERR_ALIAS, "y partially overlaps residual");
+    }
+    const size_t need = pq2_matvec_workspace_bytes(n, k);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "pq2_matvec"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps the weights");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, tiled, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    if (nseg_of(k) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
+    if (n > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "n = %lld > %lld rows", (long long)n, (long long)kMaxLutRows);
+    if (wb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrix above 2 GiB");
+    float *part = static_cast<float *>(ws);
+    hipError_t e = profiled(kProfPq2, stream, [&] {
+        return ptq1::launch_pq2_matvec(tiled, n, k, x, signs1024, part, stream);
+    });
+    if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
+    return hip_status(e, "pq2_matvec");
 }
 
 }  // extern "C"

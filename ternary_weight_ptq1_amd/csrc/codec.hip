@@ -92,6 +92,87 @@ __global__ void __launch_bounds__(256) k_tile(const uint8_t *__restrict__ blocks
     }
 }
 
+// ---- PQ2_0 codec -------------------------------------------------------------
+// One thread per output byte: code bytes carry sum_f (t_f + 1) << 2f over the
+// four weights 4i + f (trits outside {-1, 0, 1} are clamped, as in k_pack);
+// bytes 32..33 are the scale, little-endian.
+__global__ void __launch_bounds__(256) k_pq2_pack(const int8_t *__restrict__ trits,
+                                                  const uint16_t *__restrict__ scales, int64_t nb,
+                                                  int64_t k, int64_t total, uint8_t *__restrict__ out)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t blk = t / kPq2BlockBytes;
+        const int i = static_cast<int>(t - blk * kPq2BlockBytes);
+        const int64_t row = blk / nb;
+        const int64_t b = blk - row * nb;
+        uint32_t byte = 0;
+        if (i < kPq2CodeBytes) {
+            const int8_t *src = trits + row * k + b * kBlockWeights + kPq2CodesPerByte * i;
+#pragma unroll
+            for (int f = 0; f < kPq2CodesPerByte; ++f) {
+                const int tv = src[f];
+                byte |= static_cast<uint32_t>(tv < -1 ? 0 : (tv > 1 ? 2 : tv + 1)) << (2 * f);
+            }
+        } else {
+            const uint32_t s = scales[row * nb + b];
+            byte = (i == kPq2CodeBytes) ? (s & 0xffu) : (s >> 8);
+        }
+        out[t] = static_cast<uint8_t>(byte);
+    }
+}
+
+// One thread per weight: field (c mod 128) mod 4 of code byte (c mod 128) / 4.
+__global__ void __launch_bounds__(256) k_pq2_dequant(const uint8_t *__restrict__ blocks, int64_t nb,
+                                                     int64_t k, int64_t total, float *__restrict__ w)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = t / k;
+        const int64_t c = t - row * k;
+        const int64_t b = c / kBlockWeights;
+        const int j = static_cast<int>(c - b * kBlockWeights);
+        const uint8_t *blk = blocks + (row * nb + b) * kPq2BlockBytes;
+        const int q = (blk[j / kPq2CodesPerByte] >> (2 * (j % kPq2CodesPerByte))) & 3;
+        const uint32_t sb = blk[kPq2CodeBytes] | (static_cast<uint32_t>(blk[kPq2CodeBytes + 1]) << 8);
+        w[t] = half_bits_to_float(sb) * static_cast<float>(q == 3 ? 0 : q - 1);
+    }
+}
+
+// Packed -> PQ2_0 tiled reorder: one thread per place of the tiled output
+// (tile order as k_tile); places past the matrix get zero codes and a zero
+// scale, so they contribute nothing.
+__global__ void __launch_bounds__(256) k_pq2_tile(const uint8_t *__restrict__ blocks, int64_t n, int64_t nb,
+                                                  int64_t bands, int64_t total, uint8_t *__restrict__ tiled)
+{
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tile = o / kTileSlots;
+        const int pos = static_cast<int>(o - tile * kTileSlots);
+        const int64_t t = tile / bands;
+        const int64_t band = tile - t * bands;
+        const int64_t r = band * kTileRows + pos / kTileBlocks;
+        const int64_t j = t * kTileBlocks + pos % kTileBlocks;
+        uint32_t d[kPq2CodeBytes / 4];
+        uint32_t sc = 0;
+#pragma unroll
+        for (int q = 0; q < kPq2CodeBytes / 4; ++q) d[q] = 0;
+        if (r < n && j < nb) {
+            // blocks are 34 bytes: only 2-byte aligned
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(blocks + (r * nb + j) * kPq2BlockBytes);
+#pragma unroll
+            for (int q = 0; q < kPq2CodeBytes / 4; ++q)
+                d[q] = static_cast<uint32_t>(src[2 * q]) | (static_cast<uint32_t>(src[2 * q + 1]) << 16);
+            sc = src[kPq2CodeBytes / 2];
+        }
+        uint8_t *tb = tiled + tile * kPq2TileBytes;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(tb + pos * kPq2CodeBytes);
+#pragma unroll
+        for (int q = 0; q < kPq2CodeBytes / 4; ++q) dst[q] = d[q];
+        reinterpret_cast<uint16_t *>(tb + kPq2TileCodeBytes)[pos] = static_cast<uint16_t>(sc);
+    }
+}
+
 static unsigned grid_for(int64_t total, int threads)
 {
     int64_t g = (total + threads - 1) / threads;
@@ -118,6 +199,37 @@ hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w,
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(k_dequant, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks,
                        k / kBlockWeights, k, total, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_pq2_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k, uint8_t *blocks,
+                           hipStream_t s)
+{
+    const int64_t nb = k / kBlockWeights;
+    const int64_t total = n * nb * kPq2BlockBytes;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pq2_pack, dim3(grid_for(total, 256)), dim3(256), 0, s, trits, scales, nb, k, total, blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_pq2_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s)
+{
+    const int64_t total = n * k;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pq2_dequant, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks, k / kBlockWeights, k,
+                       total, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_pq2_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t s)
+{
+    const int64_t nb = k / kBlockWeights;
+    const int64_t tiles_k = (nb + kTileBlocks - 1) / kTileBlocks;
+    const int64_t bands = (n + kTileRows - 1) / kTileRows;
+    const int64_t total = bands * tiles_k * kTileSlots;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pq2_tile, dim3(grid_for(total, 256)), dim3(256), 0, s, blocks, n, nb, bands, total,
+                       tiled);
     return hipGetLastError();
 }
 

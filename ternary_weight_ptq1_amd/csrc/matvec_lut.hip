@@ -514,6 +514,40 @@ int64_t lut_nslices(int64_t k) { return (k + kLutSliceW - 1) / kLutSliceW; }
 
 size_t lut_part_floats(int64_t n, int nmat, int64_t k) { return static_cast<size_t>(lut_nslices(k) * nmat * n); }
 
+// Up to two workgroups per CU (at most one per 8 units), the same number cs
+// of workgroups for every slice, each taking per_wg = ceil(units / cs)
+// consecutive units; U = units per wave of a full workgroup, chunks = the
+// workgroups per slice that get units.
+struct LutPlan {
+    int U;
+    int per_wg;
+    int64_t chunks;
+};
+
+static LutPlan lut_plan(int64_t per_slice, int64_t nslices)
+{
+    const int64_t total = per_slice * nslices;
+    int64_t wgs = kLutWgPerCu * static_cast<int64_t>(device_cus());
+    if (wgs > total / kLutWaves) wgs = total / kLutWaves;
+    int64_t cs = wgs / nslices;
+    if (cs < 1) cs = 1;
+    static const int kUs[] = {1, 2, 3, 4, 6, 8};
+    int U = 0;
+    int64_t per_wg = 0;
+    for (;;) {
+        per_wg = (per_slice + cs - 1) / cs;
+        const int64_t need = (per_wg + kLutWaves - 1) / kLutWaves;
+        for (int cand : kUs)
+            if (cand >= need) {
+                U = cand;
+                break;
+            }
+        if (U != 0) break;
+        ++cs;  // parts above 64 units: more workgroups per slice
+    }
+    return LutPlan{U, static_cast<int>(per_wg), (per_slice + per_wg - 1) / per_wg};
+}
+
 template <int U>
 static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
 {
@@ -550,39 +584,303 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.signs = signs;
     a.gain = gain;
     a.part = part;
-    // up to two workgroups per CU (at most one per 8 units), the same number
-    // cs of workgroups for every slice, each taking per_wg = ceil(units / cs)
-    // consecutive units; U = units per wave of a full workgroup
-    const int64_t per_slice = static_cast<int64_t>(nmat) * a.groups;
-    const int64_t total = per_slice * a.nslices;
-    const int cus = device_cus();
-    int64_t wgs = kLutWgPerCu * static_cast<int64_t>(cus);
-    if (wgs > total / kLutWaves) wgs = total / kLutWaves;
-    int64_t cs = wgs / a.nslices;
-    if (cs < 1) cs = 1;
-    static const int kUs[] = {1, 2, 3, 4, 6, 8};
-    int U = 0;
-    int64_t per_wg = 0;
-    for (;;) {
-        per_wg = (per_slice + cs - 1) / cs;
-        const int64_t need = (per_wg + kLutWaves - 1) / kLutWaves;
-        for (int cand : kUs)
-            if (cand >= need) {
-                U = cand;
-                break;
-            }
-        if (U != 0) break;
-        ++cs;  // parts above 64 units: more workgroups per slice
-    }
-    a.per_wg = static_cast<int>(per_wg);
-    const int64_t chunks = (per_slice + per_wg - 1) / per_wg;  // workgroups per slice that get units
-    switch (U) {
+    const LutPlan pl = lut_plan(static_cast<int64_t>(nmat) * a.groups, a.nslices);
+    a.per_wg = pl.per_wg;
+    const int64_t chunks = pl.chunks;
+    switch (pl.U) {
         case 1: return lut_launch<1>(a, chunks, s);
         case 2: return lut_launch<2>(a, chunks, s);
         case 3: return lut_launch<3>(a, chunks, s);
         case 4: return lut_launch<4>(a, chunks, s);
         case 6: return lut_launch<6>(a, chunks, s);
         default: return lut_launch<8>(a, chunks, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// PQ2_0 decode matvec ("Why I Am Building Another Inference Engine", Level 2:
+// two bits per ternary weight and one 16-bit scale per 128 weights).  The
+// same table scheme: a byte holds four 2-bit codes, so a 2-block slice has
+// 64 byte slots and T[slot][b] = sum_f w(field f of b) xr[k(slot, f)], with
+// w(q) = q - 1 and w(3) = 0.  What differs from PTQ1_0:
+//   - a lane's block is 32 code bytes, read with two 16-byte loads from its
+//     tile record, and its scale comes from the tile's scale area;
+//   - the 64 slots fill the table's 64 slot columns, and the per-lane
+//     rotation can make every lookup conflict-free: lane 2i + b rotates its
+//     8 dwords by rho = (4 b + i / 4) mod 8 and its bytes by sig = i mod 4.
+//     At lookup (j, c) it reads slot 32 b + 4 ((j + rho) mod 8) +
+//     (c + sig) mod 4.  Over a half-wave (i < 16 or i >= 16) the block-0
+//     lanes read 16 distinct slots of dwords j + i/4 .. (four of them) and
+//     the block-1 lanes the other four dwords, so the 32 slots differ
+//     mod 32; over the whole wave each block's 32 lanes read 32 distinct
+//     slots, so all 64 differ.  Either way no two lanes share a bank
+//     (a slot's dwords sit 64 dwords apart, one per byte value);
+//   - 32 lookups per block and no scale-byte lookups.
+// Partials and their sums are those of the PTQ1_0 kernel.
+// ---------------------------------------------------------------------------
+constexpr int kPq2Slots = kLutBlocks * kPq2CodeBytes;  // 64
+constexpr int kPq2Dwords = kPq2CodeBytes / 4;          // 8
+static_assert(kPq2Slots * 256 * 4 == kLutTableBytes, "the PQ2_0 table fills the 64 KB array");
+
+struct Pq2Args {
+    const uint8_t *w;        // PQ2_0 tiled [n][k]
+    int64_t n, k;
+    int nslices;
+    int64_t groups;          // ceil(n / 32)
+    int per_wg;
+    const float *x, *signs;  // x [k], rotated here when signs != nullptr
+    float *part;             // [nslices][n]
+};
+
+__device__ __forceinline__ int pq2_rho(int lane) { return (4 * (lane & 1) + (lane >> 3)) & 7; }
+__device__ __forceinline__ int pq2_sig(int lane) { return (lane >> 1) & 3; }
+
+// d[j] <- d[(j + rho) mod 8]: conditional rotations by 1, 2 and 4
+__device__ __forceinline__ void pq2_rotate(uint32_t (&d)[kPq2Dwords], int rho)
+{
+#pragma unroll
+    for (int sh = 1; sh <= 4; sh <<= 1) {
+        const uint32_t m = (rho & sh) ? 0xffffffffu : 0u;
+        uint32_t t[kPq2Dwords];
+#pragma unroll
+        for (int j = 0; j < kPq2Dwords; ++j) t[j] = (d[(j + sh) % kPq2Dwords] & m) | (d[j] & ~m);
+#pragma unroll
+        for (int j = 0; j < kPq2Dwords; ++j) d[j] = t[j];
+    }
+}
+
+// T[slot][b] for b in [32 BQ, 32 BQ + 32): b = f0 | f1 << 2 | f2 << 4 | f3 << 6;
+// T = A[b & 15] + B[b >> 4] with A = w(f0) x0 + w(f1) x1, B = w(f2) x2 + w(f3) x3.
+template <int BQ>
+__device__ __forceinline__ void pq2_build_range(float *tab, int slot, const float (&xv)[4])
+{
+    float A[16], B[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int q0 = q & 3, q1 = q >> 2;
+        const float w0 = q0 == 3 ? 0.0f : static_cast<float>(q0 - 1), w1 = q1 == 3 ? 0.0f : static_cast<float>(q1 - 1);
+        A[q] = w0 * xv[0] + w1 * xv[1];
+        B[q] = w0 * xv[2] + w1 * xv[3];
+    }
+    const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
+#pragma unroll
+    for (int i = 0; i < kLutBuildPer; ++i) {
+        const int b = kLutBuildPer * BQ + i;
+        *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
+            A[b & 15] + B[b >> 4];
+    }
+}
+
+template <int BQ>
+__device__ __forceinline__ void pq2_build_dispatch(int bq, float *tab, int slot, const float (&xv)[4])
+{
+    if constexpr (BQ < kLutBuildRanges) {
+        if (bq == BQ)
+            pq2_build_range<BQ>(tab, slot, xv);
+        else
+            pq2_build_dispatch<BQ + 1>(bq, tab, slot, xv);
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float *xs, int s, int u0, int u1)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int64_t k0 = static_cast<int64_t>(s) * kLutSliceW;
+    const int kw = static_cast<int>(a.k - k0 < kLutSliceW ? a.k - k0 : kLutSliceW);
+    const int nblk = kw / kBlockWeights;
+    const int row_l = lane >> 1;
+    const int blk_l = lane & 1;
+    const int rho = pq2_rho(lane), sig = pq2_sig(lane);
+
+    // ---- 1. x for the slice's rotation, requested before any weights
+    const int64_t c0 = (k0 / kHadamard) * kHadamard;
+    float xv16[kRotPerLane], sv16[kRotPerLane];
+    if (wave == 0) {
+        if (a.signs != nullptr) {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane; ++j) {
+                const int e = kLutSliceW * (j >> 2) + lane + kWave * (j & 3);
+                xv16[j] = a.x[c0 + e];
+                sv16[j] = a.signs[e];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane / 4; ++j) {
+                const int e = lane + kWave * j;
+                xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. weights: one unit before x arrives, up to kLutDepth after
+    uint32_t dat[U][kPq2Dwords];
+    uint32_t scw[U];
+    auto unit_of = [&](int i) { return u0 + wave + kLutWaves * i; };
+    auto issue = [&](int i) {
+        const int un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
+        // tiled matrices are below 2 GiB (checked by the caller)
+        const uint8_t *tb = a.w + (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
+                                   static_cast<uint32_t>(un)) * static_cast<uint32_t>(kPq2TileBytes);
+        const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(tb + lane * kPq2CodeBytes);
+        const lut_u32x4 hi = *reinterpret_cast<const lut_u32x4 *>(tb + lane * kPq2CodeBytes + 16);
+        dat[i][0] = lo.x; dat[i][1] = lo.y; dat[i][2] = lo.z; dat[i][3] = lo.w;
+        dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z; dat[i][7] = hi.w;
+        scw[i] = *reinterpret_cast<const uint32_t *>(tb + kPq2TileCodeBytes + 4 * (lane >> 1));  // scales of 2i, 2i+1
+    };
+#pragma unroll
+    for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- per-lane lookup constants (as in the PTQ1_0 kernel; slot < 64)
+    uint32_t P[kPq2Dwords];
+    uint32_t S[4];
+    uint32_t boff = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t e = static_cast<uint32_t>((c + sig) & 3);
+        S[c] = 0x0C0C0000u | (e << 8) | static_cast<uint32_t>(4 + c);
+        boff |= (e << 2) << (8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < kPq2Dwords; ++j) {
+        const int q = (j + rho) & (kPq2Dwords - 1);
+        const uint32_t base = static_cast<uint32_t>(kPq2CodeBytes * blk_l + 4 * q) << 2;
+        P[j] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;
+    }
+#pragma unroll
+    for (int j = 0; j < kPq2Dwords; ++j) asm volatile("" : "+v"(P[j]));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. the slice's x, rotated
+    if (wave == 0) {
+        if (a.signs != nullptr) {
+            const int part = static_cast<int>((k0 - c0) / kLutSliceW);
+            const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
+            float z[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float t0 = xv16[kk] * sv16[kk], t1 = xv16[4 + kk] * sv16[4 + kk];
+                const float t2 = xv16[8 + kk] * sv16[8 + kk], t3 = xv16[12 + kk] * sv16[12 + kk];
+                z[kk] = fmaf(sa, t1, t0) + sb * fmaf(sa, t3, t2);
+            }
+            lut_fwht256(z, lane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) xs[lane + kWave * kk] = z[kk] * (1.0f / 32.0f);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane / 4; ++j) {
+                const int e = lane + kWave * j;
+                xs[e] = e < kw ? xv16[j] : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = kLutEarly; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- 4. table: thread = (slot, 32-value range of the byte)
+    {
+        const int bq = tid >> 6;
+        const int slot = tid & 63;  // all 64 slots are used
+        const int blk = slot / kPq2CodeBytes, i = slot % kPq2CodeBytes;
+        float xv[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) xv[f] = blk < nblk ? xs[blk * kBlockWeights + kPq2CodesPerByte * i + f] : 0.0f;
+        pq2_build_dispatch<0>(bq, tab, slot, xv);
+    }
+    pq2_rotate(dat[0], rho);
+    __syncthreads();
+
+    // ---- 5. lookups, scale, 2-lane reduction, partial store
+    typedef __attribute__((address_space(3))) const float lds_f32;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        if (i + kLutDepth < U) issue(i + kLutDepth);
+        const bool unit_ok = unit_of(i) < u1;
+        const int un = unit_ok ? unit_of(i) : u1 - 1;
+        const int r = un * kLutRows + row_l;
+        const bool live = unit_ok && r < a.n && blk_l < nblk;
+        const uint32_t sh = blk_l ? (scw[i] >> 16) : (scw[i] & 0xffffu);
+        const float scale = live ? half_bits_to_float(sh) : 0.0f;
+        if (i > 0) pq2_rotate(dat[i], rho);
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kPq2Dwords; ++j) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
+                const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
+                if ((c & 1) == 0) acc0 += t; else acc1 += t;
+            }
+        }
+        float p = (acc0 + acc1) * scale;
+        const int ip = __builtin_bit_cast(int, p);
+        p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
+        if (unit_ok && blk_l == 0 && r < a.n) a.part[static_cast<int64_t>(s) * a.n + r] = p;
+    }
+}
+
+template <int U>
+__global__ void __launch_bounds__(kLutThreads, 4) k_pq2_matvec(Pq2Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float *tab = reinterpret_cast<float *>(lds);
+    float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);
+    const int per_slice = static_cast<int>(a.groups);
+    const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
+    const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
+    if (u0 < u1) pq2_segment<U>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);
+}
+
+template <int U>
+static hipError_t pq2_launch(const Pq2Args &a, int64_t chunks, hipStream_t st)
+{
+    static std::atomic<uint64_t> lds_done{0};
+    const size_t lds = kLutTableBytes + kLutSliceW * sizeof(float);
+    const hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&k_pq2_matvec<U>), static_cast<int>(lds), lds_done);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.nslices));
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(k_pq2_matvec<U>, grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
+                              pe.stop, 0u, a);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(k_pq2_matvec<U>, grid, dim3(kLutThreads), lds, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pq2_matvec(const uint8_t *w, int64_t n, int64_t k, const float *x, const float *signs,
+                             float *part, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    Pq2Args a{};
+    a.w = w;
+    a.n = n;
+    a.k = k;
+    a.nslices = static_cast<int>(lut_nslices(k));
+    a.groups = (n + kLutRows - 1) / kLutRows;
+    a.x = x;
+    a.signs = signs;
+    a.part = part;
+    const LutPlan pl = lut_plan(a.groups, a.nslices);
+    a.per_wg = pl.per_wg;
+    switch (pl.U) {
+        case 1: return pq2_launch<1>(a, pl.chunks, s);
+        case 2: return pq2_launch<2>(a, pl.chunks, s);
+        case 3: return pq2_launch<3>(a, pl.chunks, s);
+        case 4: return pq2_launch<4>(a, pl.chunks, s);
+        case 6: return pq2_launch<6>(a, pl.chunks, s);
+        default: return pq2_launch<8>(a, pl.chunks, s);
     }
 }
 

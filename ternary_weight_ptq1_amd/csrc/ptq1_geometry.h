@@ -38,6 +38,21 @@ constexpr int kTileSlots = kTileRows * kTileBlocks;   // 64 blocks
 constexpr int kTileBytes = kTileSlots * kBlockBytes;  // 1792
 static_assert(kTileBytes % 128 == 0, "tiles are whole 128-byte lines");
 
+// ---- PQ2_0 ("Why I Am Building Another Inference Engine", Level 2: two bits
+// per ternary weight plus one 16-bit scale per 128 weights).  Block: 32 code
+// bytes (weight 4i+n = 2-bit field n of byte i, low field first; code q is
+// weight q - 1, code 3 reads as 0), then the scale: 34 bytes.  Device tile:
+// 32 rows x 2 blocks as above, the 64 code records first (32 bytes each,
+// place 2i + b = block b of row i) and then the 64 scales in the same order,
+// so every record is 16-byte aligned.
+constexpr int kPq2CodesPerByte = 4;
+constexpr int kPq2CodeBytes = 32;                                  // 128 / 4
+constexpr int kPq2BlockBytes = 34;                                 // 32 + 2
+constexpr int kPq2TileCodeBytes = kTileSlots * kPq2CodeBytes;      // 2048
+constexpr int kPq2TileBytes = kPq2TileCodeBytes + kTileSlots * 2;  // 2176
+static_assert(kPq2CodeBytes * kPq2CodesPerByte == kBlockWeights, "code bytes hold a block");
+static_assert(kPq2TileBytes % 16 == 0, "PQ2_0 tiles keep 16-byte alignment");
+
 // ---- launch geometry -------------------------------------------------------
 constexpr int kWave = 64;                       // CDNA wavefront
 

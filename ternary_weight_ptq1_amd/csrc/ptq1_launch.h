@@ -28,6 +28,13 @@ hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w,
 // packed [n][k] -> tiled layout (kTileRows x kTileBlocks tiles, zero padding)
 hipError_t launch_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t s);
 
+// PQ2_0: pack, dequant, and the reorder into its tiled layout (kPq2TileBytes
+// per tile of 32 rows x 2 blocks)
+hipError_t launch_pq2_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k, uint8_t *blocks,
+                           hipStream_t s);
+hipError_t launch_pq2_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s);
+hipError_t launch_pq2_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled, hipStream_t s);
+
 // rows of x [m][k] -> y, each 1024-chunk (1/32) H (signs * chunk)
 hipError_t launch_rotate(const float *x, float *y, int64_t m, int64_t k, const float *signs,
                          hipStream_t s);
@@ -62,6 +69,10 @@ int64_t lut_nslices(int64_t k);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
                              const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
+// The same lookup matvec over a PQ2_0 tiled matrix (one matrix): part as
+// above, summed by launch_lut_sum_rows.
+hipError_t launch_pq2_matvec(const uint8_t *w, int64_t n, int64_t k, const float *x, const float *signs,
+                             float *part, hipStream_t s);
 // y[r] = (residual ? residual[r] : 0) + sum over slices of part[s][r] (nmat = 1)
 hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
                                hipStream_t s);

@@ -193,3 +193,56 @@ def test_empty_calls_enqueue_nothing():
     assert L().hadamard_unrotate_rows(X, 100, 1024, None, 0, S, Y, None) == 0
     assert L().ptq1_swiglu(X, X, Y, 0, None) == 0
     assert L().ptq1_dequant(B, 0, 128, Y, None) == 0
+
+
+def test_pq2_sizes():
+    """PQ2_0 ("Why I Am Building Another Inference Engine", Level 2): 34-byte
+    blocks, held against the oracle's block size; tiles of 32 rows x 2 blocks
+    of 2176 bytes (64 records of 32 code bytes, then 64 scales)."""
+    assert oracle.lib().orc_pq2_block_bytes() == P.PQ2_BLOCK_BYTES == 34
+    assert P.pq2_packed_bytes(17408, 5120) == 17408 * 40 * 34
+    assert P.pq2_packed_bytes(0, 128) == 0
+    assert P.pq2_packed_bytes(1, 100) == -1
+    assert P.pq2_packed_bytes(1 << 62, 1 << 20) == -1
+    assert P.pq2_tiled_bytes(17408, 5120) == (17408 // 32) * 20 * 2176
+    assert P.pq2_tiled_bytes(1, 128) == 2176
+    assert P.pq2_tiled_bytes(33, 384) == 2 * 2 * 2176
+    assert P.pq2_tiled_bytes(1, 100) == -1
+    assert P.pq2_tiled_bytes(1 << 62, 1 << 20) == -1
+    # bytes per weight at a whole tile: 2176 / (32 * 256) = 2.125 bits / 8
+    assert P.pq2_tiled_bytes(32, 256) * 8 / (32 * 256) == 2.125
+
+
+def test_pq2_validation():
+    B, X, Y, WS, S = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400, 500))
+    rc, msg = _err(L().pq2_pack(None, C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE * 2), None))
+    assert rc == 1 and "trits" in msg
+    rc, msg = _err(L().pq2_pack(C.c_void_p(FAKE), C.c_void_p(FAKE), 4, 100, C.c_void_p(FAKE * 2), None))
+    assert rc == 2
+    rc, msg = _err(L().pq2_pack(C.c_void_p(FAKE), C.c_void_p(FAKE * 4), 4, 128, C.c_void_p(FAKE + 16), None))
+    assert rc == 7
+    rc, msg = _err(L().pq2_tile(C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE * 2 + 8), None))
+    assert rc == 3 and "tiled" in msg
+    rc, msg = _err(L().pq2_tile(C.c_void_p(FAKE), 4, 128, C.c_void_p(FAKE + 64), None))
+    assert rc == 7
+    rc, msg = _err(L().pq2_dequant(B, 4, 128, C.c_void_p(FAKE + 64), None))
+    assert rc == 7
+    need = L().pq2_matvec_workspace_bytes(5120, 17408)
+    assert need == L().ptq1_matvec_workspace_bytes(5120, 17408) or need >= 68 * 5120 * 4
+    rc, msg = _err(L().pq2_matvec(B, 5120, 17408, X, S, None, Y, None, 0, None))
+    assert rc == 6 and "ws" in msg
+    rc, msg = _err(L().pq2_matvec(B, 5120, 17408 + 128, X, S, None, Y, WS, 1 << 30, None))
+    assert rc == 2 and "1024" in msg
+    rc, msg = _err(L().pq2_matvec(B, 5120, 17408, X, S, None, C.c_void_p(FAKE * 200 + 64), WS, 1 << 30, None))
+    assert rc == 7
+    rc, msg = _err(L().pq2_matvec(C.c_void_p(FAKE + 8), 5120, 17408, X, S, None, Y, WS, 1 << 30, None))
+    assert rc == 3
+    # 1 << 20 rows x 4096: the tiled matrix is above 2 GiB
+    far = [C.c_void_p((1 << 40) * i) for i in (1, 2, 3, 4)]
+    rc, msg = _err(L().pq2_matvec(B, 1 << 20, 1 << 13, far[0], far[1], None, far[2], far[3], 1 << 40, None))
+    assert rc == 5 and "2 GiB" in msg
+    assert L().pq2_matvec(B, 0, 5120, X, S, None, Y, WS, 0, None) == 0
+    assert L().pq2_pack(None, None, 0, 128, None, None) == 0
+    assert L().pq2_tile(None, 0, 128, None, None) == 0
+    assert L().pq2_dequant(B, 0, 128, Y, None) == 0
+    assert L().ptq1_profile_arm(b"pq2_matvec", None, None, 0) == 0

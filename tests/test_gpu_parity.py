@@ -593,3 +593,105 @@ def test_ffn_block_graph_replay_matches_eager():
         P.ptq1_ffn_block(other, tg, tu, td, s, d, f, 1e-6, ws=ws)  # eager work between replays
         torch.cuda.synchronize()
 
+
+
+# ---------------------------------------------------------------- PQ2_0 ----
+# "Why I Am Building Another Inference Engine", Level 2: two bits per ternary
+# weight, one 16-bit scale per 128 weights.  Codec work is compared byte for
+# byte; the matvec to TOL_FP32 against the oracle's fp64 product.
+
+def pq2_host(seed, n, k):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    return oracle.pq2_pack(t, s)
+
+
+def pq2_tile_host(blocks, n, k):
+    """The PQ2_0 tiled layout written out from its definition in
+    include/ptq1.h: tiles of 32 rows x 2 blocks, K-slices outermost; in tile
+    t * G + g, the 32 code bytes of block (32g + i, 2t + b) at (2i + b) * 32,
+    then its scale at 2048 + (2i + b) * 2; zeros past the matrix."""
+    nb = k // 128
+    bands, tk = -(-n // 32), -(-nb // 2)
+    full = np.zeros((bands * 32, tk * 2, 34), np.uint8)
+    full[:n, :nb] = np.asarray(blocks).reshape(n, nb, 34)
+    per_tile = full.reshape(bands, 32, tk, 2, 34).transpose(2, 0, 1, 3, 4).reshape(tk * bands, 64, 34)
+    codes = per_tile[:, :, :32].reshape(-1, 2048)
+    scales = per_tile[:, :, 32:].reshape(-1, 128)
+    return np.concatenate([codes, scales], axis=1).reshape(-1)
+
+
+@pytest.mark.parametrize("n,k,seed", [(1024, 1024, 0), (37, 384, 1), (1, 128, 2), (17408, 5120, 3)])
+def test_pq2_pack_bit_exact(n, k, seed):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    t[0, :5] = [-3, 2, 127, -128, 0]  # out-of-range trits are clamped on both sides
+    got = host(P.pq2_pack(to_dev(t), to_dev(s.view(np.int16))))
+    np.testing.assert_array_equal(got, oracle.pq2_pack(t, s))
+
+
+def test_pq2_dequant_every_byte():
+    """Arbitrary code bytes, code 3 included (it reads as weight 0), and
+    every scale class (normal, subnormal, zero, negative)."""
+    n, k = 64, 1024
+    rng = np.random.default_rng(11)
+    b = rng.integers(0, 256, size=(n, k // 128, 34), dtype=np.uint8)
+    b[0, 0, :32] = np.arange(256, dtype=np.uint8)[:32]
+    b[1, :, :32] = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    sc = np.array([0x3C00, 0x0001, 0x0000, 0xBC00, 0x7BFF, 0x8001, 0x3555, 0x2E66], np.uint16)
+    b[:, :, 32:] = sc[rng.integers(0, len(sc), size=(n, k // 128))].view(np.uint8).reshape(n, k // 128, 2)
+    b = b.reshape(n, -1)
+    got = host(P.pq2_dequant(to_dev(b), n, k))
+    np.testing.assert_array_equal(got.astype(np.float64), oracle.pq2_dequant(b, n, k))
+
+
+@pytest.mark.parametrize("n,k,seed", [(1, 128, 0), (33, 384, 1), (64, 1024, 2), (100, 640, 3)])
+def test_pq2_tile_bit_exact(n, k, seed):
+    b = pq2_host(seed, n, k)
+    got = host(P.pq2_tile(to_dev(b), n, k))
+    assert got.size == P.pq2_tiled_bytes(n, k)
+    np.testing.assert_array_equal(got, pq2_tile_host(b, n, k))
+
+
+@pytest.mark.parametrize("n,k,seed,rot", [(1024, 1024, 0, True), (300, 384, 1, False), (257, 3072, 2, True),
+                                          (1, 128, 3, False), (17, 640, 4, False), (5120, 17408, 2, True)])
+def test_pq2_matvec(n, k, seed, rot):
+    b = pq2_host(seed, n, k)
+    x = synth.activations(seed, 1, k)[0]
+    sg = synth.signs(seed)
+    got = host(P.pq2_matvec(P.pq2_tile(to_dev(b), n, k), n, k, to_dev(x), to_dev(sg) if rot else None))
+    xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
+    assert rel_l2(got, oracle.pq2_matvec(b, n, k, xr)) <= TOL_FP32
+
+
+def test_pq2_matvec_code3_residual_and_in_place():
+    """Code 3 in the stream (never written by pq2_pack, read as 0), a
+    residual, and y == residual."""
+    n, k = 96, 2048
+    rng = np.random.default_rng(5)
+    b = rng.integers(0, 256, size=(n, k // 128, 34), dtype=np.uint8)
+    b[:, :, 32:] = synth.scales(5, synth.S_W_SCALES, n, k // 128).view(np.uint8).reshape(n, k // 128, 2)
+    b = b.reshape(n, -1)
+    x = synth.activations(5, 1, k)[0]
+    sg = synth.signs(5)
+    res = synth.gauss(5, 77, n)
+    tb = P.pq2_tile(to_dev(b), n, k)
+    ref = oracle.pq2_matvec(b, n, k, oracle.rotate(x, sg)) + res
+    got = host(P.pq2_matvec(tb, n, k, to_dev(x), to_dev(sg), residual=to_dev(res)))
+    assert rel_l2(got, ref) <= TOL_FP32
+    y = to_dev(res.copy())
+    P.pq2_matvec(tb, n, k, to_dev(x), to_dev(sg), residual=y, out=y)
+    assert rel_l2(host(y), ref) <= TOL_FP32
+
+
+def test_pq2_matvec_gate_up_shape():
+    """The stacked gate and up projections of one layer, 34816 x 5120, in
+    PQ2_0; 256 sampled rows (first, last, random) against the oracle."""
+    n, k, seed = 34816, 5120, 6
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pq2_pack(t, s)
+    del t
+    x = synth.activations(seed, 1, k)[0]
+    sg = synth.signs(seed)
+    got = host(P.pq2_matvec(P.pq2_tile(to_dev(b), n, k), n, k, to_dev(x), to_dev(sg)))
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 254, n)])).astype(np.int64)
+    ref = oracle.pq2_matvec(b[rows], len(rows), k, oracle.rotate(x, sg))
+    assert rel_l2(got[rows], ref) <= TOL_FP32
