@@ -197,8 +197,8 @@ int orc_dequant(const uint8_t *blocks, int64_t n, int64_t k, double *w)
 }
 
 /* ---- PQ2_0: the 2-bit ternary format of "Why I Am Building Another
- * Inference Engine", Level 2 ("each ternary weight in 2 bits plus one
- * 16-bit scale per 128 weights, 2.125 bits per weight").  Readings (the
+ * Inference Engine", Level 2 (two bits for every ternary weight and a
+ * 16-bit scale for every 128 of them: 2.125 bits per weight).  Readings (the
  * page gives neither field order nor code map): weight 4i+n of a block is
  * the 2-bit field n (n = 0 least significant) of byte i; code q in {0,1,2}
  * is the weight q - 1; code 3 (never written) decodes as weight 0; the 32
