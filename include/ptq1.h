@@ -273,13 +273,22 @@ size_t pq2_matvec_workspace_bytes(int64_t n, int64_t k);
 ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *signs1024,
                        const float *residual, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Multi-token prefill GEMM over a PQ2_0 tiled matrix, with the arguments,
+ * numerics, limits and errors of ptq1_gemm: Y [m][n] fp32 = bf16(R X) . W^T,
+ * codes entering bf16 MFMA exactly as -1 / 0 / +1 and each block's partial
+ * sum scaled by its fp16 scale in fp32. */
+size_t pq2_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m, const float *signs1024,
+                     float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
  * next `count` launches of one kernel family (hipExtLaunchKernel: they take
  * the kernel's own start and end times on its stream), so a caller can time
  * a kernel inside a composite call (ptq1_ffn_block) with events.  Families: "lut_matvec_2" (the
  * table-lookup matvec over two matrices: gate and up), "lut_matvec_1" (over
  * one matrix: ptq1_matvec, the down projection), "gemm" (the MFMA GEMM),
- * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec).
+ * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec); pq2_gemm's
+ * kernel counts as "gemm".
  * Events are created and owned by the caller; both arrays must stay valid
  * until `count` launches have happened or the family is re-armed.  count =
  * 0 disarms.  Process-wide; not meant for concurrent use by several

@@ -180,6 +180,15 @@ def pq2_matvec(blocks: np.ndarray, n: int, k: int, xr: np.ndarray, rows=None) ->
     return w @ _f64(xr).reshape(k)
 
 
+def pq2_gemm(blocks: np.ndarray, n: int, k: int, xr: np.ndarray, rows=None) -> np.ndarray:
+    """Y [m, len(rows) or n] = xr [m, k] . W^T, W the dequantised PQ2_0 rows (fp64)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, -1)
+    if rows is not None:
+        b = b[np.asarray(rows, dtype=np.int64)]
+    w = pq2_dequant(b, b.shape[0], k)
+    return _f64(xr).reshape(-1, k) @ w.T
+
+
 def hadamard_entry(i: int, j: int) -> float:
     return lib().orc_hadamard_entry(int(i), int(j))
 

@@ -69,6 +69,8 @@ _SIGS = {
     "pq2_tile": ([p, i64, i64, p, p], C.c_int),
     "pq2_matvec_workspace_bytes": ([i64, i64], sz),
     "pq2_matvec": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
+    "pq2_gemm_workspace_bytes": ([i64, i64, i64], sz),
+    "pq2_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
@@ -373,10 +375,25 @@ def pq2_matvec(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: 
     return out
 
 
+def pq2_gemm(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
+             out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y [m, n] = bf16(R X) . W^T over a PQ2_0 tiled matrix (pq2_tile)."""
+    _dev(tiled, "tiled", torch.uint8)
+    _dev(x, "x", torch.float32)
+    m = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, "y", torch.float32)
+    ws, wsb = _ws(lib().pq2_gemm_workspace_bytes(m, n, k), x.device, ws)
+    _check("pq2_gemm", lib().pq2_gemm(_ptr(tiled), n, k, _ptr(x), m, _ptr(signs1024), _ptr(out), _ptr(ws), wsb,
+                                      _stream(stream)))
+    return out
+
+
 def workspace_bytes(kind: str, *shape) -> int:
     fn = {"matvec": "ptq1_matvec_workspace_bytes", "gate_up": "ptq1_gate_up_workspace_bytes",
           "gemm": "ptq1_gemm_workspace_bytes", "ffn": "ptq1_ffn_workspace_bytes",
-          "pq2_matvec": "pq2_matvec_workspace_bytes"}[kind]
+          "pq2_matvec": "pq2_matvec_workspace_bytes", "pq2_gemm": "pq2_gemm_workspace_bytes"}[kind]
     return int(getattr(lib(), fn)(*shape))
 
 

@@ -791,4 +791,41 @@ ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *
     return hip_status(e, "pq2_matvec");
 }
 
+size_t pq2_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (pq2_packed(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
+    if (m == 0) return 0;
+    return gemm_layout(ptq1::gemm_plan(m, n, k, true), k).total;
+}
+
+ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m, const float *signs1024,
+                     float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, mk, mn, xb, yb;
+    PTQ1_TRY(check_pq2(tiled, "tiled", n, k, signs1024 != nullptr, &wb, true));
+    if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
+    if (!mul_ok(m, k, &mk) || !mul_ok(m, n, &mn)) return fail(PTQ1_ERR_OVERFLOW, "m * k or m * n overflows");
+    PTQ1_TRY(check_floats(y, "y", mn, &yb));
+    if (mn == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", mk, &xb));
+    PTQ1_TRY(check_signs(signs1024, false));
+    const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k, true);
+    const GemmWs L = gemm_layout(plan, k);
+    const size_t need = L.total;
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "pq2_gemm"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps tiled");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, tiled, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    char *w = static_cast<char *>(ws);
+    uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
+    float *part = reinterpret_cast<float *>(w + L.part);
+    hipError_t e = ptq1::launch_prep_frag_pq2(x, m, k, signs1024, xf, stream);
+    if (e == hipSuccess)
+        e = profiled(kProfGemm, stream, [&] { return ptq1::launch_gemm_pq2(plan, xf, m, tiled, n, y, part, stream); });
+    return hip_status(e, "pq2_gemm");
+}
+
 }  // extern "C"

@@ -60,7 +60,11 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 // v_mfma_f32_32x32x16_bf16 for that step.
 // Rows >= m are never written: an output row of the MFMA depends only on
 // its own A row, so whatever they hold only reaches outputs nobody stores.
+// Q2 (the PQ2_0 GEMM): fragment f = 8 h + s holds weights 8 f .. 8 f + 7 in
+// order, i.e. step s, half h takes block positions 64 h + 8 s + j, which are
+// the two code bytes 16 h + 2 s, 16 h + 2 s + 1 of a PQ2_0 block.
 // ---------------------------------------------------------------------------
+template <bool Q2>
 __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
     int64_t k, const float *__restrict__ signs, float rms_eps, const float *__restrict__ gain,
@@ -180,12 +184,14 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
         gm_u32x4 o;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t lo = f32_to_bf16_rne(src[gemm_kperm(8 * f + 2 * jj)]);
-            const uint32_t hi = f32_to_bf16_rne(src[gemm_kperm(8 * f + 2 * jj + 1)]);
+            const int w0 = Q2 ? 8 * f + 2 * jj : gemm_kperm(8 * f + 2 * jj);
+            const int w1 = Q2 ? 8 * f + 2 * jj + 1 : gemm_kperm(8 * f + 2 * jj + 1);
+            const uint32_t lo = f32_to_bf16_rne(src[w0]);
+            const uint32_t hi = f32_to_bf16_rne(src[w1]);
             o[jj] = lo | (hi << 16);
         }
         // (step, half) that carries fragment f
-        const int fs = f < 8 ? f : (f < 10 ? f - 3 : (f < 15 ? f - 10 : 7));
+        const int fs = Q2 ? (f & 7) : (f < 8 ? f : (f < 10 ? f - 3 : (f < 15 ? f - 10 : 7)));
         const int fh = f < 8 ? 0 : 1;
         const int64_t off = (((mt * nb + kb) * 8 + fs) * kWave + rl + 32 * fh) * 8;
         *reinterpret_cast<gm_u32x4 *>(xf + off) = o;
@@ -640,6 +646,14 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
 // bytes 8-15 (0, 1, 2 in lanes 0-31; 3, 4 and fragment 15 in lanes 32-63).
 // Table entries here are [H0 H1 H2 H3 | H4 H1 H2 H3] so that the two halves'
 // digits of steps 5 and 6 sit in the same dword.
+//
+// Q2: the same kernel over a PQ2_0 tiled matrix ("Why I Am Building Another
+// Inference Engine", Level 2).  A table entry is the four weights of a code
+// byte as bf16 (-1, 0, +1; code 3 -> 0), low field first, so the fragment of
+// step s is the entries of code bytes 16 h + 2 s and 16 h + 2 s + 1 side by
+// side (activations in the prep kernel's Q2 order).  Lane l loads the 16
+// code bytes 16 h .. 16 h + 15 of its column's block and the tile's dword
+// of that row's two scales; the scale is applied unhalved.
 // ---------------------------------------------------------------------------
 constexpr int kRdThreads = 256;
 constexpr int kRdTabCopies = 32;                    // conflict-free 8-byte reads
@@ -653,7 +667,7 @@ __device__ __forceinline__ constexpr uint32_t rd_sel(int b)
 
 // LR: 8-row groups of the last row tile that hold activation rows (the
 // others are zero padding and are neither scaled nor stored).
-template <int TM, int PD, int LR>
+template <int TM, int PD, int LR, bool Q2>
 __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
 {
     static_assert(LR >= 1 && LR <= 4, "8-row groups of a 32-row tile");
@@ -671,15 +685,26 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     // (built in the first segment, once its first loads are in flight)
     auto build_table = [&]() {
         const uint32_t b = static_cast<uint32_t>(tid);
-        uint32_t r = b, h[5];
+        gm_u32x2 e;
+        if constexpr (Q2) {
+            uint32_t q[4];
 #pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const uint32_t t = 3u * r;
-            h[n] = trit_hi(t >> 8);
-            r = t & 0xffu;
+            for (int f = 0; f < 4; ++f) {
+                const uint32_t c = (b >> (2 * f)) & 3u;
+                q[f] = c == 0 ? 0xBF80u : (c == 2 ? 0x3F80u : 0u);  // bf16 -1, +1; codes 1 and 3 -> 0
+            }
+            e = gm_u32x2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+        } else {
+            uint32_t r = b, h[5];
+#pragma unroll
+            for (int n = 0; n < 5; ++n) {
+                const uint32_t t = 3u * r;
+                h[n] = trit_hi(t >> 8);
+                r = t & 0xffu;
+            }
+            e = gm_u32x2{h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24),
+                         h[4] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24)};
         }
-        const gm_u32x2 e = {h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24),
-                            h[4] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24)};
 #pragma unroll 8
         for (int i = 0; i < kRdTabCopies; ++i)
             *reinterpret_cast<gm_u32x2 *>(lds + b * 256 + ((b + i) & (kRdTabCopies - 1)) * 8) = e;
@@ -725,22 +750,42 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
         const int64_t gcol = tile_n + wave * 32 + (lane & 31);
         const uint8_t *wcol = a.w0;
         int64_t sstride = 0;
+        int64_t sc_off = 0;  // Q2: from the row's first record to its scale pair
         if (gcol < rows) {
             const bool first = gcol < a.n0;
             const int64_t rr = first ? gcol : gcol - a.n0;
-            wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
-            sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+            if constexpr (Q2) {
+                // records of row i of a tile at 64 i, its scale pair at 2048 + 4 i
+                const int64_t i = rr % kTileRows;
+                wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kPq2TileBytes + i * (kTileBlocks * kPq2CodeBytes);
+                sstride = (first ? a.bands0 : a.bands1) * kPq2TileBytes;
+                sc_off = kPq2TileCodeBytes + 4 * i - i * (kTileBlocks * kPq2CodeBytes);
+            } else {
+                wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes +
+                       (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+                sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+            }
         }
 
         struct WRegs {
-            gm_u32x4 v;  // bytes 8 h .. 8 h + 15
-            uint32_t w;  // bytes 24..27
+            gm_u32x4 v;  // bytes 8 h .. 8 h + 15 (Q2: code bytes 16 h .. 16 h + 15)
+            uint32_t w;  // bytes 24..27 (Q2: the row's two scales)
+            int sh;      // Q2: 16 for the slice's second block
         };
         auto load_w = [&](WRegs &r, int64_t kb) {
-            const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
-            const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 8 * hi);
-            r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
-            r.w = *reinterpret_cast<const uint32_t *>(p + 24);
+            if constexpr (Q2) {
+                const uint8_t *t = wcol + (kb >> 1) * sstride;
+                const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(t + (kb & 1) * kPq2CodeBytes + 16 * hi);
+                r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
+                r.w = *reinterpret_cast<const uint32_t *>(t + sc_off);
+                r.sh = static_cast<int>(kb & 1) * 16;
+            } else {
+                const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+                const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 8 * hi);
+                r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
+                r.w = *reinterpret_cast<const uint32_t *>(p + 24);
+                r.sh = 0;
+            }
         };
         auto tab_read = [&](uint32_t w, int byte) -> gm_u32x2 {
             const uint32_t addr = __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
@@ -753,6 +798,17 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
             float scale;    // the block's scale, halved (trits are stored as +-2)
         };
         auto tab_reads = [&](const WRegs &r, Ent &e) {
+            if constexpr (Q2) {  // g: code bytes of steps 0-3, m: of steps 4-7
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e.g[i] = tab_read(r.v[0], i);
+                    e.g[4 + i] = tab_read(r.v[1], i);
+                    e.m[i] = tab_read(r.v[2], i);
+                    e.m[4 + i] = tab_read(r.v[3], i);
+                }
+                e.scale = half_bits_to_float((r.w >> r.sh) & 0xffffu);
+                return;
+            }
             const uint32_t g0 = hi ? r.v[2] : r.v[0], g1 = hi ? r.v[3] : r.v[1];
             const uint32_t m0 = hi ? r.v[0] : r.v[2], m1 = hi ? r.v[1] : r.v[3];
 #pragma unroll
@@ -771,6 +827,12 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
         const uint32_t sel6 = hi ? rd_sel(0) : rd_sel(1);
         auto bfrag = [&](const Ent &e, int st) -> bf16x8 {
             gm_u32x4 o;
+            if constexpr (Q2) {
+                const gm_u32x2 *src = st < 4 ? e.g : e.m;
+                const int j = 2 * (st & 3);
+                o = gm_u32x4{src[j][0], src[j][1], src[j + 1][0], src[j + 1][1]};
+                return __builtin_bit_cast(bf16x8, o);
+            }
             if (st < 5) {
                 const int c = st == 4 ? 1 : 0;
                 const uint32_t sl = rd_sel(st == 4 ? 0 : st);
@@ -988,7 +1050,7 @@ constexpr int kPlanCus = 256;   // compute units the grid is sized for
 constexpr int kMinBlocks = 4;   // fewest units a workgroup takes
 }  // namespace
 
-GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
+GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k, bool rd_only)
 {
     // cfg 0 / 1: register-decode kernel, 32 / 64 rows, two workgroups per
     // CU; cfg 2: LDS-decode kernel, 128 rows with 8 waves, one per CU.
@@ -998,7 +1060,7 @@ GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k)
     static const int64_t kBm[3] = {32, 64, 128};
     static const int64_t kPerCu[3] = {2, 2, 1};
     GemmPlan p;
-    p.cfg = m <= 32 ? 0 : (m <= 64 ? 1 : 2);
+    p.cfg = m <= 32 ? 0 : (m <= 64 || rd_only ? 1 : 2);
     const int64_t bm = kBm[p.cfg];
     p.m_pad = (m + bm - 1) / bm * bm;
     p.nb = k / kBlockWeights;
@@ -1028,8 +1090,19 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prep_frag, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u, k,
-                       signs, rms_eps, gain, xf);
+    hipLaunchKernelGGL(k_prep_frag<false>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u,
+                       k, signs, rms_eps, gain, xf);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_frag_pq2(const float *x, int64_t m, int64_t k, const float *signs, uint16_t *xf,
+                                hipStream_t s)
+{
+    const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
+    if (nchunks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_prep_frag<true>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+                       static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k, signs, 0.0f,
+                       static_cast<const float *>(nullptr), xf);
     return hipGetLastError();
 }
 
@@ -1054,11 +1127,11 @@ static hipError_t gemm_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
     return hipGetLastError();
 }
 
-template <int TM, int PD, int LR>
+template <int TM, int PD, int LR, bool Q2 = false>
 static hipError_t gemm_rd_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
 {
     static std::atomic<uint64_t> lds_done{0};
-    const auto kernel = k_gemm_rd<TM, PD, LR>;
+    const auto kernel = k_gemm_rd<TM, PD, LR, Q2>;
     const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), kRdLds, lds_done);
     if (e != hipSuccess) return e;
     ProfEvents &pe = prof_events();
@@ -1072,12 +1145,9 @@ static hipError_t gemm_rd_dispatch(dim3 grid, hipStream_t s, const GemmArgs &arg
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
-                       const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
-                       hipStream_t s)
+static GemmArgs gemm_args(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                          const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part)
 {
-    const int64_t rows = n0 + n1;
-    if (rows == 0 || m == 0 || p.nb == 0) return hipSuccess;
     GemmArgs a;
     a.xf = xf;
     a.w0 = w0;
@@ -1099,6 +1169,24 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     a.dp_tiles = p.dp_rounds * p.wgs;
     a.sk_units = p.sk_tiles * p.nb;
     a.sk_wgs = a.sk_units < p.wgs ? a.sk_units : p.wgs;
+    return a;
+}
+
+static hipError_t gemm_fix(const GemmPlan &p, const GemmArgs &a, hipStream_t s)
+{
+    if (p.sk_tiles == 0) return hipSuccess;
+    const unsigned ey = static_cast<unsigned>((p.prow + kFixRows - 1) / kFixRows);
+    hipLaunchKernelGGL(k_gemm_fix, dim3(static_cast<unsigned>(p.sk_tiles), ey), dim3(kEwThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                       const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
+                       hipStream_t s)
+{
+    const int64_t rows = n0 + n1;
+    if (rows == 0 || m == 0 || p.nb == 0) return hipSuccess;
+    const GemmArgs a = gemm_args(p, xf, m, w0, n0, w1, n1, y0, y1, residual, part);
     const dim3 grid(static_cast<unsigned>(p.wgs));
     hipError_t e;
     if (p.cfg == 0) {
@@ -1114,10 +1202,29 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
         e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     }
     if (e != hipSuccess) return e;
-    if (p.sk_tiles == 0) return hipSuccess;
-    const unsigned ey = static_cast<unsigned>((p.prow + kFixRows - 1) / kFixRows);
-    hipLaunchKernelGGL(k_gemm_fix, dim3(static_cast<unsigned>(p.sk_tiles), ey), dim3(kEwThreads), 0, s, a);
-    return hipGetLastError();
+    return gemm_fix(p, a, s);
+}
+
+hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w, int64_t n, float *y,
+                           float *part, hipStream_t s)
+{
+    if (n == 0 || m == 0 || p.nb == 0) return hipSuccess;
+    if (p.cfg > 1) return hipErrorInvalidValue;  // register-decode plans only (gemm_plan(..., true))
+    const GemmArgs a = gemm_args(p, xf, m, w, n, nullptr, 0, y, nullptr, nullptr, part);
+    const dim3 grid(static_cast<unsigned>(p.wgs));
+    hipError_t e;
+    if (p.cfg == 0) {
+        if (m <= 8)
+            e = gemm_rd_dispatch<1, 4, 1, true>(grid, s, a);
+        else if (m <= 16)
+            e = gemm_rd_dispatch<1, 4, 2, true>(grid, s, a);
+        else
+            e = gemm_rd_dispatch<1, 4, 4, true>(grid, s, a);
+    } else {
+        e = gemm_rd_dispatch<2, 4, 4, true>(grid, s, a);
+    }
+    if (e != hipSuccess) return e;
+    return gemm_fix(p, a, s);
 }
 
 }  // namespace ptq1

@@ -92,7 +92,8 @@ struct GemmPlan {
     int64_t wgs = 0;   // workgroups
     int64_t dp_rounds = 0, sk_tiles = 0;  // whole-tile rounds; tiles shared by (tile, block) units
 };
-GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k);
+// rd_only: register-decode configurations (32 or 64 rows per row tile) at any m
+GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k, bool rd_only = false);
 size_t gemm_frag_elems(const GemmPlan &p, int64_t k);  // bf16 A fragments
 size_t gemm_part_floats(const GemmPlan &p);            // partial tiles of the work split
 // xf = bf16 MFMA A fragments of R (a * gain * x) (rows < m only); a = RMS
@@ -106,5 +107,11 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
                        hipStream_t s);
+// PQ2_0: A fragments in the Q2 order (launch_prep_frag_pq2), y [m][n] =
+// A . W^T over a PQ2_0 tiled matrix; p from gemm_plan(m, n, k, true).
+hipError_t launch_prep_frag_pq2(const float *x, int64_t m, int64_t k, const float *signs, uint16_t *xf,
+                                hipStream_t s);
+hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w, int64_t n, float *y,
+                           float *part, hipStream_t s);
 
 }  // namespace ptq1

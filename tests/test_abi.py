@@ -246,3 +246,13 @@ def test_pq2_validation():
     assert L().pq2_tile(None, 0, 128, None, None) == 0
     assert L().pq2_dequant(B, 0, 128, Y, None) == 0
     assert L().ptq1_profile_arm(b"pq2_matvec", None, None, 0) == 0
+    # the PQ2_0 GEMM: same argument rules as ptq1_gemm
+    gneed = L().pq2_gemm_workspace_bytes(256, 17408, 5120)
+    assert gneed >= 256 * 5120 * 2  # bf16 activation fragments at least
+    rc, msg = _err(L().pq2_gemm(B, 17408, 5120, X, 256, S, Y, WS, gneed - 1, None))
+    assert rc == 6
+    rc, msg = _err(L().pq2_gemm(B, 17408, 5120 + 128, X, 256, S, Y, WS, 1 << 40, None))
+    assert rc == 2 and "1024" in msg
+    rc, msg = _err(L().pq2_gemm(B, 17408, 5120, X, 65537, S, Y, WS, 1 << 40, None))
+    assert rc == 5
+    assert L().pq2_gemm(B, 17408, 5120, X, 0, S, Y, WS, 0, None) == 0

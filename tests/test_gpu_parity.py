@@ -695,3 +695,28 @@ def test_pq2_matvec_gate_up_shape():
     rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 254, n)])).astype(np.int64)
     ref = oracle.pq2_matvec(b[rows], len(rows), k, oracle.rotate(x, sg))
     assert rel_l2(got[rows], ref) <= TOL_FP32
+
+
+@pytest.mark.parametrize("m,n,k,rot", [(1, 300, 384, False), (8, 1024, 1024, True), (17, 257, 3072, True),
+                                       (40, 200, 640, False), (64, 1024, 2048, True), (100, 513, 1024, True),
+                                       (256, 1000, 2048, True)])
+def test_pq2_gemm_small(m, n, k, rot):
+    b = pq2_host(7, n, k)
+    x = synth.activations(7, m, k)
+    sg = synth.signs(7)
+    got = host(P.pq2_gemm(P.pq2_tile(to_dev(b), n, k), n, k, to_dev(x), to_dev(sg) if rot else None))
+    xr = oracle.rotate(x, sg) if rot else x.astype(np.float64)
+    assert rel_l2(got, oracle.pq2_gemm(b, n, k, xr)) <= TOL_BF16
+
+
+def test_pq2_gemm_prefill_shape():
+    """M = 256 prefill over the stacked gate+up shape 34816 x 5120 in PQ2_0,
+    on 256 sampled columns (weight rows)."""
+    m, n, k, seed = 256, 34816, 5120, 8
+    b = pq2_host(seed, n, k)
+    x = synth.activations(seed, m, k)
+    sg = synth.signs(seed)
+    got = host(P.pq2_gemm(P.pq2_tile(to_dev(b), n, k), n, k, to_dev(x), to_dev(sg)))
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 254, n)])).astype(np.int64)
+    ref = oracle.pq2_gemm(b, n, k, oracle.rotate(x, sg), rows=rows)
+    assert rel_l2(got[:, rows], ref) <= TOL_BF16

@@ -436,3 +436,20 @@ def test_generator_counter_based_and_distributions():
     assert x.dtype == np.float32 and len(synth.outlier_channels(0, synth.S_OUTLIERS, 1024)) == 8
     s = synth.signs(0)
     assert set(np.unique(s).tolist()) == {-1.0, 1.0}
+
+
+def test_pq2_gemm_is_rowwise_matvec():
+    """The PQ2_0 GEMM oracle row by row equals the matvec oracle (and a
+    sampled-row call equals the same rows of the whole product)."""
+    n, k, m = 37, 384, 3
+    rng = np.random.default_rng(2)
+    t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+    s = np.full((n, k // 128), 0x3C00, np.uint16)
+    b = oracle.pq2_pack(t, s)
+    x = rng.standard_normal((m, k))
+    y = oracle.pq2_gemm(b, n, k, x)
+    for i in range(m):
+        np.testing.assert_allclose(y[i], oracle.pq2_matvec(b, n, k, x[i]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y, x @ t.astype(np.float64).T, rtol=0, atol=1e-12)
+    rows = [0, 5, 36]
+    np.testing.assert_allclose(oracle.pq2_gemm(b, n, k, x, rows=rows), y[:, rows], rtol=0, atol=1e-12)
