@@ -392,7 +392,20 @@ def main() -> int:
         breakdown["pq2_gate_up_decode"] = {"us_kernel": us_q2, "GB/s": q2_bytes / (us_q2 * 1e-6) / 1e9,
                                            "bytes": q2_bytes, "call_us": ms_q2 * 1e3,
                                            "ptq1_kernel_us": us_gu}
-        del q2sets, y2, ws2
+        # and its M = 256 prefill GEMM (register-decode kernel at every M)
+        xq = torch.from_numpy(synth.activations(seed, 256, D)).to(dev)
+        yq = torch.empty((256, n2), dtype=torch.float32, device=dev)
+        wsq = torch.zeros(P.workspace_bytes("pq2_gemm", 256, n2, D), dtype=torch.uint8, device=dev)
+        timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 3, 0)  # warm-up
+        tq = P.KernelTimer("gemm", 30)
+        with tq:
+            timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 30, 0)
+        dq = tq.durations_ms()
+        tq.close()
+        us_gq = 1e3 * sum(dq) / len(dq)
+        breakdown["pq2_gate_up_prefill_M256"] = {"us_kernel": us_gq,
+                                                 "TFLOP/s": 2.0 * 256 * n2 * D / (us_gq * 1e-6) / 1e12}
+        del q2sets, y2, ws2, xq, yq, wsq
         torch.cuda.empty_cache()
 
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
