@@ -281,6 +281,14 @@ size_t pq2_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m, const float *signs1024,
                      float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The feed-forward block of ptq1_ffn_block over PQ2_0 tiled matrices: the
+ * same arguments, numerics (m = 1: fp32 table lookups; m >= 2: bf16 MFMA),
+ * workspace rule and errors; every matrix must be below 2 GiB at m = 1. */
+size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
+ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f, const uint8_t *w_gate,
+                          const uint8_t *w_up, const uint8_t *w_down, const float *signs1024, float rms_eps,
+                          const float *rms_gain, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
  * next `count` launches of one kernel family (hipExtLaunchKernel: they take
  * the kernel's own start and end times on its stream), so a caller can time

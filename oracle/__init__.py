@@ -261,6 +261,21 @@ def ffn_block(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     return out
 
 
+def pq2_ffn_block(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, signs: np.ndarray, d: int,
+                  f: int, rms_eps: float, gain: np.ndarray | None = None) -> np.ndarray:
+    """ffn_block over PQ2_0 matrices, composed step by step from the oracle's
+    rotate, PQ2_0 product, SwiGLU and RMS scale (the same definition)."""
+    x2 = _f64(x).reshape(-1, d)
+    xn = x2 * (rms_scale(x2, rms_eps).reshape(-1, 1) if rms_eps > 0 else 1.0)
+    if gain is not None:
+        xn = xn * _f64(gain).reshape(1, d)
+    xr = rotate(xn, signs)
+    g = pq2_gemm(wg, f, d, xr)
+    u = pq2_gemm(wu, f, d, xr)
+    h = swiglu(g, u)
+    return x2 + pq2_gemm(wd, d, f, rotate(h, signs))
+
+
 def embedding_unrotate(table_rows: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """Restore looked-up rows of a rotated embedding table: unrotate each row."""
     return unrotate(table_rows, signs)

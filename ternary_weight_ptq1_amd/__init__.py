@@ -71,6 +71,8 @@ _SIGS = {
     "pq2_matvec": ([p, i64, i64, p, p, p, p, p, sz, p], C.c_int),
     "pq2_gemm_workspace_bytes": ([i64, i64, i64], sz),
     "pq2_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
+    "pq2_ffn_workspace_bytes": ([i64, i64, i64], sz),
+    "pq2_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
@@ -290,9 +292,10 @@ def ptq1_gemm(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: 
 def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                    signs1024: torch.Tensor, d: int, f: int, rms_eps: float = 0.0,
                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                   stream=None, rms_gain: torch.Tensor | None = None) -> torch.Tensor:
+                   stream=None, rms_gain: torch.Tensor | None = None, fn: str = "ptq1_ffn_block") -> torch.Tensor:
     """x [m, d] -> x + W_down R(silu(W_gate R xn) * (W_up R xn)), xn = a * rms_gain * x (a = RMS
-    scale of x when rms_eps > 0; rms_gain [d] or None); out may be x."""
+    scale of x when rms_eps > 0; rms_gain [d] or None); out may be x.  fn = "pq2_ffn_block" takes
+    PQ2_0 tiled matrices (pq2_tile)."""
     _dev(x, "x", torch.float32)
     if rms_gain is not None:
         _dev(rms_gain, "rms_gain", torch.float32)
@@ -302,12 +305,19 @@ def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_
     if out is None:
         out = torch.empty_like(x)
     _dev(out, "x_out", torch.float32)
-    ws, wsb = _ws(lib().ptq1_ffn_workspace_bytes(m, d, f), x.device, ws)
-    _check("ptq1_ffn_block", lib().ptq1_ffn_block(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up),
-                                                  _ptr(w_down), _ptr(signs1024), float(rms_eps),
-                                                  _ptr(rms_gain) if rms_gain is not None else None, _ptr(ws),
-                                                  wsb, _stream(stream)))
+    wsfn = "pq2_ffn_workspace_bytes" if fn == "pq2_ffn_block" else "ptq1_ffn_workspace_bytes"
+    ws, wsb = _ws(getattr(lib(), wsfn)(m, d, f), x.device, ws)
+    _check(fn, getattr(lib(), fn)(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                  _ptr(signs1024), float(rms_eps), _ptr(rms_gain) if rms_gain is not None else None,
+                                  _ptr(ws), wsb, _stream(stream)))
     return out
+
+
+def pq2_ffn_block(x, w_gate, w_up, w_down, signs1024, d, f, rms_eps=0.0, out=None, ws=None, stream=None,
+                  rms_gain=None):
+    """ptq1_ffn_block over PQ2_0 tiled matrices."""
+    return ptq1_ffn_block(x, w_gate, w_up, w_down, signs1024, d, f, rms_eps, out, ws, stream, rms_gain,
+                          fn="pq2_ffn_block")
 
 
 # ------------------------------------------------------------------ PQ2_0 ----

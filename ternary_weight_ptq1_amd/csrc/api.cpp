@@ -238,7 +238,8 @@ struct FfnWs {
     ptq1::GemmPlan gu, dn;                                      // m >= 2: gate+up and down GEMMs
 };
 
-FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
+// rd_only: the PQ2_0 block (register-decode GEMM plans at every m)
+FfnWs ffn_layout(int64_t m, int64_t d, int64_t f, bool rd_only = false)
 {
     FfnWs L;
     size_t off = 0;
@@ -248,8 +249,8 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f)
         off += part_a > part_b ? part_a : part_b;
         L.hr = off; off += round_up(static_cast<size_t>(f) * 4, kWsAlign);
     } else {
-        L.gu = ptq1::gemm_plan(m, 2 * f, d);
-        L.dn = ptq1::gemm_plan(m, d, f);
+        L.gu = ptq1::gemm_plan(m, 2 * f, d, rd_only);
+        L.dn = ptq1::gemm_plan(m, d, f, rd_only);
         const size_t fa = ptq1::gemm_frag_elems(L.gu, d), fb = ptq1::gemm_frag_elems(L.dn, f);
         const size_t pa = ptq1::gemm_part_floats(L.gu), pb = ptq1::gemm_part_floats(L.dn);
         L.xb = off; off += round_up((fa > fb ? fa : fb) * 2, kWsAlign);
@@ -785,7 +786,7 @@ ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *
     if (wb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrix above 2 GiB");
     float *part = static_cast<float *>(ws);
     hipError_t e = profiled(kProfPq2, stream, [&] {
-        return ptq1::launch_pq2_matvec(tiled, n, k, x, signs1024, part, stream);
+        return ptq1::launch_pq2_matvec(tiled, nullptr, 1, n, k, x, signs1024, nullptr, part, stream);
     });
     if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
     return hip_status(e, "pq2_matvec");
@@ -822,10 +823,92 @@ ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
     char *w = static_cast<char *>(ws);
     uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
     float *part = reinterpret_cast<float *>(w + L.part);
-    hipError_t e = ptq1::launch_prep_frag_pq2(x, m, k, signs1024, xf, stream);
+    hipError_t e = ptq1::launch_prep_frag_pq2(x, nullptr, nullptr, m, k, signs1024, 0.0f, nullptr, xf, stream);
     if (e == hipSuccess)
-        e = profiled(kProfGemm, stream, [&] { return ptq1::launch_gemm_pq2(plan, xf, m, tiled, n, y, part, stream); });
+        e = profiled(kProfGemm, stream, [&] {
+            return ptq1::launch_gemm_pq2(plan, xf, m, tiled, n, nullptr, 0, y, nullptr, nullptr, part, stream);
+        });
     return hip_status(e, "pq2_gemm");
+}
+
+size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
+{
+    if (m < 0 || m > kMaxGemmM || pq2_packed(f, d) < 0 || pq2_packed(d, f) < 0 || f > INT64_MAX / 2) return 0;
+    if (m == 0) return 0;
+    return ffn_layout(m, d, f, true).total;
+}
+
+ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f, const uint8_t *w_gate,
+                          const uint8_t *w_up, const uint8_t *w_down, const float *signs1024, float rms_eps,
+                          const float *rms_gain, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wgb, wub, wdb, md, xb, ob;
+    if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
+    PTQ1_TRY(check_pq2(w_gate, "w_gate", f, d, true, &wgb, true));
+    PTQ1_TRY(check_pq2(w_up, "w_up", f, d, true, &wub, true));
+    PTQ1_TRY(check_pq2(w_down, "w_down", d, f, true, &wdb, true));
+    if (!mul_ok(m, d, &md)) return fail(PTQ1_ERR_OVERFLOW, "m * d overflows");
+    PTQ1_TRY(check_floats(x_out, "x_out", md, &ob));
+    if (md == 0) return ok();
+    PTQ1_TRY(check_floats(x, "x", md, &xb));
+    PTQ1_TRY(check_signs(signs1024, true));
+    int64_t gb = 0;
+    if (rms_gain != nullptr) {
+        PTQ1_TRY(check_floats(rms_gain, "rms_gain", d, &gb));
+        if (overlaps(x_out, ob, rms_gain, gb)) return fail(PTQ1_ERR_ALIAS, "x_out overlaps rms_gain");
+    }
+    if (x_out != x && overlaps(x_out, ob, x, xb)) return fail(PTQ1_ERR_ALIAS, "x_out partially overlaps x");
+    if (overlaps(x_out, ob, w_gate, wgb) || overlaps(x_out, ob, w_up, wub) || overlaps(x_out, ob, w_down, wdb))
+        return fail(PTQ1_ERR_ALIAS, "x_out overlaps a weight matrix");
+    if (f == 0) return fail(PTQ1_ERR_SHAPE, "f = 0");
+    const FfnWs L = ffn_layout(m, d, f, true);
+    PTQ1_TRY(check_ws(ws, ws_bytes, L.total, "pq2_ffn_block"));
+    if (overlaps(ws, (int64_t)L.total, x, xb) || overlaps(ws, (int64_t)L.total, x_out, ob))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps x or x_out");
+    if (rms_gain != nullptr && overlaps(ws, (int64_t)L.total, rms_gain, gb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps rms_gain");
+    if (nseg_of(f) * 4 > kMaxGridY || nseg_of(d) * 4 > kMaxGridY)
+        return fail(PTQ1_ERR_UNSUPPORTED, "d or f too large");
+    if (m == 1 && (f > kMaxLutRows || d > kMaxLutRows))
+        return fail(PTQ1_ERR_UNSUPPORTED, "d or f > %lld rows", (long long)kMaxLutRows);
+    if (m == 1 && (wgb > kMaxLutMatrixBytes || wub > kMaxLutMatrixBytes || wdb > kMaxLutMatrixBytes))
+        return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrices above 2 GiB");
+    char *w = static_cast<char *>(ws);
+    hipError_t e;
+    if (m == 1) {
+        // the PTQ1_0 block's composition over the PQ2_0 lookup kernel
+        float *part = reinterpret_cast<float *>(w + L.part);
+        float *h = reinterpret_cast<float *>(w + L.hr);
+        e = profiled(kProfPq2, stream, [&] {
+            return ptq1::launch_pq2_matvec(w_gate, w_up, 2, f, d, x, signs1024, rms_gain, part, stream);
+        });
+        if (e == hipSuccess)
+            e = ptq1::launch_lut_gate_up_sum(part, f, d, rms_eps > 0.0f ? x : nullptr, d, rms_eps, nullptr, nullptr,
+                                             h, stream);
+        if (e == hipSuccess)
+            e = profiled(kProfPq2, stream, [&] {
+                return ptq1::launch_pq2_matvec(w_down, nullptr, 1, d, f, h, signs1024, nullptr, part, stream);
+            });
+        if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, d, f, x, x_out, stream);
+    } else {
+        uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.xb);
+        float *g = reinterpret_cast<float *>(w + L.g);
+        float *u = reinterpret_cast<float *>(w + L.u);
+        float *part = reinterpret_cast<float *>(w + L.part);
+        e = ptq1::launch_prep_frag_pq2(x, nullptr, nullptr, m, d, signs1024, rms_eps, rms_gain, xf, stream);
+        if (e == hipSuccess)
+            e = profiled(kProfGemm, stream, [&] {
+                return ptq1::launch_gemm_pq2(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream);
+            });
+        if (e == hipSuccess)
+            e = ptq1::launch_prep_frag_pq2(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream);
+        if (e == hipSuccess)
+            e = profiled(kProfGemm, stream, [&] {
+                return ptq1::launch_gemm_pq2(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);
+            });
+    }
+    return hip_status(e, "pq2_ffn_block");
 }
 
 }  // extern "C"

@@ -1095,14 +1095,13 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
     return hipGetLastError();
 }
 
-hipError_t launch_prep_frag_pq2(const float *x, int64_t m, int64_t k, const float *signs, uint16_t *xf,
-                                hipStream_t s)
+hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, int64_t m, int64_t k,
+                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s)
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prep_frag<true>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
-                       static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k, signs, 0.0f,
-                       static_cast<const float *>(nullptr), xf);
+    hipLaunchKernelGGL(k_prep_frag<true>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u,
+                       k, signs, rms_eps, gain, xf);
     return hipGetLastError();
 }
 
@@ -1205,12 +1204,13 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     return gemm_fix(p, a, s);
 }
 
-hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w, int64_t n, float *y,
-                           float *part, hipStream_t s)
+hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                           const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
+                           hipStream_t s)
 {
-    if (n == 0 || m == 0 || p.nb == 0) return hipSuccess;
+    if (n0 + n1 == 0 || m == 0 || p.nb == 0) return hipSuccess;
     if (p.cfg > 1) return hipErrorInvalidValue;  // register-decode plans only (gemm_plan(..., true))
-    const GemmArgs a = gemm_args(p, xf, m, w, n, nullptr, 0, y, nullptr, nullptr, part);
+    const GemmArgs a = gemm_args(p, xf, m, w0, n0, w1, n1, y0, y1, residual, part);
     const dim3 grid(static_cast<unsigned>(p.wgs));
     hipError_t e;
     if (p.cfg == 0) {

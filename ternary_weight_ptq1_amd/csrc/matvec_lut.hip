@@ -623,13 +623,14 @@ constexpr int kPq2Dwords = kPq2CodeBytes / 4;          // 8
 static_assert(kPq2Slots * 256 * 4 == kLutTableBytes, "the PQ2_0 table fills the 64 KB array");
 
 struct Pq2Args {
-    const uint8_t *w;        // PQ2_0 tiled [n][k]
+    const uint8_t *w0, *w1;  // PQ2_0 tiled [n][k]; w1 used when nmat == 2
     int64_t n, k;
-    int nslices;
+    int nmat, nslices;
     int64_t groups;          // ceil(n / 32)
     int per_wg;
     const float *x, *signs;  // x [k], rotated here when signs != nullptr
-    float *part;             // [nslices][n]
+    const float *gain;       // [k] or nullptr: x is used as gain * x
+    float *part;             // [nslices][nmat][n]
 };
 
 __device__ __forceinline__ int pq2_rho(int lane) { return (4 * (lane & 1) + (lane >> 3)) & 7; }
@@ -697,7 +698,7 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
 
     // ---- 1. x for the slice's rotation, requested before any weights
     const int64_t c0 = (k0 / kHadamard) * kHadamard;
-    float xv16[kRotPerLane], sv16[kRotPerLane];
+    float xv16[kRotPerLane], sv16[kRotPerLane], gv16[kRotPerLane];
     if (wave == 0) {
         if (a.signs != nullptr) {
 #pragma unroll
@@ -706,11 +707,22 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
                 xv16[j] = a.x[c0 + e];
                 sv16[j] = a.signs[e];
             }
+            if (a.gain != nullptr) {
+#pragma unroll
+                for (int j = 0; j < kRotPerLane; ++j) gv16[j] = a.gain[c0 + kLutSliceW * (j >> 2) + lane + kWave * (j & 3)];
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < kRotPerLane / 4; ++j) {
                 const int e = lane + kWave * j;
                 xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];
+            }
+            if (a.gain != nullptr) {
+#pragma unroll
+                for (int j = 0; j < kRotPerLane / 4; ++j) {
+                    const int e = lane + kWave * j;
+                    gv16[j] = a.gain[k0 + (e < kw ? e : kw - 1)];
+                }
             }
         }
     }
@@ -722,9 +734,11 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     auto unit_of = [&](int i) { return u0 + wave + kLutWaves * i; };
     auto issue = [&](int i) {
         const int un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
+        const int mat = un >= static_cast<int>(a.groups) ? 1 : 0;
+        const int grp = un - mat * static_cast<int>(a.groups);
         // tiled matrices are below 2 GiB (checked by the caller)
-        const uint8_t *tb = a.w + (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
-                                   static_cast<uint32_t>(un)) * static_cast<uint32_t>(kPq2TileBytes);
+        const uint8_t *tb = (mat ? a.w1 : a.w0) + (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
+                                                   static_cast<uint32_t>(grp)) * static_cast<uint32_t>(kPq2TileBytes);
         const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(tb + lane * kPq2CodeBytes);
         const lut_u32x4 hi = *reinterpret_cast<const lut_u32x4 *>(tb + lane * kPq2CodeBytes + 16);
         dat[i][0] = lo.x; dat[i][1] = lo.y; dat[i][2] = lo.z; dat[i][3] = lo.w;
@@ -757,8 +771,13 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. the slice's x, rotated
+    // ---- 3. the slice's x (times the gain), rotated
     if (wave == 0) {
+        if (a.gain != nullptr) {
+#pragma unroll
+            for (int j = 0; j < kRotPerLane; ++j)
+                if (a.signs != nullptr || j < kRotPerLane / 4) xv16[j] *= gv16[j];
+        }
         if (a.signs != nullptr) {
             const int part = static_cast<int>((k0 - c0) / kLutSliceW);
             const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
@@ -805,7 +824,8 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
         if (i + kLutDepth < U) issue(i + kLutDepth);
         const bool unit_ok = unit_of(i) < u1;
         const int un = unit_ok ? unit_of(i) : u1 - 1;
-        const int r = un * kLutRows + row_l;
+        const int mat = un >= static_cast<int>(a.groups) ? 1 : 0;
+        const int r = (un - mat * static_cast<int>(a.groups)) * kLutRows + row_l;
         const bool live = unit_ok && r < a.n && blk_l < nblk;
         const uint32_t sh = blk_l ? (scw[i] >> 16) : (scw[i] & 0xffffu);
         const float scale = live ? half_bits_to_float(sh) : 0.0f;
@@ -823,7 +843,7 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
         float p = (acc0 + acc1) * scale;
         const int ip = __builtin_bit_cast(int, p);
         p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
-        if (unit_ok && blk_l == 0 && r < a.n) a.part[static_cast<int64_t>(s) * a.n + r] = p;
+        if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + mat) * a.n + r] = p;
     }
 }
 
@@ -833,7 +853,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_pq2_matvec(Pq2Args a)
     extern __shared__ __attribute__((aligned(16))) char lds[];
     float *tab = reinterpret_cast<float *>(lds);
     float *xs = reinterpret_cast<float *>(lds + kLutTableBytes);
-    const int per_slice = static_cast<int>(a.groups);
+    const int per_slice = a.nmat * static_cast<int>(a.groups);
     const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
     const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
     if (u0 < u1) pq2_segment<U>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);
@@ -859,12 +879,15 @@ static hipError_t pq2_launch(const Pq2Args &a, int64_t chunks, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_pq2_matvec(const uint8_t *w, int64_t n, int64_t k, const float *x, const float *signs,
-                             float *part, hipStream_t s)
+hipError_t launch_pq2_matvec(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k, const float *x,
+                             const float *signs, const float *gain, float *part, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
     Pq2Args a{};
-    a.w = w;
+    a.w0 = w0;
+    a.w1 = w1;
+    a.nmat = nmat;
+    a.gain = gain;
     a.n = n;
     a.k = k;
     a.nslices = static_cast<int>(lut_nslices(k));
@@ -872,7 +895,7 @@ hipError_t launch_pq2_matvec(const uint8_t *w, int64_t n, int64_t k, const float
     a.x = x;
     a.signs = signs;
     a.part = part;
-    const LutPlan pl = lut_plan(a.groups, a.nslices);
+    const LutPlan pl = lut_plan(static_cast<int64_t>(nmat) * a.groups, a.nslices);
     a.per_wg = pl.per_wg;
     switch (pl.U) {
         case 1: return pq2_launch<1>(a, pl.chunks, s);

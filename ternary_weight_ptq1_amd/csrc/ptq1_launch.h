@@ -71,8 +71,8 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
                              const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
 // The same lookup matvec over a PQ2_0 tiled matrix (one matrix): part as
 // above, summed by launch_lut_sum_rows.
-hipError_t launch_pq2_matvec(const uint8_t *w, int64_t n, int64_t k, const float *x, const float *signs,
-                             float *part, hipStream_t s);
+hipError_t launch_pq2_matvec(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k, const float *x,
+                             const float *signs, const float *gain, float *part, hipStream_t s);
 // y[r] = (residual ? residual[r] : 0) + sum over slices of part[s][r] (nmat = 1)
 hipError_t launch_lut_sum_rows(const float *part, int64_t n, int64_t k, const float *residual, float *y,
                                hipStream_t s);
@@ -109,9 +109,10 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
                        hipStream_t s);
 // PQ2_0: A fragments in the Q2 order (launch_prep_frag_pq2), y [m][n] =
 // A . W^T over a PQ2_0 tiled matrix; p from gemm_plan(m, n, k, true).
-hipError_t launch_prep_frag_pq2(const float *x, int64_t m, int64_t k, const float *signs, uint16_t *xf,
-                                hipStream_t s);
-hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w, int64_t n, float *y,
-                           float *part, hipStream_t s);
+hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, int64_t m, int64_t k,
+                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s);
+hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
+                           const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
+                           hipStream_t s);
 
 }  // namespace ptq1

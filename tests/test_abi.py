@@ -256,3 +256,11 @@ def test_pq2_validation():
     rc, msg = _err(L().pq2_gemm(B, 17408, 5120, X, 65537, S, Y, WS, 1 << 40, None))
     assert rc == 5
     assert L().pq2_gemm(B, 17408, 5120, X, 0, S, Y, WS, 0, None) == 0
+    # the PQ2_0 feed-forward block
+    fneed = L().pq2_ffn_workspace_bytes(1, 5120, 17408)
+    assert fneed >= 68 * 5120 * 4
+    rc, msg = _err(L().pq2_ffn_block(X, Y, 1, 5120, 17408, B, B, B, S, 0.0, None, WS, fneed - 1, None))
+    assert rc == 6
+    rc, msg = _err(L().pq2_ffn_block(X, Y, 1, 5120, 17408, B, B, B, None, 0.0, None, WS, 1 << 40, None))
+    assert rc == 1 and "signs" in msg
+    assert L().pq2_ffn_block(X, Y, 0, 5120, 17408, B, B, B, S, 0.0, None, WS, 0, None) == 0

@@ -720,3 +720,42 @@ def test_pq2_gemm_prefill_shape():
     rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 254, n)])).astype(np.int64)
     ref = oracle.pq2_gemm(b, n, k, oracle.rotate(x, sg), rows=rows)
     assert rel_l2(got[:, rows], ref) <= TOL_BF16
+
+
+def _pq2_ffn_host(seed, d, f):
+    mats = []
+    for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, f, d),
+                         (synth.S_UP_TRITS, synth.S_UP_SCALES, f, d),
+                         (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, d, f)):
+        t, s = host_matrix(seed, tr, sc, n, k)
+        mats.append(oracle.pq2_pack(t, s))
+    return mats
+
+
+@pytest.mark.parametrize("m,d,f,eps,gain", [(1, 1024, 2048, 1e-6, False), (1, 2048, 1024, 0.0, True),
+                                            (2, 1024, 2048, 1e-6, True), (8, 1024, 3072, 0.0, False),
+                                            (100, 1024, 2048, 1e-6, True)])
+def test_pq2_ffn_block(m, d, f, eps, gain):
+    seed = 10
+    wg, wu, wd = _pq2_ffn_host(seed, d, f)
+    x = synth.activations(seed, m, d)
+    s = synth.signs(seed)
+    gv = _gain(seed, d) if gain else None
+    got = host(P.pq2_ffn_block(to_dev(x), P.pq2_tile(to_dev(wg), f, d), P.pq2_tile(to_dev(wu), f, d),
+                               P.pq2_tile(to_dev(wd), d, f), to_dev(s), d, f, eps,
+                               rms_gain=to_dev(gv) if gain else None))
+    ref = oracle.pq2_ffn_block(x, wg, wu, wd, s, d, f, eps, gain=gv)
+    assert rel_l2(got, ref) <= (TOL_FP32 if m == 1 else TOL_FFN_BF16)
+
+
+def test_pq2_ffn_block_full_shape():
+    """One 27B-shaped layer (d = 5120, f = 17408) in PQ2_0 at batch 1, in place."""
+    d, f, seed = 5120, 17408, 11
+    wg, wu, wd = _pq2_ffn_host(seed, d, f)
+    x = synth.activations(seed, 1, d)
+    s = synth.signs(seed)
+    xd = to_dev(x)
+    P.pq2_ffn_block(xd, P.pq2_tile(to_dev(wg), f, d), P.pq2_tile(to_dev(wu), f, d), P.pq2_tile(to_dev(wd), d, f),
+                    to_dev(s), d, f, 1e-6, out=xd)
+    ref = oracle.pq2_ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
+    assert rel_l2(host(xd), ref) <= TOL_FP32

@@ -453,3 +453,24 @@ def test_pq2_gemm_is_rowwise_matvec():
     np.testing.assert_allclose(y, x @ t.astype(np.float64).T, rtol=0, atol=1e-12)
     rows = [0, 5, 36]
     np.testing.assert_allclose(oracle.pq2_gemm(b, n, k, x, rows=rows), y[:, rows], rtol=0, atol=1e-12)
+
+
+def test_pq2_ffn_block_equals_ptq1_block_on_the_same_weights():
+    """The same trits and scales packed in both formats give the same block:
+    the PQ2_0 composition (numpy steps over the PQ2_0 product) against the C
+    oracle's PTQ1_0 block, with and without the RMS scale and the gain."""
+    d, f, m = 1024, 2048, 2
+    mats2, mats1 = [], []
+    for (tr, sc, n, k) in [(synth.S_GATE_TRITS, synth.S_GATE_SCALES, f, d),
+                           (synth.S_UP_TRITS, synth.S_UP_SCALES, f, d),
+                           (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, d, f)]:
+        t, s = synth.trits(4, tr, n, k), synth.scales(4, sc, n, k // 128)
+        mats1.append(oracle.pack(t, s))
+        mats2.append(oracle.pq2_pack(t, s))
+    sg = synth.signs(4)
+    x = synth.activations(4, m, d).astype(np.float64)
+    gain = 0.5 + synth.gauss(4, 7, d).astype(np.float64) ** 2
+    for eps, gv in ((0.0, None), (1e-6, gain)):
+        a = oracle.pq2_ffn_block(x, *mats2, sg, d, f, eps, gain=gv)
+        b = oracle.ffn_block(x, *mats1, sg, d, f, eps, gain=gv)
+        assert np.linalg.norm(a - b) <= 1e-12 * np.linalg.norm(b)
