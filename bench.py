@@ -408,6 +408,25 @@ def main() -> int:
         del q2sets, y2, ws2, xq, yq, wsq
         torch.cuda.empty_cache()
 
+        # the whole batch-1 block in PQ2_0 (eager calls, 16 rotating layers)
+        def pq2_mat(role_t, role_s, j, n_, k_):
+            return P.pq2_tile(P.pq2_pack(sdev.trits(seed, synth.layer_stream(role_t, j), n_, k_, device=dev),
+                                         sdev.scales(seed, synth.layer_stream(role_s, j), n_, k_ // 128,
+                                                     device=dev)), n_, k_)
+
+        l2 = [(pq2_mat(synth.S_GATE_TRITS, synth.S_GATE_SCALES, j, F, D),
+               pq2_mat(synth.S_UP_TRITS, synth.S_UP_SCALES, j, F, D),
+               pq2_mat(synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, j, D, F)) for j in range(16)]
+        xb2 = torch.from_numpy(synth.activations(seed, 1, D)).to(dev)
+        ob2 = torch.empty_like(xb2)
+        wsb2 = torch.zeros(P.lib().pq2_ffn_workspace_bytes(1, D, F), dtype=torch.uint8, device=dev)
+        ms_b2 = timed(lambda i: P.pq2_ffn_block(xb2, *l2[i % 16], signs, D, F, 1e-6, out=ob2, ws=wsb2), 200, 20)
+        b2_bytes = 2 * P.pq2_tiled_bytes(F, D) + P.pq2_tiled_bytes(D, F) + 4 * D
+        breakdown["pq2_ffn_block_decode_eager"] = {"us": ms_b2 * 1e3, "GB/s": b2_bytes / (ms_b2 * 1e-3) / 1e9,
+                                                   "bytes": b2_bytes}
+        del l2, xb2, ob2, wsb2
+        torch.cuda.empty_cache()
+
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)
         w0 = P.ptq1_tile(P.ptq1_pack(sdev.trits(0, synth.S_W_TRITS, 1024, 1024),
                                      sdev.scales(0, synth.S_W_SCALES, 1024, 8)), 1024, 1024)
