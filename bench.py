@@ -127,17 +127,22 @@ def ffn_only(args, torch, synth, sdev, P, dev) -> int:
     """One 27B-shaped FFN block at batch M alone (for kernel traces): --steps
     calls replayed from a HIP graph after --warmup eager ones."""
     m = args.ffn_only
-    w = [P.ptq1_tile(P.ptq1_pack(sdev.trits(4, tr, n, k), sdev.scales(4, sc, n, k // 128)), n, k)
+    q2 = args.format == "pq2"
+    pack, tile = (P.pq2_pack, P.pq2_tile) if q2 else (P.ptq1_pack, P.ptq1_tile)
+    w = [tile(pack(sdev.trits(4, tr, n, k), sdev.scales(4, sc, n, k // 128)), n, k)
          for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
                               (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
                               (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F))]
     x = torch.from_numpy(synth.activations(4, m, D)).to(dev)
     sg = torch.from_numpy(synth.signs(4)).to(dev)
     out = torch.empty_like(x)
-    ws = torch.empty(P.workspace_bytes("ffn", m, D, F), dtype=torch.uint8, device=dev)
+    nws = P.lib().pq2_ffn_workspace_bytes(m, D, F) if q2 else P.workspace_bytes("ffn", m, D, F)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    block = P.pq2_ffn_block if q2 else P.ptq1_ffn_block
+    wbytes = 2 * P.pq2_tiled_bytes(F, D) + P.pq2_tiled_bytes(D, F) if q2 else LAYER_WEIGHT_BYTES
 
     def call():
-        P.ptq1_ffn_block(x, w[0], w[1], w[2], sg, D, F, rms_eps=1e-6, out=out, ws=ws)
+        block(x, w[0], w[1], w[2], sg, D, F, rms_eps=1e-6, out=out, ws=ws)
 
     for _ in range(args.warmup):
         call()
@@ -155,8 +160,9 @@ def ffn_only(args, torch, synth, sdev, P, dev) -> int:
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / args.steps
-    print(json.dumps({"workload": f"FFN block {m} x {D} -> {F} -> {D} (PTQ1_0), HIP graph", "us_per_layer": us,
-                      "weight_GB/s": LAYER_WEIGHT_BYTES / (us * 1e-6) / 1e9}))
+    fmt = "PQ2_0" if q2 else "PTQ1_0"
+    print(json.dumps({"workload": f"FFN block {m} x {D} -> {F} -> {D} ({fmt}), HIP graph", "us_per_layer": us,
+                      "weight_GB/s": wbytes / (us * 1e-6) / 1e9}))
     return 0
 
 
@@ -172,6 +178,8 @@ def main() -> int:
     ap.add_argument("--gemm-only", type=int, default=0, metavar="M",
                     help="profiling aid: run the prefill GEMM (M x 5120 -> 17408) --steps times, print its "
                          "kernel time, and exit")
+    ap.add_argument("--format", choices=("ptq1", "pq2"), default="ptq1",
+                    help="weight format of --ffn-only (PTQ1_0 or PQ2_0)")
     ap.add_argument("--ffn-only", type=int, default=0, metavar="M",
                     help="profiling aid: replay one FFN block at batch M --steps times from a HIP graph, print "
                          "its time per layer, and exit")
