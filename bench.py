@@ -433,6 +433,16 @@ def main() -> int:
         breakdown["pq2_ffn_block_decode_eager"] = {"us": ms_b2 * 1e3, "GB/s": b2_bytes / (ms_b2 * 1e-3) / 1e9,
                                                    "bytes": b2_bytes}
         del l2, xb2, ob2, wsb2
+
+        # W2A8: the down projection's matvec with 8-bit activations (quantise,
+        # lookups over integer-valued q, scaled sum), 16 weight sets as above
+        ws8 = torch.zeros(P.lib().ptq1_matvec_w2a8_workspace_bytes(D, F), dtype=torch.uint8, device=dev)
+        y8 = torch.empty(D, dtype=torch.float32, device=dev)
+        ms8 = timed(lambda i: P.ptq1_matvec_w2a8(sets[i % WEIGHT_SETS][2], D, F, h, residual=xg, out=y8, ws=ws8),
+                    200, 20)
+        breakdown["w2a8_down_call_cold"] = {"us": ms8 * 1e3, "GB/s": DOWN_BYTES / (ms8 * 1e-3) / 1e9,
+                                            "bytes": DOWN_BYTES, "float_call_us": ms_dn * 1e3}
+        del ws8, y8
         torch.cuda.empty_cache()
 
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)

@@ -289,12 +289,27 @@ ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, in
                           const uint8_t *w_up, const uint8_t *w_down, const float *signs1024, float rms_eps,
                           const float *rms_gain, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Batch-1 decode matvec with 8-bit activations (W2A8: "Why I Am Building
+ * Another Inference Engine", Level 5, the integer kernels' numerics; Level 4,
+ * the activations quantised before the ternary projections):
+ *   c = float(127 / max|x|) (0 when x is all zeros), q[i] = rint(x[i] * c) in
+ *   fp32 (integers in [-127, 127], ties to even), step = max|x| / 127;
+ *   y[r] = (residual ? residual[r] : 0) + step * sum_b s_rb * sum_{i in b} t_ri q_i.
+ * x is used as given (rotate it first with hadamard_rotate for a folded
+ * layer).  The per-block integer sums are exact; the block scales, the sum
+ * over blocks and the step are fp32.  Same tiled matrix, residual and
+ * aliasing rules as ptq1_matvec; k % 128 == 0, k > 0.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED. */
+size_t ptq1_matvec_w2a8_workspace_bytes(int64_t n, int64_t k);
+ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *residual,
+                             float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Profiling: attaches start[i] / stop[i] to the dispatch of the i-th of the
  * next `count` launches of one kernel family (hipExtLaunchKernel: they take
  * the kernel's own start and end times on its stream), so a caller can time
  * a kernel inside a composite call (ptq1_ffn_block) with events.  Families: "lut_matvec_2" (the
  * table-lookup matvec over two matrices: gate and up), "lut_matvec_1" (over
- * one matrix: ptq1_matvec, the down projection), "gemm" (the MFMA GEMM),
+ * one matrix: ptq1_matvec, ptq1_matvec_w2a8, the down projection), "gemm" (the MFMA GEMM),
  * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec); pq2_gemm's
  * kernel counts as "gemm".
  * Events are created and owned by the caller; both arrays must stay valid

@@ -276,6 +276,34 @@ def pq2_ffn_block(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
     return x2 + pq2_gemm(wd, d, f, rotate(h, signs))
 
 
+def w2a8_quant(x: np.ndarray):
+    """8-bit activations ("Why I Am Building Another Inference Engine", Level 5:
+    the integer kernels multiply ternary weights with 8-bit activations;
+    Level 4: the activations are quantised before the ternary projections).
+    Reading (the pages name the step, not its formula): one absmax scale per
+    call, c = 127 / max|x| rounded once to fp32 (0 for an all-zero x), then
+    q = rint(x * c) in fp32 with ties to even; the step back is max|x| / 127.
+    The decisions are taken in fp32, as the kernel takes them."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    g = float(np.max(np.abs(x32))) if x32.size else 0.0
+    c = np.float32(127.0 / g) if g > 0.0 else np.float32(0.0)
+    q = np.rint(x32 * c).astype(np.int64)
+    return q, g / 127.0
+
+
+def w2a8_matvec(blocks: np.ndarray, n: int, k: int, x: np.ndarray, rows=None) -> np.ndarray:
+    """step * sum_b scale_rb * (integer sum over block b of trit * q), the
+    per-block sums in exact integer arithmetic (W2A8)."""
+    q, step = w2a8_quant(x)
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, -1)
+    if rows is not None:
+        b = b[np.asarray(rows, dtype=np.int64)]
+    nr, nb = b.shape[0], k // BLOCK_W
+    t, sc = unpack(b, nr, k)
+    isum = (t.reshape(nr, nb, BLOCK_W).astype(np.int64) * q.reshape(1, nb, BLOCK_W)).sum(axis=2)
+    return step * (f16_to_f64(sc).reshape(nr, nb) * isum).sum(axis=1)
+
+
 def embedding_unrotate(table_rows: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """Restore looked-up rows of a rotated embedding table: unrotate each row."""
     return unrotate(table_rows, signs)

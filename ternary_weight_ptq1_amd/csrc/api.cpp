@@ -831,6 +831,53 @@ ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
     return hip_status(e, "pq2_gemm");
 }
 
+size_t ptq1_matvec_w2a8_workspace_bytes(int64_t n, int64_t k)
+{
+    if (packed_bytes(n, k) < 0) return 0;
+    // partials, then q [k] and the step
+    return lut_ws(n, 1, k) + round_up(static_cast<size_t>(k) * 4 + 4, kWsAlign);
+}
+
+ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *residual,
+                             float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, xb, yb;
+    PTQ1_TRY(check_matrix(tiled, "tiled", n, k, false, &wb, true));
+    PTQ1_TRY(check_floats(y, "y", n, &yb));
+    if (n == 0) return ok();
+    if (k == 0) return fail(PTQ1_ERR_SHAPE, "k = 0");
+    PTQ1_TRY(check_floats(x, "x", k, &xb));
+    if (residual != nullptr) {
+        int64_t rb;
+        PTQ1_TRY(check_floats(residual, "residual", n, &rb));
+        if (residual != y && overlaps(residual, rb, y, yb))
+            return fail(PTQ1_ERR_ALIAS, "y partially overlaps residual");
+    }
+    const size_t need = ptq1_matvec_w2a8_workspace_bytes(n, k);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_matvec_w2a8"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps the weights");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, tiled, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    if (residual != nullptr && overlaps(ws, (int64_t)need, residual, 4 * n))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps residual");
+    if (nseg_of(k) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
+    if (n > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "n = %lld > %lld rows", (long long)n, (long long)kMaxLutRows);
+    if (wb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrix above 2 GiB");
+    char *w = static_cast<char *>(ws);
+    float *part = reinterpret_cast<float *>(w);
+    float *q = reinterpret_cast<float *>(w + lut_ws(n, 1, k));
+    float *step = q + k;
+    hipError_t e = ptq1::launch_w2a8_quant(x, k, q, step, stream);
+    if (e == hipSuccess)
+        e = profiled(kProfLut1, stream, [&] {
+            return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, q, nullptr, nullptr, part, stream);
+        });
+    if (e == hipSuccess) e = ptq1::launch_w2a8_sum(part, n, k, step, residual, y, stream);
+    return hip_status(e, "ptq1_matvec_w2a8");
+}
+
 size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
 {
     if (m < 0 || m > kMaxGemmM || pq2_packed(f, d) < 0 || pq2_packed(d, f) < 0 || f > INT64_MAX / 2) return 0;

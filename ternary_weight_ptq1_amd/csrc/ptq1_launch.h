@@ -66,6 +66,12 @@ hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, 
 // (nmat = 1) or two sharing x (nmat = 2); x (times gain [k], if given)
 // rotated per 1024-chunk when signs != nullptr, else used as given.
 int64_t lut_nslices(int64_t k);
+// 8-bit activations: q = rint(x * float(127 / max|x|)) as fp32 integers and
+// step = max|x| / 127 (one workgroup); y = residual + step * sum of the
+// lookup matvec's partials over q.
+hipError_t launch_w2a8_quant(const float *x, int64_t k, float *q, float *step, hipStream_t s);
+hipError_t launch_w2a8_sum(const float *part, int64_t n, int64_t k, const float *step, const float *residual,
+                           float *y, hipStream_t s);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
                              const float *x, const float *signs, const float *gain, float *part, hipStream_t s);

@@ -264,3 +264,19 @@ def test_pq2_validation():
     rc, msg = _err(L().pq2_ffn_block(X, Y, 1, 5120, 17408, B, B, B, None, 0.0, None, WS, 1 << 40, None))
     assert rc == 1 and "signs" in msg
     assert L().pq2_ffn_block(X, Y, 0, 5120, 17408, B, B, B, S, 0.0, None, WS, 0, None) == 0
+
+
+
+def test_w2a8_validation():
+    B, X, Y, WS = (C.c_void_p(FAKE * i) for i in (1, 200, 300, 400))
+    need = L().ptq1_matvec_w2a8_workspace_bytes(5120, 17408)
+    assert need >= L().ptq1_matvec_workspace_bytes(5120, 17408) + 17408 * 4
+    rc, msg = _err(L().ptq1_matvec_w2a8(B, 5120, 17408, X, None, Y, WS, need - 1, None))
+    assert rc == 6
+    rc, msg = _err(L().ptq1_matvec_w2a8(B, 5120, 17408 + 64, X, None, Y, WS, 1 << 30, None))
+    assert rc == 2
+    rc, msg = _err(L().ptq1_matvec_w2a8(B, 5120, 17408, None, None, Y, WS, 1 << 30, None))
+    assert rc == 1 and "x" in msg
+    rc, msg = _err(L().ptq1_matvec_w2a8(B, 5120, 17408, X, None, C.c_void_p(FAKE * 200 + 64), WS, 1 << 30, None))
+    assert rc == 7
+    assert L().ptq1_matvec_w2a8(B, 0, 17408, X, None, Y, WS, 0, None) == 0

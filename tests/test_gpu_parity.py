@@ -759,3 +759,31 @@ def test_pq2_ffn_block_full_shape():
                     to_dev(s), d, f, 1e-6, out=xd)
     ref = oracle.pq2_ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
     assert rel_l2(host(xd), ref) <= TOL_FP32
+
+
+# ----------------------------------------------------------------- W2A8 ----
+
+@pytest.mark.parametrize("n,k,seed", [(1024, 1024, 0), (300, 384, 1), (257, 3072, 2), (1, 128, 3), (17, 640, 4)])
+def test_w2a8_matvec(n, k, seed):
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    x = synth.activations(seed, 1, k)[0]
+    got = host(P.ptq1_matvec_w2a8(tiled(b, n, k), n, k, to_dev(x)))
+    assert rel_l2(got, oracle.w2a8_matvec(b, n, k, x)) <= TOL_FP32
+
+
+def test_w2a8_matvec_full_shape_residual_zero_input():
+    """The down projection's shape (5120 x 17408) on rotated activations, with
+    a residual, in place; an all-zero x leaves exactly the residual."""
+    n, k, seed = 5120, 17408, 2
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    del t
+    bd = tiled(b, n, k)
+    xr = oracle.rotate(synth.activations(seed, 1, k)[0], synth.signs(seed)).astype(np.float32)
+    res = synth.gauss(seed, 77, n)
+    y = to_dev(res.copy())
+    P.ptq1_matvec_w2a8(bd, n, k, to_dev(xr), residual=y, out=y)
+    assert rel_l2(host(y), oracle.w2a8_matvec(b, n, k, xr) + res) <= TOL_FP32
+    z = host(P.ptq1_matvec_w2a8(bd, n, k, to_dev(np.zeros(k, np.float32)), residual=to_dev(res)))
+    np.testing.assert_array_equal(z, res)

@@ -474,3 +474,54 @@ def test_pq2_ffn_block_equals_ptq1_block_on_the_same_weights():
         a = oracle.pq2_ffn_block(x, *mats2, sg, d, f, eps, gain=gv)
         b = oracle.ffn_block(x, *mats1, sg, d, f, eps, gain=gv)
         assert np.linalg.norm(a - b) <= 1e-12 * np.linalg.norm(b)
+
+
+# ----------------------------------------------------------------- W2A8 ----
+# "Why I Am Building Another Inference Engine", Level 5 (8-bit activations
+# times ternary weights) and Level 4 (quantised before the projections).
+
+def test_w2a8_quant_worked_values():
+    """max|x| = 1 -> c = 127: 0.5 -> 63.5 -> 64 and -0.5 -> -64 (ties to even),
+    0.25 -> 31.75 -> 32, 1/256 -> 0.496 -> 0, the extreme -> -127."""
+    q, step = oracle.w2a8_quant(np.array([0.5, -1.0, 0.25, 1.0 / 256, -0.5], np.float32))
+    assert q.tolist() == [64, -127, 32, 0, -64]
+    assert step == 1.0 / 127
+    q, step = oracle.w2a8_quant(np.zeros(256, np.float32))
+    assert not q.any() and step == 0.0
+
+
+def test_w2a8_quant_range_and_grid_fixed_point():
+    x = synth.activations(3, 1, 5120)[0]
+    q, step = oracle.w2a8_quant(x)
+    assert np.abs(q).max() == 127 and q[np.argmax(np.abs(x))] == np.sign(x[np.argmax(np.abs(x))]) * 127
+    # quantising q itself (already on the grid, max 127) returns q with step 1
+    q2, step2 = oracle.w2a8_quant(q.astype(np.float32))
+    np.testing.assert_array_equal(q2, q)
+    assert step2 == 1.0
+    # the error of q * step is at most half a step per element
+    assert np.abs(q * step - x.astype(np.float64)).max() <= 0.5 * step * (1 + 1e-6)
+
+
+def test_w2a8_matvec_on_the_grid_equals_the_float_matvec():
+    """Activations already on the 8-bit grid (integers, max 127): the W2A8
+    product equals the C oracle's fp64 matvec of the same x."""
+    n, k = 64, 1024
+    rng = np.random.default_rng(4)
+    t, s = synth.trits(4, synth.S_W_TRITS, n, k), synth.scales(4, synth.S_W_SCALES, n, k // 128)
+    b = oracle.pack(t, s)
+    x = rng.integers(-127, 128, size=k).astype(np.float64)
+    x[7] = 127
+    np.testing.assert_allclose(oracle.w2a8_matvec(b, n, k, x), oracle.matvec(b, n, k, x), rtol=1e-13, atol=0)
+
+
+def test_w2a8_matvec_brute_force():
+    """Two rows of one block, written out term by term."""
+    rng = np.random.default_rng(6)
+    t = rng.integers(-1, 2, size=(2, 128), dtype=np.int8)
+    s = np.array([[0x3C00], [0xB800]], np.uint16)  # 1.0, -0.5
+    x = rng.standard_normal(128).astype(np.float32)
+    g = max(abs(float(v)) for v in x)
+    c = float(np.float32(127.0 / g))
+    q = [int(np.rint(np.float32(float(v)) * np.float32(c))) for v in x]
+    ref = [sc * sum(int(t[r, i]) * q[i] for i in range(128)) * (g / 127.0) for r, sc in ((0, 1.0), (1, -0.5))]
+    np.testing.assert_allclose(oracle.w2a8_matvec(oracle.pack(t, s), 2, 128, x), ref, rtol=1e-15, atol=0)
