@@ -16,15 +16,27 @@
 namespace ptq1 {
 
 constexpr int kQThreads = 1024;
+constexpr int kQPer = 24;  // values per thread held in registers (k <= 24576 in one pass)
+constexpr int kSumBatch = 16;
 
-// One workgroup: max |x| over k, then q and the step.
+// One workgroup: max |x| over k, then q and the step.  Every load of the
+// first kQPer x 1024 values is requested before the reduction (clamped
+// addresses); longer vectors loop over the rest.
 __global__ void __launch_bounds__(kQThreads) k_w2a8_quant(const float *__restrict__ x, int64_t k,
                                                           float *__restrict__ q, float *__restrict__ step)
 {
     __shared__ float red[kQThreads / kWave];
     const int tid = threadIdx.x;
+    float v[kQPer];
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+        const int64_t i = tid + static_cast<int64_t>(kQThreads) * j;
+        v[j] = x[i < k ? i : k - 1];
+    }
     float mx = 0.0f;
-    for (int64_t i = tid; i < k; i += kQThreads) mx = fmaxf(mx, fabsf(x[i]));
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) mx = fmaxf(mx, fabsf(v[j]));  // clamped copies repeat x[k - 1]
+    for (int64_t i = tid + static_cast<int64_t>(kQThreads) * kQPer; i < k; i += kQThreads) mx = fmaxf(mx, fabsf(x[i]));
 #pragma unroll
     for (int h = kWave / 2; h > 0; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h, kWave));
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
@@ -35,26 +47,43 @@ __global__ void __launch_bounds__(kQThreads) k_w2a8_quant(const float *__restric
     // the multiplier rounded once from its exact quotient (double division
     // is correctly rounded; the conversion rounds to nearest)
     const float c = g > 0.0f ? static_cast<float>(127.0 / static_cast<double>(g)) : 0.0f;
-    for (int64_t i = tid; i < k; i += kQThreads) q[i] = rintf(x[i] * c);
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+        const int64_t i = tid + static_cast<int64_t>(kQThreads) * j;
+        if (i < k) q[i] = rintf(v[j] * c);
+    }
+    for (int64_t i = tid + static_cast<int64_t>(kQThreads) * kQPer; i < k; i += kQThreads) q[i] = rintf(x[i] * c);
     if (tid == 0) step[0] = static_cast<float>(static_cast<double>(g) / 127.0);
 }
 
-// y[r] = (residual ? residual[r] : 0) + step * sum_s part[s][r], slices in order.
+// y[r] = (residual ? residual[r] : 0) + step * sum_s part[s][r], slices in
+// order, loaded kSumBatch slices at a time.
 __global__ void __launch_bounds__(kEwThreads) k_w2a8_sum(const float *__restrict__ part, int64_t n, int ns,
                                                          const float *__restrict__ step,
                                                          const float *__restrict__ residual, float *__restrict__ y)
 {
-    const int64_t r = blockIdx.x * static_cast<int64_t>(kEwThreads) + threadIdx.x;
-    if (r >= n) return;
+    const int64_t r0 = blockIdx.x * static_cast<int64_t>(kEwThreads) + threadIdx.x;
+    const int64_t r = r0 < n ? r0 : n - 1;  // clamped: the loads stay uniform
     const float st = step[0];
     const float res = residual != nullptr ? residual[r] : 0.0f;
     float t = 0.0f;
-    for (int s = 0; s < ns; ++s) t += part[static_cast<int64_t>(s) * n + r];
-    y[r] = residual != nullptr ? fmaf(st, t, res) : st * t;
+    for (int s0 = 0; s0 < ns; s0 += kSumBatch) {
+        float b[kSumBatch];
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j) {
+            const int sj = s0 + j < ns ? s0 + j : ns - 1;
+            b[j] = part[static_cast<int64_t>(sj) * n + r];
+        }
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j)
+            if (s0 + j < ns) t += b[j];
+    }
+    if (r0 < n) y[r] = residual != nullptr ? fmaf(st, t, res) : st * t;
 }
 
 hipError_t launch_w2a8_quant(const float *x, int64_t k, float *q, float *step, hipStream_t s)
 {
+    if (k == 0) return hipSuccess;
     hipLaunchKernelGGL(k_w2a8_quant, dim3(1), dim3(kQThreads), 0, s, x, k, q, step);
     return hipGetLastError();
 }
