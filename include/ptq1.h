@@ -290,8 +290,9 @@ ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, in
                           const float *rms_gain, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Batch-1 decode matvec with 8-bit activations (W2A8: "Why I Am Building
- * Another Inference Engine", Level 5, the integer kernels' numerics; Level 4,
- * the activations quantised before the ternary projections):
+ * Another Inference Engine", Level 5, the numerics of integer kernels; Level
+ * 4, where a BitNet layer rounds its activations to int8 ahead of its ternary
+ * matmuls):
  *   c = float(127 / max|x|) (0 when x is all zeros), q[i] = rint(x[i] * c) in
  *   fp32 (integers in [-127, 127], ties to even), step = max|x| / 127;
  *   y[r] = (residual ? residual[r] : 0) + step * sum_b s_rb * sum_{i in b} t_ri q_i.

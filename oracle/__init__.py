@@ -278,8 +278,8 @@ def pq2_ffn_block(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
 
 def w2a8_quant(x: np.ndarray):
     """8-bit activations ("Why I Am Building Another Inference Engine", Level 5:
-    the integer kernels multiply ternary weights with 8-bit activations;
-    Level 4: the activations are quantised before the ternary projections).
+    integer kernels pair ternary weights with int8 activations; Level 4: a
+    BitNet layer rounds its activations to int8 ahead of its ternary matmuls).
     Reading (the pages name the step, not its formula): one absmax scale per
     call, c = 127 / max|x| rounded once to fp32 (0 for an all-zero x), then
     q = rint(x * c) in fp32 with ties to even; the step back is max|x| / 127.

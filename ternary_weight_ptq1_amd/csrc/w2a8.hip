@@ -1,8 +1,7 @@
 // w2a8.hip -- the 8-bit-activation decode matvec ("Why I Am Building Another
-// Inference Engine", Level 5: the fast kernels multiply the ternary weights
-// with 8-bit integer activations, which is the model BitNet b1.58 was trained
-// as; Level 4's BitNet layer quantises its activations before the ternary
-// projections).
+// Inference Engine", Level 5: integer kernels pair ternary weights with
+// int8 activations, the numerics BitNet b1.58 was trained with; Level 4: a
+// BitNet layer rounds its activations to int8 ahead of its ternary matmuls).
 //
 // x [k] -> q = rint(x * c) with c = float(127 / max|x|) (c = 0 when x is all
 // zeros), integers in [-127, 127] held as fp32; the lookup-table matvec then
