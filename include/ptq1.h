@@ -1,7 +1,7 @@
 /*
  * ptq1.h -- C ABI of the MI355X (gfx950) PTQ1_0 ternary linear layer.
  *
- * The method: weights quantised to -1, 0, +1 with one 16-bit scale per 128
+ * The method: weights quantised to -1, 0, +1 with a 16-bit scale for every 128
  * weights, five trits packed into a byte in base 3 (1.75 bits per weight),
  * after every weight matrix was multiplied by a 1024-wide Walsh-Hadamard
  * butterfly with a sign pattern; at inference the same rotation is applied to
@@ -229,7 +229,7 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
                            size_t ws_bytes, hipStream_t stream);
 
 /* ---- PQ2_0: the two-bit ternary format ("Why I Am Building Another
- * Inference Engine", Level 2: two bits per weight and one 16-bit scale per
+ * Inference Engine", Level 2: two bits per weight and a 16-bit scale for every
  * 128 weights, 2.125 bits per weight).  A block is 32 code bytes, weight
  * 4i + f in bits 2f..2f+1 of byte i (code q is the trit q - 1; code 3, never
  * written, reads as 0), then the binary16 scale, little-endian: 34 bytes.

@@ -2,8 +2,8 @@
 // reorder of packed blocks into the library's tiled device layout.
 //
 // Format: "A 27B model in 5.5 GB: Bonsai ternary on Ferrox, locally",
-// section "What Bonsai is" (five trits per byte in base 3, one 16-bit scale
-// per 128 weights); the decode reads digits on the float pipeline as in
+// section "What Bonsai is" (five trits per byte in base 3, a 16-bit scale
+// for every 128 weights); the decode reads digits on the float pipeline as in
 // section "What Ferrox does with it".
 #include "ptq1_device.h"
 #include "ptq1_launch.h"

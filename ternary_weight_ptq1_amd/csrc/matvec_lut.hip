@@ -599,7 +599,7 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
 
 // ---------------------------------------------------------------------------
 // PQ2_0 decode matvec ("Why I Am Building Another Inference Engine", Level 2:
-// two bits per ternary weight and one 16-bit scale per 128 weights).  The
+// two bits per ternary weight and a 16-bit scale for every 128 weights).  The
 // same table scheme: a byte holds four 2-bit codes, so a 2-block slice has
 // 64 byte slots and T[slot][b] = sum_f w(field f of b) xr[k(slot, f)], with
 // w(q) = q - 1 and w(3) = 0.  What differs from PTQ1_0:

@@ -39,7 +39,7 @@ constexpr int kTileBytes = kTileSlots * kBlockBytes;  // 1792
 static_assert(kTileBytes % 128 == 0, "tiles are whole 128-byte lines");
 
 // ---- PQ2_0 ("Why I Am Building Another Inference Engine", Level 2: two bits
-// per ternary weight plus one 16-bit scale per 128 weights).  Block: 32 code
+// per ternary weight plus a 16-bit scale for every 128 weights).  Block: 32 code
 // bytes (weight 4i+n = 2-bit field n of byte i, low field first; code q is
 // weight q - 1, code 3 reads as 0), then the scale: 34 bytes.  Device tile:
 // 32 rows x 2 blocks as above, the 64 code records first (32 bytes each,

@@ -597,7 +597,7 @@ def test_ffn_block_graph_replay_matches_eager():
 
 # ---------------------------------------------------------------- PQ2_0 ----
 # "Why I Am Building Another Inference Engine", Level 2: two bits per ternary
-# weight, one 16-bit scale per 128 weights.  Codec work is compared byte for
+# weight, a 16-bit scale for every 128 weights.  Codec work is compared byte for
 # byte; the matvec to TOL_FP32 against the oracle's fp64 product.
 
 def pq2_host(seed, n, k):

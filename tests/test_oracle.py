@@ -314,7 +314,7 @@ def _ffn_weights(seed, d, f):
 # --------------------------------------------------------------- PQ2_0 ----
 
 def test_pq2_worked_block_and_accounting():
-    """[page 2, Level 2]: 2 bits per weight + one 16-bit scale per 128 weights
+    """[page 2, Level 2]: 2 bits per weight + a 16-bit scale for every 128 weights
     = 2.125 bits per weight, 7.2 GB for 27e9 weights; the block in the fixture
     is worked out by hand."""
     g = _golden("pq2_worked_block.txt")
