@@ -787,3 +787,44 @@ def test_w2a8_matvec_full_shape_residual_zero_input():
     assert rel_l2(host(y), oracle.w2a8_matvec(b, n, k, xr) + res) <= TOL_FP32
     z = host(P.ptq1_matvec_w2a8(bd, n, k, to_dev(np.zeros(k, np.float32)), residual=to_dev(res)))
     np.testing.assert_array_equal(z, res)
+
+
+def test_pq2_and_w2a8_graph_replay_matches_eager():
+    """The PQ2_0 block (m = 1 and m = 4) and the W2A8 matvec captured in one
+    HIP graph: every replay, with eager work between replays, reproduces the
+    eager results bit for bit."""
+    d, f, seed = 1024, 2048, 12
+    wg, wu, wd = _pq2_ffn_host(seed, d, f)
+    tg, tu, td = P.pq2_tile(to_dev(wg), f, d), P.pq2_tile(to_dev(wu), f, d), P.pq2_tile(to_dev(wd), d, f)
+    t, sc = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, d, f)
+    tw = tiled(oracle.pack(t, sc), d, f)
+    s = to_dev(synth.signs(seed))
+    x1 = to_dev(synth.activations(seed, 1, d))
+    x4 = to_dev(synth.activations(seed + 1, 4, d))
+    h = to_dev(synth.activations(seed + 3, 1, f)[0])
+    o1, o4, y8 = torch.empty_like(x1), torch.empty_like(x4), torch.empty(d, dtype=torch.float32, device=DEV)
+    lib = P.lib()
+    ws = torch.empty(max(lib.pq2_ffn_workspace_bytes(1, d, f), lib.pq2_ffn_workspace_bytes(4, d, f)),
+                     dtype=torch.uint8, device=DEV)
+    ws8 = torch.empty(lib.ptq1_matvec_w2a8_workspace_bytes(d, f), dtype=torch.uint8, device=DEV)
+    ref1 = host(P.pq2_ffn_block(x1, tg, tu, td, s, d, f, 1e-6, ws=ws))
+    ref4 = host(P.pq2_ffn_block(x4, tg, tu, td, s, d, f, 1e-6, ws=ws))
+    ref8 = host(P.ptq1_matvec_w2a8(tw, d, f, h, ws=ws8))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.pq2_ffn_block(x1, tg, tu, td, s, d, f, 1e-6, out=o1, ws=ws)
+        P.pq2_ffn_block(x4, tg, tu, td, s, d, f, 1e-6, out=o4, ws=ws)
+        P.ptq1_matvec_w2a8(tw, d, f, h, out=y8, ws=ws8)
+    other = to_dev(synth.activations(seed + 2, 1, d))
+    for rep in range(3):
+        for o in (o1, o4, y8):
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(o1), ref1, err_msg=f"replay {rep}, m = 1")
+        np.testing.assert_array_equal(host(o4), ref4, err_msg=f"replay {rep}, m = 4")
+        np.testing.assert_array_equal(host(y8), ref8, err_msg=f"replay {rep}, w2a8")
+        P.pq2_ffn_block(other, tg, tu, td, s, d, f, 1e-6, ws=ws)  # eager work between replays
+        P.ptq1_matvec_w2a8(tw, d, f, other[0].repeat(f // d), ws=ws8)
+        torch.cuda.synchronize()
