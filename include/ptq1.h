@@ -33,6 +33,10 @@
  * (ptq1_tile makes it from a packed matrix, once, at load time); pack,
  * dequant and the float-peel matvec use the packed layout.
  *
+ * Beyond PTQ1_0 with fp32 activations, two more numerics of the same layer:
+ * the PQ2_0 format (pq2_*: two bits per weight, described before pq2_packed_bytes)
+ * and 8-bit activations (ptq1_matvec_w2a8).
+ *
  * Rotation R of a row x of width k (k a multiple of 1024): every 1024-wide
  * chunk c becomes (1/32) H (s * c), with H the natural-order Sylvester
  * Hadamard matrix and s the 1024 signs (one vector for every chunk).
