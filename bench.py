@@ -443,6 +443,13 @@ def main() -> int:
         breakdown["w2a8_down_call_cold"] = {"us": ms8 * 1e3, "GB/s": DOWN_BYTES / (ms8 * 1e-3) / 1e9,
                                             "bytes": DOWN_BYTES, "float_call_us": ms_dn * 1e3}
         del ws8, y8
+        # and the W2A8 prefill GEMM (per-token int8 rows on the bf16 MFMA path), M = 256, gate-sized matrix
+        x8 = torch.from_numpy(synth.activations(seed, 256, D)).to(dev)
+        yg8 = torch.empty((256, F), dtype=torch.float32, device=dev)
+        wsg8 = torch.zeros(P.lib().ptq1_gemm_w2a8_workspace_bytes(256, F, D), dtype=torch.uint8, device=dev)
+        ms_g8 = timed(lambda i: P.ptq1_gemm_w2a8(sets[i % WEIGHT_SETS][0], F, D, x8, out=yg8, ws=wsg8), 30, 3)
+        breakdown["w2a8_gemm_M256_call"] = {"us": ms_g8 * 1e3, "TFLOP/s": 2.0 * 256 * F * D / (ms_g8 * 1e-3) / 1e12}
+        del x8, yg8, wsg8
         torch.cuda.empty_cache()
 
         # hot 1024 x 1024 matvec (configuration 0; L2-resident, latency-bound)

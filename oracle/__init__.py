@@ -304,6 +304,13 @@ def w2a8_matvec(blocks: np.ndarray, n: int, k: int, x: np.ndarray, rows=None) ->
     return step * (f16_to_f64(sc).reshape(nr, nb) * isum).sum(axis=1)
 
 
+def w2a8_gemm(blocks: np.ndarray, n: int, k: int, x: np.ndarray, rows=None) -> np.ndarray:
+    """Y [m, len(rows) or n]: every row of x quantised on its own (one absmax
+    per token), then the W2A8 product of w2a8_matvec."""
+    x2 = np.asarray(x, dtype=np.float32).reshape(-1, k)
+    return np.stack([w2a8_matvec(blocks, n, k, xi, rows=rows) for xi in x2])
+
+
 def embedding_unrotate(table_rows: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """Restore looked-up rows of a rotated embedding table: unrotate each row."""
     return unrotate(table_rows, signs)

@@ -73,6 +73,8 @@ _SIGS = {
     "pq2_gemm": ([p, i64, i64, p, i64, p, p, p, sz, p], C.c_int),
     "pq2_ffn_workspace_bytes": ([i64, i64, i64], sz),
     "ptq1_matvec_w2a8_workspace_bytes": ([i64, i64], sz),
+    "ptq1_gemm_w2a8_workspace_bytes": ([i64, i64, i64], sz),
+    "ptq1_gemm_w2a8": ([p, i64, i64, p, i64, p, p, sz, p], C.c_int),
     "ptq1_matvec_w2a8": ([p, i64, i64, p, p, p, p, sz, p], C.c_int),
     "pq2_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
@@ -413,6 +415,21 @@ def ptq1_matvec_w2a8(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, resid
     ws, wsb = _ws(lib().ptq1_matvec_w2a8_workspace_bytes(n, k), x.device, ws)
     _check("ptq1_matvec_w2a8", lib().ptq1_matvec_w2a8(_ptr(tiled), n, k, _ptr(x), _ptr(residual), _ptr(out),
                                                       _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def ptq1_gemm_w2a8(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, out: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y [m, n] with each row of x quantised to 8-bit integers (its own absmax)."""
+    _dev(tiled, "tiled", torch.uint8)
+    _dev(x, "x", torch.float32)
+    m = x.numel() // k if k else 0
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(out, "y", torch.float32)
+    ws, wsb = _ws(lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k), x.device, ws)
+    _check("ptq1_gemm_w2a8", lib().ptq1_gemm_w2a8(_ptr(tiled), n, k, _ptr(x), m, _ptr(out), _ptr(ws), wsb,
+                                                  _stream(stream)))
     return out
 
 

@@ -878,6 +878,47 @@ ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const f
     return hip_status(e, "ptq1_matvec_w2a8");
 }
 
+size_t ptq1_gemm_w2a8_workspace_bytes(int64_t m, int64_t n, int64_t k)
+{
+    if (packed_bytes(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
+    if (m == 0) return 0;
+    return gemm_layout(ptq1::gemm_plan(m, n, k), k).total + round_up(static_cast<size_t>(m) * 4, kWsAlign);
+}
+
+ptq1_status ptq1_gemm_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m, float *y, void *ws,
+                           size_t ws_bytes, hipStream_t stream)
+{
+    int64_t wb, mk, mn, xb, yb;
+    PTQ1_TRY(check_matrix(tiled, "tiled", n, k, false, &wb, true));
+    if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "m = %lld > %lld", (long long)m, (long long)kMaxGemmM);
+    if (!mul_ok(m, k, &mk) || !mul_ok(m, n, &mn)) return fail(PTQ1_ERR_OVERFLOW, "m * k or m * n overflows");
+    PTQ1_TRY(check_floats(y, "y", mn, &yb));
+    if (mn == 0) return ok();
+    if (k == 0) return fail(PTQ1_ERR_SHAPE, "k = 0");
+    PTQ1_TRY(check_floats(x, "x", mk, &xb));
+    const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k);
+    const GemmWs L = gemm_layout(plan, k);
+    const size_t need = ptq1_gemm_w2a8_workspace_bytes(m, n, k);
+    PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm_w2a8"));
+    if (overlaps(y, yb, x, xb)) return fail(PTQ1_ERR_ALIAS, "y overlaps x");
+    if (overlaps(y, yb, tiled, wb)) return fail(PTQ1_ERR_ALIAS, "y overlaps tiled");
+    if (overlaps(ws, (int64_t)need, y, yb) || overlaps(ws, (int64_t)need, x, xb) ||
+        overlaps(ws, (int64_t)need, tiled, wb))
+        return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
+    char *w = static_cast<char *>(ws);
+    uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
+    float *part = reinterpret_cast<float *>(w + L.part);
+    float *step = reinterpret_cast<float *>(w + L.total);
+    hipError_t e = ptq1::launch_prep_frag_w8(x, m, k, xf, step, stream);
+    if (e == hipSuccess)
+        e = profiled(kProfGemm, stream, [&] {
+            return ptq1::launch_gemm(plan, xf, m, tiled, n, nullptr, 0, y, nullptr, nullptr, part, stream);
+        });
+    if (e == hipSuccess) e = ptq1::launch_w2a8_scale_rows(y, m, n, step, stream);
+    return hip_status(e, "ptq1_gemm_w2a8");
+}
+
 size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
 {
     if (m < 0 || m > kMaxGemmM || pq2_packed(f, d) < 0 || pq2_packed(d, f) < 0 || f > INT64_MAX / 2) return 0;

@@ -64,11 +64,15 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 // order, i.e. step s, half h takes block positions 64 h + 8 s + j, which are
 // the two code bytes 16 h + 2 s, 16 h + 2 s + 1 of a PQ2_0 block.
 // ---------------------------------------------------------------------------
-template <bool Q2>
+// W8: 8-bit activations instead (x given, no rotation, no norm): the row's
+// max |x| comes from the same whole-row loads as the mean square, and the
+// chunk is written as q = rint(x * float(127 / max|x|)), integers that bf16
+// holds exactly; wave 0 of the row also stores its step max|x| / 127.
+template <bool Q2, bool W8>
 __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
     int64_t k, const float *__restrict__ signs, float rms_eps, const float *__restrict__ gain,
-    uint16_t *__restrict__ xf)
+    uint16_t *__restrict__ xf, float *__restrict__ step)
 {
     __shared__ float st[kHadamard];
     const int64_t cpr = (k + kHadamard - 1) / kHadamard;  // == k / 1024 when signs are given
@@ -85,7 +89,7 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     float v[kRotPerLane], uw[kRotPerLane], sg[kRotPerLane];
     float4 xv[kQ];
     const float *src0 = x != nullptr ? x : g;
-    const bool rms = x != nullptr && rms_eps > 0.0f;
+    const bool rms = !W8 && x != nullptr && rms_eps > 0.0f;
     const float4 *xr = reinterpret_cast<const float4 *>(src0 + row * k);
     const int64_t k4 = k / 4;  // k is a multiple of 128
 #pragma unroll
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) sg[j] = 1.0f;
     }
-    if (rms) {
+    if (rms || W8) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             const int64_t i = q * kWave + lane;
@@ -159,6 +163,28 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
         const float a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) v[j] *= a;
+    }
+    if constexpr (W8) {
+        // the row's max |x|, batch by batch (clamped copies repeat a real element)
+        float mx = 0.0f;
+        for (int64_t i0 = 0; i0 < k4; i0 += kQ * kWave) {
+            if (i0 > 0) {
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    const int64_t i = i0 + q * kWave + lane;
+                    xv[q] = xr[i < k4 ? i : k4 - 1];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
+        }
+#pragma unroll
+        for (int h = kWave / 2; h > 0; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h, kWave));
+        const float c = mx > 0.0f ? static_cast<float>(127.0 / static_cast<double>(mx)) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kRotPerLane; ++j) v[j] = rintf(v[j] * c);
+        if (ch == 0 && lane == 0) step[row] = static_cast<float>(static_cast<double>(mx) / 127.0);
     }
     if (signs != nullptr) {
 #pragma unroll
@@ -1090,8 +1116,8 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prep_frag<false>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u,
-                       k, signs, rms_eps, gain, xf);
+    hipLaunchKernelGGL((k_prep_frag<false, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
     return hipGetLastError();
 }
 
@@ -1100,8 +1126,18 @@ hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, 
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prep_frag<true>, dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x, g, u,
-                       k, signs, rms_eps, gain, xf);
+    hipLaunchKernelGGL((k_prep_frag<true, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint16_t *xf, float *step, hipStream_t s)
+{
+    const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
+    if (nchunks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_prep_frag<false, true>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+                       static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k,
+                       static_cast<const float *>(nullptr), 0.0f, static_cast<const float *>(nullptr), xf, step);
     return hipGetLastError();
 }
 

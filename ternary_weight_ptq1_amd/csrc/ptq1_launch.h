@@ -70,6 +70,10 @@ int64_t lut_nslices(int64_t k);
 // step = max|x| / 127 (one workgroup); y = residual + step * sum of the
 // lookup matvec's partials over q.
 hipError_t launch_w2a8_quant(const float *x, int64_t k, float *q, float *step, hipStream_t s);
+// GEMM side: bf16 fragments of the per-row quantised x (integer values,
+// exact in bf16) and step[row]; then y [m][n] *= step[row].
+hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint16_t *xf, float *step, hipStream_t s);
+hipError_t launch_w2a8_scale_rows(float *y, int64_t m, int64_t n, const float *step, hipStream_t s);
 hipError_t launch_w2a8_sum(const float *part, int64_t n, int64_t k, const float *step, const float *residual,
                            float *y, hipStream_t s);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);

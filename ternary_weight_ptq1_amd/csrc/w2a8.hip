@@ -80,6 +80,24 @@ __global__ void __launch_bounds__(kEwThreads) k_w2a8_sum(const float *__restrict
     if (r0 < n) y[r] = residual != nullptr ? fmaf(st, t, res) : st * t;
 }
 
+// y [m][n] *= step[row]
+__global__ void __launch_bounds__(kEwThreads) k_w2a8_scale_rows(float *__restrict__ y, int64_t m, int64_t n,
+                                                                const float *__restrict__ step)
+{
+    const int64_t i = blockIdx.x * static_cast<int64_t>(kEwThreads) + threadIdx.x;
+    if (i >= m * n) return;
+    y[i] *= step[i / n];
+}
+
+hipError_t launch_w2a8_scale_rows(float *y, int64_t m, int64_t n, const float *step, hipStream_t s)
+{
+    const int64_t total = m * n;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_w2a8_scale_rows, dim3(static_cast<unsigned>((total + kEwThreads - 1) / kEwThreads)),
+                       dim3(kEwThreads), 0, s, y, m, n, step);
+    return hipGetLastError();
+}
+
 hipError_t launch_w2a8_quant(const float *x, int64_t k, float *q, float *step, hipStream_t s)
 {
     if (k == 0) return hipSuccess;

@@ -828,3 +828,25 @@ def test_pq2_and_w2a8_graph_replay_matches_eager():
         P.pq2_ffn_block(other, tg, tu, td, s, d, f, 1e-6, ws=ws)  # eager work between replays
         P.ptq1_matvec_w2a8(tw, d, f, other[0].repeat(f // d), ws=ws8)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 384), (8, 1024, 1024), (40, 200, 640), (100, 513, 1024),
+                                   (256, 1000, 2048)])
+def test_w2a8_gemm(m, n, k):
+    t, s = host_matrix(13, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    x = synth.activations(13, m, k)
+    got = host(P.ptq1_gemm_w2a8(tiled(b, n, k), n, k, to_dev(x)))
+    assert rel_l2(got, oracle.w2a8_gemm(b, n, k, x)) <= TOL_FP32
+
+
+def test_w2a8_gemm_prefill_shape():
+    """M = 256 over one 17408 x 5120 projection on rotated rows, 256 sampled columns."""
+    m, n, k, seed = 256, 17408, 5120, 14
+    t, s = host_matrix(seed, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    del t
+    xr = oracle.rotate(synth.activations(seed, m, k), synth.signs(seed)).astype(np.float32)
+    got = host(P.ptq1_gemm_w2a8(tiled(b, n, k), n, k, to_dev(xr)))
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 254, n)])).astype(np.int64)
+    assert rel_l2(got[:, rows], oracle.w2a8_gemm(b, n, k, xr, rows=rows)) <= TOL_FP32

@@ -525,3 +525,14 @@ def test_w2a8_matvec_brute_force():
     q = [int(np.rint(np.float32(float(v)) * np.float32(c))) for v in x]
     ref = [sc * sum(int(t[r, i]) * q[i] for i in range(128)) * (g / 127.0) for r, sc in ((0, 1.0), (1, -0.5))]
     np.testing.assert_allclose(oracle.w2a8_matvec(oracle.pack(t, s), 2, 128, x), ref, rtol=1e-15, atol=0)
+
+
+def test_w2a8_gemm_rows_on_the_grid_equal_the_float_gemm():
+    """Rows already on the integer grid, each with max |x| = 127: the
+    per-token W2A8 product equals the C oracle's fp64 GEMM."""
+    n, k, m = 40, 640, 3
+    rng = np.random.default_rng(8)
+    b = oracle.pack(synth.trits(8, synth.S_W_TRITS, n, k), synth.scales(8, synth.S_W_SCALES, n, k // 128))
+    x = rng.integers(-127, 128, size=(m, k)).astype(np.float64)
+    x[:, 3] = 127
+    np.testing.assert_allclose(oracle.w2a8_gemm(b, n, k, x), oracle.gemm(b, n, k, x), rtol=1e-13, atol=0)
