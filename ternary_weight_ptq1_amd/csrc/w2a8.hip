@@ -16,7 +16,7 @@ namespace ptq1 {
 
 constexpr int kQThreads = 1024;
 constexpr int kQPer = 24;  // values per thread held in registers (k <= 24576 in one pass)
-constexpr int kSumBatch = 16;
+constexpr int kSumBatch = 72;  // slices loaded at once (all of them up to K = 18432)
 
 // One workgroup: max |x| over k, then q and the step.  Every load of the
 // first kQPer x 1024 values is requested before the reduction (clamped
