@@ -77,6 +77,8 @@ _SIGS = {
     "ptq1_gemm_w2a8": ([p, i64, i64, p, i64, p, p, sz, p], C.c_int),
     "ptq1_matvec_w2a8": ([p, i64, i64, p, p, p, p, sz, p], C.c_int),
     "pq2_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
+    "ptq1_ffn_workspace_offsets": ([i64, i64, i64, p], C.c_int),
+    "pq2_ffn_workspace_offsets": ([i64, i64, i64, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
 }
@@ -119,22 +121,76 @@ def _stream(stream):
     return C.c_void_p(s.cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_cuda:
+# ------------------------------------------------------------- validation ----
+# The C library sees only pointers and sizes, so every tensor is checked here
+# against the sizes the call will read or write before anything is enqueued:
+# a host tensor or a short one would become an out-of-range device access.
+
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, numel: int | None = None, min_numel: int | None = None,
+         device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call uses {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call reads or writes {min_numel}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     return t
+
+
+def _opt(t, name, dtype, numel=None, device=None):
+    return None if t is None else _dev(t, name, dtype, numel=numel, device=device)
+
+
+def _signs(s, device, required=True):
+    if s is None:
+        if required:
+            raise ValueError("signs1024 is required")
+        return None
+    return _dev(s, "signs1024", torch.float32, numel=HADAMARD, device=device)
+
+
+def _rows_of(x: torch.Tensor, k: int, name: str = "x") -> int:
+    """Rows of an activation tensor of width k (its element count must be a multiple of k)."""
+    if k <= 0:
+        raise ValueError(f"k = {k} must be positive")
+    if x.numel() % k != 0:
+        raise ValueError(f"{name} has {x.numel()} elements, not a multiple of k = {k}")
+    return x.numel() // k
+
+
+def _mat(w: torch.Tensor, name: str, nbytes: int, device):
+    """A weight matrix of nbytes bytes (a negative nbytes is a bad shape, refused by the library)."""
+    return _dev(w, name, torch.uint8, min_numel=nbytes if nbytes > 0 else None, device=device)
 
 
 def _ws(nbytes: int, device, ws):
     if nbytes == 0:
         return None, 0
-    if ws is not None and ws.numel() >= nbytes:
-        return ws, ws.numel()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    _dev(ws, "ws", torch.uint8, min_numel=nbytes, device=device)
+    return ws, ws.numel()
+
+
+def _out(out, name, shape, device, dtype=torch.float32):
+    count = 1
+    for s in shape:
+        count *= s
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _dev(out, name, dtype, numel=count, device=device)
 
 
 # ------------------------------------------------------------------ codec ----
@@ -150,15 +206,23 @@ def ptq1_packed_bytes(n: int, k: int) -> int:
     return lib().ptq1_packed_bytes(n, k)
 
 
+def _trits_scales(trits, scales_f16):
+    _dev(trits, "trits", torch.int8)
+    if trits.dim() != 2:
+        raise ValueError("trits must be [n, k]")
+    n, k = trits.shape
+    if k % BLOCK_WEIGHTS != 0:
+        raise ValueError(f"k = {k} is not a multiple of {BLOCK_WEIGHTS}")
+    _dev(scales_f16, "scales_f16", (torch.int16, torch.float16, torch.uint16), numel=n * (k // BLOCK_WEIGHTS),
+         device=trits.device)
+    return n, k
+
+
 def ptq1_pack(trits: torch.Tensor, scales_f16: torch.Tensor, out: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
     """int8 trits [n, k] + binary16 bit patterns [n, k/128] (int16 or float16) -> uint8 [n, k/128*28]."""
-    _dev(trits, "trits", torch.int8)
-    _dev(scales_f16, "scales_f16", (torch.int16, torch.float16, torch.uint16))
-    n, k = trits.shape
-    if out is None:
-        out = torch.empty((n, (k // BLOCK_WEIGHTS) * BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
-    _dev(out, "blocks", torch.uint8)
+    n, k = _trits_scales(trits, scales_f16)
+    out = _out(out, "blocks", (n, (k // BLOCK_WEIGHTS) * BLOCK_BYTES), trits.device, torch.uint8)
     _check("ptq1_pack", lib().ptq1_pack(_ptr(trits), _ptr(scales_f16), n, k, _ptr(out), _stream(stream)))
     return out
 
@@ -171,23 +235,19 @@ def ptq1_tile(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = N
               stream=None) -> torch.Tensor:
     """Packed [n, k/128*28] uint8 -> the tiled device layout (flat uint8) the
     matvec, gate/up, GEMM and feed-forward calls read."""
-    _dev(blocks, "blocks", torch.uint8)
     nbytes = ptq1_tiled_bytes(n, k)
     if nbytes < 0:
         raise ValueError(f"bad shape [{n}][{k}]")
-    if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
-    _dev(out, "tiled", torch.uint8)
+    _mat(blocks, "blocks", ptq1_packed_bytes(n, k), None)
+    out = _out(out, "tiled", (nbytes,), blocks.device, torch.uint8)
     _check("ptq1_tile", lib().ptq1_tile(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
     return out
 
 
 def ptq1_dequant(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
-    _dev(blocks, "blocks", torch.uint8)
-    if out is None:
-        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
-    _dev(out, "w", torch.float32)
+    _mat(blocks, "blocks", ptq1_packed_bytes(n, k), None)
+    out = _out(out, "w", (n, k), blocks.device)
     _check("ptq1_dequant", lib().ptq1_dequant(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
     return out
 
@@ -198,12 +258,12 @@ def hadamard_rotate(x: torch.Tensor, signs1024: torch.Tensor, out: torch.Tensor 
                     stream=None) -> torch.Tensor:
     """Rotate the rows of x [m, k] (or [k]); out may be x."""
     _dev(x, "x", torch.float32)
-    _dev(signs1024, "signs1024", torch.float32)
-    k = x.shape[-1]
-    m = x.numel() // k if k else 0
+    _signs(signs1024, x.device)
+    k = x.shape[-1] if x.dim() > 0 else 0
+    m = _rows_of(x, k)
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "y", torch.float32)
+    _dev(out, "y", torch.float32, numel=x.numel(), device=x.device)
     _check("hadamard_rotate", lib().hadamard_rotate(_ptr(x), _ptr(out), m, k, _ptr(signs1024),
                                                     _stream(stream)))
     return out
@@ -213,16 +273,16 @@ def hadamard_unrotate_rows(table: torch.Tensor, signs1024: torch.Tensor, ids: to
                            n_rows: int | None = None, out: torch.Tensor | None = None,
                            stream=None) -> torch.Tensor:
     _dev(table, "table", torch.float32)
-    _dev(signs1024, "signs1024", torch.float32)
+    if table.dim() != 2:
+        raise ValueError("table must be [n_table, d]")
+    _signs(signs1024, table.device)
     n_table, d = table.shape
     if ids is not None:
-        _dev(ids, "ids", torch.int32)
+        _dev(ids, "ids", torch.int32, device=table.device)
         n_rows = ids.numel()
     elif n_rows is None:
         n_rows = n_table
-    if out is None:
-        out = torch.empty((n_rows, d), dtype=torch.float32, device=table.device)
-    _dev(out, "out", torch.float32)
+    out = _out(out, "out", (n_rows, d), table.device)
     _check("hadamard_unrotate_rows",
            lib().hadamard_unrotate_rows(_ptr(table), n_table, d, _ptr(ids), n_rows, _ptr(signs1024),
                                         _ptr(out), _stream(stream)))
@@ -236,33 +296,35 @@ def ptq1_matvec(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024
                 ws: torch.Tensor | None = None, stream=None, fn: str = "ptq1_matvec") -> torch.Tensor:
     """y = residual + W R x, W tiled (ptq1_tile).  ws: optional scratch of
     at least workspace_bytes("matvec", n, k) bytes."""
-    _dev(blocks, "blocks", torch.uint8)
-    _dev(x, "x", torch.float32)
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().ptq1_matvec_workspace_bytes(n, k), x.device, ws)
+    _dev(x, "x", torch.float32, numel=k)
+    dv = x.device
+    _mat(blocks, "blocks", ptq1_tiled_bytes(n, k), dv)
+    _signs(signs1024, dv, required=False)
+    _opt(residual, "residual", torch.float32, numel=n, device=dv)
+    out = _out(out, "y", (n,), dv)
+    ws, wsb = _ws(lib().ptq1_matvec_workspace_bytes(n, k), dv, ws)
     _check(fn, getattr(lib(), fn)(_ptr(blocks), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
                                   _ptr(out), _ptr(ws), wsb, _stream(stream)))
     return out
 
 
 def ptq1_matvec_float_peel(blocks, n, k, x, signs1024, residual=None, out=None, ws=None, stream=None):
-    """The same matvec over the packed (row-major) layout, trits peeled on the float pipeline."""
+    """The same matvec with every trit peeled on the float pipeline, eight lanes per block (tiled layout)."""
     return ptq1_matvec(blocks, n, k, x, signs1024, residual, out, ws, stream, fn="ptq1_matvec_float_peel")
 
 
 def ptq1_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, f: int, d: int, x: torch.Tensor,
                  signs1024: torch.Tensor | None, g: torch.Tensor | None = None,
                  u: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
-    _dev(w_gate, "w_gate", torch.uint8)
-    _dev(w_up, "w_up", torch.uint8)
-    _dev(x, "x", torch.float32)
-    if g is None:
-        g = torch.empty(f, dtype=torch.float32, device=x.device)
-    if u is None:
-        u = torch.empty(f, dtype=torch.float32, device=x.device)
-    ws, wsb = _ws(lib().ptq1_gate_up_workspace_bytes(f, d), x.device, ws)
+    _dev(x, "x", torch.float32, numel=d)
+    dv = x.device
+    tb = ptq1_tiled_bytes(f, d)
+    _mat(w_gate, "w_gate", tb, dv)
+    _mat(w_up, "w_up", tb, dv)
+    _signs(signs1024, dv, required=False)
+    g = _out(g, "g", (f,), dv)
+    u = _out(u, "u", (f,), dv)
+    ws, wsb = _ws(lib().ptq1_gate_up_workspace_bytes(f, d), dv, ws)
     _check("ptq1_gate_up", lib().ptq1_gate_up(_ptr(w_gate), _ptr(w_up), f, d, _ptr(x), _ptr(signs1024),
                                               _ptr(g), _ptr(u), _ptr(ws), wsb, _stream(stream)))
     return g, u
@@ -270,9 +332,10 @@ def ptq1_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, f: int, d: int, x: to
 
 def ptq1_swiglu(g: torch.Tensor, u: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     _dev(g, "g", torch.float32)
-    _dev(u, "u", torch.float32)
+    _dev(u, "u", torch.float32, numel=g.numel(), device=g.device)
     if out is None:
         out = torch.empty_like(g)
+    _dev(out, "h", torch.float32, numel=g.numel(), device=g.device)
     _check("ptq1_swiglu", lib().ptq1_swiglu(_ptr(g), _ptr(u), _ptr(out), g.numel(), _stream(stream)))
     return out
 
@@ -281,13 +344,13 @@ def ptq1_swiglu(g: torch.Tensor, u: torch.Tensor, out: torch.Tensor | None = Non
 
 def ptq1_gemm(blocks: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
               out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    _dev(blocks, "blocks", torch.uint8)
     _dev(x, "x", torch.float32)
-    m = x.numel() // k if k else 0
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().ptq1_gemm_workspace_bytes(m, n, k), x.device, ws)
+    dv = x.device
+    m = _rows_of(x, k)
+    _mat(blocks, "blocks", ptq1_tiled_bytes(n, k), dv)
+    _signs(signs1024, dv, required=False)
+    out = _out(out, "y", (m, n), dv)
+    ws, wsb = _ws(lib().ptq1_gemm_workspace_bytes(m, n, k), dv, ws)
     _check("ptq1_gemm", lib().ptq1_gemm(_ptr(blocks), n, k, _ptr(x), m, _ptr(signs1024), _ptr(out),
                                         _ptr(ws), wsb, _stream(stream)))
     return out
@@ -301,16 +364,19 @@ def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_
     scale of x when rms_eps > 0; rms_gain [d] or None); out may be x.  fn = "pq2_ffn_block" takes
     PQ2_0 tiled matrices (pq2_tile)."""
     _dev(x, "x", torch.float32)
-    if rms_gain is not None:
-        _dev(rms_gain, "rms_gain", torch.float32)
-    for w, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
-        _dev(w, nm, torch.uint8)
-    m = x.numel() // d if d else 0
+    dv = x.device
+    m = _rows_of(x, d)
+    tiled = pq2_tiled_bytes if fn == "pq2_ffn_block" else ptq1_tiled_bytes
+    _mat(w_gate, "w_gate", tiled(f, d), dv)
+    _mat(w_up, "w_up", tiled(f, d), dv)
+    _mat(w_down, "w_down", tiled(d, f), dv)
+    _signs(signs1024, dv)
+    _opt(rms_gain, "rms_gain", torch.float32, numel=d, device=dv)
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "x_out", torch.float32)
+    _dev(out, "x_out", torch.float32, numel=m * d, device=dv)
     wsfn = "pq2_ffn_workspace_bytes" if fn == "pq2_ffn_block" else "ptq1_ffn_workspace_bytes"
-    ws, wsb = _ws(getattr(lib(), wsfn)(m, d, f), x.device, ws)
+    ws, wsb = _ws(getattr(lib(), wsfn)(m, d, f), dv, ws)
     _check(fn, getattr(lib(), fn)(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                   _ptr(signs1024), float(rms_eps), _ptr(rms_gain) if rms_gain is not None else None,
                                   _ptr(ws), wsb, _stream(stream)))
@@ -336,22 +402,16 @@ def pq2_packed_bytes(n: int, k: int) -> int:
 def pq2_pack(trits: torch.Tensor, scales_f16: torch.Tensor, out: torch.Tensor | None = None,
              stream=None) -> torch.Tensor:
     """int8 trits [n, k] + binary16 bit patterns [n, k/128] -> uint8 [n, k/128*34]."""
-    _dev(trits, "trits", torch.int8)
-    _dev(scales_f16, "scales_f16", (torch.int16, torch.float16, torch.uint16))
-    n, k = trits.shape
-    if out is None:
-        out = torch.empty((n, (k // BLOCK_WEIGHTS) * PQ2_BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
-    _dev(out, "blocks", torch.uint8)
+    n, k = _trits_scales(trits, scales_f16)
+    out = _out(out, "blocks", (n, (k // BLOCK_WEIGHTS) * PQ2_BLOCK_BYTES), trits.device, torch.uint8)
     _check("pq2_pack", lib().pq2_pack(_ptr(trits), _ptr(scales_f16), n, k, _ptr(out), _stream(stream)))
     return out
 
 
 def pq2_dequant(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
                 stream=None) -> torch.Tensor:
-    _dev(blocks, "blocks", torch.uint8)
-    if out is None:
-        out = torch.empty((n, k), dtype=torch.float32, device=blocks.device)
-    _dev(out, "w", torch.float32)
+    _mat(blocks, "blocks", pq2_packed_bytes(n, k), None)
+    out = _out(out, "w", (n, k), blocks.device)
     _check("pq2_dequant", lib().pq2_dequant(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
     return out
 
@@ -363,13 +423,11 @@ def pq2_tiled_bytes(n: int, k: int) -> int:
 def pq2_tile(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None,
              stream=None) -> torch.Tensor:
     """Packed PQ2_0 [n, k/128*34] uint8 -> the tiled layout pq2_matvec reads (flat uint8)."""
-    _dev(blocks, "blocks", torch.uint8)
     nbytes = pq2_tiled_bytes(n, k)
     if nbytes < 0:
         raise ValueError(f"bad shape [{n}][{k}]")
-    if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
-    _dev(out, "tiled", torch.uint8)
+    _mat(blocks, "blocks", pq2_packed_bytes(n, k), None)
+    out = _out(out, "tiled", (nbytes,), blocks.device, torch.uint8)
     _check("pq2_tile", lib().pq2_tile(_ptr(blocks), n, k, _ptr(out), _stream(stream)))
     return out
 
@@ -378,12 +436,13 @@ def pq2_matvec(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: 
                residual: torch.Tensor | None = None, out: torch.Tensor | None = None,
                ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y = residual + W R x over a PQ2_0 tiled matrix (pq2_tile)."""
-    _dev(tiled, "tiled", torch.uint8)
-    _dev(x, "x", torch.float32)
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().pq2_matvec_workspace_bytes(n, k), x.device, ws)
+    _dev(x, "x", torch.float32, numel=k)
+    dv = x.device
+    _mat(tiled, "tiled", pq2_tiled_bytes(n, k), dv)
+    _signs(signs1024, dv, required=False)
+    _opt(residual, "residual", torch.float32, numel=n, device=dv)
+    out = _out(out, "y", (n,), dv)
+    ws, wsb = _ws(lib().pq2_matvec_workspace_bytes(n, k), dv, ws)
     _check("pq2_matvec", lib().pq2_matvec(_ptr(tiled), n, k, _ptr(x), _ptr(signs1024), _ptr(residual),
                                           _ptr(out), _ptr(ws), wsb, _stream(stream)))
     return out
@@ -392,13 +451,13 @@ def pq2_matvec(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: 
 def pq2_gemm(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: torch.Tensor | None,
              out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y [m, n] = bf16(R X) . W^T over a PQ2_0 tiled matrix (pq2_tile)."""
-    _dev(tiled, "tiled", torch.uint8)
     _dev(x, "x", torch.float32)
-    m = x.numel() // k if k else 0
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().pq2_gemm_workspace_bytes(m, n, k), x.device, ws)
+    dv = x.device
+    m = _rows_of(x, k)
+    _mat(tiled, "tiled", pq2_tiled_bytes(n, k), dv)
+    _signs(signs1024, dv, required=False)
+    out = _out(out, "y", (m, n), dv)
+    ws, wsb = _ws(lib().pq2_gemm_workspace_bytes(m, n, k), dv, ws)
     _check("pq2_gemm", lib().pq2_gemm(_ptr(tiled), n, k, _ptr(x), m, _ptr(signs1024), _ptr(out), _ptr(ws), wsb,
                                       _stream(stream)))
     return out
@@ -407,12 +466,12 @@ def pq2_gemm(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, signs1024: to
 def ptq1_matvec_w2a8(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, residual: torch.Tensor | None = None,
                      out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y = residual + W q * step with x quantised to 8-bit integers (per call, absmax)."""
-    _dev(tiled, "tiled", torch.uint8)
-    _dev(x, "x", torch.float32)
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().ptq1_matvec_w2a8_workspace_bytes(n, k), x.device, ws)
+    _dev(x, "x", torch.float32, numel=k)
+    dv = x.device
+    _mat(tiled, "tiled", ptq1_tiled_bytes(n, k), dv)
+    _opt(residual, "residual", torch.float32, numel=n, device=dv)
+    out = _out(out, "y", (n,), dv)
+    ws, wsb = _ws(lib().ptq1_matvec_w2a8_workspace_bytes(n, k), dv, ws)
     _check("ptq1_matvec_w2a8", lib().ptq1_matvec_w2a8(_ptr(tiled), n, k, _ptr(x), _ptr(residual), _ptr(out),
                                                       _ptr(ws), wsb, _stream(stream)))
     return out
@@ -421,16 +480,23 @@ def ptq1_matvec_w2a8(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, resid
 def ptq1_gemm_w2a8(tiled: torch.Tensor, n: int, k: int, x: torch.Tensor, out: torch.Tensor | None = None,
                    ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y [m, n] with each row of x quantised to 8-bit integers (its own absmax)."""
-    _dev(tiled, "tiled", torch.uint8)
     _dev(x, "x", torch.float32)
-    m = x.numel() // k if k else 0
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _dev(out, "y", torch.float32)
-    ws, wsb = _ws(lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k), x.device, ws)
+    dv = x.device
+    m = _rows_of(x, k)
+    _mat(tiled, "tiled", ptq1_tiled_bytes(n, k), dv)
+    out = _out(out, "y", (m, n), dv)
+    ws, wsb = _ws(lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k), dv, ws)
     _check("ptq1_gemm_w2a8", lib().ptq1_gemm_w2a8(_ptr(tiled), n, k, _ptr(x), m, _ptr(out), _ptr(ws), wsb,
                                                   _stream(stream)))
     return out
+
+
+def ffn_workspace_offsets(m: int, d: int, f: int, fmt: str = "ptq1") -> tuple[int, int, int]:
+    """Byte offsets of (g, u, h) in an FFN block's workspace (-1: not stored on that path)."""
+    out = (C.c_int64 * 3)()
+    fn = "pq2_ffn_workspace_offsets" if fmt == "pq2" else "ptq1_ffn_workspace_offsets"
+    _check(fn, getattr(lib(), fn)(m, d, f, C.cast(out, p)))
+    return tuple(out)
 
 
 def workspace_bytes(kind: str, *shape) -> int:
