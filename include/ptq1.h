@@ -30,8 +30,8 @@
  * byte (2i + b) * 28 of the tile; places past the matrix (r >= n or
  * j >= k/128) hold zero bytes.  The
  * matvec, gate/up, GEMM and feed-forward calls read weights in this layout
- * (ptq1_tile makes it from a packed matrix, once, at load time); pack,
- * dequant and the float-peel matvec use the packed layout.
+ * (ptq1_tile makes it from a packed matrix, once, at load time); pack
+ * and dequant use the packed layout.
  *
  * Beyond PTQ1_0 with fp32 activations, two more numerics of the same layer:
  * the PQ2_0 format (pq2_*: two bits per weight, described before pq2_packed_bytes)
@@ -176,11 +176,12 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
                         size_t ws_bytes, hipStream_t stream);
 
 /* The same matvec with every trit peeled on the float pipeline as the page
- * describes ("What Ferrox does with it": floor(3^(n+1) u) - 3 floor(3^n u)),
- * one lane per output row, reading the packed (row-major) layout the page's
- * kernel streams.  Same results and workspace size as ptq1_matvec, but
- * `blocks` is packed [n][k], not tiled; kept as the page's own decode. */
-ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+ * describes ("What Ferrox does with it": eight lanes share one 128-weight
+ * block, each lane owns whole bytes, and a trit is floor(3^(n+1) u) -
+ * 3 floor(3^n u), u = byte/256).  Same tiled matrix, results (to rounding
+ * order), workspace size and errors as ptq1_matvec; kept as the page's own
+ * decode, to be measured beside the table lookups. */
+ptq1_status ptq1_matvec_float_peel(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                                    const float *signs1024, const float *residual, float *y, void *ws,
                                    size_t ws_bytes, hipStream_t stream);
 
@@ -231,6 +232,21 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
                            const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
                            const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* Where ptq1_ffn_block leaves the block's intermediate activations in its
+ * workspace, so a caller can inspect each stage after the call ("A 27B model
+ * in 5.5 GB: Bonsai ternary on Ferrox, locally", "Accuracy: measured, not
+ * eyeballed": every execution path is compared stage by stage):
+ *   offsets[0], offsets[1]  byte offsets of g and u, fp32 [m][f] (the gate
+ *                           and up projections of the normalised input), for
+ *                           m >= 2; -1 for m == 1;
+ *   offsets[2]              byte offset of h = silu(g) * u, fp32 [f], for
+ *                           m == 1; -1 for m >= 2 (there h is only formed in
+ *                           bf16 inside the down projection's input).
+ * They hold the values of the last call with this (m, d, f) until the
+ * workspace is reused.  Errors: NULL, SHAPE (m < 1, d or f not a multiple of
+ * 1024), UNSUPPORTED (m). */
+ptq1_status ptq1_ffn_workspace_offsets(int64_t m, int64_t d, int64_t f, int64_t *offsets);
 
 /* ---- PQ2_0: the two-bit ternary format ("Why I Am Building Another
  * Inference Engine", Level 2: two bits per weight and a 16-bit scale for every
@@ -293,6 +309,9 @@ ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, in
                           const uint8_t *w_up, const uint8_t *w_down, const float *signs1024, float rms_eps,
                           const float *rms_gain, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The same stage offsets for pq2_ffn_block's workspace. */
+ptq1_status pq2_ffn_workspace_offsets(int64_t m, int64_t d, int64_t f, int64_t *offsets);
+
 /* Batch-1 decode matvec with 8-bit activations (W2A8: "Why I Am Building
  * Another Inference Engine", Level 5, the numerics of integer kernels; Level
  * 4, where a BitNet layer rounds its activations to int8 ahead of its ternary
@@ -326,8 +345,9 @@ ptq1_status ptq1_gemm_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const flo
  * a kernel inside a composite call (ptq1_ffn_block) with events.  Families: "lut_matvec_2" (the
  * table-lookup matvec over two matrices: gate and up), "lut_matvec_1" (over
  * one matrix: ptq1_matvec, ptq1_matvec_w2a8, the down projection), "gemm" (the MFMA GEMM),
- * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec); pq2_gemm's
- * kernel counts as "gemm".
+ * "pq2_matvec" (the PQ2_0 table-lookup matvec of pq2_matvec), "peel_matvec"
+ * (the float-peel matvec of ptq1_matvec_float_peel); pq2_gemm's kernel
+ * counts as "gemm".
  * Events are created and owned by the caller; both arrays must stay valid
  * until `count` launches have happened or the family is re-armed.  count =
  * 0 disarms.  Process-wide; not meant for concurrent use by several

@@ -206,12 +206,6 @@ ptq1_status check_ws(const void *ws, size_t ws_bytes, size_t need, const char *f
 int64_t nseg_of(int64_t k) { return (k + ptq1::kHadamard - 1) / ptq1::kHadamard; }
 
 // ---- workspace layouts -------------------------------------------------------
-// float-peel matvec: partials [1024-segment][row]
-size_t mv_ws(int64_t rows, int64_t k)
-{
-    return round_up(ptq1::matvec_part_floats(rows, k) * sizeof(float), kWsAlign);
-}
-
 // lookup-table decode: split-K partials [slice][matrix][row]
 size_t lut_ws(int64_t n, int nmat, int64_t k)
 {
@@ -264,8 +258,8 @@ FfnWs ffn_layout(int64_t m, int64_t d, int64_t f, bool rd_only = false)
 
 // ---- profiling hook ----------------------------------------------------------
 // Armed kernel families record caller events around their next launches.
-enum ProfKind { kProfLut2 = 0, kProfLut1 = 1, kProfGemm = 2, kProfPq2 = 3, kProfKinds = 4 };
-const char *const kProfNames[kProfKinds] = {"lut_matvec_2", "lut_matvec_1", "gemm", "pq2_matvec"};
+enum ProfKind { kProfLut2 = 0, kProfLut1 = 1, kProfGemm = 2, kProfPq2 = 3, kProfPeel = 4, kProfKinds = 5 };
+const char *const kProfNames[kProfKinds] = {"lut_matvec_2", "lut_matvec_1", "gemm", "pq2_matvec", "peel_matvec"};
 
 struct ProfArm {
     hipEvent_t *start = nullptr, *stop = nullptr;
@@ -470,8 +464,7 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0) return 0;
-    const size_t a = mv_ws(n, k), b = lut_ws(n, 1, k);
-    return a > b ? a : b;
+    return lut_ws(n, 1, k);
 }
 
 namespace {
@@ -526,17 +519,19 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
     return hip_status(e, "ptq1_matvec");
 }
 
-ptq1_status ptq1_matvec_float_peel(const uint8_t *blocks, int64_t n, int64_t k, const float *x,
+ptq1_status ptq1_matvec_float_peel(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                                    const float *signs1024, const float *residual, float *y, void *ws,
                                    size_t ws_bytes, hipStream_t stream)
 {
     bool empty;
-    PTQ1_TRY(check_matvec(blocks, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec_float_peel",
-                          false, &empty));
+    PTQ1_TRY(check_matvec(tiled, n, k, x, signs1024, residual, y, ws, ws_bytes, "ptq1_matvec_float_peel", true,
+                          &empty));
     if (empty) return ok();
     float *part = static_cast<float *>(ws);
-    hipError_t e = ptq1::launch_matvec_part(blocks, n, nullptr, 0, k, x, signs1024, part, stream);
-    if (e == hipSuccess) e = ptq1::launch_reduce_rows(part, n, nseg_of(k), residual, y, stream);
+    hipError_t e = profiled(kProfPeel, stream, [&] {
+        return ptq1::launch_matvec_peel(tiled, nullptr, 1, n, k, x, signs1024, nullptr, part, stream);
+    });
+    if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
     return hip_status(e, "ptq1_matvec_float_peel");
 }
 
@@ -707,6 +702,35 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
             });
     }
     return hip_status(e, "ptq1_ffn_block");
+}
+
+namespace {
+
+ptq1_status ffn_offsets(int64_t m, int64_t d, int64_t f, bool rd_only, int64_t *offsets, const char *fn)
+{
+    if (offsets == nullptr) return fail(PTQ1_ERR_NULL, "%s: offsets is NULL", fn);
+    if (m < 1 || d < 0 || f < 1) return fail(PTQ1_ERR_SHAPE, "%s: m = %lld, d = %lld, f = %lld", fn, (long long)m,
+                                             (long long)d, (long long)f);
+    if (m > kMaxGemmM) return fail(PTQ1_ERR_UNSUPPORTED, "%s: m = %lld > %lld", fn, (long long)m, (long long)kMaxGemmM);
+    if (d % ptq1::kHadamard != 0 || f % ptq1::kHadamard != 0)
+        return fail(PTQ1_ERR_SHAPE, "%s: d and f must be multiples of %d", fn, ptq1::kHadamard);
+    const FfnWs L = ffn_layout(m, d, f, rd_only);
+    offsets[0] = m >= 2 ? static_cast<int64_t>(L.g) : -1;
+    offsets[1] = m >= 2 ? static_cast<int64_t>(L.u) : -1;
+    offsets[2] = m == 1 ? static_cast<int64_t>(L.hr) : -1;
+    return ok();
+}
+
+}  // namespace
+
+ptq1_status ptq1_ffn_workspace_offsets(int64_t m, int64_t d, int64_t f, int64_t *offsets)
+{
+    return ffn_offsets(m, d, f, false, offsets, "ptq1_ffn_workspace_offsets");
+}
+
+ptq1_status pq2_ffn_workspace_offsets(int64_t m, int64_t d, int64_t f, int64_t *offsets)
+{
+    return ffn_offsets(m, d, f, true, offsets, "pq2_ffn_workspace_offsets");
 }
 
 // ---- PQ2_0 ------------------------------------------------------------------

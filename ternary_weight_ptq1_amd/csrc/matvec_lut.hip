@@ -67,7 +67,6 @@ namespace ptq1 {
 
 constexpr int kLutBlocks = 2;                          // blocks per K-slice
 constexpr int kLutSliceW = kLutBlocks * kBlockWeights;  // 256 weights
-constexpr int kLutSlots = kLutBlocks * kBlockBytes;    // 56 byte slots
 #ifndef PTQ1_LUT_THREADS
 #define PTQ1_LUT_THREADS 512
 #endif
@@ -78,47 +77,39 @@ constexpr int kLutBuildRanges = kLutThreads / kWave;   // table build: threads =
 constexpr int kLutBuildPer = 256 / kLutBuildRanges;    // byte values per thread
 constexpr int kLutRows = 32;                           // rows per unit
 constexpr int kLutTableBytes = 65536;                  // 256 byte values x 64 slot columns x fp32
-constexpr int kLutDepth = 3;                           // units of weights in flight per wave
-constexpr int kLutEarly = 1;                           // of which requested before x arrives
+#ifndef PTQ1_LUT_EARLY
+#define PTQ1_LUT_EARLY 1
+#endif
+#ifndef PTQ1_LUT_DEPTH
+#define PTQ1_LUT_DEPTH 3
+#endif
+constexpr int kLutEarly = PTQ1_LUT_EARLY;              // units per wave requested before x arrives
+constexpr int kLutDepth = PTQ1_LUT_DEPTH;              // units of weights in flight per wave
+static_assert(kLutEarly >= 1 && kLutEarly <= kLutDepth, "at least one unit before x, at most the depth");
+typedef uint32_t lut_u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 static_assert(kLutRows == kTileRows && kLutBlocks == kTileBlocks, "a unit is one tile");
 static_assert(kLutRows * kLutBlocks == kWave, "one block per lane");
 
-// Per-lane dword rotation (rho) and byte rotation (sigma) for lanes 0..31
-// (lanes 32..63 repeat them; lane 2i + b reads block b of row i): found by a
-// search that minimises LDS bank collisions of the 32 slots a half-wave
-// reads per lookup.  Packed into 64-bit immediates so a lane derives its own
-// pair arithmetically (a table in memory would put a load latency in front
-// of the weight requests).
-constexpr uint8_t kLutRho[32] = {4, 6, 6, 1, 1, 5, 3, 2, 5, 3, 3, 3, 3, 6, 0, 5,
-                                 1, 6, 3, 0, 2, 3, 1, 6, 6, 1, 6, 0, 4, 2, 0, 5};
-constexpr uint8_t kLutSig[32] = {0, 3, 1, 2, 1, 1, 1, 0, 0, 0, 3, 2, 0, 2, 1, 2,
-                                 0, 1, 2, 1, 3, 1, 2, 0, 2, 3, 3, 0, 3, 3, 0, 3};
+// Table columns: byte position p (0..31) of block b of the slice is column
+// 32 b + p.  Positions 0..25 are the trit bytes; 26, 27 (the scale) and
+// 28..31 (past the block) are columns of zeros.  Entry (column, byte value v)
+// sits at byte v * 256 + column * 4, so its LDS bank is the column.
+constexpr int kLutColsPerBlock = 32;
+constexpr int kLutDwords = kLutColsPerBlock / 4;  // 8 dword positions per block, 7 of them in memory
+static_assert(kLutBlocks * kLutColsPerBlock * 256 * 4 == 65536, "the table fills 64 KB");
 
-constexpr uint64_t lut_pack_nibbles(const uint8_t (&t)[32], int first)
-{
-    uint64_t v = 0;
-    for (int i = 0; i < 16; ++i) v |= static_cast<uint64_t>(t[first + i] & 15) << (4 * i);
-    return v;
-}
-
-constexpr uint64_t lut_pack_pairs(const uint8_t (&t)[32])
-{
-    uint64_t v = 0;
-    for (int i = 0; i < 32; ++i) v |= static_cast<uint64_t>(t[i] & 3) << (2 * i);
-    return v;
-}
-
-constexpr uint64_t kLutRhoLo = lut_pack_nibbles(kLutRho, 0);
-constexpr uint64_t kLutRhoHi = lut_pack_nibbles(kLutRho, 16);
-constexpr uint64_t kLutSigAll = lut_pack_pairs(kLutSig);
-
-__device__ __forceinline__ int lut_rho(int lane)
-{
-    const int l = lane & 31;
-    return static_cast<int>(((l < 16 ? kLutRhoLo : kLutRhoHi) >> (4 * (l & 15))) & 15u);
-}
-
-__device__ __forceinline__ int lut_sig(int lane) { return static_cast<int>((kLutSigAll >> (2 * (lane & 31))) & 3u); }
+// Lane 2i + b (row i, block b of a tile) holds in register r dword
+// (r + rho) mod 8 of its block and reads byte (c + sig) mod 4 of it at step
+// c, i.e. column 32 b + 4 ((r + rho) mod 8) + (c + sig) mod 4, with
+// rho = (4 b + i / 4) mod 8 and sig = i mod 4.  At every step the 32 lanes of
+// a block then read 32 different columns, and in each half-wave (rows 0..15
+// or 16..31) the block-0 lanes cover four dword positions and the block-1
+// lanes the other four: no two lanes of a wave, or of a half-wave, share an
+// LDS bank.  (Rotating through the loads instead -- four 8-byte loads per
+// block at lane-dependent offsets -- measured no faster than two wide loads
+// and three rounds of selects.)
+__device__ __forceinline__ int lut_rho(int lane) { return (4 * (lane & 1) + (lane >> 3)) & 7; }
+__device__ __forceinline__ int lut_sig(int lane) { return (lane >> 1) & 3; }
 
 struct LutArgs {
     const uint8_t *w0, *w1;  // one or two tiled [n][k] matrices
@@ -136,9 +127,9 @@ struct LutArgs {
 // H_4 (x) H_256 (the top two index bits are the H_4 factor), so outputs
 // 256 p .. 256 p + 255 of a 1024-chunk are the 256-point transform of
 // z_d = sum_c (-1)^popcount(p & c) s[256 c + d] x[256 c + d]: one wave, four
-// values per lane (d = lane + 64 k), butterflies across lanes by DPP and the
-// gfx950 lane-swap instructions (no LDS traffic), the two in-lane stages in
-// registers.  A butterfly leaves x_i + x_(i^h) at the lane whose bit h is 0
+// values per lane (six bits of d in the lane index, two in the register
+// index), butterflies across lanes by DPP and the gfx950 lane-swap
+// instructions (no LDS traffic), the two in-lane stages in registers.  A butterfly leaves x_i + x_(i^h) at the lane whose bit h is 0
 // and x_(i^h) - x_i at the other: partner + sgn * own, sgn = +-1.
 // ---------------------------------------------------------------------------
 template <int kRowShl, int kRowShr>
@@ -195,6 +186,70 @@ __device__ __forceinline__ void lut_fwht256(float (&v)[4], int lane)
     v[1] = t1 + t3;
     v[2] = t0 - t2;
     v[3] = t1 - t3;
+}
+
+// ---------------------------------------------------------------------------
+// x of one 256-wide K-slice, loaded by one wave before anything else: with
+// signs, the four quarters of the 1024-chunk holding the slice (lane l holds
+// elements 256 c + 4 l .. 256 c + 4 l + 3 of quarter c, one 16-byte load per
+// quarter and array); without, the slice itself (elements 4 l .. 4 l + 3,
+// clamped into the slice when it is a 128-wide tail).  The FWHT above does
+// not depend on which index bits sit in lanes and which in registers, so
+// with d = 4 l + k the slice's outputs come back as xs[4 l + k].
+// ---------------------------------------------------------------------------
+typedef float lut_f32x4 __attribute__((ext_vector_type(4)));
+
+struct SliceX {
+    lut_f32x4 x[4], s[4], g[4];
+};
+
+__device__ __forceinline__ void slice_x_load(const float *x, const float *signs, const float *gain, int64_t k0, int kw,
+                                             int lane, SliceX &v)
+{
+    if (signs != nullptr) {
+        const int64_t c0 = (k0 / kHadamard) * kHadamard;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v.x[c] = *reinterpret_cast<const lut_f32x4 *>(x + c0 + kLutSliceW * c + 4 * lane);
+            v.s[c] = *reinterpret_cast<const lut_f32x4 *>(signs + kLutSliceW * c + 4 * lane);
+        }
+        if (gain != nullptr) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                v.g[c] = *reinterpret_cast<const lut_f32x4 *>(gain + c0 + kLutSliceW * c + 4 * lane);
+        }
+    } else {
+        const int e = 4 * lane < kw ? 4 * lane : kw - 4;  // clamped; zeroed when stored
+        v.x[0] = *reinterpret_cast<const lut_f32x4 *>(x + k0 + e);
+        if (gain != nullptr) v.g[0] = *reinterpret_cast<const lut_f32x4 *>(gain + k0 + e);
+    }
+}
+
+// xs[0..256) = the slice of R (gain * x) (or of gain * x when signs == nullptr)
+__device__ __forceinline__ void slice_x_store(const SliceX &v, bool rotate, bool gained, int64_t k0, int kw, int lane,
+                                              float *xs)
+{
+    lut_f32x4 out;
+    if (rotate) {
+        const int part = static_cast<int>((k0 % kHadamard) / kLutSliceW);  // 0..3: this slice's quarter
+        const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
+        float z[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float t[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = (gained ? v.x[c][k] * v.g[c][k] : v.x[c][k]) * v.s[c][k];
+            z[k] = fmaf(sa, t[1], t[0]) + sb * fmaf(sa, t[3], t[2]);  // row `part` of H_4
+        }
+        lut_fwht256(z, lane);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = z[k] * (1.0f / 32.0f);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            out[k] = 4 * lane + k < kw ? (gained ? v.x[0][k] * v.g[0][k] : v.x[0][k]) : 0.0f;
+    }
+    *reinterpret_cast<lut_f32x4 *>(xs + 4 * lane) = out;
 }
 
 // T[slot][b] for b in [32 BQ, 32 BQ + 32): with v = floor(243 b / 256) the
@@ -260,23 +315,6 @@ __device__ __forceinline__ LutUnit lut_unit(const LutArgs &a, int64_t un)
 }
 
 typedef uint32_t lut_u32x4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t lut_u32x3 __attribute__((ext_vector_type(3), aligned(4)));
-
-// d[j] <- d[(j + rho) mod 7]: a three-stage rotate by 1, 2 and 4.  The
-// stages merge values with a lane mask; a select of array elements would
-// become a dynamically indexed (private-memory) array.
-__device__ __forceinline__ void lut_rotate(uint32_t (&d)[kBlockDwords], int rho)
-{
-#pragma unroll
-    for (int sh = 1; sh <= 4; sh <<= 1) {
-        const uint32_t m = (rho & sh) ? 0xffffffffu : 0u;
-        uint32_t t[kBlockDwords];
-#pragma unroll
-        for (int j = 0; j < kBlockDwords; ++j) t[j] = (d[(j + sh) % kBlockDwords] & m) | (d[j] & ~m);
-#pragma unroll
-        for (int j = 0; j < kBlockDwords; ++j) d[j] = t[j];
-    }
-}
 
 // U: units per wave.
 // One segment of a workgroup's work: units [u0, u1) of slice s, unit
@@ -297,50 +335,22 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     // ---- 1. the table's input is requested before the weights: vector
     // memory returns in order, so anything requested after the weights
     // would wait for all of them.
-    const int64_t c0 = (k0 / kHadamard) * kHadamard;  // 1024-chunk holding the slice
-    float xv16[kRotPerLane], sv16[kRotPerLane];        // [4 c + k]: element 256 c + lane + 64 k of the chunk
-    float gv16[kRotPerLane];                           // the gain at the same elements (when given)
-    if (wave == 0) {
-        if (a.signs != nullptr) {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j) {
-                const int e = kLutSliceW * (j >> 2) + lane + kWave * (j & 3);
-                xv16[j] = a.x[c0 + e];
-                sv16[j] = a.signs[e];
-            }
-            if (a.gain != nullptr) {
-#pragma unroll
-                for (int j = 0; j < kRotPerLane; ++j) gv16[j] = a.gain[c0 + kLutSliceW * (j >> 2) + lane + kWave * (j & 3)];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane / 4; ++j) {
-                const int e = lane + kWave * j;
-                xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];  // clamped; zeroed below
-            }
-            if (a.gain != nullptr) {
-#pragma unroll
-                for (int j = 0; j < kRotPerLane / 4; ++j) {
-                    const int e = lane + kWave * j;
-                    gv16[j] = a.gain[k0 + (e < kw ? e : kw - 1)];
-                }
-            }
-        }
-    }
+    SliceX xv;
+    if (wave == 0) slice_x_load(a.x, a.signs, a.gain, k0, kw, lane, xv);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. weights of this wave's first kLutEarly units; units up to
     // kLutDepth follow once x has arrived (after the first barrier) and the
     // rest one unit ahead of use during the lookups, so a wave never has more
-    // than kLutDepth units in flight and reaches each barrier without waiting
-    // for the memory queue.  Requests are served roughly in arrival order:
-    // with all kLutDepth units requested at entry (22 MB over the chip at
-    // 17408 x 5120 x 2), x's loads queued behind them and arrived about
-    // 0.7 us later; one unit per wave (7 MB) still keeps HBM busy meanwhile.
-    // A lane reads its 28-byte block with two wide loads (16 + 12 bytes;
-    // blocks are only dword-aligned, which gfx950 global loads accept) at a
-    // wave-uniform tile base.
-    uint32_t dat[U][kBlockDwords];
+    // than kLutDepth units in flight.  Requests are served roughly in arrival
+    // order: with every unit requested at entry, x's loads queued behind the
+    // weights and the table was built later (measured slower); one unit per
+    // wave still keeps HBM busy meanwhile.  A lane reads its 28-byte block
+    // with two wide loads (16 + 12 bytes; blocks are only dword-aligned,
+    // which gfx950 global loads accept) into registers 0..6; register 7 is a
+    // zero dword (position 7 of the block, whose columns are zeros).
+    uint32_t dat[U][kLutDwords];
+    uint32_t scb[U];
     auto unit_of = [&](int i) { return u0 + wave + static_cast<int64_t>(kLutWaves) * i; };
     auto issue = [&](int i) {
         const int64_t un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
@@ -353,7 +363,23 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(blk);
         const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(blk + 16);
         dat[i][0] = lo.x; dat[i][1] = lo.y; dat[i][2] = lo.z; dat[i][3] = lo.w;
-        dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z;
+        dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z; dat[i][7] = 0u;
+    };
+    // the scale (the block's upper half dword 6) is kept, then register r
+    // receives dword (r + rho) mod 8: rotations by 1, 2 and 4 merged with a
+    // lane mask (a select of array elements would become a dynamically
+    // indexed, private-memory array)
+    auto rotate = [&](int i) {
+        scb[i] = dat[i][6] >> 16;
+#pragma unroll
+        for (int sh = 1; sh <= 4; sh <<= 1) {
+            const uint32_t m = (rho & sh) ? 0xffffffffu : 0u;
+            uint32_t t[kLutDwords];
+#pragma unroll
+            for (int j = 0; j < kLutDwords; ++j) t[j] = (dat[i][(j + sh) & 7] & m) | (dat[i][j] & ~m);
+#pragma unroll
+            for (int j = 0; j < kLutDwords; ++j) dat[i][j] = t[j];
+        }
     };
 #pragma unroll
     for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
@@ -362,15 +388,13 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     // ---- per-lane lookup constants, formed while x is in flight (they
     // depend on neither x nor the table; formed after the table barrier they
     // held every wave of a SIMD for ~150 VALU operations while the LDS
-    // idled).  After the rotation, register dword j holds dword
-    // (j + rho) mod 7 of the block; the address of the lookup for its byte c
-    // is byte << 8 | slot << 2 with slot = 28 blk + 4 ((j + rho) mod 7) +
-    // ((c + sig) & 3); the four slot bytes of a dword are packed in one
-    // register (byte c) and v_perm_b32 inserts the data byte (selector:
+    // idled).  The address of the lookup of byte c of register r is
+    // byte << 8 | column << 2; the four column bytes of a register are packed
+    // in P[r] (byte c) and v_perm_b32 inserts the data byte (selector:
     // byte 0 <- P byte c, byte 1 <- data byte (c + sig) & 3, 0, 0).  The
-    // packed form is the dword's base slot replicated into four bytes plus
-    // the per-lane byte offsets (no carries: slot << 2 < 256).
-    uint32_t P[kBlockDwords];
+    // packed form is the register's base column replicated into four bytes
+    // plus the per-lane byte offsets (no carries: column << 2 < 256).
+    uint32_t P[kLutDwords];
     uint32_t S[4];
     uint32_t boff = 0;  // byte c: ((c + sig) & 3) << 2
 #pragma unroll
@@ -380,72 +404,40 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         boff |= (e << 2) << (8 * c);
     }
 #pragma unroll
-    for (int j = 0; j < kBlockDwords; ++j) {
-        const int q = j + rho < kBlockDwords ? j + rho : j + rho - kBlockDwords;
-        const uint32_t base = static_cast<uint32_t>(kBlockBytes * blk_l + 4 * q) << 2;
-        P[j] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;  // base in all four bytes
+    for (int r = 0; r < kLutDwords; ++r) {
+        const int q = (r + rho) & (kLutDwords - 1);
+        const uint32_t base = static_cast<uint32_t>(kLutColsPerBlock * blk_l + 4 * q) << 2;
+        P[r] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;  // base in all four bytes
     }
     // opaque from here on: otherwise the compiler recomputes them next to
     // their uses, after the table barrier
 #pragma unroll
-    for (int j = 0; j < kBlockDwords; ++j) asm volatile("" : "+v"(P[j]));
+    for (int r = 0; r < kLutDwords; ++r) asm volatile("" : "+v"(P[r]));
 #pragma unroll
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
-    if (wave == 0) {
-        if (a.gain != nullptr) {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j)
-                if (a.signs != nullptr || j < kRotPerLane / 4) xv16[j] *= gv16[j];
-        }
-        if (a.signs != nullptr) {
-            const int part = static_cast<int>((k0 - c0) / kLutSliceW);  // 0..3: this slice's quarter
-            const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
-            float z[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float t0 = xv16[k] * sv16[k], t1 = xv16[4 + k] * sv16[4 + k];
-                const float t2 = xv16[8 + k] * sv16[8 + k], t3 = xv16[12 + k] * sv16[12 + k];
-                z[k] = fmaf(sa, t1, t0) + sb * fmaf(sa, t3, t2);  // row `part` of H_4
-            }
-            lut_fwht256(z, lane);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) xs[lane + kWave * k] = z[k] * (1.0f / 32.0f);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane / 4; ++j) {
-                const int e = lane + kWave * j;
-                xs[e] = e < kw ? xv16[j] : 0.0f;
-            }
-        }
-    }
+    if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = kLutEarly; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);  // in flight during the build
     __builtin_amdgcn_sched_barrier(0);
-    // ---- 4. table: thread = (slot, 32-value range of the byte)
+    // ---- 4. table: thread = (column, 32-value range of the byte)
     {
         const int bq = tid >> 6;  // 0 .. kLutBuildRanges - 1
-        const int slot = tid & 63;
-        if (slot < kLutSlots) {
-            const int blk = slot / kBlockBytes, i = slot % kBlockBytes;
-            float xv[5];
+        const int col = tid & 63;
+        const int blk = col / kLutColsPerBlock, i = col % kLutColsPerBlock;
+        float xv[5];
 #pragma unroll
-            for (int n = 0; n < 5; ++n) {
-                const int j = kTritsPerByte * i + n;  // weight index in the block
-                xv[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
-            }
-            lut_build_dispatch<0>(bq, tab, slot, xv);
+        for (int n = 0; n < 5; ++n) {
+            const int j = kTritsPerByte * i + n;  // weight index in the block
+            xv[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
         }
+        lut_build_dispatch<0>(bq, tab, col, xv);
     }
-    // unit 0 (requested at entry, long arrived) is rotated before the
-    // barrier, so the lookups start right after it; its scale dword is kept
-    // from before the rotation
-    const uint32_t scale_w0 = dat[0][kBlockDwords - 1];
-    lut_rotate(dat[0], rho);
+    rotate(0);
     __syncthreads();
 
     // ---- 5. lookups, scale, 2-lane reduction, partial store
@@ -453,17 +445,16 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         if (i + kLutDepth < U) issue(i + kLutDepth);  // compile-time condition
+        if (i > 0) rotate(i);
         const bool unit_ok = unit_of(i) < u1;  // wave-uniform
         const int64_t un = unit_ok ? unit_of(i) : u1 - 1;
         const LutUnit u = lut_unit(a, un);
         const int r = u.grp * kLutRows + row_l;
         const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
-        const uint32_t scale_w = i == 0 ? scale_w0 : dat[i][kBlockDwords - 1];  // compile-time choice
-        const float scale = live ? half_bits_to_float(scale_w >> 16) : 0.0f;
-        if (i > 0) lut_rotate(dat[i], rho);
+        const float scale = live ? half_bits_to_float(scb[i]) : 0.0f;
         float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kBlockDwords; ++j) {
+        for (int j = 0; j < kLutDwords; ++j) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
@@ -531,7 +522,9 @@ static LutPlan lut_plan(int64_t per_slice, int64_t nslices)
     if (wgs > total / kLutWaves) wgs = total / kLutWaves;
     int64_t cs = wgs / nslices;
     if (cs < 1) cs = 1;
-    static const int kUs[] = {1, 2, 3, 4, 6, 8};
+    // at most 6 units per wave: a wave holds all of its units' weights in
+    // registers, and 8 would not fit beside the rotation's inputs
+    static const int kUs[] = {1, 2, 3, 4, 6};
     int U = 0;
     int64_t per_wg = 0;
     for (;;) {
@@ -543,7 +536,7 @@ static LutPlan lut_plan(int64_t per_slice, int64_t nslices)
                 break;
             }
         if (U != 0) break;
-        ++cs;  // parts above 64 units: more workgroups per slice
+        ++cs;  // parts above 48 units: more workgroups per slice
     }
     return LutPlan{U, static_cast<int>(per_wg), (per_slice + per_wg - 1) / per_wg};
 }
@@ -592,8 +585,178 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
         case 2: return lut_launch<2>(a, chunks, s);
         case 3: return lut_launch<3>(a, chunks, s);
         case 4: return lut_launch<4>(a, chunks, s);
-        case 6: return lut_launch<6>(a, chunks, s);
-        default: return lut_launch<8>(a, chunks, s);
+        default: return lut_launch<6>(a, chunks, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The pages' own decode ("A 27B model in 5.5 GB: Bonsai ternary on Ferrox,
+// locally", "What Ferrox does with it": eight lanes share one 128-weight
+// block, each lane owns whole bytes, every block is read once, and each trit
+// is peeled on the float pipeline as floor(3^(n+1) u) - 3 floor(3^n u),
+// u = byte / 256), on the same tiled layout, K-slices, rotation prologue and
+// split-K partials as the lookup kernel above, so the two decodes differ only
+// in how a block's dot product is formed.
+//
+// Lane l: b = l / 32 is the block of the slice, r = (l / 8) mod 4 a row of
+// the step's four, j = l mod 8 the dword of the block the lane owns (bytes
+// 4j .. 4j + 3, i.e. weights 20j .. 20j + 19; dword 6 holds the last two
+// trit bytes and the scale; lane 7 owns nothing).  A step covers rows
+// 4 st .. 4 st + 3 of a tile, i.e. its blocks 8 st .. 8 st + 7: one dword
+// load per lane reads 224 contiguous bytes.  A lane keeps the 20 rotated
+// activations of its bytes in registers for the whole kernel (zeros for
+// weights past the block and for lane 7), so every step is
+//   sum_n (digit_n - 1) x_n = sum_n digit_n x_n - sum_n x_n
+// over its bytes, then a sum over the eight lanes (DPP), times the scale
+// (lane 6), plus the other block of the row (lane l ^ 32).  Cost on gfx950:
+// about 20 VALU operations per byte (byte to float, five products and
+// floors, four digit differences, five FMAs), i.e. 4 per weight, against
+// the lookup kernel's 2 per five weights.
+// ---------------------------------------------------------------------------
+constexpr int kPeelSteps = kLutRows / 4;  // 8 steps of 4 rows x 2 blocks per tile
+
+template <int U>
+__device__ __forceinline__ void peel_segment(const LutArgs &a, float *xs, int s, int64_t u0, int64_t u1)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int64_t k0 = static_cast<int64_t>(s) * kLutSliceW;
+    const int kw = static_cast<int>(a.k - k0 < kLutSliceW ? a.k - k0 : kLutSliceW);
+    const int nblk = kw / kBlockWeights;
+    const int hb = lane >> 5;        // block of the slice
+    const int rr = (lane >> 3) & 3;  // row of the step
+    const int jd = lane & 7;         // owned dword (7: none)
+    const int jl = jd < kBlockDwords ? jd : kBlockDwords - 1;  // dword actually loaded (lane 7 repeats 6)
+
+    // ---- 1. x for the slice (wave 0), requested before any weights
+    SliceX xv;
+    if (wave == 0) slice_x_load(a.x, a.signs, a.gain, k0, kw, lane, xv);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. weights: one dword per lane and step, two units in flight
+    uint32_t dat[2][kPeelSteps];
+    auto unit_of = [&](int i) { return u0 + wave + static_cast<int64_t>(kLutWaves) * i; };
+    auto issue = [&](int i) {
+        const int64_t un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
+        const LutUnit u = lut_unit(a, un);
+        const uint8_t *tile = (u.mat ? a.w1 : a.w0) +
+                              (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
+                               static_cast<uint32_t>(u.grp)) * static_cast<uint32_t>(kTileBytes);
+#pragma unroll
+        for (int st = 0; st < kPeelSteps; ++st)
+            dat[i & 1][st] = *reinterpret_cast<const uint32_t *>(
+                tile + (2 * (4 * st + rr) + hb) * kBlockBytes + 4 * jl);
+    };
+    issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. the slice's x (times the gain), rotated
+    if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
+    __syncthreads();
+
+    // ---- 4. this lane's 20 activations (zero past the block, for lane 7
+    // and for a block the slice does not have) and their sum
+    float xr[20];
+    float xsum = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 20; ++n) {
+        const int w = 20 * jd + n;  // weight index in the block
+        xr[n] = (hb < nblk && jd < kBlockDwords && w < kBlockWeights) ? xs[kBlockWeights * hb + (w < kBlockWeights ? w : 0)]
+                                                                     : 0.0f;
+        xsum += xr[n];
+    }
+
+    // ---- 5. per unit: 8 steps of peel, 8-lane sum, scale, the row's two blocks
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        if (i + 1 < U) issue(i + 1);  // compile-time condition
+        const bool unit_ok = unit_of(i) < u1;  // wave-uniform
+        const int64_t un = unit_ok ? unit_of(i) : u1 - 1;
+        const LutUnit u = lut_unit(a, un);
+#pragma unroll
+        for (int st = 0; st < kPeelSteps; ++st) {
+            const uint32_t d = dat[i & 1][st];
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const Peel5 pd = peel5(static_cast<float>((d >> (8 * c)) & 0xffu));
+                acc = fmaf(pd.d0, xr[5 * c + 0], acc);
+                acc = fmaf(pd.d1, xr[5 * c + 1], acc);
+                acc = fmaf(pd.d2, xr[5 * c + 2], acc);
+                acc = fmaf(pd.d3, xr[5 * c + 3], acc);
+                acc = fmaf(pd.d4, xr[5 * c + 4], acc);
+            }
+            float t = acc - xsum;
+            // sum over the 8 lanes of the block: mirror within 8, then quad swaps
+            int it = __builtin_bit_cast(int, t);
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(it, it, 0x141, 0xF, 0xF, false));
+            it = __builtin_bit_cast(int, t);
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(it, it, 0xB1, 0xF, 0xF, false));
+            it = __builtin_bit_cast(int, t);
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(it, it, 0x4E, 0xF, 0xF, false));
+            const int r = u.grp * kLutRows + 4 * st + rr;
+            const bool live = unit_ok && r < a.n && hb < nblk;
+            float v = live ? t * half_bits_to_float(d >> 16) : 0.0f;  // lane 6 holds the scale
+            // + the row's other block (lane ^ 32)
+            const uint32_t uv = __builtin_bit_cast(uint32_t, v);
+            const auto sw = __builtin_amdgcn_permlane32_swap(uv, uv, false, false);
+            const uint32_t s0 = sw[0], s1 = sw[1];
+            v = __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+            if (jd == kBlockDwords - 1 && hb == 0 && unit_ok && r < a.n)
+                a.part[(static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r] = v;
+        }
+    }
+}
+
+template <int U>
+__global__ void __launch_bounds__(kLutThreads) k_matvec_peel(LutArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float xs[kLutSliceW];
+    const int per_slice = a.nmat * static_cast<int>(a.groups);
+    const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
+    const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
+    if (u0 < u1) peel_segment<U>(a, xs, static_cast<int>(blockIdx.y), u0, u1);
+}
+
+template <int U>
+static hipError_t peel_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
+{
+    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.nslices));
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(k_matvec_peel<U>, grid, dim3(kLutThreads), 0u, st, pe.start, pe.stop, 0u, a);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(k_matvec_peel<U>, grid, dim3(kLutThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_matvec_peel(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k, const float *x,
+                              const float *signs, const float *gain, float *part, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    LutArgs a{};
+    a.w0 = w0;
+    a.w1 = w1;
+    a.n = n;
+    a.k = k;
+    a.nmat = nmat;
+    a.nslices = static_cast<int>(lut_nslices(k));
+    a.groups = (n + kLutRows - 1) / kLutRows;
+    a.x = x;
+    a.signs = signs;
+    a.gain = gain;
+    a.part = part;
+    const LutPlan pl = lut_plan(static_cast<int64_t>(nmat) * a.groups, a.nslices);
+    a.per_wg = pl.per_wg;
+    switch (pl.U) {
+        case 1: return peel_launch<1>(a, pl.chunks, s);
+        case 2: return peel_launch<2>(a, pl.chunks, s);
+        case 3: return peel_launch<3>(a, pl.chunks, s);
+        case 4: return peel_launch<4>(a, pl.chunks, s);
+        default: return peel_launch<6>(a, pl.chunks, s);
     }
 }
 
@@ -697,38 +860,11 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     const int rho = pq2_rho(lane), sig = pq2_sig(lane);
 
     // ---- 1. x for the slice's rotation, requested before any weights
-    const int64_t c0 = (k0 / kHadamard) * kHadamard;
-    float xv16[kRotPerLane], sv16[kRotPerLane], gv16[kRotPerLane];
-    if (wave == 0) {
-        if (a.signs != nullptr) {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j) {
-                const int e = kLutSliceW * (j >> 2) + lane + kWave * (j & 3);
-                xv16[j] = a.x[c0 + e];
-                sv16[j] = a.signs[e];
-            }
-            if (a.gain != nullptr) {
-#pragma unroll
-                for (int j = 0; j < kRotPerLane; ++j) gv16[j] = a.gain[c0 + kLutSliceW * (j >> 2) + lane + kWave * (j & 3)];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane / 4; ++j) {
-                const int e = lane + kWave * j;
-                xv16[j] = a.x[k0 + (e < kw ? e : kw - 1)];
-            }
-            if (a.gain != nullptr) {
-#pragma unroll
-                for (int j = 0; j < kRotPerLane / 4; ++j) {
-                    const int e = lane + kWave * j;
-                    gv16[j] = a.gain[k0 + (e < kw ? e : kw - 1)];
-                }
-            }
-        }
-    }
+    SliceX xv;
+    if (wave == 0) slice_x_load(a.x, a.signs, a.gain, k0, kw, lane, xv);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 2. weights: one unit before x arrives, up to kLutDepth after
+    // ---- 2. weights: kLutEarly units before x arrives, up to kLutDepth after
     uint32_t dat[U][kPq2Dwords];
     uint32_t scw[U];
     auto unit_of = [&](int i) { return u0 + wave + kLutWaves * i; };
@@ -772,33 +908,7 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. the slice's x (times the gain), rotated
-    if (wave == 0) {
-        if (a.gain != nullptr) {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane; ++j)
-                if (a.signs != nullptr || j < kRotPerLane / 4) xv16[j] *= gv16[j];
-        }
-        if (a.signs != nullptr) {
-            const int part = static_cast<int>((k0 - c0) / kLutSliceW);
-            const float sa = (part & 1) ? -1.0f : 1.0f, sb = (part & 2) ? -1.0f : 1.0f;
-            float z[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const float t0 = xv16[kk] * sv16[kk], t1 = xv16[4 + kk] * sv16[4 + kk];
-                const float t2 = xv16[8 + kk] * sv16[8 + kk], t3 = xv16[12 + kk] * sv16[12 + kk];
-                z[kk] = fmaf(sa, t1, t0) + sb * fmaf(sa, t3, t2);
-            }
-            lut_fwht256(z, lane);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) xs[lane + kWave * kk] = z[kk] * (1.0f / 32.0f);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kRotPerLane / 4; ++j) {
-                const int e = lane + kWave * j;
-                xs[e] = e < kw ? xv16[j] : 0.0f;
-            }
-        }
-    }
+    if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -902,8 +1012,7 @@ hipError_t launch_pq2_matvec(const uint8_t *w0, const uint8_t *w1, int nmat, int
         case 2: return pq2_launch<2>(a, pl.chunks, s);
         case 3: return pq2_launch<3>(a, pl.chunks, s);
         case 4: return pq2_launch<4>(a, pl.chunks, s);
-        case 6: return pq2_launch<6>(a, pl.chunks, s);
-        default: return pq2_launch<8>(a, pl.chunks, s);
+        default: return pq2_launch<6>(a, pl.chunks, s);
     }
 }
 

@@ -43,22 +43,6 @@ hipError_t launch_unrotate_rows(const float *table, int64_t n_table, int64_t d, 
                                 int64_t n_rows, const float *signs, float *out, hipStream_t s);
 
 // ---- decode (m = 1) --------------------------------------------------------
-// Partial sums of the float-peel matvec over a "virtual" matrix whose rows
-// [0, n0) come from w0 and [n0, n0 + n1) from w1 (n1 = 0: one matrix).
-// part[seg][row], seg = 1024-wide K segment; x rotated per segment when
-// signs != nullptr.
-size_t matvec_part_floats(int64_t rows, int64_t k);
-hipError_t launch_matvec_part(const uint8_t *w0, int64_t n0, const uint8_t *w1, int64_t n1,
-                              int64_t k, const float *x, const float *signs, float *part,
-                              hipStream_t s);
-// y[r] = residual[r] + sum_seg part[seg][r]
-hipError_t launch_reduce_rows(const float *part, int64_t n, int64_t nseg, const float *residual,
-                              float *y, hipStream_t s);
-// g, u from the two halves of the virtual matrix; optionally h = silu(a g) (a u)
-// with a the RMS scale of x_rms (x_rms == nullptr: a = 1).
-hipError_t launch_reduce_gate_up(const float *part, int64_t f, int64_t nseg, float *g, float *u,
-                                 float *h, const float *x_rms, int64_t d, float rms_eps,
-                                 hipStream_t s);
 hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, hipStream_t s);
 
 // Lookup-table decode matvec over tiled weights, split over 256-wide
@@ -79,6 +63,10 @@ hipError_t launch_w2a8_sum(const float *part, int64_t n, int64_t k, const float 
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
                              const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
+// The same partials with every trit peeled on the float pipeline (eight
+// lanes per block), over the same tiled layout and slices.
+hipError_t launch_matvec_peel(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
+                              const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
 // The same lookup matvec over a PQ2_0 tiled matrix (one matrix): part as
 // above, summed by launch_lut_sum_rows.
 hipError_t launch_pq2_matvec(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k, const float *x,
