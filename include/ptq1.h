@@ -248,6 +248,25 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
  * 1024), UNSUPPORTED (m). */
 ptq1_status ptq1_ffn_workspace_offsets(int64_t m, int64_t d, int64_t f, int64_t *offsets);
 
+/* ptq1_ffn_block for callers that cannot allocate memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments, kernels, results and errors,
+ * without ws / ws_bytes.  Its scratch is a buffer of 8 MiB (8388608 bytes)
+ * that the library holds statically on every GPU it runs on, until the
+ * process ends; a call whose ptq1_ffn_workspace_bytes(m, d, f) exceeds it is
+ * refused with PTQ1_ERR_UNSUPPORTED before anything is enqueued (m = 1 up to
+ * d = 8192, f = 28672; m <= 8 at d = 5120, f = 17408).  Nothing in it needs
+ * to start at zero: every call writes the scratch it reads.  All calls on
+ * one GPU share that buffer, so two calls that may overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race:
+ * order them on one stream, or use ptq1_ffn_block with a workspace each.
+ * The stage offsets of ptq1_ffn_workspace_offsets hold for this buffer too,
+ * but it is not reachable from outside the library. */
+ptq1_status ptq1_ffn_block_noalloc(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                                   const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                                   const float *signs1024, float rms_eps, const float *rms_gain,
+                                   hipStream_t stream);
+
 /* ---- PQ2_0: the two-bit ternary format ("Why I Am Building Another
  * Inference Engine", Level 2: two bits per weight and a 16-bit scale for every
  * 128 weights, 2.125 bits per weight).  A block is 32 code bytes, weight

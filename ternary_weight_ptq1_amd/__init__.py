@@ -78,6 +78,7 @@ _SIGS = {
     "ptq1_matvec_w2a8": ([p, i64, i64, p, p, p, p, sz, p], C.c_int),
     "pq2_ffn_block": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p, sz, p], C.c_int),
     "ptq1_ffn_workspace_offsets": ([i64, i64, i64, p], C.c_int),
+    "ptq1_ffn_block_noalloc": ([p, p, i64, i64, i64, p, p, p, p, C.c_float, p, p], C.c_int),
     "pq2_ffn_workspace_offsets": ([i64, i64, i64, p], C.c_int),
     "ptq1_profile_arm": ([C.c_char_p, p, p, C.c_int32], C.c_int),
     "ptq1_profile_count": ([C.c_char_p], C.c_int32),
@@ -380,6 +381,30 @@ def ptq1_ffn_block(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_
     _check(fn, getattr(lib(), fn)(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                   _ptr(signs1024), float(rms_eps), _ptr(rms_gain) if rms_gain is not None else None,
                                   _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def ptq1_ffn_block_noalloc(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                           signs1024: torch.Tensor, d: int, f: int, rms_eps: float = 0.0,
+                           out: torch.Tensor | None = None, stream=None,
+                           rms_gain: torch.Tensor | None = None) -> torch.Tensor:
+    """ptq1_ffn_block on the library's own static scratch buffer (no workspace argument; calls on one GPU
+    must not overlap).  `out` must be given by a caller that cannot allocate."""
+    _dev(x, "x", torch.float32)
+    dv = x.device
+    m = _rows_of(x, d)
+    _mat(w_gate, "w_gate", ptq1_tiled_bytes(f, d), dv)
+    _mat(w_up, "w_up", ptq1_tiled_bytes(f, d), dv)
+    _mat(w_down, "w_down", ptq1_tiled_bytes(d, f), dv)
+    _signs(signs1024, dv)
+    _opt(rms_gain, "rms_gain", torch.float32, numel=d, device=dv)
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "x_out", torch.float32, numel=m * d, device=dv)
+    _check("ptq1_ffn_block_noalloc",
+           lib().ptq1_ffn_block_noalloc(_ptr(x), _ptr(out), m, d, f, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                        _ptr(signs1024), float(rms_eps),
+                                        _ptr(rms_gain) if rms_gain is not None else None, _stream(stream)))
     return out
 
 

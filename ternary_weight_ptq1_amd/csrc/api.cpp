@@ -631,10 +631,10 @@ size_t ptq1_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f)
     return ffn_layout(m, d, f).total;
 }
 
-ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
-                           const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
-                           const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
-                           size_t ws_bytes, hipStream_t stream)
+static ptq1_status ffn_block_impl(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                                  const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                                  const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
+                                  size_t ws_bytes, hipStream_t stream, bool scratch)
 {
     int64_t wgb, wub, wdb, md, xb, ob;
     if (m < 0) return fail(PTQ1_ERR_SHAPE, "m = %lld is negative", (long long)m);
@@ -657,7 +657,17 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
         return fail(PTQ1_ERR_ALIAS, "x_out overlaps a weight matrix");
     if (f == 0) return fail(PTQ1_ERR_SHAPE, "f = 0");
     const FfnWs L = ffn_layout(m, d, f);
-    PTQ1_TRY(check_ws(ws, ws_bytes, L.total, "ptq1_ffn_block"));
+    if (scratch) {
+        if (L.total > ptq1::kScratchBytes)
+            return fail(PTQ1_ERR_UNSUPPORTED,
+                        "ptq1_ffn_block_noalloc: m = %lld, d = %lld, f = %lld needs %zu bytes of scratch, more than "
+                        "the library's %zu (use ptq1_ffn_block with a workspace)",
+                        (long long)m, (long long)d, (long long)f, L.total, ptq1::kScratchBytes);
+        const hipError_t es = ptq1::scratch_device_ptr(&ws);
+        if (es != hipSuccess) return hip_status(es, "ptq1_ffn_block_noalloc: scratch address");
+        ws_bytes = ptq1::kScratchBytes;
+    }
+    PTQ1_TRY(check_ws(ws, ws_bytes, L.total, scratch ? "ptq1_ffn_block_noalloc" : "ptq1_ffn_block"));
     if (overlaps(ws, (int64_t)L.total, x, xb) || overlaps(ws, (int64_t)L.total, x_out, ob))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps x or x_out");
     if (rms_gain != nullptr && overlaps(ws, (int64_t)L.total, rms_gain, gb))
@@ -701,7 +711,24 @@ ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, i
                 return ptq1::launch_gemm(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);
             });
     }
-    return hip_status(e, "ptq1_ffn_block");
+    return hip_status(e, scratch ? "ptq1_ffn_block_noalloc" : "ptq1_ffn_block");
+}
+
+ptq1_status ptq1_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                           const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                           const float *signs1024, float rms_eps, const float *rms_gain, void *ws,
+                           size_t ws_bytes, hipStream_t stream)
+{
+    return ffn_block_impl(x, x_out, m, d, f, w_gate, w_up, w_down, signs1024, rms_eps, rms_gain, ws, ws_bytes, stream,
+                          false);
+}
+
+ptq1_status ptq1_ffn_block_noalloc(const float *x, float *x_out, int64_t m, int64_t d, int64_t f,
+                                   const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                                   const float *signs1024, float rms_eps, const float *rms_gain, hipStream_t stream)
+{
+    return ffn_block_impl(x, x_out, m, d, f, w_gate, w_up, w_down, signs1024, rms_eps, rms_gain, nullptr, 0, stream,
+                          true);
 }
 
 namespace {

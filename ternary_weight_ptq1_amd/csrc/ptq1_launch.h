@@ -22,6 +22,12 @@ ProfEvents &prof_events();  // per host thread
 // per device (bit d of done_mask; calls that race set the same value).
 hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<uint64_t> &done_mask);
 
+// The statically allocated per-device scratch buffer (scratch.hip): its
+// device address on the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t{8} << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_device_ptr(void **ptr);
+
 hipError_t launch_pack(const int8_t *trits, const uint16_t *scales, int64_t n, int64_t k,
                        uint8_t *blocks, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *blocks, int64_t n, int64_t k, float *w, hipStream_t s);
