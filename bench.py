@@ -24,10 +24,13 @@ profiles/lut_matvec_gate_up_decode_27b_traffic.md, or null when that
 kernel's source changed after the counters were taken.
 
 Also reported (breakdown): the down-projection lookup kernel inside the
-same steps, cold gate+up and down calls alone, the hot 1024 x 1024 matvec,
-the prefill GEMM at M = 128 / 256 / 512 (TFLOP/s, fraction of the bf16
-MFMA peak), and the 64-layer FFN stack at batch 1 and 8 (layers/s); the
-fp64 oracle timed on the host's cores on a bounded sample (cpu_baseline).
+same steps, cold gate+up and down calls alone, the pages' float-peel decode
+on the same matrices, the hot 1024 x 1024 matvec, the prefill GEMM at
+M = 128 / 256 / 512 (TFLOP/s, fraction of the bf16 MFMA peak), and the
+64-layer FFN stack at batch 1 and 8 (layers/s, and the relative L2 of its
+output against the oracle).  cpu_baseline: the fp64 oracle timed on the
+host's cores on bounded samples of every configuration, in the GPU's units.
+receipt: GPU, ROCm, clocks, host CPU and load average.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
                     [--copy-calibration]
@@ -200,6 +203,7 @@ def main() -> int:
         return 2
     P.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    rec = receipt(torch, dev)
     stream = torch.cuda.current_stream()
     if args.gemm_only > 0:
         return gemm_only(args, torch, synth, sdev, P, dev)
@@ -282,6 +286,7 @@ def main() -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clk_end = clocks()
     ms_step = e0.elapsed_time(e1) / args.steps
     gbs = STEP_BYTES / (ms_step * 1e-3) / 1e9
     del graphs
@@ -338,6 +343,27 @@ def main() -> int:
         ms_dn = timed(down, 200, 20)
         breakdown["down_call_cold"] = {"us": ms_dn * 1e3, "GB/s": DOWN_BYTES / (ms_dn * 1e-3) / 1e9,
                                        "bytes": DOWN_BYTES}
+
+        # the pages' own decode (float peel, eight lanes per block, tiled layout) on the same
+        # cold matrices: the down projection and one 17408 x 5120 (gate-shaped) matrix
+        peel = {}
+        for tag, (wi, n_, k_, xin, yb) in {"down_17408_to_5120": (2, D, F, h, y),
+                                           "gate_5120_to_17408": (0, F, D, xg, g_buf)}.items():
+            wsp = torch.zeros(P.workspace_bytes("matvec", n_, k_), dtype=torch.uint8, device=dev)
+            timed(lambda i: P.ptq1_matvec_float_peel(sets[i % WEIGHT_SETS][wi], n_, k_, xin, signs, out=yb, ws=wsp),
+                  5, 0)
+            tp = P.KernelTimer("peel_matvec", 64)
+            with tp:
+                timed(lambda i: P.ptq1_matvec_float_peel(sets[i % WEIGHT_SETS][wi], n_, k_, xin, signs, out=yb,
+                                                         ws=wsp), 64, 0)
+            dp = tp.durations_ms()
+            tp.close()
+            us_p = 1e3 * sum(dp) / len(dp)
+            pb = packed(n_, k_) + 4 * k_
+            peel[tag] = {"us_kernel": us_p, "GB/s": pb / (us_p * 1e-6) / 1e9, "frac_hbm": pb / (us_p * 1e-6) / 8e12}
+            del wsp
+        peel["lookup_kernel_down_us_in_step"] = us_dn
+        breakdown["float_peel_decode"] = peel
 
         def unrot(i):
             P.hadamard_unrotate_rows(table, signs, ids=ids[i % 4096:i % 4096 + 1], out=emb)
@@ -500,6 +526,7 @@ def main() -> int:
         torch.cuda.empty_cache()
         stack = [weight_set(4, L) for L in range(LAYERS)]
         stk = {}
+        stack_out = {}
         for m in (1, 8):
             xs = torch.from_numpy(synth.activations(4, m, D)).to(dev)
             wss = torch.zeros(P.workspace_bytes("ffn", m, D, F), dtype=torch.uint8, device=dev)
@@ -518,12 +545,19 @@ def main() -> int:
                 run_stack(0)
             torch.cuda.synchronize()
             ms = timed(lambda i: g.replay(), 5, 1)
-            del g
             stk[f"M{m}"] = {"ms_per_stack": ms, "us_per_layer": ms * 1e3 / LAYERS,
                             "layers_per_s": LAYERS / (ms * 1e-3),
                             "weight_GB/s": LAYERS * LAYER_WEIGHT_BYTES / (ms * 1e-3) / 1e9,
                             "us_per_layer_eager": ms_eager * 1e3 / LAYERS,
                             "finite": bool(torch.isfinite(xa).all().item())}
+            # one fresh pass of the 64 layers from the seeded input, kept for
+            # the end-to-end comparison with the oracle (token 0; at M = 8 it
+            # has the same input row as the M = 1 stack)
+            xa.copy_(xs)
+            run_stack(0)
+            torch.cuda.synchronize()
+            stack_out[f"M{m}"] = xa[0].cpu().numpy().copy()
+            del g, wss, xa
         breakdown["ffn_stack_64"] = stk
         del stack
 
@@ -539,7 +573,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu:
         log("bench: oracle CPU baseline")
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(torch, dev, None if args.quick else stack_out)
+        if "stack_64_vs_oracle" in cpu:
+            breakdown.setdefault("ffn_stack_64", {})["rel_l2_vs_oracle"] = cpu["stack_64_vs_oracle"]
+    load_end = os.getloadavg()
 
     line = {
         "metric": "decode matvec GB/s (27B-shaped FFN block, batch 1, cold weights)",
@@ -567,25 +604,90 @@ def main() -> int:
                      "bytes_per_launch": LUT_GATE_UP_BYTES, "us_per_launch": round(us_gu, 3),
                      "launches_timed": len(d_gu), "source_sha256_16": lut_source_hash()},
         "cpu_baseline": cpu,
+        "receipt": dict(rec, loadavg_end=[round(v, 2) for v in load_end], clocks_after_timed_work=clk_end),
         "breakdown": breakdown,
     }
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline():
-    """The fp64 oracle (as it stands) on this host's cores: one full-shape
-    FFN block at batch 1 (x[5120], 17408 x 5120 gate/up, 5120 x 17408 down),
-    repeated for about 10 s; same algorithmic bytes as the GPU step."""
+def clocks():
+    """Current GPU clocks as rocm-smi reports them (an idle GPU reports its idle clock)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30).stdout
+        card = next(iter(json.loads(out[out.index("{"):]).values()))
+        return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower()}
+    except Exception as e:  # the tool is optional on a box
+        return f"unavailable ({type(e).__name__})"
+
+
+def receipt(torch, dev):
+    """Where the numbers were taken: GPU, ROCm, clocks, host CPU and load."""
+    import subprocess
+
+    props = torch.cuda.get_device_properties(dev)
+    r = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+         "hbm_GiB": round(props.total_memory / 2 ** 30, 1), "hip_runtime": torch.version.hip,
+         "torch": torch.__version__}
+    try:
+        r["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        r["rocm"] = None
+    r["clocks_at_start"] = clocks()
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    r["host_cpu"] = model
+    r["host_logical_cpus"] = os.cpu_count()
+    r["host_cpus_usable"] = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    r["loadavg_start"] = [round(v, 2) for v in os.getloadavg()]
+    return r
+
+
+def cpu_baseline(torch, dev, stack_out=None):
+    """The fp64 oracle (as it stands, never tuned for this) on this host's
+    cores, timed on bounded samples of each configuration in the GPU's units:
+    the decode step (the headline, GB/s), the 1024 x 1024 matvec (GB/s), the
+    prefill GEMM at M = 128 / 256 / 512 on 64 sampled output columns
+    (GFLOP/s of the sample, rotation included), and the 27B FFN layer at M = 1
+    and M = 8 (layers/s).  With stack_out (the GPU's 64-layer outputs for
+    token 0 at M = 1 and M = 8, which share their input row) the oracle also
+    runs the whole 64-layer stack once and reports the end-to-end relative L2
+    of each (reported, not gated).  Weights come from the seeded generator's
+    device fill (bit-exact with its host version), copied to the host and
+    packed by the oracle."""
+    import concurrent.futures as cf
+
     import oracle
     import synth
+    import synth.device as sdev
 
+    pool = cf.ThreadPoolExecutor(3)
+
+    def host_pack(seed, tr, sc, n, k, rows=None):
+        t = sdev.trits(seed, tr, rows or n, k, device=dev).cpu().numpy()
+        sv = sdev.scales(seed, sc, rows or n, k // 128, device=dev).cpu().numpy().view(np.uint16)
+        return oracle.pack(t, sv)
+
+    def layer_mats(seed, layer):
+        ls = synth.layer_stream
+        jobs = [pool.submit(host_pack, seed, ls(tr, layer), ls(sc, layer), n, k)
+                for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
+                                     (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
+                                     (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F))]
+        return [j.result() for j in jobs]
+
+    out = {"kind": "oracle", "cores": oracle.threads()}
+    # ---- headline: the decode step (1 embedding row + 1 FFN block, batch 1)
     seed = 1
-    mats = []
-    for tr, sc, n, k in ((synth.S_GATE_TRITS, synth.S_GATE_SCALES, F, D),
-                         (synth.S_UP_TRITS, synth.S_UP_SCALES, F, D),
-                         (synth.S_DOWN_TRITS, synth.S_DOWN_SCALES, D, F)):
-        mats.append(oracle.pack(synth.trits(seed, tr, n, k), synth.scales(seed, sc, n, k // 128)))
+    mats = layer_mats(seed, 0)
     s = synth.signs(seed)
     row = synth.table_rows(2, synth.S_TABLE, np.array([7]), D)
     reps, t0 = 0, time.perf_counter()
@@ -594,11 +696,60 @@ def cpu_baseline():
         oracle.ffn_block(e, mats[0], mats[1], mats[2], s, D, F, 1e-6)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 50:
+        if el > 8.0 or reps >= 50:
             break
-    return {"value": round(STEP_BYTES * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{reps} decode steps (1 embedding row + 1 full 5120/17408 FFN block, fp64) in {el:.1f} s"}
+    out.update({"value": round(STEP_BYTES * reps / el / 1e9, 4), "unit": "GB/s",
+                "sample": f"{reps} decode steps (1 embedding row + 1 full 5120/17408 FFN block, fp64) in "
+                          f"{el:.1f} s"})
+    cfg = {}
+    # ---- 1024 x 1024 matvec with its rotation
+    b0 = host_pack(0, synth.S_W_TRITS, synth.S_W_SCALES, 1024, 1024)
+    x0, s0 = synth.activations(0, 1, 1024)[0], synth.signs(0)
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        oracle.matvec(b0, 1024, 1024, oracle.rotate(x0, s0))
+        reps += 1
+    el = time.perf_counter() - t0
+    cfg["matvec_1024"] = {"GB/s": round((packed(1024, 1024) + 8 * 1024) * reps / el / 1e9, 4), "calls": reps}
+    # ---- prefill GEMM on 64 sampled output columns (rows 0..63 of the 17408 x 5120 matrix)
+    bq = host_pack(3, synth.S_W_TRITS, synth.S_W_SCALES, F, D, rows=64)
+    s3 = synth.signs(1)
+    for m in (128, 256, 512):
+        xm = synth.activations(3, m, D)
+        t0 = time.perf_counter()
+        oracle.gemm(bq, 64, D, oracle.rotate(xm, s3))
+        el = time.perf_counter() - t0
+        cfg[f"gemm_M{m}"] = {"GFLOP/s": round(2.0 * m * 64 * D / el / 1e9, 4),
+                             "sample": f"{m} x 5120 rotated, times 64 of the 17408 weight rows, {el:.2f} s"}
+    # ---- FFN layer at M = 8 (one layer), and the 64-layer stack at M = 1
+    s1 = synth.signs(1)
+    m0 = layer_mats(4, 0)
+    x8 = synth.activations(4, 8, D)
+    t0 = time.perf_counter()
+    oracle.ffn_block(x8, m0[0], m0[1], m0[2], s1, D, F, 1e-6)
+    el = time.perf_counter() - t0
+    cfg["ffn_layer_M8"] = {"layers/s": round(1.0 / el, 4), "sample": f"layer 0 at M = 8 in {el:.2f} s"}
+    xs = synth.activations(4, 1, D)[0].astype(np.float64)
+    layers = LAYERS if stack_out else 2
+    t_comp = 0.0
+    for L in range(layers):
+        if L % 16 == 0:
+            log(f"bench: oracle stack, layer {L} of {layers}")
+        mL = m0 if L == 0 else layer_mats(4, L)
+        t0 = time.perf_counter()
+        xs = oracle.ffn_block(xs, mL[0], mL[1], mL[2], s1, D, F, 1e-6)[0]
+        t_comp += time.perf_counter() - t0
+    cfg["ffn_layer_M1"] = {"layers/s": round(layers / t_comp, 4),
+                           "sample": f"{layers} layers at M = 1 in {t_comp:.2f} s of oracle time"}
+    out["configs"] = cfg
+    if stack_out:
+        ref = np.linalg.norm(xs)
+        out["stack_64_vs_oracle"] = {
+            k: float(np.linalg.norm(np.asarray(v, dtype=np.float64) - xs) / ref) for k, v in stack_out.items()}
+        out["stack_64_vs_oracle"]["note"] = ("relative L2 of token 0 after 64 layers against the fp64 oracle "
+                                             "(M1: fp32 lookup path; M8: bf16 MFMA path); reported, not gated")
+    pool.shutdown()
+    return out
 
 
 if __name__ == "__main__":
