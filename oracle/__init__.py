@@ -29,15 +29,23 @@ BLOCK_BYTES = 28
 HAD = 1024
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no fast-math, fp64, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+_LIB_SAN = os.path.join(_HERE, "libptq1_oracle_asan.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, fp64, OpenMP); with
+    sanitize, a second copy instrumented by AddressSanitizer and
+    UndefinedBehaviorSanitizer (loaded when PTQ1_ORACLE_LIB names it)."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
-             "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+            ["gcc", "-O1" if sanitize else "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off", "-Wall", "-Wextra", *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, _SRC,
+             "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -46,9 +54,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = C.CDLL(_LIB)
+        path = os.environ.get("PTQ1_ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = C.CDLL(path)
         i64, p = C.c_int64, C.c_void_p
         L.orc_f16_to_f64.argtypes = [C.c_uint16]
         L.orc_f16_to_f64.restype = C.c_double

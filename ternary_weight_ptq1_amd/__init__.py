@@ -16,7 +16,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libptq1.so")
+# PTQ1_LIB may name another build of the same library (the sanitizer build
+# of build.py --sanitize, for host-only test runs)
+LIB_PATH = os.environ.get("PTQ1_LIB", os.path.join(_HERE, "libptq1.so"))
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "ptq1.h")
 
 BLOCK_WEIGHTS = 128

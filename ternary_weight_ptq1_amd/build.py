@@ -65,5 +65,40 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(ROOT, "_build", "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libptq1.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The same library with its host code (argument validation, workspace
+    layout, launch planning: api.cpp) compiled by g++ under AddressSanitizer
+    and UndefinedBehaviorSanitizer, linked with the GPU objects of build().
+    Loaded by the binding when PTQ1_LIB names it; for host-only test runs
+    (the sanitizers instrument no GPU code)."""
+    build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    obj = os.path.join(SAN_DIR, "api.cpp.o")
+    cmd = ["g++", "-std=c++17", "-O1", "-fPIC", "-Wall", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I",
+           os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, "api.cpp"), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    gpu_objs = [os.path.join(BUILD_DIR, os.path.basename(src) + ".o") for src in sources() if not src.endswith(".cpp")]
+    cmd = ["g++", "-shared", "-fsanitize=address,undefined", "-o", SAN_LIB, obj, *gpu_objs, "-L/opt/rocm/lib",
+           "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
