@@ -885,8 +885,7 @@ ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
 size_t ptq1_matvec_w2a8_workspace_bytes(int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0) return 0;
-    // partials, then q [k] and the step
-    return lut_ws(n, 1, k) + round_up(static_cast<size_t>(k) * 4 + 4, kWsAlign);
+    return lut_ws(n, 1, k);  // the split-K partials
 }
 
 ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *residual,
@@ -916,16 +915,11 @@ ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const f
     if (nseg_of(k) * 4 > kMaxGridY) return fail(PTQ1_ERR_UNSUPPORTED, "k = %lld too large", (long long)k);
     if (n > kMaxLutRows) return fail(PTQ1_ERR_UNSUPPORTED, "n = %lld > %lld rows", (long long)n, (long long)kMaxLutRows);
     if (wb > kMaxLutMatrixBytes) return fail(PTQ1_ERR_UNSUPPORTED, "tiled matrix above 2 GiB");
-    char *w = static_cast<char *>(ws);
-    float *part = reinterpret_cast<float *>(w);
-    float *q = reinterpret_cast<float *>(w + lut_ws(n, 1, k));
-    float *step = q + k;
-    hipError_t e = ptq1::launch_w2a8_quant(x, k, q, step, stream);
-    if (e == hipSuccess)
-        e = profiled(kProfLut1, stream, [&] {
-            return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, q, nullptr, nullptr, part, stream);
-        });
-    if (e == hipSuccess) e = ptq1::launch_w2a8_sum(part, n, k, step, residual, y, stream);
+    float *part = static_cast<float *>(ws);
+    hipError_t e = profiled(kProfLut1, stream, [&] {
+        return ptq1::launch_matvec_lut(tiled, nullptr, 1, n, k, x, nullptr, nullptr, part, stream, true);
+    });
+    if (e == hipSuccess) e = ptq1::launch_lut_sum_rows(part, n, k, residual, y, stream);
     return hip_status(e, "ptq1_matvec_w2a8");
 }
 

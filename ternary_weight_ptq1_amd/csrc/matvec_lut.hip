@@ -257,43 +257,43 @@ __device__ __forceinline__ void slice_x_store(const SliceX &v, bool rotate, bool
 // where A = (d0-1) x0 + (d1-1) x1 and B = ((d2-1) x2 + (d3-1) x3) + (d4-1) x4
 // are formed once per thread (9 + 27 sums); the digits are compile-time
 // constants of the unrolled loop, so each entry costs one add.
-template <int BQ>
-__device__ __forceinline__ void lut_build_range(float *tab, int slot, const float (&xv)[5])  // bytes kLutBuildPer * BQ ..
+template <int BQ, class T>
+__device__ __forceinline__ void lut_build_range(float *tab, int slot, const T (&xv)[5])  // bytes kLutBuildPer * BQ ..
 {
-    float A[9], B[27];
+    T A[9], B[27];
 #pragma unroll
     for (int d0 = 0; d0 < 3; ++d0)
 #pragma unroll
         for (int d1 = 0; d1 < 3; ++d1)
-            A[3 * d0 + d1] = static_cast<float>(d0 - 1) * xv[0] + static_cast<float>(d1 - 1) * xv[1];
+            A[3 * d0 + d1] = static_cast<T>(d0 - 1) * xv[0] + static_cast<T>(d1 - 1) * xv[1];
 #pragma unroll
     for (int d2 = 0; d2 < 3; ++d2)
 #pragma unroll
         for (int d3 = 0; d3 < 3; ++d3) {
-            const float c = static_cast<float>(d2 - 1) * xv[2] + static_cast<float>(d3 - 1) * xv[3];
+            const T c = static_cast<T>(d2 - 1) * xv[2] + static_cast<T>(d3 - 1) * xv[3];
 #pragma unroll
-            for (int d4 = 0; d4 < 3; ++d4) B[9 * d2 + 3 * d3 + d4] = c + static_cast<float>(d4 - 1) * xv[4];
+            for (int d4 = 0; d4 < 3; ++d4) B[9 * d2 + 3 * d3 + d4] = c + static_cast<T>(d4 - 1) * xv[4];
         }
     const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
 #pragma unroll
     for (int i = 0; i < kLutBuildPer; ++i) {
         const int b = kLutBuildPer * BQ + i;
         const int v = (243 * b) >> 8;
-        *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
+        *reinterpret_cast<T *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
             A[v / 27] + B[v % 27];
     }
 }
 
 // bq (wave-uniform) -> lut_build_range<bq>: the digits of each entry stay
 // compile-time constants.
-template <int BQ>
-__device__ __forceinline__ void lut_build_dispatch(int bq, float *tab, int slot, const float (&xv)[5])
+template <int BQ, class T>
+__device__ __forceinline__ void lut_build_dispatch(int bq, float *tab, int slot, const T (&xv)[5])
 {
     if constexpr (BQ < kLutBuildRanges) {
         if (bq == BQ)
-            lut_build_range<BQ>(tab, slot, xv);
+            lut_build_range<BQ, T>(tab, slot, xv);
         else
-            lut_build_dispatch<BQ + 1>(bq, tab, slot, xv);
+            lut_build_dispatch<BQ + 1, T>(bq, tab, slot, xv);
     }
 }
 
@@ -319,7 +319,7 @@ typedef uint32_t lut_u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 // U: units per wave.
 // One segment of a workgroup's work: units [u0, u1) of slice s, unit
 // u0 + w + 8 i going to wave w (i < U).
-template <int U>
+template <int U, bool W8>
 __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float *xs, int s, int64_t u0, int64_t u1)
 {
     const int tid = threadIdx.x;
@@ -337,6 +337,23 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     // would wait for all of them.
     SliceX xv;
     if (wave == 0) slice_x_load(a.x, a.signs, a.gain, k0, kw, lane, xv);
+    float amax = 0.0f;  // W8: this thread's part of max|x|, 16 bytes per load, all requested at once
+    if constexpr (W8) {
+        constexpr int kPer = 9;  // float4 loads per thread requested before the reduction (k <= 18432 in one pass)
+        lut_f32x4 v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t e = 4 * (tid + static_cast<int64_t>(kLutThreads) * j);
+            v[j] = *reinterpret_cast<const lut_f32x4 *>(a.x + (e < a.k ? e : a.k - 4));  // clamped copies repeat
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+        for (int64_t e = 4 * (tid + static_cast<int64_t>(kLutThreads) * kPer); e < a.k; e += 4 * kLutThreads) {
+            const lut_f32x4 w = *reinterpret_cast<const lut_f32x4 *>(a.x + e);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3]))));
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. weights of this wave's first kLutEarly units; units up to
@@ -417,8 +434,33 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0)
-    if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
+    // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0);
+    // W8: the workgroup's max|x| first, then q = rint(x c) (integers in
+    // [-127, 127], held as int32 in xs)
+    float step = 1.0f;
+    if constexpr (W8) {
+        float *red = xs + kLutSliceW;  // kLutWaves floats after the slice
+#pragma unroll
+        for (int h = kWave / 2; h > 0; h >>= 1) amax = fmaxf(amax, __shfl_xor(amax, h, kWave));
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        float g = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kLutWaves; ++w) g = fmaxf(g, red[w]);
+        // the multiplier rounded once from its exact quotient (the double
+        // division is correctly rounded, the conversion rounds to nearest)
+        const float c = g > 0.0f ? static_cast<float>(127.0 / static_cast<double>(g)) : 0.0f;
+        step = static_cast<float>(static_cast<double>(g) / 127.0);
+        if (wave == 0) {
+            int32_t qv[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qv[kk] = 4 * lane + kk < kw ? static_cast<int32_t>(rintf(xv.x[0][kk] * c)) : 0;
+            *reinterpret_cast<int4 *>(xs + 4 * lane) = make_int4(qv[0], qv[1], qv[2], qv[3]);
+        }
+    } else {
+        if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
+    }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -429,13 +471,24 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         const int bq = tid >> 6;  // 0 .. kLutBuildRanges - 1
         const int col = tid & 63;
         const int blk = col / kLutColsPerBlock, i = col % kLutColsPerBlock;
-        float xv[5];
+        if constexpr (W8) {
+            const int32_t *xq = reinterpret_cast<const int32_t *>(xs);
+            int32_t xv5[5];
 #pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const int j = kTritsPerByte * i + n;  // weight index in the block
-            xv[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
+            for (int n = 0; n < 5; ++n) {
+                const int j = kTritsPerByte * i + n;
+                xv5[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xq[blk * kBlockWeights + j] : 0;
+            }
+            lut_build_dispatch<0, int32_t>(bq, tab, col, xv5);
+        } else {
+            float xv5[5];
+#pragma unroll
+            for (int n = 0; n < 5; ++n) {
+                const int j = kTritsPerByte * i + n;  // weight index in the block
+                xv5[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
+            }
+            lut_build_dispatch<0, float>(bq, tab, col, xv5);
         }
-        lut_build_dispatch<0>(bq, tab, col, xv);
     }
     rotate(0);
     __syncthreads();
@@ -452,19 +505,38 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
         const int r = u.grp * kLutRows + row_l;
         const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
         const float scale = live ? half_bits_to_float(scb[i]) : 0.0f;
-        float acc0 = 0.0f, acc1 = 0.0f;
+        float p;
+        if constexpr (W8) {
+            // exact int32 sums; two lookups per add (v_add3_u32)
+            typedef __attribute__((address_space(3))) const int32_t lds_i32;
+            int32_t acc = 0;
 #pragma unroll
-        for (int j = 0; j < kLutDwords; ++j) {
+            for (int j = 0; j < kLutDwords; ++j) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
-                const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
-                if ((c & 1) == 0) acc0 += t; else acc1 += t;
+                for (int c = 0; c < 4; c += 2) {
+                    const uint32_t a0 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
+                    const uint32_t a1 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c + 1]);
+                    acc = acc + *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a0)) +
+                          *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a1));
+                }
             }
+            p = static_cast<float>(acc) * scale;  // |acc| <= 26 * 635 < 2^24: exact in fp32
+        } else {
+            float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kLutDwords; ++j) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
+                    const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
+                    if ((c & 1) == 0) acc0 += t; else acc1 += t;
+                }
+            }
+            p = (acc0 + acc1) * scale;
         }
-        float p = (acc0 + acc1) * scale;
         const int ip = __builtin_bit_cast(int, p);
         p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
+        if (W8) p *= step;
         if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r] = p;
     }
 }
@@ -475,7 +547,7 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
 // units.  The grid shape carries the partition: no division at entry (the
 // 64-bit divisions of an even split cost a dependent chain of scalar and
 // reciprocal steps before the first load could be issued).
-template <int U>
+template <int U, bool W8>
 __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 waves per SIMD (1024 threads per CU)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -484,7 +556,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     const int per_slice = a.nmat * static_cast<int>(a.groups);  // rows < 2^20 (checked by the caller)
     const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
     const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
-    if (u0 < u1) lut_segment<U>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);  // workgroup-uniform
+    if (u0 < u1) lut_segment<U, W8>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);  // workgroup-uniform
 }
 
 static int device_cus()
@@ -541,28 +613,41 @@ static LutPlan lut_plan(int64_t per_slice, int64_t nslices)
     return LutPlan{U, static_cast<int>(per_wg), (per_slice + per_wg - 1) / per_wg};
 }
 
-template <int U>
+template <int U, bool W8>
 static hipError_t lut_launch(const LutArgs &a, int64_t chunks, hipStream_t st)
 {
     static std::atomic<uint64_t> lds_done{0};
-    const size_t lds = kLutTableBytes + kLutSliceW * sizeof(float);
+    const size_t lds = kLutTableBytes + (kLutSliceW + kLutWaves) * sizeof(float);
     const hipError_t e =
-        allow_dynamic_lds(reinterpret_cast<const void *>(&k_matvec_lut<U>), static_cast<int>(lds), lds_done);
+        allow_dynamic_lds(reinterpret_cast<const void *>(&k_matvec_lut<U, W8>), static_cast<int>(lds), lds_done);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.nslices));
     ProfEvents &pe = prof_events();
     if (pe.start != nullptr) {
-        hipExtLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
+        hipExtLaunchKernelGGL((k_matvec_lut<U, W8>), grid, dim3(kLutThreads), static_cast<uint32_t>(lds), st, pe.start,
                               pe.stop, 0u, a);
         pe = ProfEvents{};
     } else {
-        hipLaunchKernelGGL(k_matvec_lut<U>, grid, dim3(kLutThreads), lds, st, a);
+        hipLaunchKernelGGL((k_matvec_lut<U, W8>), grid, dim3(kLutThreads), lds, st, a);
     }
     return hipGetLastError();
 }
 
+template <bool W8>
+static hipError_t lut_dispatch(const LutArgs &a, int U, int64_t chunks, hipStream_t s)
+{
+    switch (U) {
+        case 1: return lut_launch<1, W8>(a, chunks, s);
+        case 2: return lut_launch<2, W8>(a, chunks, s);
+        case 3: return lut_launch<3, W8>(a, chunks, s);
+        case 4: return lut_launch<4, W8>(a, chunks, s);
+        default: return lut_launch<6, W8>(a, chunks, s);
+    }
+}
+
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s)
+                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s,
+                             bool w8)
 {
     if (n == 0) return hipSuccess;
     LutArgs a{};
@@ -574,19 +659,12 @@ hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int
     a.nslices = static_cast<int>(lut_nslices(k));
     a.groups = (n + kLutRows - 1) / kLutRows;
     a.x = x;
-    a.signs = signs;
-    a.gain = gain;
+    a.signs = w8 ? nullptr : signs;
+    a.gain = w8 ? nullptr : gain;
     a.part = part;
     const LutPlan pl = lut_plan(static_cast<int64_t>(nmat) * a.groups, a.nslices);
     a.per_wg = pl.per_wg;
-    const int64_t chunks = pl.chunks;
-    switch (pl.U) {
-        case 1: return lut_launch<1>(a, chunks, s);
-        case 2: return lut_launch<2>(a, chunks, s);
-        case 3: return lut_launch<3>(a, chunks, s);
-        case 4: return lut_launch<4>(a, chunks, s);
-        default: return lut_launch<6>(a, chunks, s);
-    }
+    return w8 ? lut_dispatch<true>(a, pl.U, pl.chunks, s) : lut_dispatch<false>(a, pl.U, pl.chunks, s);
 }
 
 // ---------------------------------------------------------------------------

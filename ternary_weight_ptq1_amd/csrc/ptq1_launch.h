@@ -56,19 +56,18 @@ hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, 
 // (nmat = 1) or two sharing x (nmat = 2); x (times gain [k], if given)
 // rotated per 1024-chunk when signs != nullptr, else used as given.
 int64_t lut_nslices(int64_t k);
-// 8-bit activations: q = rint(x * float(127 / max|x|)) as fp32 integers and
-// step = max|x| / 127 (one workgroup); y = residual + step * sum of the
-// lookup matvec's partials over q.
-hipError_t launch_w2a8_quant(const float *x, int64_t k, float *q, float *step, hipStream_t s);
 // GEMM side: bf16 fragments of the per-row quantised x (integer values,
 // exact in bf16) and step[row]; then y [m][n] *= step[row].
 hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint16_t *xf, float *step, hipStream_t s);
 hipError_t launch_w2a8_scale_rows(float *y, int64_t m, int64_t n, const float *step, hipStream_t s);
-hipError_t launch_w2a8_sum(const float *part, int64_t n, int64_t k, const float *step, const float *residual,
-                           float *y, hipStream_t s);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
+// w8: 8-bit activations (W2A8) -- signs and gain are ignored; every
+// workgroup takes max|x| itself, forms q = rint(x * float(127 / max|x|)),
+// sums trits times q per block in int32 and stores step * sum_b scale_b * isum_b
+// (step = max|x| / 127), so launch_lut_sum_rows gives the W2A8 product.
 hipError_t launch_matvec_lut(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,
-                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s);
+                             const float *x, const float *signs, const float *gain, float *part, hipStream_t s,
+                             bool w8 = false);
 // The same partials with every trit peeled on the float pipeline (eight
 // lanes per block), over the same tiled layout and slices.
 hipError_t launch_matvec_peel(const uint8_t *w0, const uint8_t *w1, int nmat, int64_t n, int64_t k,

@@ -436,6 +436,39 @@ def test_gemm_prefill_full_shape(m, prefill_weights):
     assert rel_l2(got[:, rows], ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("m,n,k", [(128, 17408, 5120), (8, 34816, 5120), (40, 3072, 2048)])
+def test_gemm_repeat_stream_k(m, n, k):
+    """The work split's shared tiles and their fix-up kernel, the most
+    ordering-sensitive part of the GEMM: 50 fresh inputs, each call repeated
+    and compared bit for bit (the partial tiles are summed in a fixed order),
+    every tenth one (and the last) against the oracle on 64 sampled weight
+    rows.  At 128 x 17408 the 136 row tiles are fewer than the workgroups, so
+    every tile is split over several of them; at 8 x 34816 the
+    register-decode kernel splits the remainder of its whole-tile rounds."""
+    seed = 40
+    # the matrix from the generator's device fill (bit-exact with its host
+    # version); only the sampled rows are generated on the host for the oracle
+    bd = P.ptq1_tile(P.ptq1_pack(sdev.trits(seed, synth.S_W_TRITS, n, k, device=DEV),
+                                 sdev.scales(seed, synth.S_W_SCALES, n, k // 128, device=DEV)), n, k)
+    rows = np.unique(np.concatenate([[0, n - 1], synth.token_ids(seed, 62, n)])).astype(np.int64)
+    b = oracle.pack(synth.trits_rows(seed, synth.S_W_TRITS, rows, k),
+                    synth.scales_rows(seed, synth.S_W_SCALES, rows, k // 128))
+    ws = torch.empty(P.workspace_bytes("gemm", m, n, k), dtype=torch.uint8, device=DEV)
+    y1 = torch.empty((m, n), dtype=torch.float32, device=DEV)
+    y2 = torch.empty_like(y1)
+    for it in range(50):
+        x = synth.activations(seed + 1 + it, m, k)
+        sg = synth.signs(seed + 1 + it)
+        xd, sd = to_dev(x), to_dev(sg)
+        P.ptq1_gemm(bd, n, k, xd, sd, out=y1, ws=ws)
+        P.ptq1_gemm(bd, n, k, xd, sd, out=y2, ws=ws)
+        g1, g2 = host(y1), host(y2)
+        np.testing.assert_array_equal(g1, g2, err_msg=f"iteration {it}")
+        if it % 10 == 0 or it == 49:
+            ref = oracle.gemm(b, len(rows), k, oracle.rotate(x, sg))
+            assert rel_l2(g1[:, rows], ref) <= TOL_BF16, f"iteration {it}"
+
+
 # ------------------------------------ other folded projections (synthetic) ----
 # The pages fold the rotation into every weight matrix but give no attention
 # shapes; a wide and a narrow projection stand in for them (seeded like the
@@ -771,6 +804,29 @@ def test_pq2_ffn_block_full_shape():
                     to_dev(s), d, f, 1e-6, out=xd)
     ref = oracle.pq2_ffn_block(x, wg, wu, wd, s, d, f, 1e-6)
     check_block(host(xd), x, ref, 1)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_ffn_block_repeat(m):
+    """50 fresh inputs through one block (d = 1024, f = 2048): each call
+    repeated and compared bit for bit, every tenth one (and the last) against
+    the oracle."""
+    d, f, seed = 1024, 2048, 41
+    wg, wu, wd = _ffn_host(seed, d, f)
+    tg, tu, td = tiled(wg, f, d), tiled(wu, f, d), tiled(wd, d, f)
+    ws = torch.empty(P.workspace_bytes("ffn", m, d, f), dtype=torch.uint8, device=DEV)
+    o1 = torch.empty((m, d), dtype=torch.float32, device=DEV)
+    o2 = torch.empty_like(o1)
+    for it in range(50):
+        x = synth.activations(seed + 1 + it, m, d)
+        s = synth.signs(seed + 1 + it)
+        xd, sd = to_dev(x), to_dev(s)
+        P.ptq1_ffn_block(xd, tg, tu, td, sd, d, f, 1e-6, out=o1, ws=ws)
+        P.ptq1_ffn_block(xd, tg, tu, td, sd, d, f, 1e-6, out=o2, ws=ws)
+        g1, g2 = host(o1), host(o2)
+        np.testing.assert_array_equal(g1, g2, err_msg=f"iteration {it}")
+        if it % 10 == 0 or it == 49:
+            check_block(g1, x, oracle.ffn_block(x, wg, wu, wd, s, d, f, 1e-6), m)
 
 
 # ------------------------------------------------- FFN block, stage by stage ----
