@@ -927,7 +927,7 @@ size_t ptq1_gemm_w2a8_workspace_bytes(int64_t m, int64_t n, int64_t k)
 {
     if (packed_bytes(n, k) < 0 || m < 0 || m > kMaxGemmM) return 0;
     if (m == 0) return 0;
-    return gemm_layout(ptq1::gemm_plan(m, n, k), k).total + round_up(static_cast<size_t>(m) * 4, kWsAlign);
+    return gemm_layout(ptq1::gemm_plan(m, n, k, true), k).total + round_up(static_cast<size_t>(m) * 4, kWsAlign);
 }
 
 ptq1_status ptq1_gemm_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const float *x, int64_t m, float *y, void *ws,
@@ -942,7 +942,7 @@ ptq1_status ptq1_gemm_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const flo
     if (mn == 0) return ok();
     if (k == 0) return fail(PTQ1_ERR_SHAPE, "k = 0");
     PTQ1_TRY(check_floats(x, "x", mk, &xb));
-    const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k);
+    const ptq1::GemmPlan plan = ptq1::gemm_plan(m, n, k, true);  // the int8 kernel has register-decode plans
     const GemmWs L = gemm_layout(plan, k);
     const size_t need = ptq1_gemm_w2a8_workspace_bytes(m, n, k);
     PTQ1_TRY(check_ws(ws, ws_bytes, need, "ptq1_gemm_w2a8"));
@@ -952,15 +952,14 @@ ptq1_status ptq1_gemm_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const flo
         overlaps(ws, (int64_t)need, tiled, wb))
         return fail(PTQ1_ERR_ALIAS, "ws overlaps an argument");
     char *w = static_cast<char *>(ws);
-    uint16_t *xf = reinterpret_cast<uint16_t *>(w + L.frag);
+    uint8_t *xq = reinterpret_cast<uint8_t *>(w + L.frag);  // int8 operands: m_pad * k bytes of the bf16 region
     float *part = reinterpret_cast<float *>(w + L.part);
     float *step = reinterpret_cast<float *>(w + L.total);
-    hipError_t e = ptq1::launch_prep_frag_w8(x, m, k, xf, step, stream);
+    hipError_t e = ptq1::launch_prep_frag_w8(x, m, k, xq, step, stream);
     if (e == hipSuccess)
         e = profiled(kProfGemm, stream, [&] {
-            return ptq1::launch_gemm(plan, xf, m, tiled, n, nullptr, 0, y, nullptr, nullptr, part, stream);
+            return ptq1::launch_gemm_i8(plan, xq, m, tiled, n, y, step, part, stream);
         });
-    if (e == hipSuccess) e = ptq1::launch_w2a8_scale_rows(y, m, n, step, stream);
     return hip_status(e, "ptq1_gemm_w2a8");
 }
 

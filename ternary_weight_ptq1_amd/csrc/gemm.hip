@@ -48,6 +48,21 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
     return (kappa >> 3) == 15 ? kappa : 5 * (8 * ((kappa >> 3) / 5) + (kappa & 7)) + (kappa >> 3) % 5;
 }
 
+// K order inside a block for the int8 MFMA (v_mfma_i32_32x32x32_i8, four
+// steps of K = 32 per block; lane half h of step s supplies K positions
+// 32 s + 16 h .. 32 s + 16 h + 15 as four dwords q of four bytes j, and
+// t = 4 s + q):
+//   t < 12:  digit j of byte 12 h + t              (weight 5 (12 h + t) + j)
+//   t = 12:  weight 120 + 4 h + j                   (bytes 24 and 25)
+//   t > 12:  digit 4 of byte 12 h + 4 (t - 13) + j
+// so each of a lane's dwords with t < 12 is one table entry (digits 0-3 of
+// one byte), and those with t > 12 gather digit 4 of four bytes.
+__host__ __device__ constexpr int gemm_i8_kperm(int kappa)
+{
+    const int h = (kappa >> 4) & 1, t = 4 * (kappa >> 5) + ((kappa >> 2) & 3), j = kappa & 3;
+    return t < 12 ? 5 * (12 * h + t) + j : (t == 12 ? 120 + 4 * h + j : 5 * (12 * h + 4 * (t - 13) + j) + 4);
+}
+
 // ---------------------------------------------------------------------------
 // Activation prep: one wavefront per (row, 1024-chunk).
 //   input  = x (times the row's RMS scale when rms_eps > 0 and the per-channel
@@ -65,9 +80,12 @@ __host__ __device__ constexpr int gemm_kperm(int kappa)
 // the two code bytes 16 h + 2 s, 16 h + 2 s + 1 of a PQ2_0 block.
 // ---------------------------------------------------------------------------
 // W8: 8-bit activations instead (x given, no rotation, no norm): the row's
-// max |x| comes from the same whole-row loads as the mean square, and the
-// chunk is written as q = rint(x * float(127 / max|x|)), integers that bf16
-// holds exactly; wave 0 of the row also stores its step max|x| / 127.
+// max |x| comes from the same whole-row loads as the mean square, the chunk
+// becomes q = rint(x * float(127 / max|x|)) and is written as int8 operands
+// of v_mfma_i32_32x32x32_i8: for 32-row group mt, block kb, step s (0..3)
+// and lane l the 16 bytes at byte offset (((mt nb + kb) 4 + s) 64 + l) 16
+// hold q[32 mt + l % 32][128 kb + gemm_i8_kperm(32 s + 16 (l / 32) + i)],
+// i = 0..15; wave 0 of the row also stores its step max|x| / 127.
 template <bool Q2, bool W8>
 __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
@@ -200,6 +218,28 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
     const int64_t nb = k / kBlockWeights;
     const int64_t mt = row / 32;
     const int rl = static_cast<int>(row % 32);
+    if constexpr (W8) {
+        // one piece per lane: block kbl of the chunk, step stp, half h
+        const int kbl = lane >> 3, stp = (lane >> 1) & 3, h = lane & 1;
+        const int64_t kb = ch * (kHadamard / kBlockWeights) + kbl;
+        if (kb < nb) {
+            const float *src = st + kBlockWeights * kbl;
+            gm_u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t d = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int32_t qi = static_cast<int32_t>(src[gemm_i8_kperm(32 * stp + 16 * h + 4 * q + j)]);
+                    d |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * j);
+                }
+                o[q] = d;
+            }
+            uint8_t *xq = reinterpret_cast<uint8_t *>(xf);
+            *reinterpret_cast<gm_u32x4 *>(xq + (((mt * nb + kb) * 4 + stp) * kWave + rl + 32 * h) * 16) = o;
+        }
+        return;
+    }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int p = lane + kWave * pp;  // fragment piece: block kbl of the chunk, fragment f
@@ -289,6 +329,7 @@ struct GemmArgs {
     float *y0, *y1;          // outputs [m][n0], [m][n1]
     const float *residual;   // [m][n0] or null
     float *part;             // partial tiles [workgroup][first / last][prow][128]
+    const float *row_scale;  // int8 path: each output row times row_scale[row] (the W2A8 step)
     int64_t m, nb;           // activation rows, K blocks
     int64_t tiles_m, prow;   // row tiles; rows of a row tile (= m with one row tile)
     int64_t wgs;             // workgroups
@@ -1001,6 +1042,268 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
     }  // segments
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit activations on the int8 matrix cores (W2A8: "Why I Am Building
+// Another Inference Engine", Level 5, integer kernels on int8 activations;
+// Level 4, a BitNet layer's int8 activations ahead of its ternary matmuls).
+// The register-decode kernel above with int8 operands: activations are the
+// per-row quantised q (k_prep_frag W8 layout), trits are exact int8
+// -1 / 0 / +1, v_mfma_i32_32x32x32_i8 sums each 128-weight block exactly in
+// int32 (|sum| <= 128 * 127), and the block's sum is scaled by its fp16
+// scale in fp32; every stored output row is multiplied by its step.
+// Table (64 KB, 32 copies per half-row): row b holds, for byte value b,
+// T_lo = [d0-1, d1-1, d2-1, d3-1] (int8) in bytes 0..127 and T_hi = d4-1
+// in every byte in 128..255.  Lane l (column l % 32, half h = l / 32) loads
+// bytes 12 h .. 12 h + 15 of its column's block and the dword at byte 24,
+// and reads 27 entries per block; step s's B operand is then dwords
+// t = 4 s .. 4 s + 3 of the gemm_i8_kperm order (t < 12: one T_lo each;
+// t = 12: T_lo of byte 24, or T_hi of 24 and three digits of 25; t > 12:
+// T_hi of four bytes, two v_perm each).
+// ---------------------------------------------------------------------------
+typedef int32_t gm_i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t gm_i32x16 __attribute__((ext_vector_type(16)));
+
+template <int TM, int PD, int LR>
+__global__ void __launch_bounds__(kRdThreads, 2) k_gemm_i8(GemmArgs a)
+{
+    static_assert(LR >= 1 && LR <= 4, "8-row groups of a 32-row tile");
+    constexpr int kSteps = 4;  // MFMA steps of K = 32 per block
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int hi = lane >> 5;
+    const int64_t rows = a.n0 + a.n1;
+    const uint8_t *xq = reinterpret_cast<const uint8_t *>(a.xf);
+
+    auto build_table = [&]() {  // thread b: entry b, every copy
+        const uint32_t b = static_cast<uint32_t>(tid);
+        const uint32_t v = (243u * b) >> 8;  // the byte's code; its base-3 digits, most significant first
+        const uint32_t d[5] = {v / 81u, (v / 27u) % 3u, (v / 9u) % 3u, (v / 3u) % 3u, v % 3u};
+        uint32_t lo = 0;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) lo |= ((d[n] + 255u) & 0xffu) << (8 * n);  // d - 1 as an int8 byte
+        const uint32_t h4 = ((d[4] + 255u) & 0xffu) * 0x01010101u;
+        const gm_u32x4 elo = {lo, lo, lo, lo}, ehi = {h4, h4, h4, h4};
+#pragma unroll
+        for (int c = 0; c < 32; c += 4) {
+            *reinterpret_cast<gm_u32x4 *>(lds + b * 256 + c * 4) = elo;
+            *reinterpret_cast<gm_u32x4 *>(lds + b * 256 + 128 + c * 4) = ehi;
+        }
+    };
+    bool table_built = false;  // workgroup-uniform
+    const uint32_t lc = static_cast<uint32_t>(lane & 31) << 2;
+
+    const int64_t G = gridDim.x, wg = blockIdx.x;
+    const int64_t Gs = a.sk_wgs;
+    const int64_t sk_lo = wg < Gs ? wg * a.sk_units / Gs : 0, sk_hi = wg < Gs ? (wg + 1) * a.sk_units / Gs : 0;
+    int64_t jdp = 0, useg = sk_lo;
+    while (jdp < a.dp_rounds || useg < sk_hi) {
+        int64_t tile, kb0;
+        int nblk, kslot = 0;
+        bool full;
+        if (jdp < a.dp_rounds) {
+            tile = wg + jdp * G;
+            kb0 = 0;
+            nblk = static_cast<int>(a.nb);
+            full = true;
+            ++jdp;
+        } else {
+            const int64_t t2 = useg / a.nb;
+            kb0 = useg - t2 * a.nb;
+            const int64_t uend = (t2 + 1) * a.nb < sk_hi ? (t2 + 1) * a.nb : sk_hi;
+            nblk = static_cast<int>(uend - useg);
+            tile = a.dp_tiles + t2;
+            full = kb0 == 0 && nblk == a.nb;
+            kslot = useg == sk_lo ? 0 : 1;
+            useg = uend;
+        }
+        const int last = nblk - 1;
+        auto blk = [&](int i) -> int64_t { return kb0 + (i < last ? i : last); };
+        const int64_t tn = tile / a.tiles_m, tm = tile - tn * a.tiles_m;
+        const int64_t tile_n = tn * kGemmBN;
+        const int64_t mt0 = tm * TM;
+        const int64_t row0 = tm * a.prow;
+
+        const int64_t gcol = tile_n + wave * 32 + (lane & 31);
+        const uint8_t *wcol = a.w0;
+        int64_t sstride = 0;
+        if (gcol < rows) {
+            const bool first = gcol < a.n0;
+            const int64_t rr = first ? gcol : gcol - a.n0;
+            wcol = (first ? a.w0 : a.w1) + (rr / kTileRows) * kTileBytes + (rr % kTileRows) * (kTileBlocks * kBlockBytes);
+            sstride = (first ? a.bands0 : a.bands1) * kTileBytes;
+        }
+        struct WRegs {
+            gm_u32x4 v;  // bytes 12 h .. 12 h + 15
+            uint32_t w;  // bytes 24..27
+        };
+        auto load_w = [&](WRegs &r, int64_t kb) {
+            const uint8_t *p = wcol + (kb >> 1) * sstride + (kb & 1) * kBlockBytes;
+            const gm_u32x4a v = *reinterpret_cast<const gm_u32x4a *>(p + 12 * hi);
+            r.v = gm_u32x4{v[0], v[1], v[2], v[3]};
+            r.w = *reinterpret_cast<const uint32_t *>(p + 24);
+        };
+        // LDS address of the entry of byte `byte` of dword w (T_lo; T_hi at + 128)
+        auto addr = [&](uint32_t w, int byte) -> uint32_t {
+            return __builtin_amdgcn_perm(lc, w, 0x0c0c0004u | (static_cast<uint32_t>(byte) << 8));
+        };
+        auto rd = [&](uint32_t ad, int off) -> uint32_t {
+            return *reinterpret_cast<lds_u32 *>(static_cast<uintptr_t>(ad + off));
+        };
+        struct Ent {
+            uint32_t lo[12], hi[12];  // bytes 12 h .. 12 h + 11
+            uint32_t lo24, hi24, lo25;
+            float scale;
+        };
+        auto tab_reads = [&](const WRegs &r, Ent &e) {
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                const uint32_t ad = addr(r.v[i >> 2], i & 3);
+                e.lo[i] = rd(ad, 0);
+                e.hi[i] = rd(ad, 128);
+            }
+            const uint32_t a24 = addr(r.w, 0), a25 = addr(r.w, 1);
+            e.lo24 = rd(a24, 0);
+            e.hi24 = rd(a24, 128);
+            e.lo25 = rd(a25, 0);
+            e.scale = half_bits_to_float(r.w >> 16);
+        };
+        auto bfrag = [&](const Ent &e, int st) -> gm_i32x4 {
+            gm_i32x4 o;
+            if (st < 3) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = static_cast<int32_t>(e.lo[4 * st + q]);
+            } else {
+                // t = 12: weights 120 + 4 h .. 123 + 4 h (byte 24 digits 0-3; or byte 24
+                // digit 4 and byte 25 digits 0-2)
+                o[0] = static_cast<int32_t>(hi ? __builtin_amdgcn_perm(e.lo25, e.hi24, 0x06050400u) : e.lo24);
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const uint32_t p01 = __builtin_amdgcn_perm(e.hi[4 * i + 1], e.hi[4 * i], 0x0c0c0400u);
+                    const uint32_t p23 = __builtin_amdgcn_perm(e.hi[4 * i + 3], e.hi[4 * i + 2], 0x04000c0cu);
+                    o[1 + i] = static_cast<int32_t>(p01 | p23);
+                }
+            }
+            return o;
+        };
+        // A lane whose row is padding (row >= m) reads row 0 of its tile
+        // instead: its output row is never stored.
+        const uint8_t *xw[TM];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const bool live_row = (mt0 + m) * 32 + (lane & 31) < a.m;
+            xw[m] = xq + ((mt0 + m) * a.nb * kSteps * kWave + (live_row ? lane : (lane & 32))) * 16;
+        }
+        auto load_a = [&](gm_i32x4 (&f)[TM], int64_t kb, int st) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+                f[m] = *reinterpret_cast<const gm_i32x4 *>(xw[m] + (kb * kSteps + st) * kWave * 16);
+        };
+
+        f32x16 acc[TM];
+        gm_i32x16 part[TM];
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc[m][r] = 0.0f;
+                part[m][r] = 0;
+            }
+        float sc_prev = 0.0f;
+
+        // prologue: PD blocks of weights, block 0's activations (all four
+        // steps: the ring is one block deep) and block 0's table entries
+        WRegs ring[PD];
+#pragma unroll
+        for (int p = 0; p < PD; ++p) load_w(ring[p], blk(p));
+        gm_i32x4 afr[kSteps][TM];
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) load_a(afr[st], blk(0), st);
+        if (!table_built) {
+            build_table();
+            __syncthreads();
+            table_built = true;
+        }
+        Ent ent[2];
+        tab_reads(ring[0], ent[0]);
+        load_w(ring[0], blk(PD));
+
+        // One block: four MFMA steps; step 0 first folds the previous block's
+        // int32 sum (times its scale) into acc, each step refills its
+        // activation slot with the next block's, and step 1 issues the next
+        // block's table reads and refills its weight slot.
+        auto iteration = [&](int i, Ent &cur, Ent &nxt, WRegs &rslot) {
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                const gm_i32x4 bv = bfrag(cur, st);
+                gm_i32x4 (&ar)[TM] = afr[st];
+#pragma unroll
+                for (int m = 0; m < TM; ++m) {
+                    if (st == 0) {
+#pragma unroll
+                        for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r)
+                            acc[m][r] = fmaf(static_cast<float>(part[m][r]), sc_prev, acc[m][r]);
+                        const gm_i32x16 z = {};
+                        part[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[m], bv, z, 0, 0, 0);
+                    } else {
+                        part[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[m], bv, part[m], 0, 0, 0);
+                    }
+                }
+                load_a(ar, blk(i + 1), st);
+                if (st == 1) {
+                    tab_reads(rslot, nxt);
+                    load_w(rslot, blk(i + 1 + PD));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sc_prev = cur.scale;
+        };
+
+        for (int base = 0; base < nblk; base += PD) {
+#pragma unroll
+            for (int u = 0; u < PD; ++u) {
+                const int i = base + u;
+                if (i >= nblk) break;
+                iteration(i, ent[u & 1], ent[(u + 1) & 1], ring[(u + 1) % PD]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r)
+                acc[m][r] = fmaf(static_cast<float>(part[m][r]), sc_prev, acc[m][r]);
+
+        // final tiles are stored, shared ones as partials for k_gemm_fix; both
+        // already carry the row's step
+        float *pp = a.part + (wg * 2 + kslot) * a.prow * kGemmBN;
+        const int64_t col = gcol;
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        if (col < rows) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+#pragma unroll
+                for (int r = 0; r < (m == TM - 1 ? 4 * LR : 16); ++r) {
+                    const int64_t row = (mt0 + m) * 32 + 8 * (r / 4) + 4 * (lane_e / 32) + (r % 4);
+                    if (row >= a.m) continue;
+                    const float v = a.row_scale != nullptr ? acc[m][r] * a.row_scale[row] : acc[m][r];
+                    if (!full) {
+                        pp[(row - row0) * kGemmBN + (col - tile_n)] = v;
+                    } else if (col < a.n0) {
+                        const int64_t o = row * a.n0 + col;
+                        a.y0[o] = a.residual ? a.residual[o] + v : v;
+                    } else {
+                        a.y1[row * a.n1 + (col - a.n0)] = v;
+                    }
+                }
+            }
+        }
+    }  // segments
+}
+
 // Workgroup of the stream-K range holding unit u: the largest w with
 // floor(w U / G) <= u, that is with w U < (u + 1) G.
 __device__ __forceinline__ int64_t gemm_owner(int64_t u, int64_t units, int64_t G)
@@ -1131,13 +1434,14 @@ hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, 
     return hipGetLastError();
 }
 
-hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint16_t *xf, float *step, hipStream_t s)
+hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint8_t *xq, float *step, hipStream_t s)
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_prep_frag<false, true>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
                        static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k,
-                       static_cast<const float *>(nullptr), 0.0f, static_cast<const float *>(nullptr), xf, step);
+                       static_cast<const float *>(nullptr), 0.0f, static_cast<const float *>(nullptr),
+                       reinterpret_cast<uint16_t *>(xq), step);
     return hipGetLastError();
 }
 
@@ -1184,6 +1488,7 @@ static GemmArgs gemm_args(const GemmPlan &p, const uint16_t *xf, int64_t m, cons
                           const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part)
 {
     GemmArgs a;
+    a.row_scale = nullptr;
     a.xf = xf;
     a.w0 = w0;
     a.w1 = w1;
@@ -1258,6 +1563,47 @@ hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, con
             e = gemm_rd_dispatch<1, 4, 4, true>(grid, s, a);
     } else {
         e = gemm_rd_dispatch<2, 4, 4, true>(grid, s, a);
+    }
+    if (e != hipSuccess) return e;
+    return gemm_fix(p, a, s);
+}
+
+template <int TM, int PD, int LR>
+static hipError_t gemm_i8_dispatch(dim3 grid, hipStream_t s, const GemmArgs &args)
+{
+    static std::atomic<uint64_t> lds_done{0};
+    const auto kernel = k_gemm_i8<TM, PD, LR>;
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), kRdLds, lds_done);
+    if (e != hipSuccess) return e;
+    ProfEvents &pe = prof_events();
+    if (pe.start != nullptr) {
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kRdThreads), static_cast<uint32_t>(kRdLds), s, pe.start, pe.stop, 0u,
+                              args);
+        pe = ProfEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, dim3(kRdThreads), kRdLds, s, args);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8(const GemmPlan &p, const uint8_t *xq, int64_t m, const uint8_t *w, int64_t n, float *y,
+                          const float *row_scale, float *part, hipStream_t s)
+{
+    if (n == 0 || m == 0 || p.nb == 0) return hipSuccess;
+    if (p.cfg > 1) return hipErrorInvalidValue;  // register-decode plans only (gemm_plan(..., true))
+    GemmArgs a = gemm_args(p, reinterpret_cast<const uint16_t *>(xq), m, w, n, nullptr, 0, y, nullptr, nullptr, part);
+    a.row_scale = row_scale;
+    const dim3 grid(static_cast<unsigned>(p.wgs));
+    hipError_t e;
+    if (p.cfg == 0) {
+        if (m <= 8)
+            e = gemm_i8_dispatch<1, 4, 1>(grid, s, a);
+        else if (m <= 16)
+            e = gemm_i8_dispatch<1, 4, 2>(grid, s, a);
+        else
+            e = gemm_i8_dispatch<1, 4, 4>(grid, s, a);
+    } else {
+        e = gemm_i8_dispatch<2, 4, 4>(grid, s, a);
     }
     if (e != hipSuccess) return e;
     return gemm_fix(p, a, s);

@@ -56,10 +56,11 @@ hipError_t launch_swiglu(const float *g, const float *u, float *h, int64_t len, 
 // (nmat = 1) or two sharing x (nmat = 2); x (times gain [k], if given)
 // rotated per 1024-chunk when signs != nullptr, else used as given.
 int64_t lut_nslices(int64_t k);
-// GEMM side: bf16 fragments of the per-row quantised x (integer values,
-// exact in bf16) and step[row]; then y [m][n] *= step[row].
-hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint16_t *xf, float *step, hipStream_t s);
-hipError_t launch_w2a8_scale_rows(float *y, int64_t m, int64_t n, const float *step, hipStream_t s);
+// W2A8 prefill: int8 MFMA operands of the per-row quantised x (k_prep_frag's
+// W8 layout, m_pad * k bytes) and step[row]; then Y = step[row] * sum over
+// blocks of scale * (int32 block sum), on a register-decode plan
+// (gemm_plan(m, n, k, true)).
+hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint8_t *xq, float *step, hipStream_t s);
 size_t lut_part_floats(int64_t n, int nmat, int64_t k);
 // w8: 8-bit activations (W2A8) -- signs and gain are ignored; every
 // workgroup takes max|x| itself, forms q = rint(x * float(127 / max|x|)),
@@ -110,6 +111,8 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
                        hipStream_t s);
+hipError_t launch_gemm_i8(const GemmPlan &p, const uint8_t *xq, int64_t m, const uint8_t *w, int64_t n, float *y,
+                          const float *row_scale, float *part, hipStream_t s);
 // PQ2_0: A fragments in the Q2 order (launch_prep_frag_pq2), y [m][n] =
 // A . W^T over a PQ2_0 tiled matrix; p from gemm_plan(m, n, k, true).
 hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, int64_t m, int64_t k,

@@ -961,9 +961,13 @@ def test_pq2_and_w2a8_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 300, 384), (8, 1024, 1024), (40, 200, 640), (100, 513, 1024),
-                                   (256, 1000, 2048)])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 384), (5, 128, 256), (8, 1024, 1024), (9, 260, 512), (16, 640, 1152),
+                                   (17, 300, 384), (32, 256, 256), (40, 200, 640), (64, 520, 768),
+                                   (65, 96, 1024), (100, 513, 1024), (256, 1000, 2048)])
 def test_w2a8_gemm(m, n, k):
+    """The int8-MFMA W2A8 GEMM at every row-tile shape of its plans (8-row
+    groups 1..4 of a last 32-row tile, 64-row tiles above m = 32, ragged n
+    and K) against the exact-integer oracle."""
     t, s = host_matrix(13, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
     b = oracle.pack(t, s)
     x = synth.activations(13, m, k)
