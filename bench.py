@@ -100,29 +100,85 @@ def measured_traffic():
     return int(m_val.group(1))
 
 
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+
+
 def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     """The prefill GEMM alone (for counter runs): M x 5120 activations against
-    one 17408 x 5120 PTQ1_0 matrix, --steps calls after --warmup."""
+    one 17408 x 5120 PTQ1_0 matrix, --steps calls after --warmup; --format
+    w2a8 runs the 8-bit-activation GEMM (int8 MFMA) instead."""
     m, n, k = args.gemm_only, F, D
+    w8 = args.format == "w2a8"
     w = P.ptq1_tile(P.ptq1_pack(sdev.trits(1, 1, n, k), sdev.scales(1, 2, n, k // 128)), n, k)
     x = torch.from_numpy(synth.activations(1, m, k)).to(dev)
     sg = torch.from_numpy(synth.signs(1)).to(dev)
     y = torch.empty(m, n, device=dev)
-    ws = torch.empty(P.workspace_bytes("gemm", m, n, k), dtype=torch.uint8, device=dev)
+    nws = P.lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k) if w8 else P.workspace_bytes("gemm", m, n, k)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def call():
+        if w8:
+            P.ptq1_gemm_w2a8(w, n, k, x, out=y, ws=ws)
+        else:
+            P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
+
     for _ in range(args.warmup):
-        P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
+        call()
     torch.cuda.synchronize()
     kt = P.KernelTimer("gemm", args.steps)
     with kt:
         for _ in range(args.steps):
-            P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
+            call()
     torch.cuda.synchronize()
     ms = sorted(kt.durations_ms())
     kt.close()
     us = ms[len(ms) // 2] * 1e3
     fl = 2.0 * m * n * k
-    print(json.dumps({"workload": f"prefill GEMM {m}x{k} -> {n}", "us_kernel_median": us,
-                      "TFLOP/s": fl / (us * 1e-6) / 1e12, "mfma_frac": fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}))
+    peak = INT8_PEAK_TOPS if w8 else BF16_PEAK_TFLOPS
+    print(json.dumps({"workload": f"prefill GEMM {m}x{k} -> {n} ({'int8 W2A8' if w8 else 'bf16'})",
+                      "us_kernel_median": us, "TFLOP/s": fl / (us * 1e-6) / 1e12,
+                      "mfma_frac": fl / (us * 1e-6) / 1e12 / peak}))
+    return 0
+
+
+def decode_only(args, torch, synth, sdev, P, dev) -> int:
+    """One decode matvec kind alone (for counter runs): the down projection's
+    17408 -> 5120 PTQ1_0 matrix over WEIGHT_SETS cold copies, --steps calls
+    after --warmup: 'lut' (table lookups, fp32), 'peel' (the pages' float
+    peel, eight lanes per block), 'w2a8' (8-bit activations, int32 sums)."""
+    kind = args.decode_only
+    mats = [P.ptq1_tile(P.ptq1_pack(sdev.trits(1, synth.layer_stream(synth.S_DOWN_TRITS, j), D, F),
+                                    sdev.scales(1, synth.layer_stream(synth.S_DOWN_SCALES, j), D, F // 128)), D, F)
+            for j in range(WEIGHT_SETS)]
+    h = torch.from_numpy(synth.activations(2, 1, F)[0]).to(dev)
+    sg = torch.from_numpy(synth.signs(1)).to(dev)
+    y = torch.empty(D, device=dev)
+    ws = torch.zeros(P.workspace_bytes("matvec", D, F), dtype=torch.uint8, device=dev)
+    fam = {"lut": "lut_matvec_1", "peel": "peel_matvec", "w2a8": "lut_matvec_1"}[kind]
+
+    def call(i):
+        W = mats[i % WEIGHT_SETS]
+        if kind == "lut":
+            P.ptq1_matvec(W, D, F, h, sg, out=y, ws=ws)
+        elif kind == "peel":
+            P.ptq1_matvec_float_peel(W, D, F, h, sg, out=y, ws=ws)
+        else:
+            P.ptq1_matvec_w2a8(W, D, F, h, out=y, ws=ws)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    kt = P.KernelTimer(fam, args.steps)
+    with kt:
+        for i in range(args.steps):
+            call(i)
+    torch.cuda.synchronize()
+    d = kt.durations_ms()
+    kt.close()
+    us = 1e3 * sum(d) / len(d)
+    b = packed(D, F) + 4 * F
+    print(json.dumps({"workload": f"decode matvec {F} -> {D} ({kind}), {WEIGHT_SETS} cold weight sets",
+                      "us_kernel_mean": us, "GB/s": b / (us * 1e-6) / 1e9, "frac_hbm": b / (us * 1e-6) / 8e12}))
     return 0
 
 
@@ -181,8 +237,12 @@ def main() -> int:
     ap.add_argument("--gemm-only", type=int, default=0, metavar="M",
                     help="profiling aid: run the prefill GEMM (M x 5120 -> 17408) --steps times, print its "
                          "kernel time, and exit")
-    ap.add_argument("--format", choices=("ptq1", "pq2"), default="ptq1",
-                    help="weight format of --ffn-only (PTQ1_0 or PQ2_0)")
+    ap.add_argument("--format", choices=("ptq1", "pq2", "w2a8"), default="ptq1",
+                    help="weight format of --ffn-only (PTQ1_0 or PQ2_0); w2a8 makes --gemm-only run the "
+                         "8-bit-activation GEMM")
+    ap.add_argument("--decode-only", choices=("lut", "peel", "w2a8"), default=None,
+                    help="profiling aid: run one decode matvec kind (17408 -> 5120, cold weights) --steps "
+                         "times, print its kernel time, and exit")
     ap.add_argument("--ffn-only", type=int, default=0, metavar="M",
                     help="profiling aid: replay one FFN block at batch M --steps times from a HIP graph, print "
                          "its time per layer, and exit")
@@ -205,6 +265,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     rec = receipt(torch, dev)
     stream = torch.cuda.current_stream()
+    if args.decode_only is not None:
+        return decode_only(args, torch, synth, sdev, P, dev)
     if args.gemm_only > 0:
         return gemm_only(args, torch, synth, sdev, P, dev)
     if args.ffn_only > 0:
@@ -611,24 +673,55 @@ def main() -> int:
     return 0
 
 
-def clocks():
-    """Current GPU clocks as rocm-smi reports them (an idle GPU reports its idle clock)."""
-    import subprocess
+def _drm_dir(props):
+    """The sysfs device directory of this GPU, matched on its PCI address (None if absent)."""
+    import glob
 
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30).stdout
-        card = next(iter(json.loads(out[out.index("{"):]).values()))
-        return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower()}
-    except Exception as e:  # the tool is optional on a box
-        return f"unavailable ({type(e).__name__})"
+    want = None
+    if props is not None and hasattr(props, "pci_bus_id"):
+        want = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}."
+    cards = sorted(glob.glob("/sys/class/drm/card*/device"))
+    for d in cards:
+        if want is None or os.path.basename(os.path.realpath(d)).startswith(want):
+            if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                return d
+    return None
+
+
+_PROPS = None
+
+
+def clocks():
+    """Current GPU clock levels, read from the driver's sysfs DPM tables (the
+    level marked active); read directly rather than through rocm-smi so that
+    no program is started (a child started under the profiler's preload would
+    replace itself with an interpreter after the GPU is initialised)."""
+    d = _drm_dir(_PROPS)
+    if d is None:
+        return "unavailable (no pp_dpm_* files)"
+    out = {}
+    for name in ("sclk", "mclk", "fclk", "socclk"):
+        try:
+            lines = open(os.path.join(d, f"pp_dpm_{name}")).read().splitlines()
+        except OSError:
+            continue
+        cur = [ln for ln in lines if ln.rstrip().endswith("*")]
+        out[name] = cur[0].split(":", 1)[1].strip(" *") if cur else None
+    return out
 
 
 def receipt(torch, dev):
     """Where the numbers were taken: GPU, ROCm, clocks, host CPU and load."""
-    import subprocess
-
-    props = torch.cuda.get_device_properties(dev)
-    r = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+    global _PROPS
+    props = _PROPS = torch.cuda.get_device_properties(dev)
+    name = props.name
+    d = _drm_dir(props)
+    if not name and d is not None:
+        try:
+            name = open(os.path.join(d, "product_name")).read().strip()
+        except OSError:
+            pass
+    r = {"gpu": name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
          "hbm_GiB": round(props.total_memory / 2 ** 30, 1), "hip_runtime": torch.version.hip,
          "torch": torch.__version__}
     try:
