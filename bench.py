@@ -714,11 +714,11 @@ def receipt(torch, dev):
     """Where the numbers were taken: GPU, ROCm, clocks, host CPU and load."""
     global _PROPS
     props = _PROPS = torch.cuda.get_device_properties(dev)
-    name = props.name
+    name = props.name  # the runtime's name can be generic or empty; the board's own name is preferred
     d = _drm_dir(props)
-    if not name and d is not None:
+    if d is not None:
         try:
-            name = open(os.path.join(d, "product_name")).read().strip()
+            name = open(os.path.join(d, "product_name")).read().strip() or name
         except OSError:
             pass
     r = {"gpu": name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,

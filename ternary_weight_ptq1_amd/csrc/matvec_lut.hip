@@ -20,10 +20,11 @@
 //
 // Layout on gfx950:
 //   - K is cut into slices of 2 blocks (256 weights, 56 bytes per row); the
-//     table of a slice is 56 slots x 256 fp32 in one 64 KB bank-interleaved
-//     array, entry address = b << 8 | slot << 2, so one v_perm_b32
-//     assembles the address from the data byte and a per-lane constant byte;
-//     slots 26, 27 of each block (the scale bytes) hold zeros; at 64 KB, two
+//     table of a slice has 64 columns (32 per block: byte positions 0..25
+//     are the trit bytes, 26..31 columns of zeros) x 256 byte values, fp32,
+//     in one 64 KB array, entry address = b << 8 | column << 2, so an
+//     entry's LDS bank is its column and one v_perm_b32 assembles the
+//     address from the data byte and a per-lane constant byte; at 64 KB, two
 //     workgroups share a CU, so one's latency-bound phases (rotation, table
 //     build) overlap the other's lookups;
 //   - weights are read in the tiled layout: the 32 rows x 2 blocks of a unit
@@ -42,14 +43,10 @@
 //     grid fits two workgroups per CU) with kLutDepth units of weights in
 //     flight (one requested before x, so that x is not queued behind a
 //     chip-wide burst of weight requests); a lane reads its 28-byte block
-//     with two wide loads and rotates its 7 dwords (and the byte order within
-//     a dword) by a lane-dependent amount so the 32 lanes of a half-wave
-//     (16 rows x 2 blocks) spread over LDS banks.  With per-lane dword
-//     rotations every lookup still meets a 2-way bank conflict (at most one
-//     of a lane's seven dword positions can be conflict-free: the two
-//     blocks' 56 slots share 32 banks); general per-lane permutations would
-//     avoid a third of the conflicts but cost more in loads or VALU moves
-//     than they save, so rotations stay;
+//     with two wide loads and rotates its 8 dwords (the 7 of the block and a
+//     zero) and the byte order within a dword by lane-dependent amounts
+//     (lut_rho, lut_sig), so that the 64 lanes of every lookup read 64
+//     different columns: no LDS bank conflicts;
 //   - a unit's 2 block partials (times their fp16 scales) are summed across
 //     neighbouring lanes (one DPP move) and stored as split-K partials
 //     part[slice][matrix][row]; a second kernel sums each row's partials in
