@@ -348,10 +348,10 @@ ptq1_status ptq1_matvec_w2a8(const uint8_t *tiled, int64_t n, int64_t k, const f
                              float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Prefill GEMM with 8-bit activations: each row of X [m][k] quantised as in
- * ptq1_matvec_w2a8 (its own absmax and step), the integer-valued rows fed
- * to the bf16 MFMA GEMM (exact in bf16; every per-block sum is an integer
- * below 2^24, so the fp32 accumulation of a block is exact), each block
- * scaled by its fp16 scale in fp32, and row i of Y multiplied by its step:
+ * ptq1_matvec_w2a8 (its own absmax and step), the int8 rows multiplied with
+ * the trits as int8 on the matrix cores (every 128-weight block summed
+ * exactly in int32), each block sum scaled by its fp16 scale in fp32, and
+ * row i of Y multiplied by its step:
  *   Y[i][r] = step_i * sum_b s_rb * sum_{c in b} t_rc q_ic.
  * X is used as given (no rotation).  Limits and errors as ptq1_gemm. */
 size_t ptq1_gemm_w2a8_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -105,12 +105,16 @@ size_t gemm_part_floats(const GemmPlan &p);            // partial tiles of the w
 // instead of x, the input is silu(g) * u (gain unused).
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
                             const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s);
-// y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; rows of the
-// virtual matrix as in launch_matvec_part, the second matrix's outputs in
-// y1 [m][n1].  part: gemm_part_floats(p) floats of scratch.
+// y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; the rows of
+// the virtual matrix are w0's n0 rows, then w1's n1 rows (gate and up stacked),
+// the first matrix's outputs in y0 [m][n0], the second's in y1 [m][n1].
+// part: gemm_part_floats(p) floats of scratch.
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
                        hipStream_t s);
+// W2A8: y [m][n] = row_scale[row] * sum_b scale_b * (int32 block sum of
+// trits x q), q the int8 activations of launch_prep_frag_w8 (their layout),
+// W tiled; p from gemm_plan(m, n, k, true).
 hipError_t launch_gemm_i8(const GemmPlan &p, const uint8_t *xq, int64_t m, const uint8_t *w, int64_t n, float *y,
                           const float *row_scale, float *part, hipStream_t s);
 // PQ2_0: A fragments in the Q2 order (launch_prep_frag_pq2), y [m][n] =
