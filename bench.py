@@ -34,6 +34,9 @@ receipt: GPU, ROCm, clocks, host CPU and load average.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
                     [--copy-calibration]
+    python bench.py --gemm-only M [--format ptq1|pq2|w2a8]   (one GEMM kind, for profilers)
+    python bench.py --ffn-only M [--format ptq1|pq2]         (one FFN block, HIP graph)
+    python bench.py --decode-only lut|peel|w2a8              (one decode matvec kind)
 """
 from __future__ import annotations
 
