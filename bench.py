@@ -109,19 +109,25 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     """The prefill GEMM alone (for counter runs): M x 5120 activations against
     one 17408 x 5120 PTQ1_0 matrix, --steps calls after --warmup; --format
-    w2a8 runs the 8-bit-activation GEMM (int8 MFMA) instead."""
+    w2a8 runs the 8-bit-activation GEMM (int8 MFMA) instead, --format pq2 the
+    same matrix in PQ2_0."""
     m, n, k = args.gemm_only, F, D
     w8 = args.format == "w2a8"
-    w = P.ptq1_tile(P.ptq1_pack(sdev.trits(1, 1, n, k), sdev.scales(1, 2, n, k // 128)), n, k)
+    q2 = args.format == "pq2"
+    pack, tile = (P.pq2_pack, P.pq2_tile) if q2 else (P.ptq1_pack, P.ptq1_tile)
+    w = tile(pack(sdev.trits(1, 1, n, k), sdev.scales(1, 2, n, k // 128)), n, k)
     x = torch.from_numpy(synth.activations(1, m, k)).to(dev)
     sg = torch.from_numpy(synth.signs(1)).to(dev)
     y = torch.empty(m, n, device=dev)
-    nws = P.lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k) if w8 else P.workspace_bytes("gemm", m, n, k)
+    nws = (P.lib().ptq1_gemm_w2a8_workspace_bytes(m, n, k) if w8 else
+           P.workspace_bytes("pq2_gemm", m, n, k) if q2 else P.workspace_bytes("gemm", m, n, k))
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
 
     def call():
         if w8:
             P.ptq1_gemm_w2a8(w, n, k, x, out=y, ws=ws)
+        elif q2:
+            P.pq2_gemm(w, n, k, x, sg, out=y, ws=ws)
         else:
             P.ptq1_gemm(w, n, k, x, sg, out=y, ws=ws)
 
@@ -138,7 +144,7 @@ def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     us = ms[len(ms) // 2] * 1e3
     fl = 2.0 * m * n * k
     peak = INT8_PEAK_TOPS if w8 else BF16_PEAK_TFLOPS
-    print(json.dumps({"workload": f"prefill GEMM {m}x{k} -> {n} ({'int8 W2A8' if w8 else 'bf16'})",
+    print(json.dumps({"workload": f"prefill GEMM {m}x{k} -> {n} ({'int8 W2A8' if w8 else 'bf16, PQ2_0' if q2 else 'bf16'})",
                       "us_kernel_median": us, "TFLOP/s": fl / (us * 1e-6) / 1e12,
                       "mfma_frac": fl / (us * 1e-6) / 1e12 / peak}))
     return 0
@@ -241,8 +247,8 @@ def main() -> int:
                     help="profiling aid: run the prefill GEMM (M x 5120 -> 17408) --steps times, print its "
                          "kernel time, and exit")
     ap.add_argument("--format", choices=("ptq1", "pq2", "w2a8"), default="ptq1",
-                    help="weight format of --ffn-only (PTQ1_0 or PQ2_0); w2a8 makes --gemm-only run the "
-                         "8-bit-activation GEMM")
+                    help="weight format of --gemm-only and --ffn-only (PTQ1_0 or PQ2_0); w2a8 makes "
+                         "--gemm-only run the 8-bit-activation GEMM (there is no W2A8 FFN block)")
     ap.add_argument("--decode-only", choices=("lut", "peel", "w2a8"), default=None,
                     help="profiling aid: run one decode matvec kind (17408 -> 5120, cold weights) --steps "
                          "times, print its kernel time, and exit")
@@ -250,6 +256,9 @@ def main() -> int:
                     help="profiling aid: replay one FFN block at batch M --steps times from a HIP graph, print "
                          "its time per layer, and exit")
     args = ap.parse_args()
+    if args.ffn_only > 0 and args.format == "w2a8":
+        print("--ffn-only takes --format ptq1 or pq2 (there is no W2A8 FFN block)", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sharded path is a "
               "design note, not built", file=sys.stderr)
