@@ -384,6 +384,10 @@ def main() -> int:
     assert len(d_gu) == args.steps and len(d_dn) == args.steps, "one gate+up and one down launch per step"
     us_gu = 1e3 * sum(d_gu) / len(d_gu)
     us_dn = 1e3 * sum(d_dn) / len(d_dn)
+
+    def spread(d):  # median, min and max of the per-launch event durations (us)
+        v = sorted(1e3 * t for t in d)
+        return {"median": round(v[len(v) // 2], 3), "min": round(v[0], 3), "max": round(v[-1], 3)}
     lut_gu_gbs = LUT_GATE_UP_BYTES / (us_gu * 1e-6) / 1e9
     lut_dn_gbs = LUT_DOWN_BYTES / (us_dn * 1e-6) / 1e9
 
@@ -401,8 +405,10 @@ def main() -> int:
     gu_gbs = GATE_UP_BYTES / (ms_gu * 1e-3) / 1e9
 
     breakdown = {"step_eager_with_kernel_events_us": ms_step_eager_profiled * 1e3,
-                 "lut_kernel_gate_up_in_step": {"us": us_gu, "GB/s": lut_gu_gbs, "bytes": LUT_GATE_UP_BYTES},
-                 "lut_kernel_down_in_step": {"us": us_dn, "GB/s": lut_dn_gbs, "bytes": LUT_DOWN_BYTES},
+                 "lut_kernel_gate_up_in_step": dict({"us": us_gu, "GB/s": lut_gu_gbs, "bytes": LUT_GATE_UP_BYTES},
+                                                    **spread(d_gu)),
+                 "lut_kernel_down_in_step": dict({"us": us_dn, "GB/s": lut_dn_gbs, "bytes": LUT_DOWN_BYTES},
+                                                 **spread(d_dn)),
                  "gate_up_call_cold": {"us": ms_gu * 1e3, "GB/s": gu_gbs, "bytes": GATE_UP_BYTES}}
     if not args.quick:
         log("bench: breakdown")
@@ -650,6 +656,7 @@ def main() -> int:
         cpu = cpu_baseline(torch, dev, None if args.quick else stack_out)
         if "stack_64_vs_oracle" in cpu:
             breakdown.setdefault("ffn_stack_64", {})["rel_l2_vs_oracle"] = cpu["stack_64_vs_oracle"]
+        cpu["gpu_over_oracle"] = gpu_over_oracle(gbs, breakdown, cpu)
     load_end = os.getloadavg()
 
     line = {
@@ -753,6 +760,25 @@ def receipt(torch, dev):
     r["host_logical_cpus"] = os.cpu_count()
     r["host_cpus_usable"] = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     r["loadavg_start"] = [round(v, 2) for v in os.getloadavg()]
+    return r
+
+
+def gpu_over_oracle(step_gbs, breakdown, cpu):
+    """The GPU's rate over the oracle's on each configuration both measured
+    (same units: bytes, flops or layers per second)."""
+    cfg = cpu.get("configs", {})
+    r = {"decode_step": round(step_gbs / cpu["value"], 1)}
+    if "matvec_1024_hot" in breakdown and "matvec_1024" in cfg:
+        gpu = (packed(1024, 1024) + 8 * 1024) / (breakdown["matvec_1024_hot"]["us"] * 1e-6) / 1e9
+        r["matvec_1024"] = round(gpu / cfg["matvec_1024"]["GB/s"], 1)
+    for m in (128, 256, 512):
+        g = breakdown.get("prefill_gemm", {}).get(f"M{m}")
+        if g and f"gemm_M{m}" in cfg:
+            r[f"gemm_M{m}"] = round(1e3 * g["TFLOP/s"] / cfg[f"gemm_M{m}"]["GFLOP/s"], 1)
+    for m in (1, 8):
+        g = breakdown.get("ffn_stack_64", {}).get(f"M{m}")
+        if g and f"ffn_layer_M{m}" in cfg:
+            r[f"ffn_layer_M{m}"] = round(g["layers_per_s"] / cfg[f"ffn_layer_M{m}"]["layers/s"], 1)
     return r
 
 
