@@ -11,7 +11,7 @@ Infinity Cache) so every step streams its 58.5 MB of PTQ1_0 blocks from HBM.
 value = algorithmic bytes per step / step time (decode matvec GB/s).
 
 The timed steps replay HIP graphs of the step (the step is five dependent
-kernels of about 40 us in all, so eager launches leave the GPU waiting on
+kernels, about 30 us in all, so eager launches leave the GPU waiting on
 the host).
 
 roofline: the dominant kernel, the table-lookup matvec over gate and up
@@ -331,7 +331,7 @@ def main() -> int:
     for i in range(args.warmup):  # eager warm-up (also settles per-kernel launch attributes)
         step(i)
     torch.cuda.synchronize()
-    # The step is launch-bound (five dependent kernels, about 40 us), so the
+    # The step is launch-bound (five dependent kernels, about 30 us), so the
     # timed steps replay HIP graphs: one of WEIGHT_SETS steps (a pass over
     # every weight set) and one of the remainder, so that exactly K steps run.
     graphs = []
