@@ -167,8 +167,13 @@ ptq1_status hadamard_unrotate_rows(const float *table, int64_t n_table, int64_t 
  *   tiled   [n][k] in the tiled layout; x fp32 [k]; residual fp32 [n] or
  *   NULL; y fp32 [n] (y may equal residual, must not overlap x or tiled).
  * Trits are decoded through a per-slice table of byte-position x byte-value
- * partial dot products built from xr, fp32 throughout; two launches (split-K
- * partials over 256-wide K-slices, then their sum in slice order).
+ * partial dot products built from xr in 32-bit fixed point: each 256-wide
+ * K-slice of xr is scaled by its own power of two so that max|xr| lies in
+ * [2^22, 2^23) and rounded to integers once (an error of at most 2^-24 of the
+ * slice's max|xr| per element); table entries and each block's sum are exact
+ * int32, the block sum is scaled by its fp16 scale in fp32 and the rest is
+ * fp32.  A NaN or an infinity in xr makes every output a NaN.  Two launches
+ * (split-K partials per slice, then their sum in slice order).
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_matvec_workspace_bytes(int64_t n, int64_t k);
 ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
@@ -179,7 +184,9 @@ ptq1_status ptq1_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float 
  * describes ("What Ferrox does with it": eight lanes share one 128-weight
  * block, each lane owns whole bytes, and a trit is floor(3^(n+1) u) -
  * 3 floor(3^n u), u = byte/256).  Same tiled matrix, results (to rounding
- * order), workspace size and errors as ptq1_matvec; kept as the page's own
+ * order and ptq1_matvec's fixed-point rounding of xr), workspace size and
+ * errors as ptq1_matvec (its sums are fp32, so a NaN or an infinity
+ * propagates as the float operations make it); kept as the page's own
  * decode, to be measured beside the table lookups. */
 ptq1_status ptq1_matvec_float_peel(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                                    const float *signs1024, const float *residual, float *y, void *ws,
@@ -189,7 +196,8 @@ ptq1_status ptq1_matvec_float_peel(const uint8_t *tiled, int64_t n, int64_t k, c
  * input ("Speed, and where it goes": paired projections fused into one GPU
  * submission).
  *   w_gate, w_up  tiled [f][d]; x fp32 [d]; g, u fp32 [f]:
- *   g = W_gate R x, u = W_up R x (R skipped when signs1024 == NULL).
+ *   g = W_gate R x, u = W_up R x (R skipped when signs1024 == NULL), with
+ * the table lookups and numerics of ptq1_matvec.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE. */
 size_t ptq1_gate_up_workspace_bytes(int64_t f, int64_t d);
 ptq1_status ptq1_gate_up(const uint8_t *w_gate, const uint8_t *w_up, int64_t f, int64_t d,
@@ -223,7 +231,8 @@ ptq1_status ptq1_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x
  *   g, u  = W_gate R xn, W_up R xn                (W_gate, W_up tiled [f][d])
  *   h     = silu(g) * u
  *   x_out = x + W_down R h                        (W_down tiled [d][f])
- * m == 1 runs the fp32 matvec path, m >= 2 the bf16-MFMA GEMM path.
+ * m == 1 runs the table-lookup matvec path (numerics of ptq1_matvec), m >= 2
+ * the bf16-MFMA GEMM path.
  * d % 1024 == 0, f % 1024 == 0; x_out may equal x; rms_gain, if given, is
  * 16-byte aligned and overlaps neither x_out nor ws.
  * Errors: NULL, SHAPE, ALIGN, ALIAS, OVERFLOW, WORKSPACE, UNSUPPORTED. */
@@ -321,7 +330,8 @@ ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                      float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The feed-forward block of ptq1_ffn_block over PQ2_0 tiled matrices: the
- * same arguments, numerics (m = 1: fp32 table lookups; m >= 2: bf16 MFMA),
+ * same arguments, numerics (m = 1: fp32 table lookups of that format;
+ * m >= 2: bf16 MFMA),
  * workspace rule and errors; every matrix must be below 2 GiB at m = 1. */
 size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
 ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f, const uint8_t *w_gate,

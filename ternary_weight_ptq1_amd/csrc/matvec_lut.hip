@@ -10,20 +10,24 @@
 // per weight an HBM-bound matvec can afford at 8 TB/s.  Instead, since every
 // row shares the same activation vector:
 //
-//   T[slot][b] = sum_n (digit_n(b) - 1) * xr[k(slot, n)]
+//   T[slot][b] = sum_n (digit_n(b) - 1) * q[k(slot, n)]
 //
 // is tabulated once per workgroup for each byte position (slot) of a 2-block
-// K-slice and each of the 256 byte values b.  A row's slice dot product is
-// then sum_blocks scale * sum_slots T[slot][byte], one LDS lookup and one
-// add per five weights.  Digits are decoded once per (slot, b) entry, not
-// per weight.
+// K-slice and each of the 256 byte values b, where q = rint(xr 2^e) holds the
+// slice's rotated activations in 32-bit fixed point (one power of two 2^e
+// per slice, |q| < 2^23).  A row's slice dot product is then
+// 2^-e sum_blocks scale * sum_slots T[slot][byte]: one LDS lookup per five
+// weights and one integer add (v_add3_u32) per two lookups, the block sums
+// exact in int32.  Digits are decoded once per (slot, b) entry, not per
+// weight.  The one rounding beyond fp32 is that of xr to q, at most 2^-24
+// of the slice's max|xr| per element.
 //
 // Layout on gfx950:
 //   - K is cut into slices of 2 blocks (256 weights, 56 bytes per row); the
 //     table of a slice has 64 columns (32 per block: byte positions 0..25
-//     are the trit bytes, 26..31 columns of zeros) x 256 byte values, fp32,
+//     are the trit bytes, 26..31 columns of zeros) x 256 byte values, int32,
 //     in one 64 KB array, entry address = b << 8 | column << 2, so an
-//     entry's LDS bank is its column and one v_perm_b32 assembles the
+//     entry's LDS bank is its column mod 32 and one v_perm_b32 assembles the
 //     address from the data byte and a per-lane constant byte; at 64 KB, two
 //     workgroups share a CU, so one's latency-bound phases (rotation, table
 //     build) overlap the other's lookups;
@@ -45,8 +49,9 @@
 //     chip-wide burst of weight requests); a lane reads its 28-byte block
 //     with two wide loads and rotates its 8 dwords (the 7 of the block and a
 //     zero) and the byte order within a dword by lane-dependent amounts
-//     (lut_rho, lut_sig), so that the 64 lanes of every lookup read 64
-//     different columns: no LDS bank conflicts;
+//     (lut_rho, lut_sig), which with block 1's columns shifted by 16 banks
+//     makes the 32 lanes of every half-wave lookup read 32 different banks:
+//     no LDS bank conflicts;
 //   - a unit's 2 block partials (times their fp16 scales) are summed across
 //     neighbouring lanes (one DPP move) and stored as split-K partials
 //     part[slice][matrix][row]; a second kernel sums each row's partials in
@@ -88,24 +93,24 @@ static_assert(kLutRows == kTileRows && kLutBlocks == kTileBlocks, "a unit is one
 static_assert(kLutRows * kLutBlocks == kWave, "one block per lane");
 
 // Table columns: byte position p (0..31) of block b of the slice is column
-// 32 b + p.  Positions 0..25 are the trit bytes; 26, 27 (the scale) and
-// 28..31 (past the block) are columns of zeros.  Entry (column, byte value v)
-// sits at byte v * 256 + column * 4, so its LDS bank is the column.
+// 32 b + (p + 16 b) mod 32.  Positions 0..25 are the trit bytes; 26, 27 (the
+// scale) and 28..31 (past the block) are columns of zeros.  Entry (column,
+// byte value v) sits at byte v * 256 + column * 4, so its LDS bank (32 banks
+// of 4 bytes) is p for block 0 and p + 16 mod 32 for block 1.
 constexpr int kLutColsPerBlock = 32;
 constexpr int kLutDwords = kLutColsPerBlock / 4;  // 8 dword positions per block, 7 of them in memory
 static_assert(kLutBlocks * kLutColsPerBlock * 256 * 4 == 65536, "the table fills 64 KB");
 
 // Lane 2i + b (row i, block b of a tile) holds in register r dword
-// (r + rho) mod 8 of its block and reads byte (c + sig) mod 4 of it at step
-// c, i.e. column 32 b + 4 ((r + rho) mod 8) + (c + sig) mod 4, with
-// rho = (4 b + i / 4) mod 8 and sig = i mod 4.  At every step the 32 lanes of
-// a block then read 32 different columns, and in each half-wave (rows 0..15
-// or 16..31) the block-0 lanes cover four dword positions and the block-1
-// lanes the other four: no two lanes of a wave, or of a half-wave, share an
-// LDS bank.  (Rotating through the loads instead -- four 8-byte loads per
-// block at lane-dependent offsets -- measured no faster than two wide loads
-// and three rounds of selects.)
-__device__ __forceinline__ int lut_rho(int lane) { return (4 * (lane & 1) + (lane >> 3)) & 7; }
+// q = (r + rho) mod 8 of its block and reads byte (c + sig) mod 4 of it at
+// step c, with rho = (i / 4) mod 4 and sig = i mod 4: in a half-wave (rows
+// 0..15 or 16..31, which the LDS serves in one pass) the 16 lanes of a block
+// hold the 16 pairs (rho, sig), so at step (r, c) block 0 reads the 16 banks
+// of dword positions r .. r + 3 (mod 8) and block 1, its columns shifted by
+// 16 banks, the other 16: no two lanes of a half-wave share a bank.  The
+// shift puts half of the spread into the table's layout, so the data is
+// rotated by 0..3 dwords (two rounds of selects) instead of 0..7.
+__device__ __forceinline__ int lut_rho(int lane) { return (lane >> 3) & 3; }
 __device__ __forceinline__ int lut_sig(int lane) { return (lane >> 1) & 3; }
 
 struct LutArgs {
@@ -222,9 +227,10 @@ __device__ __forceinline__ void slice_x_load(const float *x, const float *signs,
     }
 }
 
-// xs[0..256) = the slice of R (gain * x) (or of gain * x when signs == nullptr)
-__device__ __forceinline__ void slice_x_store(const SliceX &v, bool rotate, bool gained, int64_t k0, int kw, int lane,
-                                              float *xs)
+// This lane's four values of the slice of R (gain * x) (or of gain * x when
+// signs == nullptr), elements 4 lane .. 4 lane + 3.
+__device__ __forceinline__ lut_f32x4 slice_x_values(const SliceX &v, bool rotate, bool gained, int64_t k0, int kw,
+                                                    int lane)
 {
     lut_f32x4 out;
     if (rotate) {
@@ -246,7 +252,59 @@ __device__ __forceinline__ void slice_x_store(const SliceX &v, bool rotate, bool
         for (int k = 0; k < 4; ++k)
             out[k] = 4 * lane + k < kw ? (gained ? v.x[0][k] * v.g[0][k] : v.x[0][k]) : 0.0f;
     }
-    *reinterpret_cast<lut_f32x4 *>(xs + 4 * lane) = out;
+    return out;
+}
+
+// xs[0..256) = the slice (see slice_x_values), fp32
+__device__ __forceinline__ void slice_x_store(const SliceX &v, bool rotate, bool gained, int64_t k0, int kw, int lane,
+                                              float *xs)
+{
+    *reinterpret_cast<lut_f32x4 *>(xs + 4 * lane) = slice_x_values(v, rotate, gained, k0, kw, lane);
+}
+
+// The slice in 32-bit fixed point, one power of two per slice: with
+// max |x| = f 2^E (f in [0.5, 1); E = 0 for an all-zero slice) and e = 23 - E,
+// q = rint(x 2^e) is exact scaling followed by one rounding to the nearest
+// integer, |q| <= 2^23, and any sum of a block's 26 table entries (each a sum
+// of five +-q) stays below 130 * 2^23 < 2^31.  xs[0..256) receives q as
+// int32, ex[0] the exponent e and ex[1] the slice's factor: 1, or a NaN when
+// the slice holds a NaN or an infinity (whose products a fixed-point sum
+// cannot carry; every output the slice feeds then becomes a NaN).
+__device__ __forceinline__ void slice_x_store_fixed(const lut_f32x4 &v, int lane, float *xs, float *ex)
+{
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    const bool bad = !(__builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) && __builtin_isfinite(v[2]) &&
+                       __builtin_isfinite(v[3]));
+    const bool any_bad = __ballot(bad) != 0;  // wave-uniform
+    {  // max over the wave: quad permutations, row rotations, then the 16- and 32-lane swaps
+        int im = __builtin_bit_cast(int, m);
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0xB1, 0xF, 0xF, false)));
+        im = __builtin_bit_cast(int, m);
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x4E, 0xF, 0xF, false)));
+        im = __builtin_bit_cast(int, m);
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x124, 0xF, 0xF, false)));
+        im = __builtin_bit_cast(int, m);
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x128, 0xF, 0xF, false)));
+        const uint32_t u16 = __builtin_bit_cast(uint32_t, m);
+        const auto r16 = __builtin_amdgcn_permlane16_swap(u16, u16, false, false);
+        const uint32_t a0 = r16[0], a1 = r16[1];
+        m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+        const uint32_t u32 = __builtin_bit_cast(uint32_t, m);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(u32, u32, false, false);
+        const uint32_t b0 = r32[0], b1 = r32[1];
+        m = fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+    }
+    int E = 0;
+    (void)frexpf(any_bad ? 0.0f : m, &E);
+    const int e = 23 - E;
+    int32_t q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = any_bad ? 0 : static_cast<int32_t>(rintf(ldexpf(v[k], e)));
+    *reinterpret_cast<int4 *>(xs + 4 * lane) = make_int4(q[0], q[1], q[2], q[3]);
+    if (lane == 0) {
+        reinterpret_cast<int32_t *>(ex)[0] = e;
+        ex[1] = any_bad ? __builtin_nanf("") : 1.0f;
+    }
 }
 
 // T[slot][b] for b in [32 BQ, 32 BQ + 32): with v = floor(243 b / 256) the
@@ -365,28 +423,31 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     // zero dword (position 7 of the block, whose columns are zeros).
     uint32_t dat[U][kLutDwords];
     uint32_t scb[U];
-    auto unit_of = [&](int i) { return u0 + wave + static_cast<int64_t>(kLutWaves) * i; };
+    // Unit indices, tile bases and row bases are wave-uniform (scalar
+    // registers); a lane adds a 32-bit offset of its own (saddr + voffset
+    // addressing, no per-unit vector address arithmetic).
+    auto unit_of = [&](int i) { return static_cast<int>(u0) + wave + kLutWaves * i; };
+    const uint32_t lane_off = static_cast<uint32_t>(lane * kBlockBytes);
     auto issue = [&](int i) {
-        const int64_t un = unit_of(i) < u1 ? unit_of(i) : u1 - 1;  // clamped: no branch
+        const int un = unit_of(i) < u1 ? unit_of(i) : static_cast<int>(u1) - 1;  // clamped: no branch
         const LutUnit u = lut_unit(a, un);
         // tiled matrices are below 2 GiB (checked by the caller)
-        const uint8_t *blk = (u.mat ? a.w1 : a.w0) +
-                             (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
-                              static_cast<uint32_t>(u.grp)) * static_cast<uint32_t>(kTileBytes) +
-                             static_cast<uint32_t>(lane * kBlockBytes);
-        const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(blk);
-        const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(blk + 16);
+        const uint8_t *tile = (u.mat ? a.w1 : a.w0) +
+                              (static_cast<uint32_t>(s) * static_cast<uint32_t>(a.groups) +
+                               static_cast<uint32_t>(u.grp)) * static_cast<uint32_t>(kTileBytes);
+        const lut_u32x4 lo = *reinterpret_cast<const lut_u32x4 *>(tile + lane_off);
+        const lut_u32x3 hi = *reinterpret_cast<const lut_u32x3 *>(tile + (lane_off + 16u));
         dat[i][0] = lo.x; dat[i][1] = lo.y; dat[i][2] = lo.z; dat[i][3] = lo.w;
         dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z; dat[i][7] = 0u;
     };
     // the scale (the block's upper half dword 6) is kept, then register r
-    // receives dword (r + rho) mod 8: rotations by 1, 2 and 4 merged with a
+    // receives dword (r + rho) mod 8: rotations by 1 and 2 merged with a
     // lane mask (a select of array elements would become a dynamically
     // indexed, private-memory array)
     auto rotate = [&](int i) {
         scb[i] = dat[i][6] >> 16;
 #pragma unroll
-        for (int sh = 1; sh <= 4; sh <<= 1) {
+        for (int sh = 1; sh <= 2; sh <<= 1) {
             const uint32_t m = (rho & sh) ? 0xffffffffu : 0u;
             uint32_t t[kLutDwords];
 #pragma unroll
@@ -419,7 +480,7 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     }
 #pragma unroll
     for (int r = 0; r < kLutDwords; ++r) {
-        const int q = (r + rho) & (kLutDwords - 1);
+        const int q = (r + rho + 4 * blk_l) & (kLutDwords - 1);  // bank group of dword (r + rho) mod 8
         const uint32_t base = static_cast<uint32_t>(kLutColsPerBlock * blk_l + 4 * q) << 2;
         P[r] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;  // base in all four bytes
     }
@@ -431,12 +492,14 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. x for this slice (rotated when signs are given: k % 1024 == 0);
-    // W8: the workgroup's max|x| first, then q = rint(x c) (integers in
-    // [-127, 127], held as int32 in xs)
+    // ---- 3. x for this slice as int32 q in xs: rotated when signs are
+    // given (k % 1024 == 0) and held in fixed point with the slice's power of
+    // two 2^-ex; W8: the workgroup's max|x| first, then q = rint(x c)
+    // (integers in [-127, 127]) and the step max|x| / 127
+    float *red = xs + kLutSliceW;  // kLutWaves floats after the slice
     float step = 1.0f;
+    int ex = 0;
     if constexpr (W8) {
-        float *red = xs + kLutSliceW;  // kLutWaves floats after the slice
 #pragma unroll
         for (int h = kWave / 2; h > 0; h >>= 1) amax = fmaxf(amax, __shfl_xor(amax, h, kWave));
         if (lane == 0) red[wave] = amax;
@@ -456,9 +519,15 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
             *reinterpret_cast<int4 *>(xs + 4 * lane) = make_int4(qv[0], qv[1], qv[2], qv[3]);
         }
     } else {
-        if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
+        if (wave == 0)
+            slice_x_store_fixed(slice_x_values(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane), lane, xs,
+                                red);
     }
     __syncthreads();
+    if constexpr (!W8) {
+        ex = reinterpret_cast<const int32_t *>(red)[0];
+        step = red[1];
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = kLutEarly; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);  // in flight during the build
@@ -467,74 +536,55 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     {
         const int bq = tid >> 6;  // 0 .. kLutBuildRanges - 1
         const int col = tid & 63;
-        const int blk = col / kLutColsPerBlock, i = col % kLutColsPerBlock;
-        if constexpr (W8) {
-            const int32_t *xq = reinterpret_cast<const int32_t *>(xs);
-            int32_t xv5[5];
+        const int blk = col / kLutColsPerBlock;
+        const int i = (col - 16 * blk) & (kLutColsPerBlock - 1);  // byte position of this column
+        const int32_t *xq = reinterpret_cast<const int32_t *>(xs);
+        int32_t xv5[5];
 #pragma unroll
-            for (int n = 0; n < 5; ++n) {
-                const int j = kTritsPerByte * i + n;
-                xv5[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xq[blk * kBlockWeights + j] : 0;
-            }
-            lut_build_dispatch<0, int32_t>(bq, tab, col, xv5);
-        } else {
-            float xv5[5];
-#pragma unroll
-            for (int n = 0; n < 5; ++n) {
-                const int j = kTritsPerByte * i + n;  // weight index in the block
-                xv5[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xs[blk * kBlockWeights + j] : 0.0f;
-            }
-            lut_build_dispatch<0, float>(bq, tab, col, xv5);
+        for (int n = 0; n < 5; ++n) {
+            const int j = kTritsPerByte * i + n;  // weight index in the block
+            xv5[n] = (blk < nblk && i < kTritBytes && j < kBlockWeights) ? xq[blk * kBlockWeights + j] : 0;
         }
+        lut_build_dispatch<0, int32_t>(bq, tab, col, xv5);
     }
     rotate(0);
     __syncthreads();
 
-    // ---- 5. lookups, scale, 2-lane reduction, partial store
-    typedef __attribute__((address_space(3))) const float lds_f32;
+    // ---- 5. lookups (exact int32 sums, two lookups per v_add3_u32), scale,
+    // 2-lane reduction, partial store
+    typedef __attribute__((address_space(3))) const int32_t lds_i32;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         if (i + kLutDepth < U) issue(i + kLutDepth);  // compile-time condition
         if (i > 0) rotate(i);
         const bool unit_ok = unit_of(i) < u1;  // wave-uniform
-        const int64_t un = unit_ok ? unit_of(i) : u1 - 1;
+        const int un = unit_ok ? unit_of(i) : static_cast<int>(u1) - 1;
         const LutUnit u = lut_unit(a, un);
-        const int r = u.grp * kLutRows + row_l;
-        const bool live = unit_ok && r < a.n && blk_l < nblk;  // padding rows / blocks contribute nothing
+        const int n = static_cast<int>(a.n);  // rows < 2^20 (checked by the caller)
+        const int r0 = u.grp * kLutRows;      // wave-uniform
+        const int r = r0 + row_l;
+        const bool live = unit_ok && r < n && blk_l < nblk;  // padding rows / blocks contribute nothing
         const float scale = live ? half_bits_to_float(scb[i]) : 0.0f;
-        float p;
-        if constexpr (W8) {
-            // exact int32 sums; two lookups per add (v_add3_u32)
-            typedef __attribute__((address_space(3))) const int32_t lds_i32;
-            int32_t acc = 0;
+        int32_t acc = 0;
 #pragma unroll
-            for (int j = 0; j < kLutDwords; ++j) {
+        for (int j = 0; j < kLutDwords; ++j) {
 #pragma unroll
-                for (int c = 0; c < 4; c += 2) {
-                    const uint32_t a0 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
-                    const uint32_t a1 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c + 1]);
-                    acc = acc + *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a0)) +
-                          *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a1));
-                }
+            for (int c = 0; c < 4; c += 2) {
+                const uint32_t a0 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
+                const uint32_t a1 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c + 1]);
+                acc = acc + *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a0)) +
+                      *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a1));
             }
-            p = static_cast<float>(acc) * scale;  // |acc| <= 26 * 635 < 2^24: exact in fp32
-        } else {
-            float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kLutDwords; ++j) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
-                    const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
-                    if ((c & 1) == 0) acc0 += t; else acc1 += t;
-                }
-            }
-            p = (acc0 + acc1) * scale;
         }
+        // W8: |acc| <= 26 * 635 < 2^24, exact in fp32; otherwise |acc| < 2^31
+        // and the conversion rounds once
+        float p = static_cast<float>(acc) * scale;
         const int ip = __builtin_bit_cast(int, p);
         p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
-        if (W8) p *= step;
-        if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r] = p;
+        if constexpr (!W8) p = ldexpf(p, -ex);
+        p *= step;
+        float *prow = a.part + ((static_cast<int64_t>(s) * a.nmat + u.mat) * a.n + r0);  // wave-uniform
+        if (unit_ok && blk_l == 0 && r < n) prow[row_l] = p;
     }
 }
 

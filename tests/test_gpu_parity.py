@@ -285,6 +285,15 @@ def test_matvec_residual_and_special_cases(fn):
     b2 = oracle.pack(t, s2)
     got2 = host(mv(mv_weights(fn, b2, n, k), n, k, to_dev(x), None))
     assert rel_l2(got2, oracle.matvec(b2, n, k, x)) <= TOL_FP32
+    # a NaN or an infinity in x reaches every output, rotated or not (never
+    # a finite value: the lookup kernel sums in fixed point and marks a slice
+    # holding a non-finite value)
+    for bad in (np.nan, np.inf):
+        xb = x.copy()
+        xb[5] = bad
+        for sgn in (to_dev(sg), None):
+            gb = host(mv(mv_weights(fn, b, n, k), n, k, to_dev(xb), sgn))
+            assert not np.isfinite(gb).any()
 
 
 def test_shared_workspace_across_calls():
