@@ -878,7 +878,7 @@ def cpu_baseline(torch, dev, stack_out=None):
         out["stack_64_vs_oracle"] = {
             k: float(np.linalg.norm(np.asarray(v, dtype=np.float64) - xs) / ref) for k, v in stack_out.items()}
         out["stack_64_vs_oracle"]["note"] = ("relative L2 of token 0 after 64 layers against the fp64 oracle "
-                                             "(M1: fp32 lookup path; M8: bf16 MFMA path); reported, not gated")
+                                             "(M1: fixed-point lookup path; M8: bf16 MFMA path); reported, not gated")
     pool.shutdown()
     return out
 
