@@ -456,6 +456,9 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
             for (int j = 0; j < kLutDwords; ++j) dat[i][j] = t[j];
         }
     };
+    // wave 0's x requests go out before any wave's weights: a bare barrier
+    // (no memory wait), so x is not queued behind the first weight burst
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -549,6 +552,10 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     }
     rotate(0);
     __syncthreads();
+    // the prologue (x, rotation, table) ran at raised wave priority, so a
+    // workgroup that starts late on a CU builds its table ahead of the
+    // other workgroup's lookups; the lookups run at the normal priority
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- 5. lookups (exact int32 sums, two lookups per v_add3_u32), scale,
     // 2-lane reduction, partial store
@@ -603,6 +610,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_matvec_lut(LutArgs a)  // 4 
     const int per_slice = a.nmat * static_cast<int>(a.groups);  // rows < 2^20 (checked by the caller)
     const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
     const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
+    __builtin_amdgcn_s_setprio(3);
     if (u0 < u1) lut_segment<U, W8>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);  // workgroup-uniform
 }
 
