@@ -314,9 +314,11 @@ ptq1_status pq2_tile(const uint8_t *blocks, int64_t n, int64_t k, uint8_t *tiled
  *   y[r] = (residual ? residual[r] : 0) + sum_c W[r][c] * xr[c],
  *   xr = R x when signs1024 != NULL (k % 1024 == 0), else x as given.
  * Codes are decoded through a per-slice table of (code byte, byte value)
- * partial dot products, fp32 throughout; split-K partials over 256-wide
- * slices, then their sum in slice order.  The tiled matrix must be below
- * 2 GiB (UNSUPPORTED otherwise). */
+ * partial dot products over xr in the same 32-bit fixed point as
+ * ptq1_matvec (exact int32 block sums; a NaN or infinity in xr makes every
+ * output a NaN); split-K partials over 256-wide slices, then their sum in
+ * slice order.  The tiled matrix must be below 2 GiB (UNSUPPORTED
+ * otherwise). */
 size_t pq2_matvec_workspace_bytes(int64_t n, int64_t k);
 ptq1_status pq2_matvec(const uint8_t *tiled, int64_t n, int64_t k, const float *x, const float *signs1024,
                        const float *residual, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -330,8 +332,8 @@ ptq1_status pq2_gemm(const uint8_t *tiled, int64_t n, int64_t k, const float *x,
                      float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The feed-forward block of ptq1_ffn_block over PQ2_0 tiled matrices: the
- * same arguments, numerics (m = 1: fp32 table lookups of that format;
- * m >= 2: bf16 MFMA),
+ * same arguments, numerics (m = 1: fixed-point table lookups as in
+ * pq2_matvec; m >= 2: bf16 MFMA),
  * workspace rule and errors; every matrix must be below 2 GiB at m = 1. */
 size_t pq2_ffn_workspace_bytes(int64_t m, int64_t d, int64_t f);
 ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, int64_t f, const uint8_t *w_gate,

@@ -901,17 +901,15 @@ hipError_t launch_matvec_peel(const uint8_t *w0, const uint8_t *w1, int nmat, in
 // w(q) = q - 1 and w(3) = 0.  What differs from PTQ1_0:
 //   - a lane's block is 32 code bytes, read with two 16-byte loads from its
 //     tile record, and its scale comes from the tile's scale area;
-//   - the 64 slots fill the table's 64 slot columns, and the per-lane
-//     rotation can make every lookup conflict-free: lane 2i + b rotates its
-//     8 dwords by rho = (4 b + i / 4) mod 8 and its bytes by sig = i mod 4.
-//     At lookup (j, c) it reads slot 32 b + 4 ((j + rho) mod 8) +
-//     (c + sig) mod 4.  Over a half-wave (i < 16 or i >= 16) the block-0
-//     lanes read 16 distinct slots of dwords j + i/4 .. (four of them) and
-//     the block-1 lanes the other four dwords, so the 32 slots differ
-//     mod 32; over the whole wave each block's 32 lanes read 32 distinct
-//     slots, so all 64 differ.  Either way no two lanes share a bank
-//     (a slot's dwords sit 64 dwords apart, one per byte value);
+//   - the 64 slots fill the table's 64 columns (block b's slot p at column
+//     32 b + (p + 16 b) mod 32), and lane 2i + b rotates its 8 dwords by
+//     rho = (i / 4) mod 4 and its bytes by sig = i mod 4, as in the PTQ1_0
+//     kernel: at lookup (j, c) the 16 block-0 lanes of a half-wave read the
+//     banks of dwords j .. j + 3 (mod 8) and the block-1 lanes, 16 banks
+//     further, the other 16, so no two lanes of a half-wave share a bank;
 //   - 32 lookups per block and no scale-byte lookups.
+// The table is int32 over the slice's fixed-point q (slice_x_store_fixed),
+// as in the PTQ1_0 kernel (|T| <= 4 * 2^23, a block's 32 entries < 2^31).
 // Partials and their sums are those of the PTQ1_0 kernel.
 // ---------------------------------------------------------------------------
 constexpr int kPq2Slots = kLutBlocks * kPq2CodeBytes;  // 64
@@ -929,14 +927,14 @@ struct Pq2Args {
     float *part;             // [nslices][nmat][n]
 };
 
-__device__ __forceinline__ int pq2_rho(int lane) { return (4 * (lane & 1) + (lane >> 3)) & 7; }
+__device__ __forceinline__ int pq2_rho(int lane) { return (lane >> 3) & 3; }
 __device__ __forceinline__ int pq2_sig(int lane) { return (lane >> 1) & 3; }
 
-// d[j] <- d[(j + rho) mod 8]: conditional rotations by 1, 2 and 4
+// d[j] <- d[(j + rho) mod 8]: conditional rotations by 1 and 2
 __device__ __forceinline__ void pq2_rotate(uint32_t (&d)[kPq2Dwords], int rho)
 {
 #pragma unroll
-    for (int sh = 1; sh <= 4; sh <<= 1) {
+    for (int sh = 1; sh <= 2; sh <<= 1) {
         const uint32_t m = (rho & sh) ? 0xffffffffu : 0u;
         uint32_t t[kPq2Dwords];
 #pragma unroll
@@ -949,27 +947,27 @@ __device__ __forceinline__ void pq2_rotate(uint32_t (&d)[kPq2Dwords], int rho)
 // T[slot][b] for b in [32 BQ, 32 BQ + 32): b = f0 | f1 << 2 | f2 << 4 | f3 << 6;
 // T = A[b & 15] + B[b >> 4] with A = w(f0) x0 + w(f1) x1, B = w(f2) x2 + w(f3) x3.
 template <int BQ>
-__device__ __forceinline__ void pq2_build_range(float *tab, int slot, const float (&xv)[4])
+__device__ __forceinline__ void pq2_build_range(float *tab, int col, const int32_t (&xv)[4])
 {
-    float A[16], B[16];
+    int32_t A[16], B[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int q0 = q & 3, q1 = q >> 2;
-        const float w0 = q0 == 3 ? 0.0f : static_cast<float>(q0 - 1), w1 = q1 == 3 ? 0.0f : static_cast<float>(q1 - 1);
+        const int32_t w0 = q0 == 3 ? 0 : q0 - 1, w1 = q1 == 3 ? 0 : q1 - 1;
         A[q] = w0 * xv[0] + w1 * xv[1];
         B[q] = w0 * xv[2] + w1 * xv[3];
     }
-    const uint32_t base = static_cast<uint32_t>(slot) << 2;  // slot < 64
+    const uint32_t base = static_cast<uint32_t>(col) << 2;  // col < 64
 #pragma unroll
     for (int i = 0; i < kLutBuildPer; ++i) {
         const int b = kLutBuildPer * BQ + i;
-        *reinterpret_cast<float *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
+        *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(tab) + (base | (static_cast<uint32_t>(b) << 8))) =
             A[b & 15] + B[b >> 4];
     }
 }
 
 template <int BQ>
-__device__ __forceinline__ void pq2_build_dispatch(int bq, float *tab, int slot, const float (&xv)[4])
+__device__ __forceinline__ void pq2_build_dispatch(int bq, float *tab, int slot, const int32_t (&xv)[4])
 {
     if constexpr (BQ < kLutBuildRanges) {
         if (bq == BQ)
@@ -1014,6 +1012,7 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
         dat[i][4] = hi.x; dat[i][5] = hi.y; dat[i][6] = hi.z; dat[i][7] = hi.w;
         scw[i] = *reinterpret_cast<const uint32_t *>(tb + kPq2TileCodeBytes + 4 * (lane >> 1));  // scales of 2i, 2i+1
     };
+    __builtin_amdgcn_s_barrier();  // wave 0's x requests go first (as in the PTQ1_0 kernel)
 #pragma unroll
     for (int i = 0; i < (U < kLutEarly ? U : kLutEarly); ++i) issue(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -1030,7 +1029,7 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     }
 #pragma unroll
     for (int j = 0; j < kPq2Dwords; ++j) {
-        const int q = (j + rho) & (kPq2Dwords - 1);
+        const int q = (j + rho + 4 * blk_l) & (kPq2Dwords - 1);  // bank group of dword (j + rho) mod 8
         const uint32_t base = static_cast<uint32_t>(kPq2CodeBytes * blk_l + 4 * q) << 2;
         P[j] = __builtin_amdgcn_perm(base, base, 0x00000000u) + boff;
     }
@@ -1040,9 +1039,13 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(S[c]));
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. the slice's x (times the gain), rotated
-    if (wave == 0) slice_x_store(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane, xs);
+    // ---- 3. the slice's x (times the gain), rotated, in fixed point
+    float *ex = xs + kLutSliceW;
+    if (wave == 0)
+        slice_x_store_fixed(slice_x_values(xv, a.signs != nullptr, a.gain != nullptr, k0, kw, lane), lane, xs, ex);
     __syncthreads();
+    const int e2 = reinterpret_cast<const int32_t *>(ex)[0];
+    const float sfix = ex[1];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = kLutEarly; i < (U < kLutDepth ? U : kLutDepth); ++i) issue(i);
@@ -1050,18 +1053,22 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
     // ---- 4. table: thread = (slot, 32-value range of the byte)
     {
         const int bq = tid >> 6;
-        const int slot = tid & 63;  // all 64 slots are used
-        const int blk = slot / kPq2CodeBytes, i = slot % kPq2CodeBytes;
-        float xv[4];
+        const int col = tid & 63;  // all 64 columns are used
+        const int blk = col / kPq2CodeBytes;
+        const int i = (col - 16 * blk) & (kPq2CodeBytes - 1);  // code-byte slot of this column
+        const int32_t *xq = reinterpret_cast<const int32_t *>(xs);
+        int32_t xv[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) xv[f] = blk < nblk ? xs[blk * kBlockWeights + kPq2CodesPerByte * i + f] : 0.0f;
-        pq2_build_dispatch<0>(bq, tab, slot, xv);
+        for (int f = 0; f < 4; ++f) xv[f] = blk < nblk ? xq[blk * kBlockWeights + kPq2CodesPerByte * i + f] : 0;
+        pq2_build_dispatch<0>(bq, tab, col, xv);
     }
     pq2_rotate(dat[0], rho);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);  // the prologue ran at raised priority, as in the PTQ1_0 kernel
 
-    // ---- 5. lookups, scale, 2-lane reduction, partial store
-    typedef __attribute__((address_space(3))) const float lds_f32;
+    // ---- 5. lookups (int32, two per v_add3_u32), scale, 2-lane reduction,
+    // partial store
+    typedef __attribute__((address_space(3))) const int32_t lds_i32;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         if (i + kLutDepth < U) issue(i + kLutDepth);
@@ -1073,19 +1080,21 @@ __device__ __forceinline__ void pq2_segment(const Pq2Args &a, float *tab, float 
         const uint32_t sh = blk_l ? (scw[i] >> 16) : (scw[i] & 0xffffu);
         const float scale = live ? half_bits_to_float(sh) : 0.0f;
         if (i > 0) pq2_rotate(dat[i], rho);
-        float acc0 = 0.0f, acc1 = 0.0f;
+        int32_t acc = 0;
 #pragma unroll
         for (int j = 0; j < kPq2Dwords; ++j) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t addr = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
-                const float t = *reinterpret_cast<lds_f32 *>(static_cast<uintptr_t>(addr));
-                if ((c & 1) == 0) acc0 += t; else acc1 += t;
+            for (int c = 0; c < 4; c += 2) {
+                const uint32_t a0 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c]);
+                const uint32_t a1 = __builtin_amdgcn_perm(P[j], dat[i][j], S[c + 1]);
+                acc = acc + *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a0)) +
+                      *reinterpret_cast<lds_i32 *>(static_cast<uintptr_t>(a1));
             }
         }
-        float p = (acc0 + acc1) * scale;
+        float p = static_cast<float>(acc) * scale;
         const int ip = __builtin_bit_cast(int, p);
         p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ip, ip, 0xB1, 0xF, 0xF, false));  // + lane ^ 1
+        p = ldexpf(p, -e2) * sfix;
         if (unit_ok && blk_l == 0 && r < a.n) a.part[(static_cast<int64_t>(s) * a.nmat + mat) * a.n + r] = p;
     }
 }
@@ -1099,6 +1108,7 @@ __global__ void __launch_bounds__(kLutThreads, 4) k_pq2_matvec(Pq2Args a)
     const int per_slice = a.nmat * static_cast<int>(a.groups);
     const int u0 = static_cast<int>(blockIdx.x) * a.per_wg;
     const int u1 = u0 + a.per_wg < per_slice ? u0 + a.per_wg : per_slice;
+    __builtin_amdgcn_s_setprio(3);  // prologue at raised priority (lowered before the lookups)
     if (u0 < u1) pq2_segment<U>(a, tab, xs, static_cast<int>(blockIdx.y), u0, u1);
 }
 
@@ -1106,7 +1116,8 @@ template <int U>
 static hipError_t pq2_launch(const Pq2Args &a, int64_t chunks, hipStream_t st)
 {
     static std::atomic<uint64_t> lds_done{0};
-    const size_t lds = kLutTableBytes + kLutSliceW * sizeof(float);
+    // the table, the slice's q and the fixed-point exponent and factor
+    const size_t lds = kLutTableBytes + (kLutSliceW + kLutWaves) * sizeof(float);
     const hipError_t e =
         allow_dynamic_lds(reinterpret_cast<const void *>(&k_pq2_matvec<U>), static_cast<int>(lds), lds_done);
     if (e != hipSuccess) return e;
