@@ -176,8 +176,7 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
 #pragma unroll
             for (int q = 0; q < h; ++q) sq[q] += sq[q + h];
         float s = (sq[0] + sq[1]) + sq[2];
-#pragma unroll
-        for (int h = kWave / 2; h > 0; h >>= 1) s += __shfl_xor(s, h, kWave);
+        s = wave_sum(s);  // the same value in every lane (and in every chunk's wave)
         const float a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) v[j] *= a;
@@ -197,8 +196,7 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
             for (int q = 0; q < kQ; ++q)
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
         }
-#pragma unroll
-        for (int h = kWave / 2; h > 0; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h, kWave));
+        mx = wave_max(mx);
         const float c = mx > 0.0f ? static_cast<float>(127.0 / static_cast<double>(mx)) : 0.0f;
 #pragma unroll
         for (int j = 0; j < kRotPerLane; ++j) v[j] = rintf(v[j] * c);

@@ -276,24 +276,7 @@ __device__ __forceinline__ void slice_x_store_fixed(const lut_f32x4 &v, int lane
     const bool bad = !(__builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) && __builtin_isfinite(v[2]) &&
                        __builtin_isfinite(v[3]));
     const bool any_bad = __ballot(bad) != 0;  // wave-uniform
-    {  // max over the wave: quad permutations, row rotations, then the 16- and 32-lane swaps
-        int im = __builtin_bit_cast(int, m);
-        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0xB1, 0xF, 0xF, false)));
-        im = __builtin_bit_cast(int, m);
-        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x4E, 0xF, 0xF, false)));
-        im = __builtin_bit_cast(int, m);
-        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x124, 0xF, 0xF, false)));
-        im = __builtin_bit_cast(int, m);
-        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x128, 0xF, 0xF, false)));
-        const uint32_t u16 = __builtin_bit_cast(uint32_t, m);
-        const auto r16 = __builtin_amdgcn_permlane16_swap(u16, u16, false, false);
-        const uint32_t a0 = r16[0], a1 = r16[1];
-        m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
-        const uint32_t u32 = __builtin_bit_cast(uint32_t, m);
-        const auto r32 = __builtin_amdgcn_permlane32_swap(u32, u32, false, false);
-        const uint32_t b0 = r32[0], b1 = r32[1];
-        m = fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
-    }
+    m = wave_max(m);
     int E = 0;
     (void)frexpf(any_bad ? 0.0f : m, &E);
     const int e = 23 - E;
@@ -503,8 +486,7 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     float step = 1.0f;
     int ex = 0;
     if constexpr (W8) {
-#pragma unroll
-        for (int h = kWave / 2; h > 0; h >>= 1) amax = fmaxf(amax, __shfl_xor(amax, h, kWave));
+        amax = wave_max(amax);
         if (lane == 0) red[wave] = amax;
         __syncthreads();
         float g = 0.0f;
@@ -1199,11 +1181,9 @@ __global__ void __launch_bounds__(kSumThreads) k_lut_sum_rows(const float *__res
         for (int c = 0; c < kSumPer; ++c)
             if (q0 + c < q_hi) t += v[c];
     }
-#pragma unroll
-    for (int h = kRowsPerWave; h < kWave; h <<= 1) {
-        const float o = __shfl_xor(t, h, kWave);
-        t = (lane & h) ? o + t : t + o;  // lower slice range first: the same order in every lane
-    }
+    // lower slice range first: the same order in every lane
+    if constexpr (T == 4) t = lane_pair_sum<16>(t);
+    if constexpr (T >= 2) t = lane_pair_sum<32>(t);
     if (j == 0 && r < n) y[r] = residual ? res + t : t;
 }
 
@@ -1268,11 +1248,14 @@ __global__ void __launch_bounds__(kSumThreads) k_lut_gate_up_sum(
             }
         }
     }
-#pragma unroll
-    for (int hh = kRowsPerWave; hh < kWave; hh <<= 1) {
-        const float og = __shfl_xor(tg, hh, kWave), ou = __shfl_xor(tu, hh, kWave);
-        tg = (lane & hh) ? og + tg : tg + og;
-        tu = (lane & hh) ? ou + tu : tu + ou;
+    // lower slice range first: the same order in every lane
+    if constexpr (T == 4) {
+        tg = lane_pair_sum<16>(tg);
+        tu = lane_pair_sum<16>(tu);
+    }
+    if constexpr (T >= 2) {
+        tg = lane_pair_sum<32>(tg);
+        tu = lane_pair_sum<32>(tu);
     }
     float a = 1.0f;
     if (x_rms != nullptr) {
@@ -1282,8 +1265,7 @@ __global__ void __launch_bounds__(kSumThreads) k_lut_gate_up_sum(
             if (tid + static_cast<int64_t>(c) * kSumThreads < d) sq = fmaf(rv[c], rv[c], sq);
         for (int64_t i = tid + static_cast<int64_t>(kRmsPer) * kSumThreads; i < d; i += kSumThreads)
             sq = fmaf(x_rms[i], x_rms[i], sq);
-#pragma unroll
-        for (int hh = kWave / 2; hh > 0; hh >>= 1) sq += __shfl_xor(sq, hh, kWave);
+        sq = wave_sum(sq);
         if (lane == 0) red[wave] = sq;
         __syncthreads();
         float t = 0.0f;

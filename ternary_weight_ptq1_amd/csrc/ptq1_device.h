@@ -58,6 +58,69 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 }
 
 // ---------------------------------------------------------------------------
+// Wave reductions without LDS round trips (DPP and the gfx950 lane swaps).
+// ---------------------------------------------------------------------------
+// Max over the wave, in every lane: quad permutations, row rotations, then
+// the 16- and 32-lane swaps.
+__device__ __forceinline__ float wave_max(float m)
+{
+    int im = __builtin_bit_cast(int, m);
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0xB1, 0xF, 0xF, false)));
+    im = __builtin_bit_cast(int, m);
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x4E, 0xF, 0xF, false)));
+    im = __builtin_bit_cast(int, m);
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x124, 0xF, 0xF, false)));
+    im = __builtin_bit_cast(int, m);
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(im, im, 0x128, 0xF, 0xF, false)));
+    const uint32_t u16 = __builtin_bit_cast(uint32_t, m);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u16, u16, false, false);
+    const uint32_t a0 = r16[0], a1 = r16[1];
+    m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+    const uint32_t u32 = __builtin_bit_cast(uint32_t, m);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(u32, u32, false, false);
+    const uint32_t b0 = r32[0], b1 = r32[1];
+    return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
+// v of lane l plus v of lane l ^ H (H = 16 or 32), the lower lane's value
+// first, so both lanes get the same sum: one lane-swap instruction instead of
+// an LDS permute round trip.  (r[0] holds the lower lane's value and r[1]
+// the upper one's in every lane.)
+template <int H>
+__device__ __forceinline__ float lane_pair_sum(float v)
+{
+    static_assert(H == 16 || H == 32, "16- or 32-lane swap");
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    uint32_t lo, hi;
+    if constexpr (H == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        lo = r[0];
+        hi = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        lo = r[0];
+        hi = r[1];
+    }
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// Sum over the wave: quad permutations, the half-row and row mirrors, then
+// the 16- and 32-lane swaps.  Every step adds two values that the two lanes
+// of a pair hold alike, so every lane ends with the same sum.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    int iv = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    iv = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    iv = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x141, 0xF, 0xF, false));  // half-row mirror
+    iv = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x140, 0xF, 0xF, false));  // row mirror
+    return lane_pair_sum<32>(lane_pair_sum<16>(v));
+}
+
+// ---------------------------------------------------------------------------
 // Walsh-Hadamard transform of one 1024-wide chunk held by one wavefront:
 // lane l holds elements l + 64 j in v[j], j = 0..15.  Natural-order
 // (Sylvester) H: the butterfly pairs element i with i ^ h for h = 1 .. 512.
