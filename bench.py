@@ -17,14 +17,17 @@ the host).
 roofline: the dominant kernel, the table-lookup matvec over gate and up
 (one launch per step), timed in a second pass of the same K steps run
 eagerly, with HIP events attached to that kernel's dispatch by the library
-(ptq1_profile_arm -> hipExtLaunchKernel: the kernel's own start and end);
-algorithmic bytes per launch = its PTQ1_0 blocks + x.  `traffic` is the
+(ptq1_profile_arm -> hipExtLaunchKernel: the kernel's own start and end)
+and a spin kernel ahead of each step, so that the GPU is as busy between
+steps as in the graph replays (busy()); algorithmic bytes per launch = its
+PTQ1_0 blocks + x.  `traffic` is the
 counter-measured HBM bytes per launch from the committed rocprofv3 summary
 profiles/lut_matvec_gate_up_decode_27b_traffic.md, or null when that
 kernel's source changed after the counters were taken.
 
-Also reported (breakdown): the down-projection lookup kernel inside the
-same steps, cold gate+up and down calls alone, the pages' float-peel decode
+Also reported (breakdown; a call's time is one HIP-graph replay of many
+calls, a kernel's time its dispatch events as above): the down-projection
+lookup kernel inside the same steps, cold gate+up and down calls alone, the pages' float-peel decode
 on the same matrices, the hot 1024 x 1024 matvec, the prefill GEMM at
 M = 128 / 256 / 512 (TFLOP/s, fraction of the bf16 MFMA peak), and the
 64-layer FFN stack at batch 1 and 8 (layers/s, and the relative L2 of its
@@ -105,6 +108,19 @@ def measured_traffic():
 
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 
+# Event-timed dispatches are launched eagerly from Python, which is slower
+# than the GPU: between calls the GPU would idle, and a kernel that follows
+# an idle gap runs longer than the same kernel inside a graph replay (the
+# gate+up lookup kernel: mean 13.0 against 11.9 us, 90th percentile 15.1
+# against 12.1).  A spin kernel (torch.cuda._sleep: a clock loop, no memory
+# traffic) ahead of each such call keeps the GPU busy while the host
+# launches, as in the timed graph replays.
+SPIN_CYCLES = 200000
+
+
+def busy(torch):
+    torch.cuda._sleep(SPIN_CYCLES)
+
 
 def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     """The prefill GEMM alone (for counter runs): M x 5120 activations against
@@ -137,6 +153,7 @@ def gemm_only(args, torch, synth, sdev, P, dev) -> int:
     kt = P.KernelTimer("gemm", args.steps)
     with kt:
         for _ in range(args.steps):
+            busy(torch)
             call()
     torch.cuda.synchronize()
     ms = sorted(kt.durations_ms())
@@ -180,6 +197,7 @@ def decode_only(args, torch, synth, sdev, P, dev) -> int:
     kt = P.KernelTimer(fam, args.steps)
     with kt:
         for i in range(args.steps):
+            busy(torch)
             call(i)
     torch.cuda.synchronize()
     d = kt.durations_ms()
@@ -287,16 +305,37 @@ def main() -> int:
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def timed(fn, reps, warm):
+    def timed(fn, reps, warm, mode="graph"):
+        """ms per call of fn(0) .. fn(reps - 1) after `warm` eager calls.  mode
+        "graph": the calls replayed from one HIP graph (GPU time, launches back
+        to back); "events": launched eagerly with a spin kernel ahead of each
+        (busy()), for passes whose kernel dispatches carry HIP events (which a
+        graph does not) -- the returned time then includes the spins and is not
+        used; "eager": plain eager calls."""
         for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
         a, b = ev(), ev()
-        a.record(stream)
-        for i in range(reps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
+        if mode == "graph":
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    fn(i)
+            g.replay()  # the first replay uploads the graph
+            torch.cuda.synchronize()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            del g
+        else:
+            a.record(stream)
+            for i in range(reps):
+                if mode == "events":
+                    busy(torch)
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
         return a.elapsed_time(b) / reps  # ms per call
 
     def weight_set(seed, layer):
@@ -366,18 +405,17 @@ def main() -> int:
     del graphs
 
     # roofline pass: the same K steps run eagerly with HIP events attached to
-    # the dispatches of the gate+up and down lookup kernels (ptq1_profile_arm)
+    # the dispatches of the gate+up and down lookup kernels (ptq1_profile_arm),
+    # a spin kernel ahead of each step keeping the GPU as busy as in the
+    # graph replays (busy())
     log("bench: roofline pass")
     t_gu = P.KernelTimer("lut_matvec_2", args.steps)
     t_dn = P.KernelTimer("lut_matvec_1", args.steps)
-    e2, e3 = ev(), ev()
     with t_gu, t_dn:
-        e2.record(stream)
         for i in range(args.steps):
+            busy(torch)
             step(i)
-        e3.record(stream)
     torch.cuda.synchronize()
-    ms_step_eager_profiled = e2.elapsed_time(e3) / args.steps
     d_gu, d_dn = t_gu.durations_ms(), t_dn.durations_ms()
     t_gu.close()
     t_dn.close()
@@ -404,8 +442,7 @@ def main() -> int:
     ms_gu = timed(gate_up, max(args.steps, 100), args.warmup)
     gu_gbs = GATE_UP_BYTES / (ms_gu * 1e-3) / 1e9
 
-    breakdown = {"step_eager_with_kernel_events_us": ms_step_eager_profiled * 1e3,
-                 "lut_kernel_gate_up_in_step": dict({"us": us_gu, "GB/s": lut_gu_gbs, "bytes": LUT_GATE_UP_BYTES},
+    breakdown = {"lut_kernel_gate_up_in_step": dict({"us": us_gu, "GB/s": lut_gu_gbs, "bytes": LUT_GATE_UP_BYTES},
                                                     **spread(d_gu)),
                  "lut_kernel_down_in_step": dict({"us": us_dn, "GB/s": lut_dn_gbs, "bytes": LUT_DOWN_BYTES},
                                                  **spread(d_dn)),
@@ -431,11 +468,11 @@ def main() -> int:
                                            "gate_5120_to_17408": (0, F, D, xg, g_buf)}.items():
             wsp = torch.zeros(P.workspace_bytes("matvec", n_, k_), dtype=torch.uint8, device=dev)
             timed(lambda i: P.ptq1_matvec_float_peel(sets[i % WEIGHT_SETS][wi], n_, k_, xin, signs, out=yb, ws=wsp),
-                  5, 0)
+                  5, 0, "eager")
             tp = P.KernelTimer("peel_matvec", 64)
             with tp:
                 timed(lambda i: P.ptq1_matvec_float_peel(sets[i % WEIGHT_SETS][wi], n_, k_, xin, signs, out=yb,
-                                                         ws=wsp), 64, 0)
+                                                         ws=wsp), 64, 0, "events")
             dp = tp.durations_ms()
             tp.close()
             us_p = 1e3 * sum(dp) / len(dp)
@@ -471,10 +508,10 @@ def main() -> int:
             ms_p = timed(lambda i: P.ptq1_matvec(psets[i % 32], n_p, k_p, xp[0], signs, out=yp, ws=wsp), 200, 20)
             yg = torch.empty((256, n_p), dtype=torch.float32, device=dev)
             wsg = torch.zeros(P.workspace_bytes("gemm", 256, n_p, k_p), dtype=torch.uint8, device=dev)
-            timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 3, 0)  # warm-up
+            timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 3, 0, "eager")  # warm-up
             tg = P.KernelTimer("gemm", 30)
             with tg:
-                timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 30, 0)
+                timed(lambda i: P.ptq1_gemm(psets[i % 32], n_p, k_p, xp, signs, out=yg, ws=wsg), 30, 0, "events")
             dg = tg.durations_ms()
             tg.close()
             us_gk = 1e3 * sum(dg) / len(dg)
@@ -495,10 +532,10 @@ def main() -> int:
                                                     device=dev)), n2, D) for j in range(32)]
         y2 = torch.empty(n2, dtype=torch.float32, device=dev)
         ws2 = torch.zeros(P.workspace_bytes("pq2_matvec", n2, D), dtype=torch.uint8, device=dev)
-        timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 20, 0)  # warm-up
+        ms_q2 = timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 200, 20)
         t2 = P.KernelTimer("pq2_matvec", 200)
         with t2:
-            ms_q2 = timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 200, 0)
+            timed(lambda i: P.pq2_matvec(q2sets[i % 32], n2, D, xg, signs, out=y2, ws=ws2), 200, 0, "events")
         d2 = t2.durations_ms()
         t2.close()
         us_q2 = 1e3 * sum(d2) / len(d2)
@@ -510,10 +547,10 @@ def main() -> int:
         xq = torch.from_numpy(synth.activations(seed, 256, D)).to(dev)
         yq = torch.empty((256, n2), dtype=torch.float32, device=dev)
         wsq = torch.zeros(P.workspace_bytes("pq2_gemm", 256, n2, D), dtype=torch.uint8, device=dev)
-        timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 3, 0)  # warm-up
+        timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 3, 0, "eager")  # warm-up
         tq = P.KernelTimer("gemm", 30)
         with tq:
-            timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 30, 0)
+            timed(lambda i: P.pq2_gemm(q2sets[i % 32], n2, D, xq, signs, out=yq, ws=wsq), 30, 0, "events")
         dq = tq.durations_ms()
         tq.close()
         us_gq = 1e3 * sum(dq) / len(dq)
@@ -522,7 +559,7 @@ def main() -> int:
         del q2sets, y2, ws2, xq, yq, wsq
         torch.cuda.empty_cache()
 
-        # the whole batch-1 block in PQ2_0 (eager calls, 16 rotating layers)
+        # the whole batch-1 block in PQ2_0 (16 rotating layers, replayed from a graph)
         def pq2_mat(role_t, role_s, j, n_, k_):
             return P.pq2_tile(P.pq2_pack(sdev.trits(seed, synth.layer_stream(role_t, j), n_, k_, device=dev),
                                          sdev.scales(seed, synth.layer_stream(role_s, j), n_, k_ // 128,
@@ -536,7 +573,7 @@ def main() -> int:
         wsb2 = torch.zeros(P.lib().pq2_ffn_workspace_bytes(1, D, F), dtype=torch.uint8, device=dev)
         ms_b2 = timed(lambda i: P.pq2_ffn_block(xb2, *l2[i % 16], signs, D, F, 1e-6, out=ob2, ws=wsb2), 200, 20)
         b2_bytes = 2 * P.pq2_tiled_bytes(F, D) + P.pq2_tiled_bytes(D, F) + 4 * D
-        breakdown["pq2_ffn_block_decode_eager"] = {"us": ms_b2 * 1e3, "GB/s": b2_bytes / (ms_b2 * 1e-3) / 1e9,
+        breakdown["pq2_ffn_block_decode"] = {"us": ms_b2 * 1e3, "GB/s": b2_bytes / (ms_b2 * 1e-3) / 1e9,
                                                    "bytes": b2_bytes}
         del l2, xb2, ob2, wsb2
 
@@ -574,7 +611,7 @@ def main() -> int:
         # output per 4 KB row (the fastest of the plain torch reductions and
         # copies tried: a full sum reads at about 4 TB/s, a copy at 4.9)
         big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
-        ms_rd = timed(lambda i: big.view(-1, 1024).sum(dim=1), 20, 3)
+        ms_rd = timed(lambda i: big.view(-1, 1024).sum(dim=1), 20, 3, "eager")
         rd_gbs = big.numel() * 4 / (ms_rd * 1e-3) / 1e9
         breakdown["hbm_read_measured"] = {"GB/s": rd_gbs, "how": "torch row sums over [2^19, 1024] fp32 (2 GiB), 20 calls",
                                           "lut_gate_up_frac_of_it": lut_gu_gbs / rd_gbs}
@@ -589,10 +626,10 @@ def main() -> int:
             xm = torch.from_numpy(synth.activations(3, m, D)).to(dev)
             ym = torch.empty((m, F), dtype=torch.float32, device=dev)
             wsm = torch.zeros(P.workspace_bytes("gemm", m, F, D), dtype=torch.uint8, device=dev)
-            timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 3, 0)  # warm-up
+            ms = timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 3)
             tg = P.KernelTimer("gemm", 50)
             with tg:
-                ms = timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 0)
+                timed(lambda i: P.ptq1_gemm(wq, F, D, xm, signs, out=ym, ws=wsm), 50, 0, "events")
             dg = tg.durations_ms()
             tg.close()
             us_k = 1e3 * sum(dg) / len(dg)
@@ -617,14 +654,14 @@ def main() -> int:
                     W = stack[L]
                     P.ptq1_ffn_block(xa, W[0], W[1], W[2], signs, D, F, rms_eps=1e-6, out=xa, ws=wss)
 
-            ms_eager = timed(run_stack, 3, 1)
+            ms_eager = timed(run_stack, 3, 1, "eager")
             # the stack replayed from one HIP graph of its 64 layers (no host
             # launch gaps between the dependent kernels), as the decode step
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_stack(0)
             torch.cuda.synchronize()
-            ms = timed(lambda i: g.replay(), 5, 1)
+            ms = timed(lambda i: g.replay(), 5, 1, "eager")
             stk[f"M{m}"] = {"ms_per_stack": ms, "us_per_layer": ms * 1e3 / LAYERS,
                             "layers_per_s": LAYERS / (ms * 1e-3),
                             "weight_GB/s": LAYERS * LAYER_WEIGHT_BYTES / (ms * 1e-3) / 1e9,
