@@ -211,7 +211,8 @@ def decode_only(args, torch, synth, sdev, P, dev) -> int:
 
 def ffn_only(args, torch, synth, sdev, P, dev) -> int:
     """One 27B-shaped FFN block at batch M alone (for kernel traces): --steps
-    calls replayed from a HIP graph after --warmup eager ones."""
+    calls (one weight set) replayed from a HIP graph of 16 calls after
+    --warmup eager ones."""
     m = args.ffn_only
     q2 = args.format == "pq2"
     pack, tile = (P.pq2_pack, P.pq2_tile) if q2 else (P.ptq1_pack, P.ptq1_tile)
@@ -233,19 +234,24 @@ def ffn_only(args, torch, synth, sdev, P, dev) -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    # one graph of `per` calls (a graph launch per call would add its own
+    # launch cost to every call), replayed until --steps calls have run
+    per = min(16, max(1, args.steps))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        call()
+        for _ in range(per):
+            call()
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
+    reps = max(1, args.steps // per)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(args.steps):
+    for _ in range(reps):
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / args.steps
+    us = a.elapsed_time(b) * 1e3 / (reps * per)
     fmt = "PQ2_0" if q2 else "PTQ1_0"
     print(json.dumps({"workload": f"FFN block {m} x {D} -> {F} -> {D} ({fmt}), HIP graph", "us_per_layer": us,
                       "weight_GB/s": wbytes / (us * 1e-6) / 1e9}))
