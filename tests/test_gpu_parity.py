@@ -261,6 +261,25 @@ def test_matvec(fn, n, k, seed, rot):
 
 
 @pytest.mark.parametrize("fn", MATVECS)
+@pytest.mark.parametrize("mag", [1e30, 1e-30, 1e-34])
+def test_matvec_extreme_magnitudes(fn, mag):
+    """Inputs far from unit size: the lookup decode scales every slice by its
+    own power of two before rounding to fixed point, so its relative error must
+    not depend on the magnitude (at 1e-34 the block partials are within a few
+    powers of ten of the fp32 normal limit; at 1e30 the outputs near 1e32)."""
+    n, k = 96, 2048
+    t, s = host_matrix(6, synth.S_W_TRITS, synth.S_W_SCALES, n, k)
+    b = oracle.pack(t, s)
+    x = synth.activations(6, 1, k)[0].astype(np.float64) * mag
+    xf = x.astype(np.float32)
+    sg = synth.signs(6)
+    got = host(getattr(P, fn)(mv_weights(fn, b, n, k), n, k, to_dev(xf), to_dev(sg)))
+    ref = oracle.matvec(b, n, k, oracle.rotate(xf, sg))
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) <= TOL_FP32
+
+
+@pytest.mark.parametrize("fn", MATVECS)
 def test_matvec_residual_and_special_cases(fn):
     mv = getattr(P, fn)
     n, k = 96, 2048
