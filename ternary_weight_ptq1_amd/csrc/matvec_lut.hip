@@ -29,8 +29,9 @@
 //     in one 64 KB array, entry address = b << 8 | column << 2, so an
 //     entry's LDS bank is its column mod 32 and one v_perm_b32 assembles the
 //     address from the data byte and a per-lane constant byte; at 64 KB, two
-//     workgroups share a CU, so one's latency-bound phases (rotation, table
-//     build) overlap the other's lookups;
+//     workgroups share a CU, and the prologue (x, rotation, table build)
+//     runs at raised wave priority, so a workgroup that starts late on a CU
+//     builds its table ahead of the other one's lookups;
 //   - weights are read in the tiled layout: the 32 rows x 2 blocks of a unit
 //     are one contiguous 1792-byte tile, lane 2i + b holding block b of row
 //     i, so a wave's loads are fully used 128-byte lines (a row-major matrix
@@ -45,8 +46,9 @@
 //     formed, see lut_fwht256), all threads build the table, and each of the 8 waves
 //     processes U units (U is a template parameter chosen per launch so the
 //     grid fits two workgroups per CU) with kLutDepth units of weights in
-//     flight (one requested before x, so that x is not queued behind a
-//     chip-wide burst of weight requests); a lane reads its 28-byte block
+//     flight (one requested before x arrives, after wave 0's x requests have
+//     gone out, so that x is not queued behind a chip-wide burst of weight
+//     requests); a lane reads its 28-byte block
 //     with two wide loads and rotates its 8 dwords (the 7 of the block and a
 //     zero) and the byte order within a dword by lane-dependent amounts
 //     (lut_rho, lut_sig), which with block 1's columns shifted by 16 banks
@@ -407,8 +409,8 @@ __device__ __forceinline__ void lut_segment(const LutArgs &a, float *tab, float 
     uint32_t dat[U][kLutDwords];
     uint32_t scb[U];
     // Unit indices, tile bases and row bases are wave-uniform (scalar
-    // registers); a lane adds a 32-bit offset of its own (saddr + voffset
-    // addressing, no per-unit vector address arithmetic).
+    // registers); a lane adds a 32-bit offset of its own (one address add per
+    // unit, no 64-bit index arithmetic in vector registers).
     auto unit_of = [&](int i) { return static_cast<int>(u0) + wave + kLutWaves * i; };
     const uint32_t lane_off = static_cast<uint32_t>(lane * kBlockBytes);
     auto issue = [&](int i) {
