@@ -343,8 +343,11 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_mfma(GemmArgs a)
     constexpr int kNT = 64 * WM * WN;  // 256 or 512 threads
     static_assert((kNT == 256 || kNT == 512) && WN * TN * 32 == kGemmBN, "4 or 8 waves x 128 columns");
     static_assert(PD % kNumBufs == 0, "weight ring: a multiple of the B buffers");
-    constexpr int kBq = 3;  // B-fragment prefetch, MFMA steps (ring of 4)
+    constexpr int kBq = 1;  // B-fragment prefetch, MFMA steps (ring of 2)
     constexpr int kAr = 4;  // activation-fragment ring, MFMA steps
+    // step s of every block uses ring slots s % (kBq + 1) and s % kAr: both
+    // rings must divide the block's eight steps so every block starts at slot 0
+    static_assert(8 % (kBq + 1) == 0 && 8 % kAr == 0, "rings divide the eight MFMA steps of a block");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char *tab = lds;
     char *bsm = lds + kTabBytes;
@@ -736,7 +739,9 @@ template <int TM, int PD, int LR, bool Q2>
 __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_rd(GemmArgs a)
 {
     static_assert(LR >= 1 && LR <= 4, "8-row groups of a 32-row tile");
+    static_assert(PD % 2 == 0, "the table entries alternate between two sets by block parity within a ring pass");
     constexpr int kAr = 4;  // activation-fragment ring, MFMA steps
+    static_assert(8 % kAr == 0, "the ring divides the eight MFMA steps of a block");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     typedef __attribute__((address_space(3))) const gm_u32x2 lds_u32x2;
 
@@ -1065,6 +1070,7 @@ template <int TM, int PD, int LR>
 __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_i8(GemmArgs a)
 {
     static_assert(LR >= 1 && LR <= 4, "8-row groups of a 32-row tile");
+    static_assert(PD % 2 == 0, "the table entries alternate between two sets by block parity within a ring pass");
     constexpr int kSteps = 4;  // MFMA steps of K = 32 per block
     extern __shared__ __attribute__((aligned(16))) char lds[];
     typedef __attribute__((address_space(3))) const uint32_t lds_u32;
@@ -1528,10 +1534,12 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     const dim3 grid(static_cast<unsigned>(p.wgs));
     hipError_t e;
     if (p.cfg == 0) {
+        // a weight ring of two blocks at m <= 16 (batch 8: the 5120 x 17408
+        // GEMM 16.4 against 17.1 us), four above (m = 64: 44.7 against 49.9)
         if (m <= 8)
-            e = gemm_rd_dispatch<1, 4, 1>(grid, s, a);
+            e = gemm_rd_dispatch<1, 2, 1>(grid, s, a);
         else if (m <= 16)
-            e = gemm_rd_dispatch<1, 4, 2>(grid, s, a);
+            e = gemm_rd_dispatch<1, 2, 2>(grid, s, a);
         else
             e = gemm_rd_dispatch<1, 4, 4>(grid, s, a);
     } else if (p.cfg == 1) {
