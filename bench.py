@@ -119,7 +119,10 @@ SPIN_CYCLES = 200000
 
 
 def busy(torch):
-    torch.cuda._sleep(SPIN_CYCLES)
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is None:
+        raise RuntimeError("torch.cuda._sleep is missing: the event-timed passes need a spin kernel")
+    spin(SPIN_CYCLES)
 
 
 def gemm_only(args, torch, synth, sdev, P, dev) -> int:
