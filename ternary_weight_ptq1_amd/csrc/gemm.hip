@@ -64,7 +64,7 @@ __host__ __device__ constexpr int gemm_i8_kperm(int kappa)
 }
 
 // ---------------------------------------------------------------------------
-// Activation prep: one wavefront per (row, 1024-chunk).
+// Activation prep: four waves per (row, 1024-chunk), wave w on quarter w.
 //   input  = x (times the row's RMS scale when rms_eps > 0 and the per-channel
 //            gain when given), or silu(g) * u
 //   value  = bf16_rne((1/32) H (signs * input))   (rotation when signs given)
@@ -86,109 +86,91 @@ __host__ __device__ constexpr int gemm_i8_kperm(int kappa)
 // and lane l the 16 bytes at byte offset (((mt nb + kb) 4 + s) 64 + l) 16
 // hold q[32 mt + l % 32][128 kb + gemm_i8_kperm(32 s + 16 (l / 32) + i)],
 // i = 0..15; wave 0 of the row also stores its step max|x| / 127.
+constexpr int kPrepThreads = 4 * kWave;
+
 template <bool Q2, bool W8>
-__global__ void __launch_bounds__(kRotThreads) k_prep_frag(
+__global__ void __launch_bounds__(kPrepThreads) k_prep_frag(
     const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
     int64_t k, const float *__restrict__ signs, float rms_eps, const float *__restrict__ gain,
     uint16_t *__restrict__ xf, float *__restrict__ step)
 {
-    __shared__ float st[kHadamard];
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ f32x4 qt[kPrepThreads];  // the four quarters' 256-point transforms
+    __shared__ float st[kHadamard];     // the finished chunk in natural order
+    __shared__ float red[kPrepThreads / kWave];
     const int64_t cpr = (k + kHadamard - 1) / kHadamard;  // == k / 1024 when signs are given
     const int64_t row = blockIdx.x / cpr;
     const int64_t ch = blockIdx.x - row * cpr;
-    const int lane = threadIdx.x;
-    const int64_t e0 = ch * kHadamard;  // first element of this chunk in the row
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;                     // quarter of the chunk
+    const int ec = (kHadamard / 4) * w + 4 * lane;  // this thread's four elements of the chunk
+    const int64_t e = ch * kHadamard + ec;         // ... of the row
+    const int64_t ecl = e < k ? e : k - 4;         // k is a multiple of 128: e < k covers all four
     // Every load is requested before any arithmetic (clamped addresses, no
-    // branches around the loads but wave-uniform ones): the chunk of x or of
-    // g and u, the signs and the first batch of the row for its mean square.
-    // Requested one after another's use, they cost a dependent round trip to
-    // memory each.
-    constexpr int kQ = 24;  // 16-byte loads of the row per lane per batch (one batch for k <= 6144)
-    float v[kRotPerLane], uw[kRotPerLane], sg[kRotPerLane];
-    float4 xv[kQ];
+    // branches around the loads but workgroup-uniform ones): the four values
+    // of x or of g and u, the gain, the signs and this thread's share of the
+    // row for its mean square or max.  Requested one after another's use,
+    // they cost a dependent round trip to memory each.
+    constexpr int kQ = 6;  // 16-byte loads of the row per thread per batch (one batch for k <= 6144)
     const float *src0 = x != nullptr ? x : g;
     const bool rms = !W8 && x != nullptr && rms_eps > 0.0f;
-    const float4 *xr = reinterpret_cast<const float4 *>(src0 + row * k);
-    const int64_t k4 = k / 4;  // k is a multiple of 128
-#pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) {
-        const int64_t e = e0 + lane + kWave * j;
-        v[j] = src0[row * k + (e < k ? e : k - 1)];
-    }
-    if (x == nullptr) {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) {
-            const int64_t e = e0 + lane + kWave * j;
-            uw[j] = u[row * k + (e < k ? e : k - 1)];
-        }
-    } else if (gain != nullptr) {  // the norm's per-channel weight (uw holds it on this path)
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) {
-            const int64_t e = e0 + lane + kWave * j;
-            uw[j] = gain[e < k ? e : k - 1];
-        }
-    }
-    if (signs != nullptr) {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) sg[j] = signs[lane + kWave * j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) sg[j] = 1.0f;
-    }
+    const f32x4 *xr = reinterpret_cast<const f32x4 *>(src0 + row * k);
+    const int64_t k4 = k / 4;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(src0 + row * k + ecl);
+    f32x4 uw = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (x == nullptr)
+        uw = *reinterpret_cast<const f32x4 *>(u + row * k + ecl);
+    else if (gain != nullptr)  // the norm's per-channel weight (uw holds it on this path)
+        uw = *reinterpret_cast<const f32x4 *>(gain + ecl);
+    f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (signs != nullptr) sg = *reinterpret_cast<const f32x4 *>(signs + ec);
+    f32x4 xv[kQ];
     if (rms || W8) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-            const int64_t i = q * kWave + lane;
+            const int64_t i = tid + static_cast<int64_t>(kPrepThreads) * q;
             xv[q] = xr[i < k4 ? i : k4 - 1];
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (x == nullptr) {
 #pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] = v[j] / (1.0f + expf(-v[j])) * uw[j];
+        for (int j = 0; j < 4; ++j) v[j] = v[j] / (1.0f + expf(-v[j])) * uw[j];
     } else if (gain != nullptr) {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] *= uw[j];
+        v *= uw;
     }
-#pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j)
-        if (e0 + lane + kWave * j >= k) v[j] = 0.0f;
+    if (e >= k) v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // this wave's part of the row's sum of squares (or of its max |x|),
+    // batch by batch (the first one requested above; clamped copies repeat
+    // a real element, so they are masked for the sum and harmless for the max)
     if (rms) {
-        // the row's mean square, batch by batch (the first one requested above)
-        float sq[kQ] = {};
-        for (int64_t i0 = 0; i0 < k4; i0 += kQ * kWave) {
+        float sq = 0.0f;
+        for (int64_t i0 = 0; i0 < k4; i0 += static_cast<int64_t>(kQ) * kPrepThreads) {
             if (i0 > 0) {
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) {
-                    const int64_t i = i0 + q * kWave + lane;
+                    const int64_t i = i0 + tid + static_cast<int64_t>(kPrepThreads) * q;
                     xv[q] = xr[i < k4 ? i : k4 - 1];
                 }
             }
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
-                const float w = i0 + q * kWave + lane < k4 ? 1.0f : 0.0f;
-                sq[q] = fmaf(w * xv[q].x, xv[q].x,
-                             fmaf(w * xv[q].y, xv[q].y, fmaf(w * xv[q].z, xv[q].z, fmaf(w * xv[q].w, xv[q].w, sq[q]))));
+                const float m = i0 + tid + static_cast<int64_t>(kPrepThreads) * q < k4 ? 1.0f : 0.0f;
+                sq = fmaf(m * xv[q].x, xv[q].x, fmaf(m * xv[q].y, xv[q].y, fmaf(m * xv[q].z, xv[q].z,
+                                                                                 fmaf(m * xv[q].w, xv[q].w, sq))));
             }
         }
-#pragma unroll
-        for (int h = kQ / 2; h >= 3; h /= 2)
-#pragma unroll
-            for (int q = 0; q < h; ++q) sq[q] += sq[q + h];
-        float s = (sq[0] + sq[1]) + sq[2];
-        s = wave_sum(s);  // the same value in every lane (and in every chunk's wave)
-        const float a = 1.0f / sqrtf(s / static_cast<float>(k) + rms_eps);
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] *= a;
+        sq = wave_sum(sq);
+        if (lane == 0) red[w] = sq;
     }
     if constexpr (W8) {
-        // the row's max |x|, batch by batch (clamped copies repeat a real element)
         float mx = 0.0f;
-        for (int64_t i0 = 0; i0 < k4; i0 += kQ * kWave) {
+        for (int64_t i0 = 0; i0 < k4; i0 += static_cast<int64_t>(kQ) * kPrepThreads) {
             if (i0 > 0) {
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) {
-                    const int64_t i = i0 + q * kWave + lane;
+                    const int64_t i = i0 + tid + static_cast<int64_t>(kPrepThreads) * q;
                     xv[q] = xr[i < k4 ? i : k4 - 1];
                 }
             }
@@ -197,28 +179,44 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
         }
         mx = wave_max(mx);
+        if (lane == 0) red[w] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         const float c = mx > 0.0f ? static_cast<float>(127.0 / static_cast<double>(mx)) : 0.0f;
 #pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] = rintf(v[j] * c);
-        if (ch == 0 && lane == 0) step[row] = static_cast<float>(static_cast<double>(mx) / 127.0);
+        for (int j = 0; j < 4; ++j) v[j] = rintf(v[j] * c);
+        if (ch == 0 && tid == 0) step[row] = static_cast<float>(static_cast<double>(mx) / 127.0);
+        *reinterpret_cast<f32x4 *>(st + ec) = v;
+    } else if (signs != nullptr) {
+        // R = (1/32) H_1024 D_s with H_1024 = H_4 (x) H_256 (the top two index
+        // bits the H_4 factor): each wave transforms its quarter, and output
+        // quarter w = sum_c (-1)^popcount(w & c) H_256 quarter c
+        float t4[4] = {v[0] * sg[0], v[1] * sg[1], v[2] * sg[2], v[3] * sg[3]};
+        fwht256_wave(t4);
+        qt[tid] = f32x4{t4[0], t4[1], t4[2], t4[3]};
+        __syncthreads();
+        const float a = rms ? 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / static_cast<float>(k) + rms_eps)
+                            : 1.0f;
+        const f32x4 q0 = qt[lane], q1 = qt[kWave + lane], q2 = qt[2 * kWave + lane], q3 = qt[3 * kWave + lane];
+        const float s1 = (w & 1) ? -1.0f : 1.0f, s2 = (w & 2) ? -1.0f : 1.0f;  // row w of H_4
+        const f32x4 t = (q0 + s1 * q1) + s2 * (q2 + s1 * q3);
+        *reinterpret_cast<f32x4 *>(st + ec) = t * ((1.0f / 32.0f) * a);
+    } else {
+        if (rms) {
+            __syncthreads();
+            v *= 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / static_cast<float>(k) + rms_eps);
+        }
+        *reinterpret_cast<f32x4 *>(st + ec) = v;
     }
-    if (signs != nullptr) {
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] *= sg[j];
-        fwht1024_wave(v);
-#pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) v[j] *= (1.0f / 32.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) st[lane + kWave * j] = v[j];
     __syncthreads();
 
     const int64_t nb = k / kBlockWeights;
     const int64_t mt = row / 32;
     const int rl = static_cast<int>(row % 32);
     if constexpr (W8) {
-        // one piece per lane: block kbl of the chunk, step stp, half h
-        const int kbl = lane >> 3, stp = (lane >> 1) & 3, h = lane & 1;
+        // one piece per thread of wave 0: block kbl of the chunk, step stp, half h
+        if (tid >= kWave) return;
+        const int kbl = tid >> 3, stp = (tid >> 1) & 3, h = tid & 1;
         const int64_t kb = ch * (kHadamard / kBlockWeights) + kbl;
         if (kb < nb) {
             const float *src = st + kBlockWeights * kbl;
@@ -238,12 +236,13 @@ __global__ void __launch_bounds__(kRotThreads) k_prep_frag(
         }
         return;
     }
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-        const int p = lane + kWave * pp;  // fragment piece: block kbl of the chunk, fragment f
+    // one fragment piece per thread of waves 0 and 1: block kbl of the chunk, fragment f
+    if (tid >= 2 * kWave) return;
+    {
+        const int p = tid;
         const int kbl = p >> 4, f = p & 15;
         const int64_t kb = ch * (kHadamard / kBlockWeights) + kbl;
-        if (kb >= nb) continue;
+        if (kb >= nb) return;
         const float *src = st + kBlockWeights * kbl;
         gm_u32x4 o;
 #pragma unroll
@@ -1423,7 +1422,7 @@ hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int6
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_prep_frag<false, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+    hipLaunchKernelGGL((k_prep_frag<false, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
                        g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
     return hipGetLastError();
 }
@@ -1433,7 +1432,7 @@ hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, 
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_prep_frag<true, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+    hipLaunchKernelGGL((k_prep_frag<true, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
                        g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
     return hipGetLastError();
 }
@@ -1442,7 +1441,7 @@ hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint8_t *xq
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_prep_frag<false, true>), dim3(static_cast<unsigned>(nchunks)), dim3(kRotThreads), 0, s, x,
+    hipLaunchKernelGGL((k_prep_frag<false, true>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
                        static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k,
                        static_cast<const float *>(nullptr), 0.0f, static_cast<const float *>(nullptr),
                        reinterpret_cast<uint16_t *>(xq), step);

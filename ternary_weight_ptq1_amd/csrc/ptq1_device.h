@@ -137,18 +137,21 @@ __device__ __forceinline__ float fwht_dpp(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, kCtrl, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
+// The six butterfly stages over the lane index (h = 1 .. 32) for each of
+// the N values a lane holds.
+template <int N>
+__device__ __forceinline__ void fwht_lane_stages(float (&v)[N])
 {
     const int lane = threadIdx.x & (kWave - 1);
     const float s1 = (lane & 1) ? -1.0f : 1.0f, s2 = (lane & 2) ? -1.0f : 1.0f;
     const float s4 = (lane & 4) ? -1.0f : 1.0f, s8 = (lane & 8) ? -1.0f : 1.0f;
     const float s16 = (lane & 16) ? -1.0f : 1.0f, s32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s1, v[j], fwht_dpp<0xB1>(v[j]));  // quad_perm [1,0,3,2]
+    for (int j = 0; j < N; ++j) v[j] = fmaf(s1, v[j], fwht_dpp<0xB1>(v[j]));  // quad_perm [1,0,3,2]
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s2, v[j], fwht_dpp<0x4E>(v[j]));  // quad_perm [2,3,0,1]
+    for (int j = 0; j < N; ++j) v[j] = fmaf(s2, v[j], fwht_dpp<0x4E>(v[j]));  // quad_perm [2,3,0,1]
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) {
+    for (int j = 0; j < N; ++j) {
         // lane + 4 (row_shl:4) or lane - 4 (row_shr:4): both are read by
         // every lane before the select (a DPP read inside a branch would see
         // the inactive lanes' old values)
@@ -157,9 +160,9 @@ __device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
         v[j] = fmaf(s4, v[j], (lane & 4) ? dn : up);
     }
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) v[j] = fmaf(s8, v[j], fwht_dpp<0x128>(v[j]));  // row_ror:8
+    for (int j = 0; j < N; ++j) v[j] = fmaf(s8, v[j], fwht_dpp<0x128>(v[j]));  // row_ror:8
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) {
+    for (int j = 0; j < N; ++j) {
         // element [0] of the swap holds the own value in lanes 0-15 of each
         // 32 and the partner's in 16-31; element [1] the other way round
         const uint32_t u = __builtin_bit_cast(uint32_t, v[j]);
@@ -168,16 +171,22 @@ __device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
         v[j] = fmaf(s16, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
     }
 #pragma unroll
-    for (int j = 0; j < kRotPerLane; ++j) {
+    for (int j = 0; j < N; ++j) {
         const uint32_t u = __builtin_bit_cast(uint32_t, v[j]);
         const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
         const uint32_t r0 = r[0], r1 = r[1];
         v[j] = fmaf(s32, __builtin_bit_cast(float, r1), __builtin_bit_cast(float, r0));
     }
+}
+
+// The stages over the value index (h = 1 .. N / 2) in registers.
+template <int N>
+__device__ __forceinline__ void fwht_value_stages(float (&v)[N])
+{
 #pragma unroll
-    for (int hj = 1; hj < kRotPerLane; hj <<= 1) {
+    for (int hj = 1; hj < N; hj <<= 1) {
 #pragma unroll
-        for (int j = 0; j < kRotPerLane; ++j) {
+        for (int j = 0; j < N; ++j) {
             if ((j & hj) == 0) {
                 const float a = v[j], b = v[j + hj];
                 v[j] = a + b;
@@ -185,6 +194,21 @@ __device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
             }
         }
     }
+}
+
+__device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
+{
+    fwht_lane_stages<kRotPerLane>(v);
+    fwht_value_stages<kRotPerLane>(v);
+}
+
+// 256 values on one wave, four per lane (element 64 j + lane in v[j], or any
+// assignment of six index bits to the lane and two to j: the transform is
+// the same butterfly on every bit).  Unnormalised: returns H_256 v.
+__device__ __forceinline__ void fwht256_wave(float (&v)[4])
+{
+    fwht_lane_stages<4>(v);
+    fwht_value_stages<4>(v);
 }
 
 }  // namespace ptq1
