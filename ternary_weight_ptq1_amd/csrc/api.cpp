@@ -700,12 +700,17 @@ static ptq1_status ffn_block_impl(const float *x, float *x_out, int64_t m, int64
         float *g = reinterpret_cast<float *>(w + L.g);
         float *u = reinterpret_cast<float *>(w + L.u);
         float *part = reinterpret_cast<float *>(w + L.part);
+        // the gate+up GEMM's fix-up is taken over by the prep of silu(g) u
+        // when its shared tiles are narrow enough (one kernel fewer)
+        const bool fold = ptq1::gemm_fold_ok(L.gu);
         e = ptq1::launch_prep_frag(x, nullptr, nullptr, m, d, signs1024, rms_eps, rms_gain, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
-                return ptq1::launch_gemm(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream);
+                return ptq1::launch_gemm(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream, !fold);
             });
-        if (e == hipSuccess) e = ptq1::launch_prep_frag(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream);
+        if (e == hipSuccess)
+            e = ptq1::launch_prep_frag(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream,
+                                       fold ? ptq1::gemm_sk_view(L.gu, part) : ptq1::SkView{});
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
                 return ptq1::launch_gemm(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);
@@ -1028,13 +1033,15 @@ ptq1_status pq2_ffn_block(const float *x, float *x_out, int64_t m, int64_t d, in
         float *g = reinterpret_cast<float *>(w + L.g);
         float *u = reinterpret_cast<float *>(w + L.u);
         float *part = reinterpret_cast<float *>(w + L.part);
+        const bool fold = ptq1::gemm_fold_ok(L.gu);  // as in ptq1_ffn_block
         e = ptq1::launch_prep_frag_pq2(x, nullptr, nullptr, m, d, signs1024, rms_eps, rms_gain, xf, stream);
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
-                return ptq1::launch_gemm_pq2(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream);
+                return ptq1::launch_gemm_pq2(L.gu, xf, m, w_gate, f, w_up, f, g, u, nullptr, part, stream, !fold);
             });
         if (e == hipSuccess)
-            e = ptq1::launch_prep_frag_pq2(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream);
+            e = ptq1::launch_prep_frag_pq2(nullptr, g, u, m, f, signs1024, 0.0f, nullptr, xf, stream,
+                                           fold ? ptq1::gemm_sk_view(L.gu, part) : ptq1::SkView{});
         if (e == hipSuccess)
             e = profiled(kProfGemm, stream, [&] {
                 return ptq1::launch_gemm_pq2(L.dn, xf, m, w_down, d, nullptr, 0, x_out, nullptr, x, part, stream);

@@ -34,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t gm_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t gm_u32x4 __attribute__((ext_vector_type(4)));
+typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t gm_u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t gm_u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -86,13 +87,71 @@ __host__ __device__ constexpr int gemm_i8_kperm(int kappa)
 // and lane l the 16 bytes at byte offset (((mt nb + kb) 4 + s) 64 + l) 16
 // hold q[32 mt + l % 32][128 kb + gemm_i8_kperm(32 s + 16 (l / 32) + i)],
 // i = 0..15; wave 0 of the row also stores its step max|x| / 127.
+// Workgroup of the stream-K range holding unit u: the largest w with
+// floor(w U / G) <= u, that is with w U < (u + 1) G.
+__device__ __forceinline__ int64_t gemm_owner(int64_t u, int64_t units, int64_t G)
+{
+    return ((u + 1) * G + units - 1) / units - 1;
+}
+
+// The gate+up outputs read by the down projection's prep when the gate+up
+// GEMM's fix-up has not run: whole tiles, and shared tiles one workgroup
+// covered, are final in y; any other shared tile is the sum of its partials
+// in workgroup order, added exactly as k_gemm_fix adds them and stored back
+// to y.  The prep takes this path only when no shared tile has more than
+// kSkPre workgroups (gemm_fold_ok), so every partial is requested up front.
+constexpr int kSkPre = 4;
+
+struct SkRead {
+    gm_f32x4 y, p[kSkPre];
+    int64_t w_lo, w_hi;
+};
+
+__device__ __forceinline__ void sk_issue(const SkView &v, const float *yp, int64_t row, int64_t vc, SkRead &s)
+{
+    s.y = *reinterpret_cast<const gm_f32x4 *>(yp);
+    const int64_t tm = row / v.prow, r = row - tm * v.prow;
+    const int64_t t = (vc / kGemmBN) * v.tiles_m + tm;
+    s.w_lo = 0;
+    s.w_hi = 0;
+    int64_t k_lo = 0;
+    if (t >= v.dp_tiles) {
+        const int64_t first_u = (t - v.dp_tiles) * v.nb;
+        s.w_lo = gemm_owner(first_u, v.sk_units, v.sk_wgs);
+        s.w_hi = gemm_owner(first_u + v.nb - 1, v.sk_units, v.sk_wgs);
+        k_lo = (s.w_lo * v.sk_units < first_u * v.sk_wgs) ? 1 : 0;
+    }
+    if (s.w_lo < s.w_hi) {
+        // w_lo's segment of this tile is its first partial unless its range
+        // began in an earlier tile; every later workgroup's is its first
+        const int64_t seg = 2 * v.prow * kGemmBN;
+        const float *p0 = v.part + r * kGemmBN + (vc % kGemmBN);
+#pragma unroll
+        for (int i = 0; i < kSkPre; ++i) {
+            const int64_t w = s.w_lo + i <= s.w_hi ? s.w_lo + i : s.w_hi;  // clamped: no branch
+            s.p[i] = *reinterpret_cast<const gm_f32x4 *>(p0 + w * seg + (i == 0 ? k_lo * v.prow * kGemmBN : 0));
+        }
+    }
+}
+
+__device__ __forceinline__ gm_f32x4 sk_finish(const SkRead &s, float *yp)
+{
+    if (s.w_lo == s.w_hi) return s.y;
+    gm_f32x4 acc = s.p[0];
+#pragma unroll
+    for (int i = 1; i < kSkPre; ++i)
+        if (s.w_lo + i <= s.w_hi) acc += s.p[i];
+    *reinterpret_cast<gm_f32x4 *>(yp) = acc;
+    return acc;
+}
+
 constexpr int kPrepThreads = 4 * kWave;
 
 template <bool Q2, bool W8>
 __global__ void __launch_bounds__(kPrepThreads) k_prep_frag(
-    const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ u,
+    const float *__restrict__ x, const float *g, const float *u,  // g, u: completed in place on the stream-K path
     int64_t k, const float *__restrict__ signs, float rms_eps, const float *__restrict__ gain,
-    uint16_t *__restrict__ xf, float *__restrict__ step)
+    uint16_t *__restrict__ xf, float *__restrict__ step, SkView sk)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ f32x4 qt[kPrepThreads];  // the four quarters' 256-point transforms
@@ -117,12 +176,22 @@ __global__ void __launch_bounds__(kPrepThreads) k_prep_frag(
     const bool rms = !W8 && x != nullptr && rms_eps > 0.0f;
     const f32x4 *xr = reinterpret_cast<const f32x4 *>(src0 + row * k);
     const int64_t k4 = k / 4;
-    f32x4 v = *reinterpret_cast<const f32x4 *>(src0 + row * k + ecl);
+    // g and u through the gate+up GEMM's stream-K partials (sk.part set,
+    // x == nullptr): the g columns are the virtual matrix's first k, u's the next k
+    const bool skv = x == nullptr && sk.part != nullptr;  // kernel-uniform
+    SkRead skg, sku;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 uw = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (x == nullptr)
-        uw = *reinterpret_cast<const f32x4 *>(u + row * k + ecl);
-    else if (gain != nullptr)  // the norm's per-channel weight (uw holds it on this path)
-        uw = *reinterpret_cast<const f32x4 *>(gain + ecl);
+    if (skv) {
+        sk_issue(sk, g + row * k + ecl, row, ecl, skg);
+        sk_issue(sk, u + row * k + ecl, row, k + ecl, sku);
+    } else {
+        v = *reinterpret_cast<const f32x4 *>(src0 + row * k + ecl);
+        if (x == nullptr)
+            uw = *reinterpret_cast<const f32x4 *>(u + row * k + ecl);
+        else if (gain != nullptr)  // the norm's per-channel weight (uw holds it on this path)
+            uw = *reinterpret_cast<const f32x4 *>(gain + ecl);
+    }
     f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f};
     if (signs != nullptr) sg = *reinterpret_cast<const f32x4 *>(signs + ec);
     f32x4 xv[kQ];
@@ -134,6 +203,10 @@ __global__ void __launch_bounds__(kPrepThreads) k_prep_frag(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (skv && e < k) {  // e < k always here (k is a multiple of 1024 on this path)
+        v = sk_finish(skg, const_cast<float *>(g) + row * k + ecl);
+        uw = sk_finish(sku, const_cast<float *>(u) + row * k + ecl);
+    }
     if (x == nullptr) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = v[j] / (1.0f + expf(-v[j])) * uw[j];
@@ -1307,13 +1380,6 @@ __global__ void __launch_bounds__(kRdThreads, 2) k_gemm_i8(GemmArgs a)
     }  // segments
 }
 
-// Workgroup of the stream-K range holding unit u: the largest w with
-// floor(w U / G) <= u, that is with w U < (u + 1) G.
-__device__ __forceinline__ int64_t gemm_owner(int64_t u, int64_t units, int64_t G)
-{
-    return ((u + 1) * G + units - 1) / units - 1;
-}
-
 // Stream-K tiles that more than one workgroup touched: the sum of their
 // partials in workgroup order (+ residual), routed to y0 / y1.  Grid:
 // (tiles - dp_tiles) x ceil(prow / kFixRows); a thread adds 4 adjacent
@@ -1417,23 +1483,50 @@ size_t gemm_part_floats(const GemmPlan &p)
     return static_cast<size_t>(2 * p.wgs) * static_cast<size_t>(p.prow) * kGemmBN;
 }
 
+bool gemm_fold_ok(const GemmPlan &p)
+{
+    const int64_t units = p.sk_tiles * p.nb, G = units < p.wgs ? units : p.wgs;
+    for (int64_t j = 0; j < p.sk_tiles; ++j) {
+        const int64_t first_u = j * p.nb;
+        const int64_t w_lo = ((first_u + 1) * G + units - 1) / units - 1;
+        const int64_t w_hi = ((first_u + p.nb) * G + units - 1) / units - 1;
+        if (w_hi - w_lo + 1 > kSkPre) return false;
+    }
+    return true;
+}
+
+SkView gemm_sk_view(const GemmPlan &p, const float *part)
+{
+    SkView v;
+    v.part = part;
+    v.prow = p.prow;
+    v.tiles_m = p.tiles_m;
+    v.nb = p.nb;
+    v.dp_tiles = p.dp_rounds * p.wgs;
+    v.sk_units = p.sk_tiles * p.nb;
+    v.sk_wgs = v.sk_units < p.wgs ? v.sk_units : p.wgs;
+    return v;
+}
+
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s)
+                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s,
+                            const SkView &sk)
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_prep_frag<false, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
-                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
+                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr), sk);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s)
+                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s,
+                                const SkView &sk)
 {
     const int64_t nchunks = m * ((k + kHadamard - 1) / kHadamard);
     if (nchunks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_prep_frag<true, false>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
-                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr));
+                       g, u, k, signs, rms_eps, gain, xf, static_cast<float *>(nullptr), sk);
     return hipGetLastError();
 }
 
@@ -1444,7 +1537,7 @@ hipError_t launch_prep_frag_w8(const float *x, int64_t m, int64_t k, uint8_t *xq
     hipLaunchKernelGGL((k_prep_frag<false, true>), dim3(static_cast<unsigned>(nchunks)), dim3(kPrepThreads), 0, s, x,
                        static_cast<const float *>(nullptr), static_cast<const float *>(nullptr), k,
                        static_cast<const float *>(nullptr), 0.0f, static_cast<const float *>(nullptr),
-                       reinterpret_cast<uint16_t *>(xq), step);
+                       reinterpret_cast<uint16_t *>(xq), step, SkView{});
     return hipGetLastError();
 }
 
@@ -1525,7 +1618,7 @@ static hipError_t gemm_fix(const GemmPlan &p, const GemmArgs &a, hipStream_t s)
 
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
-                       hipStream_t s)
+                       hipStream_t s, bool fix)
 {
     const int64_t rows = n0 + n1;
     if (rows == 0 || m == 0 || p.nb == 0) return hipSuccess;
@@ -1546,13 +1639,13 @@ hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const u
     } else {
         e = gemm_dispatch<4, 2, 1, 2, 3>(grid, s, a);
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !fix) return e;
     return gemm_fix(p, a, s);
 }
 
 hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                            const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
-                           hipStream_t s)
+                           hipStream_t s, bool fix)
 {
     if (n0 + n1 == 0 || m == 0 || p.nb == 0) return hipSuccess;
     if (p.cfg > 1) return hipErrorInvalidValue;  // register-decode plans only (gemm_plan(..., true))
@@ -1569,7 +1662,7 @@ hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, con
     } else {
         e = gemm_rd_dispatch<2, 4, 4, true>(grid, s, a);
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !fix) return e;
     return gemm_fix(p, a, s);
 }
 

@@ -121,14 +121,13 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 // ---------------------------------------------------------------------------
-// Walsh-Hadamard transform of one 1024-wide chunk held by one wavefront:
-// lane l holds elements l + 64 j in v[j], j = 0..15.  Natural-order
-// (Sylvester) H: the butterfly pairs element i with i ^ h for h = 1 .. 512.
-// Pairs with h >= 64 sit in one lane (index j ^ (h/64)); pairs with h < 64
-// are in lanes l and l ^ h, exchanged without LDS traffic: DPP quad
-// permutations (h = 1, 2), row shifts (h = 4), a half-row rotation (h = 8)
-// and the gfx950 lane swaps (h = 16, 32).  A butterfly leaves v + o at the
-// lane whose bit h is 0 and o - v at the other.  Unnormalised: returns H v.
+// Walsh-Hadamard butterflies on one wavefront, natural-order (Sylvester) H:
+// the butterfly pairs element i with i ^ h.  Six index bits sit in the lane
+// and the rest in the register index; pairs across lanes are exchanged
+// without LDS traffic: DPP quad permutations (h = 1, 2), row shifts (h = 4),
+// a half-row rotation (h = 8) and the gfx950 lane swaps (h = 16, 32).  A
+// butterfly leaves v + o at the lane whose bit h is 0 and o - v at the
+// other.  Unnormalised.
 // ---------------------------------------------------------------------------
 template <int kCtrl>
 __device__ __forceinline__ float fwht_dpp(float v)
@@ -194,12 +193,6 @@ __device__ __forceinline__ void fwht_value_stages(float (&v)[N])
             }
         }
     }
-}
-
-__device__ __forceinline__ void fwht1024_wave(float (&v)[kRotPerLane])
-{
-    fwht_lane_stages<kRotPerLane>(v);
-    fwht_value_stages<kRotPerLane>(v);
 }
 
 // 256 values on one wave, four per lane (element 64 j + lane in v[j], or any

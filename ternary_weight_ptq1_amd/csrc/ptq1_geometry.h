@@ -56,10 +56,6 @@ static_assert(kPq2TileBytes % 16 == 0, "PQ2_0 tiles keep 16-byte alignment");
 // ---- launch geometry -------------------------------------------------------
 constexpr int kWave = 64;                       // CDNA wavefront
 
-// rotation: one wave per 1024-chunk, 16 values per lane
-constexpr int kRotThreads = kWave;
-constexpr int kRotPerLane = kHadamard / kWave;  // 16
-
 // float-peel matvec: lane <-> output row, workgroup <-> (row tile, 1024-chunk)
 constexpr int kMvWaves = 4;
 constexpr int kMvThreads = kMvWaves * kWave;    // 256 rows per workgroup

@@ -100,18 +100,33 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t m, int64_t rows, int64_t k, bool rd_only = false);
 size_t gemm_frag_elems(const GemmPlan &p, int64_t k);  // bf16 A fragments
 size_t gemm_part_floats(const GemmPlan &p);            // partial tiles of the work split
+// The stream-K layout of one GEMM launch, for a consumer that adds the
+// partials of shared tiles itself (the launch made with fix = false).
+struct SkView {
+    const float *part = nullptr;  // nullptr: no partials to add (y is final)
+    int64_t prow = 0, tiles_m = 0, nb = 0, dp_tiles = 0, sk_units = 0, sk_wgs = 0;
+};
+// True when no shared tile of p spans more workgroups than the prep reads
+// up front, so launch_prep_frag can take over p's fix-up.
+bool gemm_fold_ok(const GemmPlan &p);
+SkView gemm_sk_view(const GemmPlan &p, const float *part);
 // xf = bf16 MFMA A fragments of R (a * gain * x) (rows < m only); a = RMS
 // scale of x if rms_eps > 0, gain [k] or nullptr (1).  When g/u are given
-// instead of x, the input is silu(g) * u (gain unused).
+// instead of x, the input is silu(g) * u (gain unused); with sk.part set, g
+// and u are the outputs of a gate+up GEMM launched with fix = false (k = its
+// n0 = n1): the prep adds the partials of its shared tiles (as the fix-up
+// would, in the same order) and stores the finished g and u back.
 hipError_t launch_prep_frag(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s);
+                            const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s,
+                            const SkView &sk = SkView{});
 // y [m][rows] = A . W^T (+ residual [m][n0] if given), W tiled; the rows of
 // the virtual matrix are w0's n0 rows, then w1's n1 rows (gate and up stacked),
 // the first matrix's outputs in y0 [m][n0], the second's in y1 [m][n1].
-// part: gemm_part_floats(p) floats of scratch.
+// part: gemm_part_floats(p) floats of scratch.  fix = false leaves the
+// shared tiles' partials in part for launch_prep_frag (no residual then).
 hipError_t launch_gemm(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                        const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
-                       hipStream_t s);
+                       hipStream_t s, bool fix = true);
 // W2A8: y [m][n] = row_scale[row] * sum_b scale_b * (int32 block sum of
 // trits x q), q the int8 activations of launch_prep_frag_w8 (their layout),
 // W tiled; p from gemm_plan(m, n, k, true).
@@ -120,9 +135,10 @@ hipError_t launch_gemm_i8(const GemmPlan &p, const uint8_t *xq, int64_t m, const
 // PQ2_0: A fragments in the Q2 order (launch_prep_frag_pq2), y [m][n] =
 // A . W^T over a PQ2_0 tiled matrix; p from gemm_plan(m, n, k, true).
 hipError_t launch_prep_frag_pq2(const float *x, const float *g, const float *u, int64_t m, int64_t k,
-                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s);
+                                const float *signs, float rms_eps, const float *gain, uint16_t *xf, hipStream_t s,
+                                const SkView &sk = SkView{});
 hipError_t launch_gemm_pq2(const GemmPlan &p, const uint16_t *xf, int64_t m, const uint8_t *w0, int64_t n0,
                            const uint8_t *w1, int64_t n1, float *y0, float *y1, const float *residual, float *part,
-                           hipStream_t s);
+                           hipStream_t s, bool fix = true);
 
 }  // namespace ptq1
