@@ -1492,15 +1492,17 @@ __global__ void __launch_bounds__(kEwThreads) k_gemm_fix(GemmArgs a)
         }
     }
     f32x4 v = *reinterpret_cast<const f32x4 *>(p0 + w_lo * seg + k_lo * a.prow * kGemmBN);
-    // the later workgroups' first partials, eight requests in flight at a
-    // time (clamped indices, no branch around the loads), added in order
-    for (int64_t base = w_lo + 1; base <= w_hi; base += 8) {
-        f32x4 q[8];
+    // the later workgroups' first partials, sixteen requests in flight at a
+    // time (clamped indices, no branch around the loads), added in order: a
+    // tile of the batch-8 down projection has up to 14 owners, one round trip
+    constexpr int kFixBatch = 16;
+    for (int64_t base = w_lo + 1; base <= w_hi; base += kFixBatch) {
+        f32x4 q[kFixBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kFixBatch; ++j)
             q[j] = *reinterpret_cast<const f32x4 *>(p0 + (base + j <= w_hi ? base + j : w_hi) * seg);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kFixBatch; ++j)
             if (base + j <= w_hi) v += q[j];
     }
 #pragma unroll
