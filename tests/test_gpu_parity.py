@@ -535,7 +535,7 @@ def _ffn_host(seed, d, f, layer=0):
 
 
 @pytest.mark.parametrize("m,d,f,eps", [(1, 1024, 2048, 1e-6), (1, 2048, 1024, 0.0), (2, 1024, 2048, 1e-6),
-                                       (3, 1024, 3072, 0.0), (8, 1024, 2048, 1e-6)])
+                                       (3, 1024, 3072, 0.0), (8, 1024, 2048, 1e-6), (13, 1024, 2048, 1e-6)])
 def test_ffn_block_small(m, d, f, eps):
     seed = 4
     wg, wu, wd = _ffn_host(seed, d, f)
@@ -770,9 +770,9 @@ def test_pq2_matvec_gate_up_shape():
     assert rel_l2(got[rows], ref) <= TOL_FP32
 
 
-@pytest.mark.parametrize("m,n,k,rot", [(1, 300, 384, False), (8, 1024, 1024, True), (17, 257, 3072, True),
-                                       (40, 200, 640, False), (64, 1024, 2048, True), (100, 513, 1024, True),
-                                       (256, 1000, 2048, True)])
+@pytest.mark.parametrize("m,n,k,rot", [(1, 300, 384, False), (8, 1024, 1024, True), (12, 520, 1024, True),
+                                       (17, 257, 3072, True), (40, 200, 640, False), (64, 1024, 2048, True),
+                                       (100, 513, 1024, True), (256, 1000, 2048, True)])
 def test_pq2_gemm_small(m, n, k, rot):
     b = pq2_host(7, n, k)
     x = synth.activations(7, m, k)
@@ -807,7 +807,7 @@ def _pq2_ffn_host(seed, d, f):
 
 @pytest.mark.parametrize("m,d,f,eps,gain", [(1, 1024, 2048, 1e-6, False), (1, 2048, 1024, 0.0, True),
                                             (2, 1024, 2048, 1e-6, True), (8, 1024, 3072, 0.0, False),
-                                            (100, 1024, 2048, 1e-6, True)])
+                                            (16, 1024, 2048, 1e-6, True), (100, 1024, 2048, 1e-6, True)])
 def test_pq2_ffn_block(m, d, f, eps, gain):
     seed = 10
     wg, wu, wd = _pq2_ffn_host(seed, d, f)
